@@ -1,0 +1,202 @@
+/*
+ * csa2.h -- C ABI of libcsa2, the MI355X (gfx950) hot path of a CSA2 layer
+ * (compressed sparse attention 2) of DeepSeek-V4.1-Flash at decode and in
+ * chunked prefill, on one GPU.
+ *
+ * Sources, by page title:
+ *   [N] "DeepSeek V4.1: model architecture and system design, close reading"
+ *       section 1 (indexer 32 heads x 128, top-k 512, query 64 heads x 512,
+ *       2048 blocks x 8 positions, window 128), section 2.2 (CSA2 Full /
+ *       Reindex / Reuse modes, hierarchical sparse indexer), section 2.3 (FP4
+ *       main KV: E2M1 with one E4M3 scale per 16 channels, quantised after
+ *       RoPE; window KV kept in FP8).
+ *   [A] "DeepSeek-V4.1-Flash: pushing KV cache compression to the limit"
+ *       (translated abstract) sections 3.3 (CSA2), 3.4 (hierarchical sparse
+ *       indexer), 3.6 (FP4 main KV cache).
+ *   [S] "DeepSeek-V4 model structure (7): structure decides the system"
+ *       (predecessor): attention over the top-k compressed entries plus 128
+ *       window entries; K = V single-head MQA on a 512-dim latent.
+ *
+ * Layer call sequences (one query row per (sequence, query)):
+ *   Full     csa2_index_full -> csa2_topk(block maxima, nb) = pool
+ *            -> csa2_index_pool(own query, pool) -> csa2_topk(k) = top-k
+ *            -> csa2_sparse_attn.
+ *            When the pool has fewer than k blocks (or there is no pool, as
+ *            in the encoder), select the top-k blocks instead of the pool for
+ *            the pool step: the top-k entries always lie in the top-k blocks.
+ *   Reindex  csa2_index_pool(own query, Full layer's pool) -> csa2_topk(k)
+ *            -> csa2_sparse_attn.
+ *   Reuse    csa2_sparse_attn with the latest top-k.
+ *
+ * Conventions for every call:
+ *   - All tensors are row-major and contiguous.  Every data pointer is a
+ *     DEVICE pointer, allocated and owned by the caller; the library never
+ *     allocates, frees or synchronises, and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is enqueued and csa2_last_error() (thread-local)
+ *     holds a message.  Device faults surface at the caller's next
+ *     synchronisation.  With CSA2_DEBUG_SYNC=1 in the environment every call
+ *     synchronises its stream and reports launch/runtime errors.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Supported model dims (CSA2_ERR_UNSUPPORTED otherwise): indexer 32
+ *     heads x 128, attention 64 heads x 512, scale group 16, block 8.
+ *   - Index inputs that are out of range are skipped (treated as -1), never
+ *     dereferenced.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape   */
+    CSA2_ERR_UNSUPPORTED = 2, /* dims outside the supported set                    */
+    CSA2_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace() */
+    CSA2_ERR_LAUNCH = 4       /* the HIP runtime refused a launch                  */
+} csa2_status;
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* csa2_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t csa2_version(void);
+
+/*
+ * MXFP4 encoder of new cache rows ([N] 2.3, [A] 3.6): rotary (optional) then
+ * E2M1 codes with one E4M3FN scale per 16 channels.
+ *   x         fp32 [rows, channels], channels % 16 == 0 (512 main KV, 128
+ *             indexer key); finite values.
+ *   rope_cos, rope_sin  fp32 [rows, rope_dim/2] or NULL when rope_dim == 0.
+ *             Row r rotates the pairs (x[rope_offset+2i], x[rope_offset+2i+1])
+ *             by (cos[r,i], sin[r,i]): a' = a*c - b*s, b' = a*s + b*c, every
+ *             product and sum rounded to fp32 (no fused multiply-add).
+ *             rope_offset and rope_dim must be even, rope_offset + rope_dim
+ *             <= channels.  Main KV: offset 448, dim 64.
+ *   codes     u8 output; row r goes to codes + r*dst_stride*channels/2
+ *             (channel 2j in the low nibble of byte j, 2j+1 in the high one).
+ *   scales    u8 output; row r goes to scales + r*dst_stride*channels/16
+ *             (byte g scales channels [16g, 16g+16)).
+ *   dst_stride  >= 1: distance in rows between consecutive output rows (1 =
+ *             contiguous; n_cap = one new row per sequence of a [B, n_cap]
+ *             cache).
+ * Encoding per group: scale = E4M3 round-to-nearest-even of max|x|/6,
+ * saturating at 448; code = nearest E2M1 value of |x|/scale, ties to the even
+ * code, saturating at 6; scale 0 gives code 0; sign only on non-zero codes.
+ * Bit-exact, deterministic.
+ */
+csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
+                             const float* rope_cos, const float* rope_sin,
+                             int32_t rope_offset, int32_t rope_dim,
+                             uint8_t* codes, uint8_t* scales, int64_t dst_stride,
+                             void* stream);
+
+/*
+ * FP8 encoder of sliding-window KV rows ([N] 2.3: the window KV stays in FP8).
+ *   x    fp32 [n] finite values;  out  u8 [n] E4M3FN, round to nearest even,
+ *        saturating at +-448, sign kept (a negative value rounding to zero
+ *        gives -0).  Elements of row r of a [rows, 512] block go to
+ *        out + r*dst_stride*512 when row_len = 512 (row_len divides n).
+ */
+csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_t* out,
+                              int64_t dst_stride, void* stream);
+
+/*
+ * Full-layer indexer scan ([N] 2.2, [A] 3.4: the first Full layer scores the
+ * whole causally visible range; a block's score is the largest index score
+ * of its positions).
+ *   q          bf16 [B, nq, 32, 128] indexer queries.
+ *   w          fp32 [B, nq, 32] per-head weights.
+ *   k_codes    u8 [B, n_cap, 64], k_scales u8 [B, n_cap, 8]: MXFP4 indexer
+ *              keys (shared by every query of a sequence).
+ *   n_visible  int32 [B, nq]: query (b, i) sees entries [0, min(n_visible, n_cap)).
+ *   block      positions per block (8).
+ *   block_max  fp32 [B, nq, ceil(n_cap/block)]: block beta of query (b,i)
+ *              receives max over visible j in [beta*block, beta*block+block)
+ *              of s_j, for beta < ceil(n_visible/block); later slots are not
+ *              written.
+ *   scores     fp32 [B, nq, n_cap] or NULL: every s_j, j < n_visible (tests).
+ * Score: s_j = sum_h w_h * max(0, q_h . k_j), dot products of the bf16 query
+ * with the dequantised key accumulated in fp32 (reading: the pages give the
+ * 32 x 128 shape, not the formula; parity unpinned beyond this reading).
+ */
+csa2_status csa2_index_full(const uint16_t* q, const float* w,
+                            const uint8_t* k_codes, const uint8_t* k_scales, int64_t n_cap,
+                            const int32_t* n_visible, int32_t B, int32_t nq, int32_t block,
+                            float* block_max, float* scores, void* stream);
+
+/*
+ * Indexer scoring restricted to a pool of blocks ([N] 2.2, [A] 3.4: Reindex
+ * layers score only the Full layer's 2048 x 8 pool with their own query).
+ *   q, w, k_codes, k_scales, n_cap, n_visible, B, nq: as csa2_index_full.
+ *   blocks     int32 [B, nq, n_blocks]: block ids (ascending, -1 padding).
+ *   pool_score fp32 [B, nq, n_blocks*block]: slot t*block + r holds the score
+ *              of position blocks[t]*block + r, or -inf if that position is
+ *              not visible or the block is -1.
+ *   pool_idx   int32 [B, nq, n_blocks*block]: the position, or -1.
+ * Scores are bit-identical to csa2_index_full's for the same entry and query.
+ */
+csa2_status csa2_index_pool(const uint16_t* q, const float* w,
+                            const uint8_t* k_codes, const uint8_t* k_scales, int64_t n_cap,
+                            const int32_t* blocks, int32_t n_blocks, int32_t block,
+                            const int32_t* n_visible, int32_t B, int32_t nq,
+                            float* pool_score, int32_t* pool_idx, void* stream);
+
+/*
+ * Top-k select ([N] 1: top-k 512; [N] 2.2 / [A] 3.4: top-2048 blocks).
+ *   score    fp32 [rows, L].
+ *   idx      int32 [rows, L] or NULL (= 0..L-1).  Entries with idx < 0, NaN
+ *            score, or position >= n_valid[row] are skipped.  Among valid
+ *            entries idx must ascend with position (true of csa2_index_pool's
+ *            output and of identity indices).
+ *   n_valid  int32 [rows] or NULL (= L): valid prefix of each row.
+ *   k        1 <= k <= 8192.
+ *   out      int32 [rows, k]: the k best under (score descending, index
+ *            ascending), -0 equal to +0, written as ascending indices, -1
+ *            padding when fewer than k are valid.  Bit-exact, deterministic.
+ *   ws       device workspace of csa2_topk_workspace(L, rows, k) bytes (0 for
+ *            L <= 16384, where ws may be NULL).
+ */
+csa2_status csa2_topk(const float* score, const int32_t* idx, int64_t L, int32_t rows,
+                      const int32_t* n_valid, int32_t k, int32_t* out,
+                      void* ws, size_t ws_bytes, void* stream);
+size_t csa2_topk_workspace(int64_t L, int32_t rows, int32_t k);
+
+/*
+ * Sparse MLA attention ([N] 1: 64 heads x 512; [S]: K = V single-head MQA on
+ * the 512-dim latent, top-k compressed entries plus 128 window entries).
+ *   q          bf16 [B, nq, 64, 512].
+ *   kv_codes   u8 [B, n_cap, 256], kv_scales u8 [B, n_cap, 32]: MXFP4 main KV.
+ *   topk       int32 [B, nq, k]: entry ids; ids outside [0, n_cap) skipped.
+ *   swa        u8 [B, swa_cap, 512] E4M3FN window rows; query (b, i) uses rows
+ *              [max(0, swa_end[b,i] - n_win), min(swa_end[b,i], swa_cap)).
+ *   softmax_scale  multiplies q . v before the softmax.
+ *   out        fp32 [B, nq, 64, 512]: o_h = sum_j p_j v_j, p = softmax over the
+ *              union of selected entries and window rows (one joint softmax);
+ *              0 for an empty key set.
+ *   lse        fp32 [B, nq, 64] or NULL: ln sum_j exp(l_j) (-inf if empty).
+ *   ws         device workspace of csa2_sparse_attn_workspace(B, nq, k, n_win)
+ *              bytes, or NULL (then the key set is not split across
+ *              workgroups: correct, slower for small batches).
+ * Dequantisation is exact in fp16; products accumulate in fp32.
+ */
+csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq,
+                             const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t n_cap,
+                             const int32_t* topk, int32_t k,
+                             const uint8_t* swa, int32_t swa_cap, const int32_t* swa_end,
+                             int32_t n_win, float softmax_scale, float* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+size_t csa2_sparse_attn_workspace(int32_t B, int32_t nq, int32_t k, int32_t n_win);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,179 @@
+"""ctypes binding of libcsa2.so: argument marshalling only.
+
+Each function takes torch tensors that live on the GPU, checks dtype, device,
+shape and contiguity, and forwards raw pointers to the C entry point of the
+same name in include/csa2.h on the current torch stream.  All computation
+happens in the library's HIP kernels; a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa2.so")
+
+CSA2_OK = 0
+STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_UNSUPPORTED",
+          3: "CSA2_ERR_WORKSPACE", 4: "CSA2_ERR_LAUNCH"}
+
+EXPORTS = ("csa2_last_error", "csa2_version", "csa2_quantize_kv", "csa2_quantize_swa",
+           "csa2_index_full", "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
+           "csa2_sparse_attn", "csa2_sparse_attn_workspace")
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libcsa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m kv_cache_decode_mxfp4_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                             ctypes.c_size_t)
+    st = ctypes.c_int
+    L.csa2_last_error.restype = ctypes.c_char_p
+    L.csa2_last_error.argtypes = []
+    L.csa2_version.restype = i32
+    L.csa2_version.argtypes = []
+    L.csa2_quantize_kv.restype = st
+    L.csa2_quantize_kv.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, vp, i64, vp]
+    L.csa2_quantize_swa.restype = st
+    L.csa2_quantize_swa.argtypes = [vp, i64, i32, vp, i64, vp]
+    L.csa2_index_full.restype = st
+    L.csa2_index_full.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, i32, vp, vp, vp]
+    L.csa2_index_pool.restype = st
+    L.csa2_index_pool.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i32, i32, vp, vp, vp]
+    L.csa2_topk.restype = st
+    L.csa2_topk.argtypes = [vp, vp, i64, i32, vp, i32, vp, vp, sz, vp]
+    L.csa2_topk_workspace.restype = sz
+    L.csa2_topk_workspace.argtypes = [i64, i32, i32]
+    L.csa2_sparse_attn.restype = st
+    L.csa2_sparse_attn.argtypes = [vp, i32, i32, vp, vp, i64, vp, i32, vp, i32, vp, i32, f32,
+                                   vp, vp, vp, sz, vp]
+    L.csa2_sparse_attn_workspace.restype = sz
+    L.csa2_sparse_attn_workspace.argtypes = [i32, i32, i32, i32]
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != CSA2_OK:
+        raise Csa2Error(fn, status, load().csa2_last_error().decode())
+
+
+def _p(t):
+    """Device pointer of a CUDA/HIP tensor (None for None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _dt(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _bf16_bits(t):
+    """bf16 tensors are passed as their bit patterns (uint16 or int16 views accepted)."""
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.uint16, torch.int16):
+        return t
+    raise TypeError(f"expected bfloat16 (or its uint16 bits), got {t.dtype}")
+
+
+def quantize_kv(x, codes, scales, rope_cos=None, rope_sin=None, rope_offset=0, rope_dim=0,
+                dst_stride=1, stream=None):
+    _dt(x, torch.float32, "x")
+    _dt(codes, torch.uint8, "codes")
+    _dt(scales, torch.uint8, "scales")
+    rows, C = x.shape
+    _check("csa2_quantize_kv", load().csa2_quantize_kv(
+        _p(x), rows, C, _p(rope_cos), _p(rope_sin), rope_offset, rope_dim, _p(codes),
+        _p(scales), dst_stride, _stream(stream)))
+
+
+def quantize_swa(x, out, row_len=512, dst_stride=1, stream=None):
+    _dt(x, torch.float32, "x")
+    _dt(out, torch.uint8, "out")
+    _check("csa2_quantize_swa", load().csa2_quantize_swa(
+        _p(x), x.numel(), row_len, _p(out), dst_stride, _stream(stream)))
+
+
+def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block=8, stream=None):
+    q = _bf16_bits(q)
+    _dt(w, torch.float32, "w")
+    _dt(n_visible, torch.int32, "n_visible")
+    B, nq = q.shape[0], q.shape[1]
+    n_cap = k_codes.shape[1]
+    _check("csa2_index_full", load().csa2_index_full(
+        _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block,
+        _p(block_max), _p(scores), _stream(stream)))
+
+
+def index_pool(q, w, k_codes, k_scales, blocks, n_visible, pool_score, pool_idx, block=8,
+               stream=None):
+    q = _bf16_bits(q)
+    _dt(blocks, torch.int32, "blocks")
+    B, nq = q.shape[0], q.shape[1]
+    n_cap = k_codes.shape[1]
+    _check("csa2_index_pool", load().csa2_index_pool(
+        _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(blocks), blocks.shape[-1], block,
+        _p(n_visible), B, nq, _p(pool_score), _p(pool_idx), _stream(stream)))
+
+
+def topk_workspace(L, rows, k) -> int:
+    return int(load().csa2_topk_workspace(L, rows, k))
+
+
+def topk(score, k, out, idx=None, n_valid=None, ws=None, stream=None):
+    _dt(score, torch.float32, "score")
+    _dt(out, torch.int32, "out")
+    L = score.shape[-1]
+    rows = score.numel() // L if L else 0
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("csa2_topk", load().csa2_topk(
+        _p(score), _p(idx), L, rows, _p(n_valid), k, _p(out), _p(ws), ws_bytes,
+        _stream(stream)))
+
+
+def sparse_attn_workspace(B, nq, k, n_win) -> int:
+    return int(load().csa2_sparse_attn_workspace(B, nq, k, n_win))
+
+
+def sparse_attn(q, kv_codes, kv_scales, topk_idx, swa, swa_end, out, lse=None, n_win=128,
+                softmax_scale=1.0, ws=None, stream=None):
+    q = _bf16_bits(q)
+    _dt(topk_idx, torch.int32, "topk")
+    _dt(out, torch.float32, "out")
+    B, nq = q.shape[0], q.shape[1]
+    n_cap = kv_codes.shape[1]
+    k = topk_idx.shape[-1]
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("csa2_sparse_attn", load().csa2_sparse_attn(
+        _p(q), B, nq, _p(kv_codes), _p(kv_scales), n_cap, _p(topk_idx), k, _p(swa),
+        swa.shape[1], _p(swa_end), n_win, float(softmax_scale), _p(out), _p(lse), _p(ws),
+        ws_bytes, _stream(stream)))

@@ -1,0 +1,240 @@
+// C ABI of libcsa2 (declared in include/csa2.h): host-side validation, then
+// one launcher per call.  Nothing is enqueued when validation fails.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/csa2.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa2_status fail(csa2_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool debug_sync()
+{
+    static const bool on = [] {
+        const char* v = getenv("CSA2_DEBUG_SYNC");
+        return v != nullptr && v[0] == '1';
+    }();
+    return on;
+}
+
+csa2_status finish(hipError_t e, hipStream_t stream, const char* what)
+{
+    if (e == hipSuccess && debug_sync())
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail(CSA2_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    g_err[0] = '\0';
+    return CSA2_OK;
+}
+
+#define REQUIRE(cond, st, ...)                 \
+    do {                                       \
+        if (!(cond))                           \
+            return fail((st), __VA_ARGS__);    \
+    } while (0)
+
+inline bool aligned(const void* p, size_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_last_error(void)
+{
+    return g_err;
+}
+
+int32_t csa2_version(void)
+{
+    return 100;
+}
+
+csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
+                             const float* rope_cos, const float* rope_sin, int32_t rope_offset,
+                             int32_t rope_dim, uint8_t* codes, uint8_t* scales,
+                             int64_t dst_stride, void* stream)
+{
+    REQUIRE(rows >= 0, CSA2_ERR_INVALID_ARG, "quantize_kv: rows < 0");
+    REQUIRE(channels > 0 && channels % 16 == 0 && channels <= 4096, CSA2_ERR_UNSUPPORTED,
+            "quantize_kv: channels must be a positive multiple of 16 up to 4096 (got %d)",
+            channels);
+    REQUIRE(dst_stride >= 1, CSA2_ERR_INVALID_ARG, "quantize_kv: dst_stride < 1");
+    REQUIRE(rope_dim >= 0 && rope_dim % 2 == 0 && rope_offset >= 0 && rope_offset % 2 == 0 &&
+                rope_offset + rope_dim <= channels,
+            CSA2_ERR_INVALID_ARG, "quantize_kv: rotary range [%d, %d) not even / inside %d",
+            rope_offset, rope_offset + rope_dim, channels);
+    if (rows == 0)
+        return CSA2_OK;
+    REQUIRE(x && codes && scales, CSA2_ERR_INVALID_ARG, "quantize_kv: null pointer");
+    REQUIRE(rope_dim == 0 || (rope_cos && rope_sin), CSA2_ERR_INVALID_ARG,
+            "quantize_kv: rope_dim > 0 needs cos/sin tables");
+    REQUIRE(aligned(x, 16) && aligned(codes, 8), CSA2_ERR_INVALID_ARG,
+            "quantize_kv: x must be 16-byte and codes 8-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_quantize_kv(x, rows, channels, rope_cos, rope_sin, rope_offset,
+                                           rope_dim, codes, scales, dst_stride, s),
+                  s, "quantize_kv");
+}
+
+csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_t* out,
+                              int64_t dst_stride, void* stream)
+{
+    REQUIRE(n >= 0, CSA2_ERR_INVALID_ARG, "quantize_swa: n < 0");
+    REQUIRE(row_len > 0 && row_len % 4 == 0 && n % row_len == 0, CSA2_ERR_INVALID_ARG,
+            "quantize_swa: row_len must be a positive multiple of 4 dividing n");
+    REQUIRE(dst_stride >= 1, CSA2_ERR_INVALID_ARG, "quantize_swa: dst_stride < 1");
+    if (n == 0)
+        return CSA2_OK;
+    REQUIRE(x && out, CSA2_ERR_INVALID_ARG, "quantize_swa: null pointer");
+    REQUIRE(aligned(x, 16) && aligned(out, 4), CSA2_ERR_INVALID_ARG,
+            "quantize_swa: x must be 16-byte and out 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_quantize_swa(x, n, row_len, out, dst_stride, s), s,
+                  "quantize_swa");
+}
+
+static csa2_status check_indexer(const char* fn, const uint16_t* q, const float* w,
+                                 const uint8_t* k_codes, const uint8_t* k_scales, int64_t n_cap,
+                                 const int32_t* n_visible, int32_t B, int32_t nq, int32_t block)
+{
+    REQUIRE(B >= 0 && nq >= 0 && n_cap >= 0, CSA2_ERR_INVALID_ARG, "%s: negative size", fn);
+    REQUIRE(block == csa2::kBlock, CSA2_ERR_UNSUPPORTED, "%s: block must be %d (got %d)", fn,
+            csa2::kBlock, block);
+    REQUIRE((int64_t)B * nq <= (1ll << 24), CSA2_ERR_INVALID_ARG, "%s: too many query rows", fn);
+    REQUIRE(n_cap <= (1ll << 30), CSA2_ERR_INVALID_ARG, "%s: n_cap above 2^30", fn);
+    if ((int64_t)B * nq == 0)
+        return CSA2_OK;
+    REQUIRE(q && w && n_visible, CSA2_ERR_INVALID_ARG, "%s: null pointer", fn);
+    REQUIRE(n_cap == 0 || (k_codes && k_scales), CSA2_ERR_INVALID_ARG, "%s: null key cache", fn);
+    REQUIRE(aligned(q, 16) && aligned(k_codes, 16) && aligned(k_scales, 4), CSA2_ERR_INVALID_ARG,
+            "%s: q and k_codes must be 16-byte, k_scales 4-byte aligned", fn);
+    return CSA2_OK;
+}
+
+csa2_status csa2_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                            const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
+                            int32_t B, int32_t nq, int32_t block, float* block_max,
+                            float* scores, void* stream)
+{
+    csa2_status st = check_indexer("index_full", q, w, k_codes, k_scales, n_cap, n_visible, B,
+                                   nq, block);
+    if (st != CSA2_OK)
+        return st;
+    if ((int64_t)B * nq == 0 || n_cap == 0)
+        return CSA2_OK;
+    REQUIRE(block_max != nullptr, CSA2_ERR_INVALID_ARG, "index_full: null block_max");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq,
+                                          block_max, scores, s),
+                  s, "index_full");
+}
+
+csa2_status csa2_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                            const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
+                            int32_t n_blocks, int32_t block, const int32_t* n_visible, int32_t B,
+                            int32_t nq, float* pool_score, int32_t* pool_idx, void* stream)
+{
+    csa2_status st = check_indexer("index_pool", q, w, k_codes, k_scales, n_cap, n_visible, B,
+                                   nq, block);
+    if (st != CSA2_OK)
+        return st;
+    REQUIRE(n_blocks >= 0 && n_blocks <= (1 << 20), CSA2_ERR_INVALID_ARG,
+            "index_pool: n_blocks out of range");
+    if ((int64_t)B * nq == 0 || n_blocks == 0)
+        return CSA2_OK;
+    REQUIRE(blocks && pool_score && pool_idx, CSA2_ERR_INVALID_ARG, "index_pool: null pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_index_pool(q, w, k_codes, k_scales, n_cap, blocks, n_blocks,
+                                          n_visible, B, nq, pool_score, pool_idx, s),
+                  s, "index_pool");
+}
+
+size_t csa2_topk_workspace(int64_t L, int32_t rows, int32_t k)
+{
+    if (L < 0 || rows < 0 || k < 1 || k > csa2::kTopkMaxK)
+        return 0;
+    return csa2::topk_workspace(L, rows, k);
+}
+
+csa2_status csa2_topk(const float* score, const int32_t* idx, int64_t L, int32_t rows,
+                      const int32_t* n_valid, int32_t k, int32_t* out, void* ws,
+                      size_t ws_bytes, void* stream)
+{
+    REQUIRE(L >= 0 && rows >= 0, CSA2_ERR_INVALID_ARG, "topk: negative size");
+    REQUIRE(k >= 1 && k <= csa2::kTopkMaxK, CSA2_ERR_UNSUPPORTED, "topk: k must be in [1, %d]",
+            csa2::kTopkMaxK);
+    REQUIRE(L <= (1ll << 31) - 1, CSA2_ERR_INVALID_ARG, "topk: L above 2^31-1");
+    REQUIRE((int64_t)rows * ((L + csa2::kTopkSegment - 1) / csa2::kTopkSegment) <= (1ll << 31) - 1,
+            CSA2_ERR_INVALID_ARG, "topk: too many segments");
+    if (rows == 0)
+        return CSA2_OK;
+    REQUIRE(out != nullptr, CSA2_ERR_INVALID_ARG, "topk: null out");
+    REQUIRE(L == 0 || score != nullptr, CSA2_ERR_INVALID_ARG, "topk: null score");
+    const size_t need = csa2::topk_workspace(L, rows, k);
+    REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
+            "topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    REQUIRE(aligned(ws, 8), CSA2_ERR_INVALID_ARG, "topk: workspace must be 8-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_topk(score, idx, L, rows, n_valid, k, out, ws, s), s, "topk");
+}
+
+size_t csa2_sparse_attn_workspace(int32_t B, int32_t nq, int32_t k, int32_t n_win)
+{
+    if (B < 0 || nq < 0 || k < 0 || n_win < 0)
+        return 0;
+    return csa2::attn_workspace(B * nq, k, n_win);
+}
+
+csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq, const uint8_t* kv_codes,
+                             const uint8_t* kv_scales, int64_t n_cap, const int32_t* topk,
+                             int32_t k, const uint8_t* swa, int32_t swa_cap,
+                             const int32_t* swa_end, int32_t n_win, float softmax_scale,
+                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream)
+{
+    REQUIRE(B >= 0 && nq >= 0 && n_cap >= 0 && k >= 0 && swa_cap >= 0 && n_win >= 0,
+            CSA2_ERR_INVALID_ARG, "sparse_attn: negative size");
+    REQUIRE((int64_t)B * nq <= (1ll << 24), CSA2_ERR_INVALID_ARG,
+            "sparse_attn: too many query rows");
+    REQUIRE(k <= 65536 && n_win <= 65536, CSA2_ERR_UNSUPPORTED, "sparse_attn: k or n_win too large");
+    const int32_t queries = B * nq;
+    if (queries == 0)
+        return CSA2_OK;
+    REQUIRE(q && out && swa_end, CSA2_ERR_INVALID_ARG, "sparse_attn: null pointer");
+    REQUIRE(k == 0 || (topk && kv_codes && kv_scales), CSA2_ERR_INVALID_ARG,
+            "sparse_attn: null top-k or KV cache");
+    REQUIRE(swa_cap == 0 || swa != nullptr, CSA2_ERR_INVALID_ARG, "sparse_attn: null window");
+    REQUIRE(aligned(q, 16) && aligned(kv_codes, 16) && aligned(kv_scales, 4) && aligned(swa, 16),
+            CSA2_ERR_INVALID_ARG, "sparse_attn: misaligned q / kv / window pointer");
+    int32_t splits = csa2::attn_splits(queries, k, n_win);
+    const size_t need = csa2::attn_workspace(queries, k, n_win);
+    if (ws == nullptr) {
+        splits = 1;
+    } else {
+        REQUIRE(ws_bytes >= need, CSA2_ERR_WORKSPACE,
+                "sparse_attn: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+        REQUIRE(aligned(ws, 16), CSA2_ERR_INVALID_ARG, "sparse_attn: misaligned workspace");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_sparse_attn(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k,
+                                           swa, swa_cap, swa_end, n_win, softmax_scale, out, lse,
+                                           ws, splits, s),
+                  s, "sparse_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// Indexer kernels of the hierarchical sparse indexer ([N] 2.2 and [A] 3.4 of
+// the DeepSeek-V4.1 pages: the first Full layer scores the whole visible range
+// and ranks blocks of 8 positions by their largest score; Reindex layers score
+// only the pool of selected blocks).
+//
+// Score of entry j for one query:  s_j = sum_h w_h * max(0, q_h . k_j),
+// h < 32 heads, dot over 128 channels (reading: the pages fix the 32 x 128
+// shape, not the formula).
+//
+// Both kernels compute scores with the same device function, so a position's
+// score is bit-identical whether it comes from the full scan or a pool scan.
+//
+// MFMA mapping (v_mfma_f32_32x32x16_f16, one wave):
+//   A = q   [32 heads x 16 channels per k-step], B = k^T [16 channels x 32
+//   entries], D [32 heads x 32 entries] in fp32.  Lane l owns entry l%32 and
+//   the channel half h = l/32: k-step t covers channels 64h + 8t .. +8 on both
+//   operands, so a lane reads 32 contiguous code bytes and one dword of
+//   scales per entry.  Keys are dequantised in registers (exact in fp16, the
+//   E4M3-per-16 scale is not gfx950's E8M0-per-32 MX scale, so the scaled MFMA
+//   cannot take it).  Each query head is pre-multiplied by a power of two that
+//   brings its largest |q| to [2^14, 2^15), which keeps the bf16 -> fp16 cast
+//   exact for every value within 2^28 of that maximum; the head weight absorbs
+//   the inverse power, so the score is unchanged.
+#include "device_common.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kTileEntries = 32;    // entries per MFMA tile
+constexpr int kTilesPerWave = 32;   // tiles each wave scans per workgroup
+constexpr int kChunk = kWaves * kTilesPerWave * kTileEntries;  // entries per workgroup
+
+struct QueryOperand {
+    half8 a[8];      // A operand of k-steps 0..7
+    float wr[16];    // weight (times 2^-shift) of the head of accumulator row r
+};
+
+// Load one query's indexer q (bf16 [32, 128]) and w (fp32 [32]) into the
+// operand layout of the calling wave.
+__device__ __forceinline__ void load_query(const uint16_t* __restrict__ q,
+                                           const float* __restrict__ w, int lane,
+                                           QueryOperand& Q)
+{
+    const int head = lane & 31;
+    const int half = lane >> 5;
+    const uint4* src = reinterpret_cast<const uint4*>(q + head * kIdxDim + 64 * half);
+    float m = 0.0f;
+    uint4 raw[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        raw[t] = src[t];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t d[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m = fmaxf(m, fabsf(__uint_as_float(d[i] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(d[i] & 0xFFFF0000u)));
+        }
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    // power of two bringing max|q_h| into [2^14, 2^15); 0 for an all-zero head
+    int shift = 0;
+    if (m > 0.0f) {
+        const int e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127;
+        shift = 14 - e;
+        shift = shift < -100 ? -100 : (shift > 100 ? 100 : shift);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t d[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Q.a[t][2 * i] = (_Float16)ldexpf(__uint_as_float(d[i] << 16), shift);
+            Q.a[t][2 * i + 1] = (_Float16)ldexpf(__uint_as_float(d[i] & 0xFFFF0000u), shift);
+        }
+    }
+    // accumulator row r of lane l is head 8*(r/4) + 4*(l/32) + r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int hr = 8 * (r / 4) + 4 * half + (r % 4);
+        const int sh = __shfl(shift, hr, kWave);
+        Q.wr[r] = ldexpf(w[hr], -sh);
+    }
+}
+
+struct KeyTile {
+    u32x4 c0, c1;   // code bytes [32h, 32h+32) of the lane's entry
+    uint32_t sc;    // scale bytes [4h, 4h+4)
+};
+
+__device__ __forceinline__ void load_key(const uint8_t* __restrict__ codes,
+                                         const uint8_t* __restrict__ scales, int64_t entry,
+                                         int half, KeyTile& K)
+{
+    const u32x4* c = reinterpret_cast<const u32x4*>(codes + entry * (kIdxDim / 2) + 32 * half);
+    K.c0 = __builtin_nontemporal_load(c);
+    K.c1 = __builtin_nontemporal_load(c + 1);
+    K.sc = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t*>(scales + entry * (kIdxDim / 16) + 4 * half));
+}
+
+// Score of the lane's entry (both lanes of an entry return the same value).
+__device__ __forceinline__ float score_entry(const QueryOperand& Q, const KeyTile& K)
+{
+    const uint32_t words[8] = {K.c0[0], K.c0[1], K.c0[2], K.c0[3], K.c1[0], K.c1[1], K.c1[2], K.c1[3]};
+    f32x16 acc = {};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const _Float16 s = e4m3_byte_to_f16(K.sc, t / 2);
+        const half8 b = dequant8_fp4(words[t], s);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q.a[t], b, acc, 0, 0, 0);
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        part = __builtin_fmaf(Q.wr[r], fmaxf(acc[r], 0.0f), part);
+    return part + __shfl_xor(part, 32, kWave);
+}
+
+// Full-range scan: one workgroup scans kChunk entries of one query row and
+// writes the maxima of the blocks of 8 it covers (and optionally every score).
+__global__ void __launch_bounds__(kWaves * kWave)
+index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                  const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                  int64_t n_cap, const int32_t* __restrict__ n_visible, int32_t nq,
+                  int32_t chunks_per_query, int64_t nblk_cap, float* __restrict__ block_max,
+                  float* __restrict__ scores)
+{
+    const int64_t row = blockIdx.x / chunks_per_query;  // query row b*nq + i
+    const int64_t chunk = blockIdx.x % chunks_per_query;
+    const int64_t b = row / nq;
+    int64_t n_vis = n_visible[row];
+    n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
+    const int64_t start = chunk * kChunk;
+    if (start >= n_vis)
+        return;
+    const int64_t end = start + kChunk < n_vis ? start + kChunk : n_vis;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+
+    QueryOperand Q;
+    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
+    const uint8_t* kc = codes + b * n_cap * (kIdxDim / 2);
+    const uint8_t* ks = scales + b * n_cap * (kIdxDim / 16);
+
+    // tiles of this wave: start + 32*(wave + kWaves*i)
+    int64_t e = start + kTileEntries * wave + (lane & 31);
+    const int64_t step = kTileEntries * kWaves;
+    KeyTile cur = {}, nxt = {};
+    if (e < end)
+        load_key(kc, ks, e, half, cur);
+    for (; e - (lane & 31) < end; e += step) {
+        const int64_t en = e + step;
+        if (en < end)
+            load_key(kc, ks, en, half, nxt);
+        float s = score_entry(Q, cur);
+        if (e >= end)
+            s = -INFINITY;
+        if (scores != nullptr && lane < 32 && e < end)
+            scores[row * n_cap + e] = s;
+        float m = fmaxf(s, __shfl_xor(s, 1, kWave));
+        m = fmaxf(m, __shfl_xor(m, 2, kWave));
+        m = fmaxf(m, __shfl_xor(m, 4, kWave));
+        if (lane < 32 && (lane & 7) == 0 && e < end)
+            block_max[row * nblk_cap + e / kBlock] = m;
+        cur = nxt;
+    }
+}
+
+// Pool scan: score the positions of a list of blocks (4 blocks per tile).
+constexpr int kPoolTilesPerWave = 4;
+
+__global__ void __launch_bounds__(kWaves * kWave)
+index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                  const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                  int64_t n_cap, const int32_t* __restrict__ blocks, int32_t n_blocks,
+                  const int32_t* __restrict__ n_visible, int32_t nq, int32_t wgs_per_query,
+                  float* __restrict__ pool_score, int32_t* __restrict__ pool_idx)
+{
+    const int64_t row = blockIdx.x / wgs_per_query;
+    const int32_t part = blockIdx.x % wgs_per_query;
+    const int64_t b = row / nq;
+    int64_t n_vis = n_visible[row];
+    n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int64_t slots = (int64_t)n_blocks * kBlock;
+
+    QueryOperand Q;
+    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
+    const uint8_t* kc = codes + b * n_cap * (kIdxDim / 2);
+    const uint8_t* ks = scales + b * n_cap * (kIdxDim / 16);
+    const int32_t* blk = blocks + row * n_blocks;
+
+    const int64_t first = ((int64_t)part * kWaves + wave) * kPoolTilesPerWave * kTileEntries;
+    for (int i = 0; i < kPoolTilesPerWave; ++i) {
+        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        if (slot - (lane & 31) >= slots)
+            break;
+        int64_t pos = -1;
+        if (slot < slots) {
+            const int32_t bl = blk[slot / kBlock];
+            const int64_t p = (int64_t)bl * kBlock + slot % kBlock;
+            pos = (bl >= 0 && p < n_vis) ? p : -1;
+        }
+        KeyTile K;
+        if (pos >= 0) {
+            load_key(kc, ks, pos, half, K);
+        } else {
+            K.c0 = u32x4{0u, 0u, 0u, 0u};
+            K.c1 = K.c0;
+            K.sc = 0;
+        }
+        float s = score_entry(Q, K);
+        if (lane < 32 && slot < slots) {
+            pool_score[row * slots + slot] = pos >= 0 ? s : -INFINITY;
+            pool_idx[row * slots + slot] = (int32_t)pos;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                             const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
+                             int32_t B, int32_t nq, float* block_max, float* scores,
+                             hipStream_t stream)
+{
+    const int64_t chunks = (n_cap + kChunk - 1) / kChunk;
+    const int64_t rows = (int64_t)B * nq;
+    const int64_t grid = rows * chunks;
+    if (grid == 0)
+        return hipSuccess;
+    const int64_t nblk_cap = (n_cap + kBlock - 1) / kBlock;
+    index_full_kernel<<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
+        q, w, k_codes, k_scales, n_cap, n_visible, nq, (int32_t)chunks, nblk_cap, block_max,
+        scores);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                             const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
+                             int32_t n_blocks, const int32_t* n_visible, int32_t B, int32_t nq,
+                             float* pool_score, int32_t* pool_idx, hipStream_t stream)
+{
+    const int64_t slots = (int64_t)n_blocks * kBlock;
+    const int64_t per_wg = (int64_t)kWaves * kPoolTilesPerWave * kTileEntries;
+    const int64_t wgs = (slots + per_wg - 1) / per_wg;
+    const int64_t grid = (int64_t)B * nq * wgs;
+    if (grid == 0)
+        return hipSuccess;
+    index_pool_kernel<<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
+        q, w, k_codes, k_scales, n_cap, blocks, n_blocks, n_visible, nq, (int32_t)wgs,
+        pool_score, pool_idx);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,52 @@
+// Host-side launchers of the libcsa2 kernels.  The C ABI (api.hip) validates
+// arguments and then calls exactly one of these; each enqueues its kernels on
+// the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kIdxHeads = 32;
+constexpr int kIdxDim = 128;
+constexpr int kHeads = 64;
+constexpr int kDim = 512;
+constexpr int kGroup = 16;
+constexpr int kBlock = 8;
+constexpr int kTopkSegment = 16384;  // elements one top-k workgroup holds
+constexpr int kTopkMaxK = 8192;
+
+hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, const float* cs,
+                              const float* sn, int32_t rope_off, int32_t rope_dim, uint8_t* codes,
+                              uint8_t* scales, int64_t dst_stride, hipStream_t stream);
+
+hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_t* out,
+                               int64_t dst_stride, hipStream_t stream);
+
+hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                             const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
+                             int32_t B, int32_t nq, float* block_max, float* scores,
+                             hipStream_t stream);
+
+hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                             const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
+                             int32_t n_blocks, const int32_t* n_visible, int32_t B, int32_t nq,
+                             float* pool_score, int32_t* pool_idx, hipStream_t stream);
+
+size_t topk_workspace(int64_t L, int32_t rows, int32_t k);
+hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_t rows,
+                       const int32_t* n_valid, int32_t k, int32_t* out, void* ws,
+                       hipStream_t stream);
+
+int32_t attn_splits(int32_t queries, int32_t k, int32_t n_win);
+size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win);
+hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
+                              const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t n_cap,
+                              const int32_t* topk, int32_t k, const uint8_t* swa,
+                              int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
+                              float softmax_scale, float* out, float* lse, void* ws,
+                              int32_t splits, hipStream_t stream);
+
+}  // namespace csa2

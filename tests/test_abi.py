@@ -1,0 +1,100 @@
+"""The C-ABI library: it loads, exports every entry point include/csa2.h declares,
+and rejects bad arguments on the host with the documented status before
+touching the GPU.  CPU only (no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+kv = pytest.importorskip("kv_cache_decode_mxfp4_amd")
+L = kv._lib
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared()
+    for n in ["csa2_quantize_kv", "csa2_index_full", "csa2_index_pool", "csa2_topk",
+              "csa2_sparse_attn"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    for n in declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for n in declared():
+        assert re.search(rf"\bT {n}$", out, flags=re.M), f"{n} not exported"
+    assert set(declared()) == set(L.EXPORTS)
+
+
+def test_version_and_workspace_queries():
+    lib = L.load()
+    assert lib.csa2_version() == 100
+    assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
+    assert lib.csa2_topk_workspace(131072, 16, 2048) == 2 * 16 * 8 * 2048 * 8
+    assert lib.csa2_topk_workspace(100, 1, 0) == 0
+    assert lib.csa2_sparse_attn_workspace(4096, 1, 512, 128) == 0
+    assert lib.csa2_sparse_attn_workspace(16, 1, 512, 128) > 0
+
+
+def _status(fn, *args):
+    lib = L.load()
+    st = getattr(lib, fn)(*args)
+    return st, lib.csa2_last_error().decode()
+
+
+def test_host_validation_rejects_bad_arguments():
+    vp = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    # channels not a multiple of 16
+    st, msg = _status("csa2_quantize_kv", vp, 4, 15, None, None, 0, 0, vp, vp, 1, None)
+    assert st == 2 and "channels" in msg
+    # rotary range outside the row
+    st, msg = _status("csa2_quantize_kv", vp, 4, 512, vp, vp, 480, 64, vp, vp, 1, None)
+    assert st == 1 and "rotary" in msg
+    # null pointers with work to do
+    st, _ = _status("csa2_quantize_kv", None, 4, 512, None, None, 0, 0, None, None, 1, None)
+    assert st == 1
+    # unsupported block size
+    st, msg = _status("csa2_index_full", vp, vp, vp, vp, 100, vp, 1, 1, 4, vp, None, None)
+    assert st == 2 and "block" in msg
+    # negative sizes
+    st, _ = _status("csa2_index_pool", vp, vp, vp, vp, 100, vp, 8, 8, vp, -1, 1, vp, vp, None)
+    assert st == 1
+    # k out of range
+    st, _ = _status("csa2_topk", vp, None, 100, 1, None, 0, vp, None, 0, None)
+    assert st == 2
+    st, _ = _status("csa2_topk", vp, None, 100, 1, None, 9000, vp, None, 0, None)
+    assert st == 2
+    # a long row needs a workspace
+    st, msg = _status("csa2_topk", vp, None, 131072, 1, None, 512, vp, None, 0, None)
+    assert st == 3 and "workspace" in msg
+    # attention workspace too small
+    st, msg = _status("csa2_sparse_attn", vp, 16, 1, vp, vp, 100, vp, 512, vp, 128, vp, 128,
+                      ctypes.c_float(1.0), vp, None, vp, 8, None)
+    assert st == 3
+    # misaligned query pointer
+    st, msg = _status("csa2_sparse_attn", ctypes.c_void_p(18), 1, 1, vp, vp, 100, vp, 4, vp, 128,
+                      vp, 128, ctypes.c_float(1.0), vp, None, None, 0, None)
+    assert st == 1 and "misaligned" in msg
+
+
+def test_empty_inputs_are_no_ops():
+    assert _status("csa2_quantize_kv", None, 0, 512, None, None, 0, 0, None, None, 1, None)[0] == 0
+    assert _status("csa2_index_full", None, None, None, None, 0, None, 0, 1, 8, None, None,
+                   None)[0] == 0
+    assert _status("csa2_topk", None, None, 0, 0, None, 5, None, None, 0, None)[0] == 0
+    assert _status("csa2_sparse_attn", None, 0, 1, None, None, 0, None, 0, None, 0, None, 128,
+                   ctypes.c_float(1.0), None, None, None, 0, None)[0] == 0

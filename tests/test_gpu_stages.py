@@ -1,0 +1,289 @@
+"""Stage-by-stage parity of the GPU library (through the C ABI) with the oracle.
+
+Each stage gets inputs from `synth` or from the oracle, never from another GPU
+stage, so a failure names one kernel.  Bars: bit-exact for codes, scales and
+selected indices; near-tie-tolerant for selections made from float scores;
+2e-3 max-abs for attention outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_harness import (ATTN_TOL, cdiv, check_set, dev, finite_close, max_abs, t)
+
+pytestmark = pytest.mark.gpu
+
+kv = pytest.importorskip("kv_cache_decode_mxfp4_amd")
+L = kv._lib
+
+
+def _ties_rows(rng, rows, C):
+    """Groups whose elements sit exactly on E2M1 midpoints of their scale, plus
+    groups whose amax/6 sits exactly on E4M3 midpoints."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    out = np.empty((rows, C), np.float32)
+    for r in range(rows):
+        for g in range(C // 16):
+            sb = int(rng.integers(1, 0x7E))
+            s = oracle.e4m3_decode(sb)
+            if rng.random() < 0.5:
+                grp = rng.choice(mids, 16) * s * rng.choice([-1, 1], 16)
+                grp[rng.integers(16)] = 6.0 * s
+            else:
+                s2 = oracle.e4m3_decode(sb + 1)
+                grp = rng.uniform(-1, 1, 16) * 3 * (s + s2)
+                grp[rng.integers(16)] = 3.0 * (s + s2)  # amax / 6 = midpoint of two scales
+            out[r, 16 * g:16 * g + 16] = grp
+    return out
+
+
+@pytest.mark.parametrize("kind", ["latent_rope", "normal_index", "ties", "extremes"])
+def test_quantize_kv_bit_exact(kind):
+    rng = np.random.default_rng(5)
+    rows = 1031  # ragged
+    cos = sin = None
+    if kind == "latent_rope":
+        x = synth.latent_rows(synth.key(7, 2), synth.key(7, 3), 0, rows, 512)
+        cos, sin = synth.rope_rows(100000, rows)
+    elif kind == "normal_index":
+        x = rng.standard_normal((rows, 128)).astype(np.float32)
+    elif kind == "ties":
+        x = _ties_rows(rng, 64, 512)
+    else:
+        x = np.concatenate([
+            rng.standard_normal((16, 128)) * 1e-5, rng.standard_normal((16, 128)) * 2000,
+            np.zeros((4, 128)), -np.zeros((4, 128)), rng.standard_normal((8, 128)) * 1e-40,
+        ]).astype(np.float32)
+    C = x.shape[1]
+    codes = torch.empty(x.shape[0], C // 2, dtype=torch.uint8, device=dev())
+    scales = torch.empty(x.shape[0], C // 16, dtype=torch.uint8, device=dev())
+    if cos is None:
+        L.quantize_kv(t(x), codes, scales)
+        ref = oracle.quantize_rows(x)
+    else:
+        L.quantize_kv(t(x), codes, scales, t(cos), t(sin), 448, 64)
+        ref = oracle.quantize_rows(x, cos, sin, 448, 64)
+    assert np.array_equal(codes.cpu().numpy(), ref[0])
+    assert np.array_equal(scales.cpu().numpy(), ref[1])
+
+
+def test_quantize_kv_strided_append():
+    """One new row per sequence written into a [B, n_cap] cache (dst_stride = n_cap)."""
+    B, n_cap = 5, 37
+    x = synth.latent_rows(synth.key(8, 2), synth.key(8, 3), 0, B, 512)
+    cos, sin = synth.rope_rows(36, B)
+    codes = torch.zeros(B, n_cap, 256, dtype=torch.uint8, device=dev())
+    scales = torch.zeros(B, n_cap, 32, dtype=torch.uint8, device=dev())
+    xd, cd, sd = t(x), t(cos), t(sin)
+    # rows go to row n_cap-1 of every sequence: base pointer of that row, stride n_cap
+    st = L.load().csa2_quantize_kv(xd.data_ptr(), B, 512, cd.data_ptr(), sd.data_ptr(), 448, 64,
+                                   codes.data_ptr() + (n_cap - 1) * 256,
+                                   scales.data_ptr() + (n_cap - 1) * 32, n_cap,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_rows(x, cos, sin, 448, 64)
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(c[:, n_cap - 1], rc) and np.array_equal(s[:, n_cap - 1], rs)
+    assert not c[:, :n_cap - 1].any() and not s[:, :n_cap - 1].any()
+
+
+def test_quantize_swa_bit_exact():
+    rng = np.random.default_rng(6)
+    grid = np.array([oracle.e4m3_decode(b) for b in range(127)])
+    mids = (grid[1:] + grid[:-1]) / 2
+    x = np.concatenate([
+        synth.latent_rows(synth.key(9, 4), synth.key(9, 5), 0, 20, 512).ravel(),
+        mids, -mids, grid, [500.0, -1e6, 1e-30, -1e-30, 0.0, -0.0],
+        rng.standard_normal(4096) * 100,
+    ]).astype(np.float32)
+    x = np.concatenate([x, np.zeros((-x.size) % 512, np.float32)]).reshape(-1, 512)
+    out = torch.empty(x.shape, dtype=torch.uint8, device=dev())
+    L.quantize_swa(t(x), out)
+    assert np.array_equal(out.cpu().numpy(), oracle.encode_fp8(x))
+
+
+# ------------------------------------------------------------------ top-k
+
+def _topk_case(rng, rows, Lr, kind):
+    if kind == "ties":
+        s = np.round(rng.standard_normal((rows, Lr)), 1).astype(np.float32)
+    elif kind == "allequal":
+        s = np.zeros((rows, Lr), np.float32)
+    else:
+        s = rng.standard_normal((rows, Lr)).astype(np.float32) * 10
+    s[:, ::97] = -0.0
+    s[:, 5::211] = np.nan
+    s[:, 7::301] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("Lr,k", [(1, 1), (100, 7), (2048, 64), (16384, 2048), (16385, 512),
+                                  (40000, 512), (131072, 2048), (300000, 512)])
+@pytest.mark.parametrize("kind", ["random", "ties"])
+def test_topk_bit_exact(Lr, k, kind):
+    rng = np.random.default_rng(Lr + k)
+    rows = 3
+    s = _topk_case(rng, rows, Lr, kind)
+    n_valid = np.array([Lr, max(0, Lr - 13), min(Lr, k // 2)], np.int32)
+    out = torch.empty(rows, k, dtype=torch.int32, device=dev())
+    ws_n = L.topk_workspace(Lr, rows, k)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev())
+    L.topk(t(s), k, out, n_valid=t(n_valid), ws=ws)
+    got = out.cpu().numpy()
+    for r in range(rows):
+        idx = np.arange(Lr, dtype=np.int32)
+        idx[np.isnan(s[r])] = -1
+        idx[n_valid[r]:] = -1
+        ref = oracle.select(s[r].astype(np.float64), k, idx)
+        assert np.array_equal(got[r], ref), f"row {r}"
+
+
+def test_topk_with_index_array_and_all_equal():
+    rng = np.random.default_rng(9)
+    rows, Lr, k = 2, 16384, 512
+    s = _topk_case(rng, rows, Lr, "allequal")
+    idx = np.tile(np.arange(0, 3 * Lr, 3, dtype=np.int32), (rows, 1))
+    idx[:, 100:200] = -1
+    out = torch.empty(rows, k, dtype=torch.int32, device=dev())
+    L.topk(t(s), k, out, idx=t(idx))
+    for r in range(rows):
+        ref = oracle.select(s[r].astype(np.float64), k, np.where(np.isnan(s[r]), -1, idx[r]))
+        assert np.array_equal(out.cpu().numpy()[r], ref)
+
+
+# ------------------------------------------------------------------ indexer
+
+def _index_case(B=3, N=5003, seed=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, N, 128)).astype(np.float32)
+    enc = [oracle.quantize_rows(x[b]) for b in range(B)]
+    kc = np.stack([e[0] for e in enc])
+    ks = np.stack([e[1] for e in enc])
+    q = np.stack([synth.normal_bf16(synth.key(11, 6, 0, b), 0, 4096, 1 / np.sqrt(128))
+                  for b in range(B)]).reshape(B, 1, 32, 128)
+    w = np.stack([synth.uniform_f32(synth.key(11, 7, 0, b), 0, 32) for b in range(B)]).reshape(B, 1, 32)
+    nv = np.array([[N], [N - 777], [1]], np.int32)[:B]
+    return x, kc, ks, q, w, nv
+
+
+def test_index_full_scores_and_block_max_match_oracle():
+    x, kc, ks, q, w, nv = _index_case()
+    B, N = kc.shape[0], kc.shape[1]
+    nblk = cdiv(N, 8)
+    bm = torch.full((B, 1, nblk), 12345.0, device=dev())
+    sc = torch.full((B, 1, N), 12345.0, device=dev())
+    L.index_full(t(q, torch.uint16), t(w), t(kc), t(ks), t(nv), bm, sc)
+    bm, sc = bm.cpu().numpy(), sc.cpu().numpy()
+    for b in range(B):
+        n = int(nv[b, 0])
+        ref = oracle.index_scores(q[b, 0], w[b, 0], kc[b], ks[b], n)
+        ok, err = finite_close(sc[b, 0, :n], ref)
+        assert ok, f"scores seq {b}: max err {err}"
+        rb = oracle.block_max(ref, 8)
+        ok, err = finite_close(bm[b, 0, :rb.size], rb)
+        assert ok, f"block max seq {b}: max err {err}"
+        assert np.all(sc[b, 0, n:] == 12345.0) and np.all(bm[b, 0, rb.size:] == 12345.0)
+
+
+def test_index_pool_scores_bit_identical_to_scan():
+    x, kc, ks, q, w, nv = _index_case(seed=1)
+    B, N = kc.shape[0], kc.shape[1]
+    sc = torch.zeros((B, 1, N), device=dev())
+    bm = torch.zeros((B, 1, cdiv(N, 8)), device=dev())
+    L.index_full(t(q, torch.uint16), t(w), t(kc), t(ks), t(nv), bm, sc)
+    rng = np.random.default_rng(2)
+    nb = 300
+    blocks = np.sort(rng.choice(cdiv(N, 8), (B, 1, nb), replace=True), axis=-1).astype(np.int32)
+    blocks[:, :, -5:] = -1
+    blocks[0, 0, -6] = cdiv(N, 8) - 1  # partial last block
+    ps = torch.empty(B, 1, nb * 8, device=dev())
+    pi = torch.empty(B, 1, nb * 8, dtype=torch.int32, device=dev())
+    L.index_pool(t(q, torch.uint16), t(w), t(kc), t(ks), t(blocks), t(nv), ps, pi)
+    ps, pi, sc = ps.cpu().numpy(), pi.cpu().numpy(), sc.cpu().numpy()
+    for b in range(B):
+        pos = oracle.pool_positions(blocks[b, 0], 8, int(nv[b, 0]))
+        assert np.array_equal(pi[b, 0], pos)
+        ok = pos >= 0
+        assert np.array_equal(ps[b, 0][ok], sc[b, 0][pos[ok]])  # bitwise equal
+        assert np.all(np.isneginf(ps[b, 0][~ok]))
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_case(B=2, N=3000, k=100, swa_cap=160, seed=3):
+    w = synth.WORKLOADS[1]
+    vc, vs, sw, sel, q = [], [], [], [], []
+    rng = np.random.default_rng(seed)
+    for b in range(B):
+        x = synth.latent_rows(synth.key(12, 2, 0, b), synth.key(12, 3, 0, b), 0, N, 512)
+        cos, sin = synth.rope_rows(0, N)
+        c, s = oracle.quantize_rows(x, cos, sin, 448, 64)
+        vc.append(c)
+        vs.append(s)
+        sw.append(oracle.encode_fp8(synth.latent_rows(synth.key(12, 4, 0, b),
+                                                      synth.key(12, 5, 0, b), 0, swa_cap, 512)))
+        sel.append(np.sort(rng.choice(N, k, replace=False)).astype(np.int32))
+        q.append(synth.normal_bf16(synth.key(12, 8, 0, b), 0, 64 * 512, 1 / np.sqrt(512)))
+    return (np.stack(vc), np.stack(vs), np.stack(sw), np.stack(sel)[:, None],
+            np.stack(q).reshape(B, 1, 64, 512))
+
+
+def _run_attn(q, vc, vs, sel, sw, swa_end, n_win=128, scale=1.0, use_ws=True):
+    B = q.shape[0]
+    k = sel.shape[-1]
+    out = torch.full((B, 1, 64, 512), 777.0, device=dev())
+    lse = torch.full((B, 1, 64), 777.0, device=dev())
+    ws = None
+    if use_ws:
+        n = L.sparse_attn_workspace(B, 1, k, n_win)
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev())
+    L.sparse_attn(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end), out, lse,
+                  n_win=n_win, softmax_scale=scale, ws=ws)
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("variant", ["plain", "padded", "window_only", "empty", "short_window",
+                                     "scale", "zero_q", "no_ws"])
+def test_sparse_attn_matches_oracle(variant):
+    vc, vs, sw, sel, q = _attn_case()
+    B = q.shape[0]
+    swa_end = np.array([[128], [150]], np.int32)
+    n_win, scale, use_ws = 128, 1.0, True
+    if variant == "padded":
+        sel = sel.copy()
+        sel[:, :, ::7] = -1
+        sel[:, :, 3] = 10 ** 6  # out of range: skipped
+    elif variant == "window_only":
+        sel = -np.ones_like(sel)
+    elif variant == "empty":
+        sel = -np.ones_like(sel)
+        swa_end = np.zeros_like(swa_end)
+    elif variant == "short_window":
+        swa_end = np.array([[40], [200]], np.int32)  # 200 > capacity 160
+    elif variant == "scale":
+        scale = 0.6
+    elif variant == "zero_q":
+        q = np.zeros_like(q)
+    elif variant == "no_ws":
+        use_ws = False
+    out, lse = _run_attn(q, vc, vs, sel, sw, swa_end, n_win, scale, use_ws)
+    for b in range(B):
+        ro, rl = oracle.attention(q[b, 0], vc[b], vs[b], sel[b, 0], sw[b], int(swa_end[b, 0]),
+                                  n_win, scale)
+        assert max_abs(out[b, 0], ro) <= ATTN_TOL, f"seq {b}: {max_abs(out[b, 0], ro)}"
+        if np.all(np.isinf(rl)):
+            assert np.all(np.isneginf(lse[b, 0])) and np.all(out[b, 0] == 0)
+        else:
+            assert max_abs(lse[b, 0], rl) <= 1e-4
+
+
+def test_sparse_attn_k_not_multiple_of_tile_and_large_k():
+    vc, vs, sw, sel, q = _attn_case(B=1, N=5000, k=1000, seed=4)
+    swa_end = np.array([[128]], np.int32)
+    out, lse = _run_attn(q, vc, vs, sel, sw, swa_end)
+    ro, rl = oracle.attention(q[0, 0], vc[0], vs[0], sel[0, 0], sw[0], 128)
+    assert max_abs(out[0, 0], ro) <= ATTN_TOL
+    assert max_abs(lse[0, 0], rl) <= 1e-4
