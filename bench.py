@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 decode hot path on one MI355X.
+
+Metric: CSA2 decode queries/s per layer at 1M context, with the achieved HBM
+bandwidth of the dominant kernel (the Full-layer indexer scan) against the
+MI355X peak.  Workload (default): 16 sequences x 1,048,576 compressed entries,
+indexer 32 heads x 128, top-k 512, pool 2048 blocks x 8, attention 64 heads x
+512 over MXFP4 main KV + 128 FP8 window rows.  Inputs are seeded synthetic
+(synth/), resident in HBM before the timed region.
+
+One step = one Full layer at decode for the whole batch: encode the new
+token's main-KV, indexer-key and window rows; block scan over every entry;
+pool select (top-2048 blocks); pool rescoring; top-512; sparse attention.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--cpu-sample 4]
+
+Prints one JSON line.  Only one GPU is supported (--gpus above 1 exits).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "CSA2 decode queries/sec per layer at 1M ctx; achieved HBM TB/s vs peak"
+PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+PEAK_F16 = 2.5e15  # MI355X dense fp16 MFMA, flop/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_full_scan_1M_b16_traffic.txt")
+SCAN_SOURCE = os.path.join(ROOT, "kv_cache_decode_mxfp4_amd", "csrc", "indexer.hip")
+CHUNK_ROWS = 1 << 18
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4])
+    ap.add_argument("--cpu-sample", type=int, default=4,
+                    help="query rows of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workload on the GPU
+
+def build_device(w: synth.Workload, torch, L):
+    """Encode the whole cache of every sequence on the GPU from synth rows."""
+    dev = torch.device("cuda:0")
+    B, N = w.B, w.n_cap
+    st = {"w": w}
+    st["kc"] = torch.empty(B, N, 64, dtype=torch.uint8, device=dev)
+    st["ks"] = torch.empty(B, N, 8, dtype=torch.uint8, device=dev)
+    st["vc"] = torch.empty(B, N, 256, dtype=torch.uint8, device=dev)
+    st["vs"] = torch.empty(B, N, 32, dtype=torch.uint8, device=dev)
+    t0 = time.time()
+    for r0 in range(0, N, CHUNK_ROWS):
+        n = min(CHUNK_ROWS, N - r0)
+        cos, sin = synth.rope_rows(r0, n)
+        cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+        for b in range(B):
+            kx = torch.from_numpy(synth.idx_k_rows(w, b, r0, n)).to(dev)
+            L.quantize_kv(kx, st["kc"][b], st["ks"][b], dst_row=r0)
+            vx = torch.from_numpy(synth.kv_rows(w, b, r0, n)).to(dev)
+            L.quantize_kv(vx, st["vc"][b], st["vs"][b], cos_d, sin_d, synth.ROPE_OFFSET,
+                          synth.ROPE_DIM, dst_row=r0)
+        torch.cuda.synchronize()
+        log(f"caches: {min(r0 + n, N)}/{N} entries x {B} sequences ({time.time() - t0:.0f} s)")
+    n_layers = len(w.layers)
+    st["swa"], st["q_idx"], st["w_idx"], st["q_main"] = [], [], [], []
+    for layer in range(n_layers):
+        sw = torch.empty(B, w.swa_rows(), 512, dtype=torch.uint8, device=dev)
+        for b in range(B):
+            L.quantize_swa(torch.from_numpy(synth.swa_rows(w, layer, b, 0, w.swa_rows())).to(dev), sw[b])
+        st["swa"].append(sw)
+        st["q_idx"].append(torch.from_numpy(synth.q_idx(w, layer)).to(dev))
+        st["w_idx"].append(torch.from_numpy(synth.w_idx(w, layer)).to(dev))
+        st["q_main"].append(torch.from_numpy(synth.q_main(w, layer)).to(dev))
+    st["n_vis"] = torch.from_numpy(w.n_visible()).to(dev)
+    st["swa_end"] = torch.from_numpy(w.swa_end()).to(dev)
+    # rows the step encodes: the entries this step appends, and the newest window row
+    first, count = w.new_entries()
+    st["new_first"], st["new_count"] = first, count
+    st["new_idx"] = torch.from_numpy(np.concatenate(
+        [synth.idx_k_rows(w, b, first, count) for b in range(B)])).to(dev)
+    st["new_kv"] = torch.from_numpy(np.concatenate(
+        [synth.kv_rows(w, b, first, count) for b in range(B)])).to(dev)
+    cos, sin = synth.rope_rows(first, count)
+    st["new_cos"] = torch.from_numpy(np.tile(cos, (B, 1))).to(dev)
+    st["new_sin"] = torch.from_numpy(np.tile(sin, (B, 1))).to(dev)
+    new_tok = w.chunk if not w.decode else 1
+    st["new_swa_row"] = w.swa_rows() - new_tok
+    st["new_swa"] = torch.from_numpy(np.concatenate(
+        [synth.swa_rows(w, 0, b, st["new_swa_row"], new_tok) for b in range(B)])).to(dev)
+    torch.cuda.synchronize()
+    return st
+
+
+def make_step(st, torch, L, layers):
+    """The timed step: one layer group of the workload over the whole batch."""
+    w = st["w"]
+    B, nq, N = w.B, w.nq, w.n_cap
+    from kv_cache_decode_mxfp4_amd.layers import Buffers, n_valid_blocks
+    buf = Buffers.create(B, nq, N, w.k, w.nb, w.n_win)
+    n_blk = n_valid_blocks(st["n_vis"])
+    first, count = st["new_first"], st["new_count"]
+    st["buf"] = buf
+    scan_events = []
+
+    def encode_new():
+        if w.decode:
+            # one row per sequence at entry N-1 of each [N]-row cache
+            L.quantize_kv(st["new_idx"], st["kc"], st["ks"], dst_row=first, dst_stride=N)
+            L.quantize_kv(st["new_kv"], st["vc"], st["vs"], st["new_cos"], st["new_sin"],
+                          synth.ROPE_OFFSET, synth.ROPE_DIM, dst_row=first, dst_stride=N)
+            L.quantize_swa(st["new_swa"], st["swa"][0], dst_row=st["new_swa_row"],
+                           dst_stride=w.swa_rows())
+        else:
+            L.quantize_kv(st["new_idx"], st["kc"], st["ks"], dst_row=first)
+            L.quantize_kv(st["new_kv"], st["vc"], st["vs"], st["new_cos"], st["new_sin"],
+                          synth.ROPE_OFFSET, synth.ROPE_DIM, dst_row=first)
+            L.quantize_swa(st["new_swa"], st["swa"][0], dst_row=st["new_swa_row"])
+
+    def step(time_scan=False):
+        encode_new()
+        if time_scan:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        L.index_full(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], st["n_vis"], buf.block_max)
+        if time_scan:
+            e1.record()
+            scan_events.append((e0, e1))
+        layers.select_blocks(buf, n_blk, w.k, w.nb)
+        L.index_pool(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], buf.sel_blocks,
+                     st["n_vis"], buf.pool_score, buf.pool_idx)
+        L.topk(buf.pool_score, w.k, buf.topk, idx=buf.pool_idx, ws=buf.ws_topk)
+        layers.attention(buf, st["q_main"][0], st["vc"], st["vs"], buf.topk, st["swa"][0],
+                         st["swa_end"], w.n_win)
+        if "reindex" in w.layers:
+            layers.reindex_indexer(buf, st["q_idx"][1], st["w_idx"][1], st["kc"], st["ks"],
+                                   st["n_vis"], buf.pool, w.k)
+            for layer in range(1, len(w.layers)):
+                layers.attention(buf, st["q_main"][layer], st["vc"], st["vs"], buf.topk,
+                                 st["swa"][layer], st["swa_end"], w.n_win)
+
+    return step, scan_events
+
+
+def scan_bytes(w: synth.Workload) -> int:
+    """Algorithmic bytes of one index_full launch at decode: every visible indexer key of
+    the query's own sequence (64 B codes + 8 B scales), the query (32x128 bf16) and
+    weights (32 fp32), the block maxima written (fp32 per 8 entries)."""
+    nv = w.n_visible().astype(np.int64)
+    return int(nv.sum()) * 72 + w.B * w.nq * (32 * 128 * 2 + 32 * 4) + int(((nv + 7) // 8).sum()) * 4
+
+
+def scan_flops(w: synth.Workload) -> int:
+    """MFMA flops of one index_full launch: 32 heads x 128 channels x 2 per visible entry."""
+    return int(w.n_visible().astype(np.int64).sum()) * 32 * 128 * 2
+
+
+def step_bytes(w: synth.Workload) -> int:
+    """Algorithmic bytes of one whole decode step (every stage), for a step-level TB/s."""
+    rows = w.B * w.nq
+    nsel = max(w.nb, w.k)
+    nblk = int(((w.n_visible().astype(np.int64) + 7) // 8).sum())
+    b = scan_bytes(w)
+    b += nblk * 4 + rows * nsel * 4                                  # block select
+    b += rows * (nsel * 8 * (72 + 8) + nsel * 4 + 32 * 128 * 2 + 128)  # pool scan
+    b += rows * (nsel * 8 * 8 + w.k * 4)                             # top-k of the pool
+    attn = rows * (w.k * (4 + 288) + w.n_win * 512 + 64 * 512 * (2 + 4) + 64 * 4)
+    b += attn * len(w.layers)
+    if "reindex" in w.layers:
+        b += rows * (w.nb * 4 + w.nb * 8 * (72 + 8 + 8) + w.k * 4 + 32 * 128 * 2 + 128)
+    first, count = w.new_entries()
+    b += w.B * count * ((128 + 512) * 4 + 72 + 288 + 32 * 4 * 2)  # encode appended entries
+    return b
+
+
+def source_hash() -> str:
+    with open(SCAN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per scan launch from the committed counter summary, if it was taken on
+    the current scan source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = line.split(None, 1)
+            vals[k] = v.strip()
+    if vals.get("source_sha256_16") != source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+def cpu_baseline(w: synth.Workload, rows: int):
+    """The oracle timed on this host's cores over the first `rows` query rows of the same
+    workload (same Full-layer step: new-row encode, full scan, top-k, pool, attention)."""
+    import oracle
+    sample = [(b, i) for b in range(w.B) for i in range(w.nq)][:rows]
+    seqs = sorted({b for b, _ in sample})
+    enc = {}
+    t0 = time.time()
+    for b in seqs:
+        cos, sin = synth.rope_rows(0, w.n_cap)
+        kc, ks = oracle.quantize_rows(synth.idx_k_rows(w, b, 0, w.n_cap))
+        vc, vs = oracle.quantize_rows(synth.kv_rows(w, b, 0, w.n_cap), cos, sin,
+                                      synth.ROPE_OFFSET, synth.ROPE_DIM)
+        sw = oracle.encode_fp8(synth.swa_rows(w, 0, b, 0, w.swa_rows()))
+        enc[b] = (kc, ks, vc, vs, sw)
+    log(f"cpu baseline: oracle caches for {len(seqs)} sequences ({time.time() - t0:.0f} s)")
+    qi, wi, qm = synth.q_idx(w, 0), synth.w_idx(w, 0), synth.q_main(w, 0)
+    nv, se = w.n_visible(), w.swa_end()
+    first, count = w.new_entries()
+    new_kv = {b: synth.kv_rows(w, b, first, count) for b in seqs}
+    new_idx = {b: synth.idx_k_rows(w, b, first, count) for b in seqs}
+    ncos, nsin = synth.rope_rows(first, count)
+    t0 = time.perf_counter()
+    for b, i in sample:
+        kc, ks, vc, vs, sw = enc[b]
+        oracle.quantize_rows(new_idx[b])
+        oracle.quantize_rows(new_kv[b], ncos, nsin, synth.ROPE_OFFSET, synth.ROPE_DIM)
+        full = oracle.full_layer(qi[b, i], wi[b, i], kc, ks, int(nv[b, i]), w.k, w.nb, w.block)
+        oracle.attention(qm[b, i], vc, vs, full["topk"], sw, int(se[b, i]), w.n_win, 1.0)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(sample) / dt, 4), "unit": "queries/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{len(sample)} query rows ({len(seqs)} sequences) of the same workload, "
+                      f"full Full-layer step per row, {dt:.1f} s wall"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus above 1 is not supported)", file=sys.stderr)
+        return 2
+    import torch
+    import kv_cache_decode_mxfp4_amd as kv
+    from kv_cache_decode_mxfp4_amd import _lib as L, layers
+    L.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    w = synth.WORKLOADS[args.config]
+    log(f"workload: {w.name}")
+    st = build_device(w, torch, L)
+    step, scan_events = make_step(st, torch, L, layers)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warm")
+    scan_events.clear()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step(time_scan=True)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in scan_events]))
+    rows = w.B * w.nq
+    value = rows / (ms_step / 1e3)
+    if w.decode:
+        sb = scan_bytes(w)
+        achieved = sb / (scan_ms / 1e3)
+        roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
+                "traffic": measured_traffic() if args.config == 3 else None,
+                "kernel": "index_full_kernel", "kernel_ms": round(scan_ms, 4),
+                "algorithmic_bytes": sb}
+    else:
+        fl = scan_flops(w)
+        achieved = fl / (scan_ms / 1e3)
+        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": PEAK_F16 / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16, 4), "traffic": None,
+                "kernel": "index_full_kernel", "kernel_ms": round(scan_ms, 4),
+                "algorithmic_flops": fl}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "queries_per_seq": w.nq, "n_cap": w.n_cap,
+                   "topk": w.k, "pool_blocks": w.nb, "block": w.block, "n_win": w.n_win,
+                   "indexer": "32x128", "attention": "64x512", "layers": list(w.layers)},
+        "roofline": roof,
+    }
+    if w.decode:
+        out["step_tbps"] = round(step_bytes(w) / (ms_step / 1e3) / 1e12, 3)
+    if args.cpu_sample > 0 and args.config in (1, 3):
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

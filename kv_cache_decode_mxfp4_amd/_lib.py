@@ -105,22 +105,35 @@ def _bf16_bits(t):
     raise TypeError(f"expected bfloat16 (or its uint16 bits), got {t.dtype}")
 
 
+def _rows_fit(t, row_bytes, dst_row, dst_stride, rows, name):
+    last = dst_row + (rows - 1) * dst_stride + 1 if rows else 0
+    if dst_row < 0 or last * row_bytes > t.numel():
+        raise ValueError(f"{name}: rows do not fit the destination")
+
+
 def quantize_kv(x, codes, scales, rope_cos=None, rope_sin=None, rope_offset=0, rope_dim=0,
-                dst_stride=1, stream=None):
+                dst_row=0, dst_stride=1, stream=None):
+    """Encode x [rows, C] into rows dst_row + r*dst_stride of the flat code/scale caches."""
     _dt(x, torch.float32, "x")
     _dt(codes, torch.uint8, "codes")
     _dt(scales, torch.uint8, "scales")
     rows, C = x.shape
+    _rows_fit(codes, C // 2, dst_row, dst_stride, rows, "codes")
+    _rows_fit(scales, C // 16, dst_row, dst_stride, rows, "scales")
     _check("csa2_quantize_kv", load().csa2_quantize_kv(
-        _p(x), rows, C, _p(rope_cos), _p(rope_sin), rope_offset, rope_dim, _p(codes),
-        _p(scales), dst_stride, _stream(stream)))
+        _p(x), rows, C, _p(rope_cos), _p(rope_sin), rope_offset, rope_dim,
+        _p(codes) + dst_row * (C // 2), _p(scales) + dst_row * (C // 16), dst_stride,
+        _stream(stream)))
 
 
-def quantize_swa(x, out, row_len=512, dst_stride=1, stream=None):
+def quantize_swa(x, out, row_len=512, dst_row=0, dst_stride=1, stream=None):
+    """Encode x [rows, row_len] into rows dst_row + r*dst_stride of the flat window buffer."""
     _dt(x, torch.float32, "x")
     _dt(out, torch.uint8, "out")
+    rows = x.numel() // row_len
+    _rows_fit(out, row_len, dst_row, dst_stride, rows, "out")
     _check("csa2_quantize_swa", load().csa2_quantize_swa(
-        _p(x), x.numel(), row_len, _p(out), dst_stride, _stream(stream)))
+        _p(x), x.numel(), row_len, _p(out) + dst_row * row_len, dst_stride, _stream(stream)))
 
 
 def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block=8, stream=None):
