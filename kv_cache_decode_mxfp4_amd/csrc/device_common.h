@@ -63,6 +63,71 @@ __device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b)
 }
 
 // --------------------------------------------------------------- reductions
+//
+// DPP forms: row_shr:n moves lane i-n -> i inside each row of 16 lanes (lanes
+// without a source read `old`); rows are then combined through v_readlane.
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, kCtrl, 0xF, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x, int lane)
+{
+    x += dpp_u32<0x111>(0u, x);
+    x += dpp_u32<0x112>(0u, x);
+    x += dpp_u32<0x114>(0u, x);
+    x += dpp_u32<0x118>(0u, x);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = lane >> 4;
+    x += row >= 1 ? r0 : 0u;
+    x += row >= 2 ? r1 : 0u;
+    x += row >= 3 ? r2 : 0u;
+    return x;
+}
+
+// Wave-uniform maximum / minimum / sum of unsigned values.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
+{
+    x = max(x, dpp_u32<0x111>(0u, x));
+    x = max(x, dpp_u32<0x112>(0u, x));
+    x = max(x, dpp_u32<0x114>(0u, x));
+    x = max(x, dpp_u32<0x118>(0u, x));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
+{
+    x = min(x, dpp_u32<0x111>(0xFFFFFFFFu, x));
+    x = min(x, dpp_u32<0x112>(0xFFFFFFFFu, x));
+    x = min(x, dpp_u32<0x114>(0xFFFFFFFFu, x));
+    x = min(x, dpp_u32<0x118>(0xFFFFFFFFu, x));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    return min(min(a, b), min(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x, int lane)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_sum(x, lane), 63);
+}
+
+// Number of lanes below `lane` whose bit is set in a wave-wide ballot.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t ballot, int lane)
+{
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    return (uint32_t)__popcll(ballot & below);
+}
 
 __device__ __forceinline__ float wave_max(float v)
 {

@@ -30,6 +30,13 @@ constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kTileEntries = 32;    // entries per MFMA tile
 constexpr int kTilesPerWave = 32;   // tiles each wave scans per workgroup
 constexpr int kChunk = kWaves * kTilesPerWave * kTileEntries;  // entries per workgroup
+#ifndef CSA2_SCAN_PREFETCH
+#define CSA2_SCAN_PREFETCH 3
+#endif
+constexpr int kPrefetch = CSA2_SCAN_PREFETCH;  // key tiles in flight per wave
+#ifndef CSA2_SCAN_NONTEMPORAL
+#define CSA2_SCAN_NONTEMPORAL 1
+#endif
 
 struct QueryOperand {
     half8 a[8];      // A operand of k-steps 0..7
@@ -95,10 +102,17 @@ __device__ __forceinline__ void load_key(const uint8_t* __restrict__ codes,
                                          int half, KeyTile& K)
 {
     const u32x4* c = reinterpret_cast<const u32x4*>(codes + entry * (kIdxDim / 2) + 32 * half);
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(scales + entry * (kIdxDim / 16) + 4 * half);
+#if CSA2_SCAN_NONTEMPORAL
+    // streamed once: do not keep the keys in the caches
     K.c0 = __builtin_nontemporal_load(c);
     K.c1 = __builtin_nontemporal_load(c + 1);
-    K.sc = __builtin_nontemporal_load(
-        reinterpret_cast<const uint32_t*>(scales + entry * (kIdxDim / 16) + 4 * half));
+    K.sc = __builtin_nontemporal_load(sp);
+#else
+    K.c0 = c[0];
+    K.c1 = c[1];
+    K.sc = *sp;
+#endif
 }
 
 // Score of the lane's entry (both lanes of an entry return the same value).
@@ -146,27 +160,38 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* kc = codes + b * n_cap * (kIdxDim / 2);
     const uint8_t* ks = scales + b * n_cap * (kIdxDim / 16);
 
-    // tiles of this wave: start + 32*(wave + kWaves*i)
-    int64_t e = start + kTileEntries * wave + (lane & 31);
+    // tiles of this wave: start + 32*(wave + kWaves*i); a ring of kPrefetch
+    // tiles is in flight while the oldest one is scored
     const int64_t step = kTileEntries * kWaves;
-    KeyTile cur = {}, nxt = {};
-    if (e < end)
-        load_key(kc, ks, e, half, cur);
-    for (; e - (lane & 31) < end; e += step) {
-        const int64_t en = e + step;
-        if (en < end)
-            load_key(kc, ks, en, half, nxt);
-        float s = score_entry(Q, cur);
-        if (e >= end)
-            s = -INFINITY;
-        if (scores != nullptr && lane < 32 && e < end)
-            scores[row * n_cap + e] = s;
-        float m = fmaxf(s, __shfl_xor(s, 1, kWave));
-        m = fmaxf(m, __shfl_xor(m, 2, kWave));
-        m = fmaxf(m, __shfl_xor(m, 4, kWave));
-        if (lane < 32 && (lane & 7) == 0 && e < end)
-            block_max[row * nblk_cap + e / kBlock] = m;
-        cur = nxt;
+    const int64_t first = start + kTileEntries * wave + (lane & 31);
+    KeyTile ring[kPrefetch];
+#pragma unroll
+    for (int p = 0; p < kPrefetch; ++p) {
+        ring[p] = KeyTile{};
+        const int64_t ep = first + p * step;
+        if (ep < end)
+            load_key(kc, ks, ep, half, ring[p]);
+    }
+    for (int64_t base = first; base - (lane & 31) < end; base += kPrefetch * step) {
+#pragma unroll
+        for (int p = 0; p < kPrefetch; ++p) {
+            const int64_t e = base + p * step;
+            if (e - (lane & 31) >= end)
+                break;
+            float s = score_entry(Q, ring[p]);
+            const int64_t en = e + kPrefetch * step;
+            if (en < end)
+                load_key(kc, ks, en, half, ring[p]);
+            if (e >= end)
+                s = -INFINITY;
+            if (scores != nullptr && lane < 32 && e < end)
+                scores[row * n_cap + e] = s;
+            float m = fmaxf(s, __shfl_xor(s, 1, kWave));
+            m = fmaxf(m, __shfl_xor(m, 2, kWave));
+            m = fmaxf(m, __shfl_xor(m, 4, kWave));
+            if (lane < 32 && (lane & 7) == 0 && e < end)
+                block_max[row * nblk_cap + e / kBlock] = m;
+        }
     }
 }
 
@@ -190,35 +215,38 @@ index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const int half = lane >> 5;
     const int64_t slots = (int64_t)n_blocks * kBlock;
 
-    QueryOperand Q;
-    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
     const uint8_t* kc = codes + b * n_cap * (kIdxDim / 2);
     const uint8_t* ks = scales + b * n_cap * (kIdxDim / 16);
     const int32_t* blk = blocks + row * n_blocks;
 
     const int64_t first = ((int64_t)part * kWaves + wave) * kPoolTilesPerWave * kTileEntries;
+    // gather every tile of this wave first, then score: all loads in flight at once
+    int64_t pos[kPoolTilesPerWave];
+    KeyTile K[kPoolTilesPerWave];
+#pragma unroll
+    for (int i = 0; i < kPoolTilesPerWave; ++i) {
+        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        pos[i] = -1;
+        if (slot < slots) {
+            const int32_t bl = blk[slot / kBlock];
+            const int64_t p = (int64_t)bl * kBlock + slot % kBlock;
+            pos[i] = (bl >= 0 && p < n_vis) ? p : -1;
+        }
+        K[i] = KeyTile{};
+        if (pos[i] >= 0)
+            load_key(kc, ks, pos[i], half, K[i]);
+    }
+    QueryOperand Q;  // loaded while the gathers are in flight
+    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
+#pragma unroll
     for (int i = 0; i < kPoolTilesPerWave; ++i) {
         const int64_t slot = first + i * kTileEntries + (lane & 31);
         if (slot - (lane & 31) >= slots)
             break;
-        int64_t pos = -1;
-        if (slot < slots) {
-            const int32_t bl = blk[slot / kBlock];
-            const int64_t p = (int64_t)bl * kBlock + slot % kBlock;
-            pos = (bl >= 0 && p < n_vis) ? p : -1;
-        }
-        KeyTile K;
-        if (pos >= 0) {
-            load_key(kc, ks, pos, half, K);
-        } else {
-            K.c0 = u32x4{0u, 0u, 0u, 0u};
-            K.c1 = K.c0;
-            K.sc = 0;
-        }
-        float s = score_entry(Q, K);
+        const float s = score_entry(Q, K[i]);
         if (lane < 32 && slot < slots) {
-            pool_score[row * slots + slot] = pos >= 0 ? s : -INFINITY;
-            pool_idx[row * slots + slot] = (int32_t)pos;
+            pool_score[row * slots + slot] = pos[i] >= 0 ? s : -INFINITY;
+            pool_idx[row * slots + slot] = (int32_t)pos[i];
         }
     }
 }

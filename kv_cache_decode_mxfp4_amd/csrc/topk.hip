@@ -1,22 +1,29 @@
 // Deterministic top-k select ([N] 1 of the DeepSeek-V4.1 reading notes: top-k
-// 512; [N] 2.2 / [A] 3.4: top-2048 blocks form the pool).
+// 512; [N] 2.2 / [A] 3.4: the top-2048 blocks form the pool).
 //
 // Order: score descending, then position ascending (the lower index wins a
 // tie); -0 equals +0; NaN and masked entries never win.  Output: the chosen
 // indices in ascending order, -1 padded.
 //
-// One workgroup of 1024 threads holds a segment of up to 16384 scores in
-// registers (16 per thread, thread t owning positions [16t, 16t+16)) and finds
-// the k-th largest key with an adaptive-range radix select: every pass
-// histograms the live key range [kmin, kmax] into 256 equal bins in LDS and
-// keeps the bin that holds the k-th key, so each pass shrinks the range by at
-// least 2^8 and at most four passes are needed.  A workgroup-wide prefix sum
-// then writes the chosen entries in position order.
+// Core: one workgroup of 1024 threads holds up to 16384 (key, index) pairs in
+// registers, 16 per thread (slot i of thread t is element 1024*i + t, so loads
+// are coalesced and position order is slot-major).  The k-th largest key is
+// found by an adaptive-range radix select: each pass histograms the live key
+// range [lo, hi] into at most 8192 equal LDS bins and keeps the bin holding the
+// k-th key, shrinking the span by at least 2^13 (three passes at most).  One
+// ballot round then gives every chosen entry its output offset:
+//   offset = (#greater before it) + min(#equal before it, #equal to take).
 //
-// Rows longer than one segment are reduced exactly in levels: every segment
-// emits its own top-k candidates (the global top-k is a subset of their
-// union, and the candidate lists keep position order), until one segment
-// remains.
+// Longer rows:
+//   grouped (g = ceil(L/16384) with k*g <= 16384): the row is cut into groups of
+//     g consecutive entries; the top-k entries lie in the top-k groups ranked by
+//     their largest key (a group ranked above a winner's group holds another
+//     winner, also under the lower-position tie-break), so a wide kernel writes
+//     the group maxima and one workgroup per row selects k groups, gathers
+//     their k*g entries and selects k of those;
+//   otherwise exact levels: every segment of 16384 emits its own top-k
+//     candidates (the global top-k is a subset of their union, and the
+//     candidate lists keep position order) until one segment remains.
 #include "device_common.h"
 
 namespace csa2 {
@@ -25,6 +32,8 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kPer = kTopkSegment / kThreads;  // 16
 constexpr int kNumWaves = kThreads / kWave;    // 16
+constexpr int kBinBits = 13;
+constexpr int kBins = 1 << kBinBits;           // 8192 bins, 8 per thread
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -40,68 +49,217 @@ __device__ __forceinline__ float key_value(uint32_t k)
 }
 
 struct Smem {
-    uint32_t hist[256];
-    uint32_t wave_a[kNumWaves];
-    uint32_t wave_b[kNumWaves];
-    uint32_t bcast[4];
+    uint32_t hist[2][kBins];
+    uint32_t part_gt[kPer * kNumWaves];
+    uint32_t part_eq[kPer * kNumWaves];
+    uint32_t wave_a[3][kNumWaves];
+    uint32_t bcast[2][2];
+    uint32_t totals[2];
 };
 
-// Workgroup sum of one value per thread.
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, Smem& sm, int lane, int wave)
-{
-    v = wave_sum(v);
-    if (lane == 0)
-        sm.wave_a[wave] = v;
-    __syncthreads();
-    uint32_t t = 0;
-#pragma unroll
-    for (int i = 0; i < kNumWaves; ++i)
-        t += sm.wave_a[i];
-    __syncthreads();
-    return t;
-}
+struct Pick {
+    uint32_t T;     // threshold key (0 = take every valid key)
+    uint32_t need;  // keys equal to T to take, in position order
+};
 
-// Workgroup min and max of one key per thread (inactive threads pass
-// min = 0xFFFFFFFF, max = 0).
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, Smem& sm, int lane,
-                                             int wave)
+// Threshold of the k largest keys held by the workgroup (key 0 = invalid).
+// Expects sm.hist[0] cleared by the caller before the first barrier here.
+__device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm, int tid,
+                               int lane, int wave)
 {
+    uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    }
+    for (int i = 0; i < kPer; ++i)
+        if (key[i] != 0u) {
+            ++cnt;
+            lo = min(lo, key[i]);
+            hi = max(hi, key[i]);
+        }
+    cnt = wave_sum_u32(cnt, lane);
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
     if (lane == 0) {
-        sm.wave_a[wave] = mn;
-        sm.wave_b[wave] = mx;
+        sm.wave_a[0][wave] = cnt;
+        sm.wave_a[1][wave] = lo;
+        sm.wave_a[2][wave] = hi;
     }
     __syncthreads();
-    mn = 0xFFFFFFFFu;
-    mx = 0u;
+    uint32_t total = 0;
+    lo = 0xFFFFFFFFu;
+    hi = 0u;
 #pragma unroll
     for (int i = 0; i < kNumWaves; ++i) {
-        mn = min(mn, sm.wave_a[i]);
-        mx = max(mx, sm.wave_b[i]);
+        total += sm.wave_a[0][i];
+        lo = min(lo, sm.wave_a[1][i]);
+        hi = max(hi, sm.wave_a[2][i]);
     }
     __syncthreads();
+    Pick pk{0u, 0u};
+    if (total <= k)
+        return pk;
+    uint32_t need = k;
+    // invariant: the threshold is the need-th largest key inside [lo, hi]
+    for (int pass = 0; pass < 4 && hi != lo; ++pass) {
+        const int buf = pass & 1;
+        const uint32_t span = hi - lo;
+        const int bits = 32 - __builtin_clz(span);
+        const int shift = bits > kBinBits ? bits - kBinBits : 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (key[i] >= lo && key[i] <= hi)
+                atomicAdd(&sm.hist[buf][(key[i] - lo) >> shift], 1u);
+        __syncthreads();
+        // thread t owns bins 8t .. 8t+7
+        uint32_t c[8], mine = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = sm.hist[buf][8 * tid + j];
+            mine += c[j];
+            sm.hist[buf ^ 1][8 * tid + j] = 0u;  // clear the buffer of the next pass
+        }
+        const uint32_t incl = wave_prefix_sum(mine, lane);
+        if (lane == kWave - 1)
+            sm.wave_a[0][wave] = incl;
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (int i = 0; i < kNumWaves; ++i) {
+            const uint32_t v = sm.wave_a[0][i];
+            before += i < wave ? v : 0u;
+            all += v;
+        }
+        uint32_t above = all - (before + incl);  // keys in bins above 8t+7
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+            if (above < need && above + c[j] >= need) {
+                sm.bcast[buf][0] = 8u * tid + j;
+                sm.bcast[buf][1] = above;
+            }
+            above += c[j];
+        }
+        __syncthreads();
+        const uint32_t bin = sm.bcast[buf][0];
+        need -= sm.bcast[buf][1];
+        lo = lo + (bin << shift);
+        const uint64_t top = (uint64_t)lo + ((1ull << shift) - 1ull);
+        hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+    }
+    pk.T = lo;
+    pk.need = need;
+    return pk;
 }
 
-// Exclusive prefix sum over the workgroup in thread order.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Smem& sm, int lane, int wave)
+// Marks the chosen slots and their output offsets (position order); returns
+// how many were chosen.
+__device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPer],
+                          uint32_t (&off)[kPer], Smem& sm, int lane, int wave)
 {
-    const uint32_t inc = wave_inclusive_scan(v, lane);
-    if (lane == kWave - 1)
-        sm.wave_a[wave] = inc;
+    uint32_t gt_below[kPer], eq_below[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const uint64_t bg = __ballot(key[i] > pk.T);
+        const uint64_t be = __ballot(pk.T != 0u && key[i] == pk.T);
+        gt_below[i] = lanes_below(bg, lane);
+        eq_below[i] = lanes_below(be, lane);
+        if (lane == 0) {
+            sm.part_gt[i * kNumWaves + wave] = (uint32_t)__popcll(bg);
+            sm.part_eq[i * kNumWaves + wave] = (uint32_t)__popcll(be);
+        }
+    }
     __syncthreads();
-    uint32_t before = 0;
-    for (int i = 0; i < wave; ++i)
-        before += sm.wave_a[i];
+    if (wave < 2) {
+        // exclusive scan of 256 (slot, wave) counts in position order, 4 per lane
+        uint32_t* part = wave == 0 ? sm.part_gt : sm.part_eq;
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            c[j] = part[4 * lane + j];
+            sum += c[j];
+        }
+        const uint32_t incl = wave_prefix_sum(sum, lane);
+        uint32_t run = incl - sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            part[4 * lane + j] = run;
+            run += c[j];
+        }
+        if (lane == kWave - 1)
+            sm.totals[wave] = incl;
+    }
     __syncthreads();
-    return before + inc - v;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const uint32_t gt_before = sm.part_gt[i * kNumWaves + wave] + gt_below[i];
+        const uint32_t eq_before = sm.part_eq[i * kNumWaves + wave] + eq_below[i];
+        const bool eq = pk.T != 0u && key[i] == pk.T;
+        take[i] = key[i] > pk.T || (eq && eq_before < pk.need);
+        off[i] = gt_before + (eq_before < pk.need ? eq_before : pk.need);
+    }
+    const uint32_t n_gt = sm.totals[0], n_eq = sm.totals[1];
+    __syncthreads();
+    return n_gt + (n_eq < pk.need ? n_eq : pk.need);
 }
 
-// Selects within rows of up to kTopkSegment entries.  Grid: rows * nseg
-// workgroups; workgroup (row, seg) covers positions [seg*seg_len, +seg_len).
+__device__ __forceinline__ void write_result(const bool (&take)[kPer], const uint32_t (&off)[kPer],
+                                             const uint32_t (&key)[kPer], const int32_t (&id)[kPer],
+                                             uint32_t chosen, int32_t k, int tid,
+                                             int32_t* __restrict__ out, float* __restrict__ cs,
+                                             int32_t* __restrict__ ci)
+{
+    if (cs == nullptr) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (take[i] && off[i] < (uint32_t)k)
+                out[off[i]] = id[i];
+        for (uint32_t p = chosen + tid; p < (uint32_t)k; p += kThreads)
+            out[p] = -1;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (take[i] && off[i] < (uint32_t)k) {
+                cs[off[i]] = key_value(key[i]);
+                ci[off[i]] = id[i];
+            }
+        for (uint32_t p = chosen + tid; p < (uint32_t)k; p += kThreads) {
+            cs[p] = 0.0f;
+            ci[p] = -1;
+        }
+    }
+}
+
+// Loads slot i of thread tid = element seg_start + 1024*i + tid (clamped
+// inside the row, masked by position < seg_end, index >= 0 and not NaN).
+__device__ __forceinline__ void load_slots(const float* __restrict__ srow,
+                                           const int32_t* __restrict__ irow, int64_t L,
+                                           int64_t seg_start, int64_t seg_end, int tid,
+                                           uint32_t (&key)[kPer], int32_t (&id)[kPer])
+{
+    float f[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        int64_t pos = seg_start + (int64_t)kThreads * i + tid;
+        pos = pos < L ? pos : L - 1;
+        f[i] = srow[pos];
+        id[i] = irow != nullptr ? irow[pos] : (int32_t)pos;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t pos = seg_start + (int64_t)kThreads * i + tid;
+        const bool ok = pos < seg_end && id[i] >= 0 && !__builtin_isnan(f[i]);
+        key[i] = ok ? order_key(f[i]) : 0u;
+    }
+}
+
+__device__ __forceinline__ int64_t valid_prefix(const int32_t* __restrict__ n_valid, int64_t row,
+                                                int64_t L)
+{
+    if (n_valid == nullptr)
+        return L;
+    const int64_t nv = n_valid[row];
+    return nv < 0 ? 0 : (nv > L ? L : nv);
+}
+
+// Direct select within segments of up to 16384 entries.  Grid: rows * nseg.
 // Final mode (cand_score == nullptr): out[row, 0..k) = ascending indices.
 // Candidate mode: cand_score/cand_idx[row, seg, 0..k) = chosen (score, index)
 // pairs in position order, padded with index -1.
@@ -117,156 +275,163 @@ topk_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, in
     const int wave = tid >> 6;
     const int64_t row = blockIdx.x / nseg;
     const int64_t seg = blockIdx.x % nseg;
-    int64_t nv = L;
-    if (n_valid != nullptr) {
-        nv = n_valid[row];
-        nv = nv < 0 ? 0 : (nv > L ? L : nv);
-    }
+    const int64_t nv = valid_prefix(n_valid, row, L);
     const int64_t seg_start = seg * seg_len;
-    int64_t seg_end = seg_start + seg_len;
-    seg_end = seg_end < nv ? seg_end : nv;
+    const int64_t seg_end = seg_start + seg_len < nv ? seg_start + seg_len : nv;
+    for (int b = tid; b < kBins; b += kThreads)
+        sm.hist[0][b] = 0u;
 
     uint32_t key[kPer];
     int32_t id[kPer];
-    uint32_t n_mine = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int64_t pos = seg_start + (int64_t)kPer * tid + i;
-        uint32_t kk = 0u;
-        int32_t ii = -1;
-        if (pos < seg_end) {
-            const float f = score[row * L + pos];
-            ii = idx != nullptr ? idx[row * L + pos] : (int32_t)pos;
-            if (ii >= 0 && !__builtin_isnan(f))
-                kk = order_key(f);
-        }
-        key[i] = kk;
-        id[i] = ii;
-        n_mine += kk != 0u;
-    }
-    const uint32_t n_total = block_sum(n_mine, sm, lane, wave);
-
-    // threshold key T and the number of keys equal to T to take
-    uint32_t T = 0u;
-    uint32_t need = 0u;
-    if (n_total > (uint32_t)k) {
-        uint32_t lo = 1u, hi = 0xFFFFFFFFu;
-        need = (uint32_t)k;
-        // each pass drops at least 8 bits of the live range: 4 passes narrow a
-        // 32-bit range to one key, the 5th sees kmin == kmax; 6 bounds the loop
-        for (int pass = 0; pass < 6; ++pass) {
-            uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-            for (int i = 0; i < kPer; ++i)
-                if (key[i] >= lo && key[i] <= hi) {
-                    mn = min(mn, key[i]);
-                    mx = max(mx, key[i]);
-                }
-            block_minmax(mn, mx, sm, lane, wave);
-            T = mn;
-            if (mn == mx)
-                break;
-            const uint32_t span = mx - mn;
-            const int bits = 32 - __builtin_clz(span);
-            const int shift = bits > 8 ? bits - 8 : 0;
-            if (tid < 256)
-                sm.hist[tid] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < kPer; ++i)
-                if (key[i] >= mn && key[i] <= mx)
-                    atomicAdd(&sm.hist[(key[i] - mn) >> shift], 1u);
-            __syncthreads();
-            if (wave == 0) {
-                // lane owns bins 4*lane .. 4*lane+3; count of keys in bins above
-                uint32_t c[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    c[j] = sm.hist[4 * lane + j];
-                const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-                // suffix sum over lanes: keys in bins of lanes > lane
-                uint32_t incl = mine;
-#pragma unroll
-                for (int o = 1; o < kWave; o <<= 1) {
-                    const uint32_t t = __shfl_down(incl, o, kWave);
-                    if (lane + o < kWave)
-                        incl += t;
-                }
-                uint32_t above = incl - mine;  // bins of higher lanes
-#pragma unroll
-                for (int j = 3; j >= 0; --j) {
-                    if (above < need && above + c[j] >= need) {
-                        sm.bcast[0] = (uint32_t)(4 * lane + j);
-                        sm.bcast[1] = above;
-                    }
-                    above += c[j];
-                }
-            }
-            __syncthreads();
-            const uint32_t bin = sm.bcast[0];
-            const uint32_t above = sm.bcast[1];
-            __syncthreads();
-            need -= above;
-            lo = mn + (bin << shift);
-            const uint64_t top = (uint64_t)lo + ((1ull << shift) - 1ull);
-            hi = top < (uint64_t)mx ? (uint32_t)top : mx;
-        }
-    }
-
-    // counts per thread, then positions in the output
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        gt += key[i] > T;
-        eq += (T != 0u) && key[i] == T;
-    }
-    const uint32_t eq_before = block_exclusive_scan(eq, sm, lane, wave);
-    uint32_t take_eq = need > eq_before ? need - eq_before : 0u;
-    take_eq = take_eq < eq ? take_eq : eq;
-    const uint32_t mine = gt + take_eq;
-    uint32_t o = block_exclusive_scan(mine, sm, lane, wave);
-    const uint32_t selected = n_total < (uint32_t)k ? n_total : (uint32_t)k;
-    uint32_t eq_seen = 0;
-    if (cand_score == nullptr) {
-        int32_t* dst = out + row * k;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            bool take = key[i] > T;
-            if (T != 0u && key[i] == T) {
-                take = eq_seen < take_eq;
-                ++eq_seen;
-            }
-            if (take && o < (uint32_t)k)
-                dst[o++] = id[i];
-        }
-        for (uint32_t p = selected + tid; p < (uint32_t)k; p += kThreads)
-            dst[p] = -1;
+    if (L > 0) {
+        load_slots(score + row * L, idx != nullptr ? idx + row * L : nullptr, L, seg_start,
+                   seg_end, tid, key, id);
     } else {
-        float* ds = cand_score + (row * nseg + seg) * k;
-        int32_t* di = cand_idx + (row * nseg + seg) * k;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            bool take = key[i] > T;
-            if (T != 0u && key[i] == T) {
-                take = eq_seen < take_eq;
-                ++eq_seen;
-            }
-            if (take && o < (uint32_t)k) {
-                ds[o] = key_value(key[i]);
-                di[o] = id[i];
-                ++o;
-            }
-        }
-        for (uint32_t p = selected + tid; p < (uint32_t)k; p += kThreads) {
-            ds[p] = 0.0f;
-            di[p] = -1;
+            key[i] = 0u;
+            id[i] = -1;
         }
     }
+    const Pick pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
+    bool take[kPer];
+    uint32_t off[kPer];
+    const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
+    write_result(take, off, key, id, chosen, k, tid, out + row * k,
+                 cand_score ? cand_score + (row * nseg + seg) * k : nullptr,
+                 cand_idx ? cand_idx + (row * nseg + seg) * k : nullptr);
+}
+
+// Group maxima of keys for the grouped path: gkey[row, grp] = largest key of
+// entries [grp*g, grp*g + g) of the row (0 if none is valid).  One thread per
+// group; grid: rows * ceil(ngroups / 256).
+template <int G>
+__global__ void __launch_bounds__(256)
+group_max_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
+                 int32_t g_runtime, int64_t ngroups, int32_t wgs_per_row,
+                 const int32_t* __restrict__ n_valid, uint32_t* __restrict__ gkey)
+{
+    const int g = G > 0 ? G : g_runtime;
+    const int64_t row = blockIdx.x / wgs_per_row;
+    const int64_t grp = (int64_t)(blockIdx.x % wgs_per_row) * 256 + threadIdx.x;
+    if (grp >= ngroups)
+        return;
+    const int64_t nv = valid_prefix(n_valid, row, L);
+    const float* srow = score + row * L;
+    const int32_t* irow = idx != nullptr ? idx + row * L : nullptr;
+    uint32_t m = 0u;
+    if (G > 0) {
+        float f[G > 0 ? G : 1];
+        int32_t ii[G > 0 ? G : 1];
+#pragma unroll
+        for (int r = 0; r < (G > 0 ? G : 1); ++r) {
+            int64_t pos = grp * G + r;
+            pos = pos < L ? pos : L - 1;
+            f[r] = srow[pos];
+            ii[r] = irow != nullptr ? irow[pos] : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < (G > 0 ? G : 1); ++r)
+            if (grp * G + r < nv && ii[r] >= 0 && !__builtin_isnan(f[r]))
+                m = max(m, order_key(f[r]));
+    } else {
+        for (int r = 0; r < g; ++r) {
+            const int64_t pos = grp * g + r;
+            if (pos < nv) {
+                const float f = srow[pos];
+                const int32_t ii = irow != nullptr ? irow[pos] : 0;
+                if (ii >= 0 && !__builtin_isnan(f))
+                    m = max(m, order_key(f));
+            }
+        }
+    }
+    gkey[row * ngroups + grp] = m;
+}
+
+struct GroupSmem {
+    Smem sm;
+    uint32_t chosen_groups[kTopkSegment / 2];  // k <= 16384 / g with g >= 2
+};
+
+// Grouped select for one row from its group maxima gkey[row, 0..ngroups)
+// (ngroups <= 16384, g * k <= 16384).  Grid: rows.
+__global__ void __launch_bounds__(kThreads)
+topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
+                    int32_t g, int64_t ngroups, const uint32_t* __restrict__ gkey,
+                    const int32_t* __restrict__ n_valid, int32_t k, int32_t* __restrict__ out)
+{
+    __shared__ GroupSmem gs;
+    Smem& sm = gs.sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t nv = valid_prefix(n_valid, row, L);
+    const float* srow = score + row * L;
+    const int32_t* irow = idx != nullptr ? idx + row * L : nullptr;
+    for (int b = tid; b < kBins; b += kThreads)
+        sm.hist[0][b] = 0u;
+
+    uint32_t key[kPer];
+    int32_t id[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t grp = (int64_t)kThreads * i + tid;
+        key[i] = grp < ngroups ? gkey[row * ngroups + grp] : 0u;
+        id[i] = (int32_t)grp;
+    }
+    Pick pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
+    bool take[kPer];
+    uint32_t off[kPer];
+    uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
+    // chosen group ids, ascending, into LDS
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (take[i] && off[i] < (uint32_t)k)
+            gs.chosen_groups[off[i]] = (uint32_t)id[i];
+    for (int b = tid; b < kBins; b += kThreads)
+        sm.hist[0][b] = 0u;
+    __syncthreads();
+    const uint32_t n_chosen = chosen < (uint32_t)k ? chosen : (uint32_t)k;
+    // candidate c*g + r is entry r of the c-th chosen group: position order
+    float f[kPer];
+    int64_t pos[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const uint32_t e = (uint32_t)(kThreads * i + tid);
+        const uint32_t c = e / (uint32_t)g;
+        pos[i] = -1;
+        if (c < n_chosen) {
+            const int64_t p = (int64_t)gs.chosen_groups[c] * g + e % (uint32_t)g;
+            pos[i] = p < nv ? p : -1;
+        }
+        const int64_t pl = pos[i] >= 0 ? pos[i] : 0;
+        f[i] = srow[pl];
+        id[i] = irow != nullptr ? irow[pl] : (int32_t)pl;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const bool ok = pos[i] >= 0 && id[i] >= 0 && !__builtin_isnan(f[i]);
+        key[i] = ok ? order_key(f[i]) : 0u;
+        id[i] = pos[i] >= 0 ? id[i] : -1;
+    }
+    pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
+    chosen = place(key, pk, take, off, sm, lane, wave);
+    write_result(take, off, key, id, chosen, k, tid, out + row * k, nullptr, nullptr);
 }
 
 int64_t segments(int64_t L)
 {
     return (L + kTopkSegment - 1) / kTopkSegment;
+}
+
+// Group size of the grouped path, or 0 when it does not apply.
+int32_t group_size(int64_t L, int32_t k)
+{
+    if (L <= kTopkSegment)
+        return 0;
+    const int64_t g = (L + kTopkSegment - 1) / kTopkSegment;
+    return (g * k <= kTopkSegment) ? (int32_t)g : 0;
 }
 
 }  // namespace
@@ -275,6 +440,9 @@ size_t topk_workspace(int64_t L, int32_t rows, int32_t k)
 {
     if (L <= kTopkSegment)
         return 0;
+    const int32_t g = group_size(L, k);
+    if (g > 0)  // group maxima
+        return (size_t)rows * (size_t)((L + g - 1) / g) * sizeof(uint32_t);
     // two ping-pong candidate buffers of the first (largest) level
     return 2ull * (size_t)rows * (size_t)segments(L) * (size_t)k * (sizeof(float) + sizeof(int32_t));
 }
@@ -285,6 +453,25 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
 {
     if (rows == 0)
         return hipSuccess;
+    const int32_t g = group_size(L, k);
+    if (g > 0) {
+        const int64_t ngroups = (L + g - 1) / g;
+        const int32_t per_row = (int32_t)((ngroups + 255) / 256);
+        uint32_t* gkey = static_cast<uint32_t*>(ws);
+        const dim3 grid((uint32_t)(rows * per_row));
+        if (g == 8)
+            group_max_kernel<8><<<grid, dim3(256), 0, stream>>>(score, idx, L, g, ngroups, per_row,
+                                                                n_valid, gkey);
+        else
+            group_max_kernel<0><<<grid, dim3(256), 0, stream>>>(score, idx, L, g, ngroups, per_row,
+                                                                n_valid, gkey);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        topk_grouped_kernel<<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
+            score, idx, L, g, ngroups, gkey, n_valid, k, out);
+        return hipGetLastError();
+    }
     const size_t half = topk_workspace(L, rows, k) / 2;
     char* bufs[2] = {static_cast<char*>(ws), static_cast<char*>(ws) + half};
     int flip = 0;

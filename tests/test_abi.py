@@ -44,7 +44,8 @@ def test_version_and_workspace_queries():
     lib = L.load()
     assert lib.csa2_version() == 100
     assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
-    assert lib.csa2_topk_workspace(131072, 16, 2048) == 2 * 16 * 8 * 2048 * 8
+    assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
+    assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
     assert lib.csa2_topk_workspace(100, 1, 0) == 0
     assert lib.csa2_sparse_attn_workspace(4096, 1, 512, 128) == 0
     assert lib.csa2_sparse_attn_workspace(16, 1, 512, 128) > 0

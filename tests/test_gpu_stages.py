@@ -121,7 +121,8 @@ def _topk_case(rng, rows, Lr, kind):
 
 
 @pytest.mark.parametrize("Lr,k", [(1, 1), (100, 7), (2048, 64), (16384, 2048), (16385, 512),
-                                  (40000, 512), (131072, 2048), (300000, 512)])
+                                  (40000, 512), (131072, 2048), (300000, 512), (300000, 2048),
+                                  (50000, 6000)])
 @pytest.mark.parametrize("kind", ["random", "ties"])
 def test_topk_bit_exact(Lr, k, kind):
     rng = np.random.default_rng(Lr + k)
