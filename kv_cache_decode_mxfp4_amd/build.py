@@ -20,8 +20,10 @@ BUILD = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "quantize.hip", "indexer.hip", "topk.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -ffp-contract=off: every floating-point operation rounds as written; fused
+# multiply-adds appear only where the sources ask for them (__builtin_fmaf).
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", "-Wno-unknown-warning-option",
 ]

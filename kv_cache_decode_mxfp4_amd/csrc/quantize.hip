@@ -7,6 +7,11 @@
 // One thread per 16-channel group; memory-bound and tiny per decode step.
 #include "device_common.h"
 
+// Every product and sum of the encoders rounds on its own (the library is built
+// with -ffp-contract=off): contracting the rotary a*c - b*s into a fused
+// multiply-add moves results by an ulp and flips rounding ties of the scale and
+// element codes.
+
 namespace csa2 {
 namespace {
 

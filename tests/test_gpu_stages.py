@@ -69,6 +69,58 @@ def test_quantize_kv_bit_exact(kind):
     assert np.array_equal(scales.cpu().numpy(), ref[1])
 
 
+def _rotary_tie_rows(n, seed=21):
+    """Rows whose rotated pair lands exactly on a rounding tie when each product and
+    difference is rounded on its own (as the encoder defines), but one ulp away when
+    a*c - b*s is evaluated as a fused multiply-add: half of them make the group
+    maximum 6x an E4M3 midpoint (a scale tie), half put an element on an E2M1
+    midpoint of the group scale (an element tie)."""
+    f32 = np.float32
+    rng = np.random.default_rng(seed)
+    rows = np.zeros((n, 512), np.float32)
+    cos = np.ones((n, 32), np.float32)
+    sin = np.zeros((n, 32), np.float32)
+    rows[:, :448] = rng.standard_normal((n, 448)).astype(np.float32) * 0.1
+    r = 0
+    while r < n:
+        scale_tie = r % 2 == 0
+        m = int(rng.integers(24, 70))
+        if scale_tie:
+            target = f32(6 * (oracle.e4m3_decode(m) + oracle.e4m3_decode(m + 1)) / 2)
+        else:
+            s = oracle.e4m3_decode(m)
+            target = f32(rng.choice([0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * s)
+        ang = rng.uniform(0, 2 * np.pi)
+        c, s_ = f32(np.cos(ang)), f32(np.sin(ang))
+        b = f32(rng.uniform(-0.5, 0.5) * target)
+        bs = f32(b * s_)
+        a0 = f32((np.float64(target) + np.float64(bs)) / np.float64(c))
+        for a in [a0, *[np.nextafter(a0, f32(d * np.inf)) for d in (1, -1)]]:
+            a = f32(a)
+            sep = f32(f32(a * c) - bs)
+            fused = f32(np.float64(a) * np.float64(c) - np.float64(bs))
+            other = abs(f32(f32(a * s_) + f32(b * c)))
+            if sep == target and fused != target and other < target:
+                rows[r, 448], rows[r, 449] = a, b
+                cos[r, 0], sin[r, 0] = c, s_
+                if not scale_tie:  # pair 1 (identity rotation) carries the group max 6*s
+                    rows[r, 450], rows[r, 451] = f32(6 * oracle.e4m3_decode(m)), 0.0
+                rows[r, 452:464] = rng.uniform(-0.1, 0.1, 12) * target
+                r += 1
+                break
+    return rows, cos, sin
+
+
+def test_quantize_kv_rotary_rounds_each_operation():
+    x, cos, sin = _rotary_tie_rows(256)
+    codes = torch.empty(256, 256, dtype=torch.uint8, device=dev())
+    scales = torch.empty(256, 32, dtype=torch.uint8, device=dev())
+    L.quantize_kv(t(x), codes, scales, t(cos), t(sin), 448, 64)
+    ref = oracle.quantize_rows(x, cos, sin, 448, 64)
+    assert np.array_equal(scales.cpu().numpy(), ref[1])
+    assert np.array_equal(codes.cpu().numpy(), ref[0])
+
+
 def test_quantize_kv_strided_append():
     """One new row per sequence written into a [B, n_cap] cache (dst_stride = n_cap)."""
     B, n_cap = 5, 37
