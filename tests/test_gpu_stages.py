@@ -340,3 +340,26 @@ def test_sparse_attn_k_not_multiple_of_tile_and_large_k():
     ro, rl = oracle.attention(q[0, 0], vc[0], vs[0], sel[0, 0], sw[0], 128)
     assert max_abs(out[0, 0], ro) <= ATTN_TOL
     assert max_abs(lse[0, 0], rl) <= 1e-4
+
+
+def test_sparse_attn_batched_kernel_many_rows():
+    """More than 256 query rows take the batched kernel (one workgroup per 32 heads)."""
+    N, nq, k, cap = 3000, 300, 96, 500
+    x = synth.latent_rows(synth.key(13, 2), synth.key(13, 3), 0, N, 512)
+    cos, sin = synth.rope_rows(0, N)
+    vc, vs = oracle.quantize_rows(x, cos, sin, 448, 64)
+    sw = oracle.encode_fp8(synth.latent_rows(synth.key(13, 4), synth.key(13, 5), 0, cap, 512))
+    rng = np.random.default_rng(14)
+    sel = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(nq)]).astype(np.int32)
+    sel[::7, ::5] = -1
+    q = synth.normal_bf16(synth.key(13, 8), 0, nq * 64 * 512, 1 / np.sqrt(512)).reshape(1, nq, 64, 512)
+    swa_end = (np.arange(nq, dtype=np.int32) + 40).reshape(1, nq)  # ragged windows, some short
+    out = torch.full((1, nq, 64, 512), 777.0, device=dev())
+    lse = torch.full((1, nq, 64), 777.0, device=dev())
+    L.sparse_attn(t(q, torch.uint16), t(vc[None]), t(vs[None]), t(sel[None]), t(sw[None]),
+                  t(swa_end), out, lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in list(range(0, nq, 23)) + [nq - 1]:
+        ro, rl = oracle.attention(q[0, i], vc, vs, sel[i], sw, int(swa_end[0, i]), 128, 1.0)
+        assert max_abs(out[0, i], ro) <= ATTN_TOL, f"query {i}"
+        assert max_abs(lse[0, i], rl) <= 1e-4
