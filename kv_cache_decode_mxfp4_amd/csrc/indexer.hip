@@ -28,12 +28,18 @@ namespace {
 
 constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kTileEntries = 32;    // entries per MFMA tile
-constexpr int kTilesPerWave = 32;   // tiles each wave scans per workgroup
-constexpr int kChunk = kWaves * kTilesPerWave * kTileEntries;  // entries per workgroup
 #ifndef CSA2_SCAN_PREFETCH
-#define CSA2_SCAN_PREFETCH 3
+#define CSA2_SCAN_PREFETCH 4
 #endif
 constexpr int kPrefetch = CSA2_SCAN_PREFETCH;  // key tiles in flight per wave
+constexpr int kStep = kTileEntries * kWaves;   // entries between a wave's tiles
+constexpr int kGroupEntries = kPrefetch * kStep;  // entries per prefetch round
+// Entries per scan workgroup: a multiple of kGroupEntries chosen at launch,
+// the largest (up to kMaxChunk) that still gives kScanTargetWorkgroups
+// workgroups (256 CUs x 4 resident workgroups), so each workgroup loads its
+// query once and keeps its prefetch ring running over a long range.
+constexpr int kMaxChunk = 16384;
+constexpr int64_t kScanTargetWorkgroups = 1024;
 #ifndef CSA2_SCAN_NONTEMPORAL
 #define CSA2_SCAN_NONTEMPORAL 1
 #endif
@@ -115,6 +121,46 @@ __device__ __forceinline__ void load_key(const uint8_t* __restrict__ codes,
 #endif
 }
 
+// Keys of one chunk, read with raw buffer loads: the descriptors hold the
+// chunk's base addresses and its visible size in bytes (scalar registers), a
+// lane keeps one 32-bit offset per array, and the hardware range check turns
+// every load past the visible size into zeros.  Tile offsets are added to
+// the vector offset, which the range check covers.  Loads are non-temporal
+// (the keys are streamed once).
+struct ChunkKeys {
+    __amdgpu_buffer_rsrc_t codes, scales;
+    int32_t vc, vs;  // byte offsets of the lane's entry and half in tile 0
+};
+
+constexpr int kBufferConfig = 0x00020000;  // raw (untyped) buffer, 32-bit data
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ ChunkKeys chunk_keys(const uint8_t* codes, const uint8_t* scales,
+                                                int64_t start, int32_t entries, int entry,
+                                                int half)
+{
+    ChunkKeys C;
+    C.codes = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes + start * (kIdxDim / 2)), 0, entries * (kIdxDim / 2),
+        kBufferConfig);
+    C.scales = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scales + start * (kIdxDim / 16)), 0, entries * (kIdxDim / 16),
+        kBufferConfig);
+    C.vc = entry * (kIdxDim / 2) + 32 * half;
+    C.vs = entry * (kIdxDim / 16) + 4 * half;
+    return C;
+}
+
+// Tile whose entries start `first_entry` entries after the lane's tile-0 entry.
+__device__ __forceinline__ void load_key(const ChunkKeys& C, int32_t first_entry, KeyTile& K)
+{
+    const int32_t oc = C.vc + first_entry * (kIdxDim / 2);
+    const int32_t os = C.vs + first_entry * (kIdxDim / 16);
+    K.c0 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc, 0, kNonTemporal);
+    K.c1 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc + 16, 0, kNonTemporal);
+    K.sc = __builtin_amdgcn_raw_buffer_load_b32(C.scales, os, 0, kNonTemporal);
+}
+
 // Score of the lane's entry (both lanes of an entry return the same value).
 __device__ __forceinline__ float score_entry(const QueryOperand& Q, const KeyTile& K)
 {
@@ -126,73 +172,106 @@ __device__ __forceinline__ float score_entry(const QueryOperand& Q, const KeyTil
         const half8 b = dequant8_fp4(words[t], s);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q.a[t], b, acc, 0, 0, 0);
     }
+    // max(0, x) as a signed-integer max of the bit pattern: one instruction,
+    // the same value as fmaxf for every non-NaN x (-0 and negatives give +0)
     float part = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-        part = __builtin_fmaf(Q.wr[r], fmaxf(acc[r], 0.0f), part);
-    return part + __shfl_xor(part, 32, kWave);
+    for (int r = 0; r < 16; ++r) {
+        const float relu = __int_as_float(max(__float_as_int(acc[r]), 0));
+        part = __builtin_fmaf(Q.wr[r], relu, part);
+    }
+    // add the two channel halves: lanes l and l^32 hold the same entry, and
+    // the swap hands every lane both partial sums (the same addition on both)
+    const auto pair = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                       __float_as_uint(part), false, false);
+    return __uint_as_float(pair[0]) + __uint_as_float(pair[1]);
 }
 
-// Full-range scan: one workgroup scans kChunk entries of one query row and
-// writes the maxima of the blocks of 8 it covers (and optionally every score).
-__global__ void __launch_bounds__(kWaves * kWave)
+// Maximum over the 8 lanes of each aligned group of 8 (DPP: swap neighbours,
+// swap pairs, then mirror within the half-row of 8).
+__device__ __forceinline__ float max8(float s)
+{
+    float m = fmaxf(s, __uint_as_float(dpp_u32<0xB1>(0u, __float_as_uint(s))));
+    m = fmaxf(m, __uint_as_float(dpp_u32<0x4E>(0u, __float_as_uint(m))));
+    return fmaxf(m, __uint_as_float(dpp_u32<0x141>(0u, __float_as_uint(m))));
+}
+
+// Full-range scan: one workgroup scans `chunk` entries of one query row and
+// writes the maxima of the blocks of 8 it covers (and, with kScores, every
+// score).  Wave w scores tiles start + 32*(w + kWaves*i).
+//
+// The loop has no data-dependent branch and stores nothing to global memory
+// (block maxima go to LDS and leave in one coalesced store at the end), so
+// the compiler keeps kPrefetch tiles per wave in flight across iterations
+// instead of draining the load counter.  The chunk's buffer descriptors end
+// at the last visible entry: tiles past it read zeros and their scores are
+// masked to -inf, which handles the partial last chunk of a row without a
+// second code path.  128 VGPRs: four workgroups per CU.
+template <bool kScores>
+__global__ void __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                   const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                   int64_t n_cap, const int32_t* __restrict__ n_visible, int32_t nq,
-                  int32_t chunks_per_query, int64_t nblk_cap, float* __restrict__ block_max,
-                  float* __restrict__ scores)
+                  int32_t chunk, int32_t chunks_per_query, int64_t nblk_cap,
+                  float* __restrict__ block_max, float* __restrict__ scores)
 {
+    __shared__ float sblk[kMaxChunk / kBlock];
+
     const int64_t row = blockIdx.x / chunks_per_query;  // query row b*nq + i
-    const int64_t chunk = blockIdx.x % chunks_per_query;
     const int64_t b = row / nq;
     int64_t n_vis = n_visible[row];
     n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
-    const int64_t start = chunk * kChunk;
+    const int64_t start = (int64_t)(blockIdx.x % chunks_per_query) * chunk;
     if (start >= n_vis)
         return;
-    const int64_t end = start + kChunk < n_vis ? start + kChunk : n_vis;
+    const int32_t n_here = (int32_t)(n_vis - start < chunk ? n_vis - start : chunk);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5;
+    const int entry0 = kTileEntries * wave + (lane & 31);  // lane's entry in tile 0
 
-    QueryOperand Q;
-    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
-    const uint8_t* kc = codes + b * n_cap * (kIdxDim / 2);
-    const uint8_t* ks = scales + b * n_cap * (kIdxDim / 16);
-
-    // tiles of this wave: start + 32*(wave + kWaves*i); a ring of kPrefetch
-    // tiles is in flight while the oldest one is scored
-    const int64_t step = kTileEntries * kWaves;
-    const int64_t first = start + kTileEntries * wave + (lane & 31);
+    const ChunkKeys C = chunk_keys(codes + b * n_cap * (kIdxDim / 2),
+                                   scales + b * n_cap * (kIdxDim / 16), start, n_here, entry0,
+                                   half);
     KeyTile ring[kPrefetch];
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p) {
-        ring[p] = KeyTile{};
-        const int64_t ep = first + p * step;
-        if (ep < end)
-            load_key(kc, ks, ep, half, ring[p]);
-    }
-    for (int64_t base = first; base - (lane & 31) < end; base += kPrefetch * step) {
+    for (int p = 0; p < kPrefetch; ++p)
+        load_key(C, p * kStep, ring[p]);
+    __builtin_amdgcn_sched_barrier(0);
+    QueryOperand Q;  // loaded while the first key tiles are in flight
+    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
+
+    const bool writer = lane < 32 && (lane & 7) == 0;
+    const int blk0 = entry0 / kBlock;  // chunk block of the lane's entry in tile 0
+    const int groups = (n_here + kGroupEntries - 1) / kGroupEntries;
+    auto finish = [&](int i, float s) {
+        const int e = entry0 + i * kStep;
+        s = e < n_here ? s : -INFINITY;
+        if (kScores && lane < 32 && e < n_here)
+            scores[row * n_cap + start + e] = s;
+        const float m = max8(s);
+        if (writer)
+            sblk[blk0 + i * (kStep / kBlock)] = m;
+    };
+    for (int g = 0; g < groups - 1; ++g) {
 #pragma unroll
         for (int p = 0; p < kPrefetch; ++p) {
-            const int64_t e = base + p * step;
-            if (e - (lane & 31) >= end)
-                break;
-            float s = score_entry(Q, ring[p]);
-            const int64_t en = e + kPrefetch * step;
-            if (en < end)
-                load_key(kc, ks, en, half, ring[p]);
-            if (e >= end)
-                s = -INFINITY;
-            if (scores != nullptr && lane < 32 && e < end)
-                scores[row * n_cap + e] = s;
-            float m = fmaxf(s, __shfl_xor(s, 1, kWave));
-            m = fmaxf(m, __shfl_xor(m, 2, kWave));
-            m = fmaxf(m, __shfl_xor(m, 4, kWave));
-            if (lane < 32 && (lane & 7) == 0 && e < end)
-                block_max[row * nblk_cap + e / kBlock] = m;
+            const int i = g * kPrefetch + p;
+            const float s = score_entry(Q, ring[p]);
+            load_key(C, (i + kPrefetch) * kStep, ring[p]);
+            finish(i, s);
         }
     }
+#pragma unroll
+    for (int p = 0; p < kPrefetch; ++p) {
+        const int i = (groups - 1) * kPrefetch + p;
+        finish(i, score_entry(Q, ring[p]));
+    }
+    __syncthreads();
+    const int nb_here = (n_here + kBlock - 1) / kBlock;
+    float* dst = block_max + row * nblk_cap + start / kBlock;
+    for (int t = threadIdx.x; t < nb_here; t += kWaves * kWave)
+        dst[t] = sblk[t];
 }
 
 // Pool scan: score the positions of a list of blocks (4 blocks per tile).
@@ -258,15 +337,23 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
                              int32_t B, int32_t nq, float* block_max, float* scores,
                              hipStream_t stream)
 {
-    const int64_t chunks = (n_cap + kChunk - 1) / kChunk;
     const int64_t rows = (int64_t)B * nq;
+    int32_t chunk = kMaxChunk;
+    while (chunk > kGroupEntries && rows * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
+        chunk /= 2;
+    const int64_t chunks = (n_cap + chunk - 1) / chunk;
     const int64_t grid = rows * chunks;
     if (grid == 0)
         return hipSuccess;
     const int64_t nblk_cap = (n_cap + kBlock - 1) / kBlock;
-    index_full_kernel<<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
-        q, w, k_codes, k_scales, n_cap, n_visible, nq, (int32_t)chunks, nblk_cap, block_max,
-        scores);
+    if (scores != nullptr)
+        index_full_kernel<true><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
+            q, w, k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,
+            block_max, scores);
+    else
+        index_full_kernel<false><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
+            q, w, k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,
+            block_max, nullptr);
     return hipGetLastError();
 }
 

@@ -163,7 +163,7 @@ def finite_close(gpu, ref, rtol=1e-5, atol=1e-5):
     ref = np.asarray(ref, np.float64)
     same_inf = np.isinf(gpu) & np.isinf(ref) & (np.sign(gpu) == np.sign(ref))
     ok = same_inf | (np.abs(gpu - ref) <= atol + rtol * np.abs(ref))
-    return bool(np.all(ok)), float(np.max(np.abs(np.where(same_inf, 0, gpu - ref))))
+    return bool(np.all(ok)), float(np.max(np.abs(np.where(same_inf, 0, gpu - ref)), initial=0.0))
 
 
 __all__ = ["Case", "build_case", "gpu_encode", "assert_encodings_equal", "check_set",

@@ -241,6 +241,37 @@ def test_index_full_scores_and_block_max_match_oracle():
         assert np.all(sc[b, 0, n:] == 12345.0) and np.all(bm[b, 0, rb.size:] == 12345.0)
 
 
+def test_index_full_long_chunks_ragged_rows():
+    """512 query rows of one sequence: the launch picks the longest chunk per
+    workgroup; visible lengths straddle chunk, prefetch-round and block edges."""
+    N, nq = 20000, 512
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((N, 128)).astype(np.float32)
+    kc, ks = oracle.quantize_rows(x)
+    q = synth.normal_bf16(synth.key(11, 8, 0, 0), 0, nq * 4096, 1 / np.sqrt(128)).reshape(1, nq, 32, 128)
+    w = synth.uniform_f32(synth.key(11, 9, 0, 0), 0, nq * 32).reshape(1, nq, 32)
+    edges = [1, 7, 8, 9, 511, 512, 513, 16383, 16384, 16385, 19999, 20000, 0, -3, 30000]
+    nv = rng.integers(1, N + 1, (1, nq)).astype(np.int32)
+    nv[0, :len(edges)] = edges
+    nblk = cdiv(N, 8)
+    bm = torch.full((1, nq, nblk), 12345.0, device=dev())
+    sc = torch.full((1, nq, N), 12345.0, device=dev())
+    L.index_full(t(q, torch.uint16), t(w), t(kc[None]), t(ks[None]), t(nv), bm, sc)
+    bm2 = torch.full((1, nq, nblk), 12345.0, device=dev())
+    L.index_full(t(q, torch.uint16), t(w), t(kc[None]), t(ks[None]), t(nv), bm2)
+    bm, sc, bm2 = bm.cpu().numpy()[0], sc.cpu().numpy()[0], bm2.cpu().numpy()[0]
+    assert np.array_equal(bm, bm2)  # with and without the score output
+    for i in list(range(len(edges))) + [100, 311, 511]:
+        n = int(min(max(nv[0, i], 0), N))
+        ref = oracle.index_scores(q[0, i], w[0, i], kc, ks, n)
+        ok, err = finite_close(sc[i, :n], ref)
+        assert ok, f"row {i} (n_visible {nv[0, i]}): max err {err}"
+        rb = oracle.block_max(ref, 8)
+        ok, err = finite_close(bm[i, :rb.size], rb)
+        assert ok, f"block max row {i}: max err {err}"
+        assert np.all(sc[i, n:] == 12345.0) and np.all(bm[i, rb.size:] == 12345.0)
+
+
 def test_index_pool_scores_bit_identical_to_scan():
     x, kc, ks, q, w, nv = _index_case(seed=1)
     B, N = kc.shape[0], kc.shape[1]
