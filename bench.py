@@ -36,15 +36,19 @@ METRIC = "CSA2 decode queries/sec per layer at 1M ctx; achieved HBM TB/s vs peak
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 PEAK_F16 = 2.5e15  # MI355X dense fp16 MFMA, flop/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_full_scan_1M_b16_traffic.txt")
-SCAN_SOURCE = os.path.join(ROOT, "kv_cache_decode_mxfp4_amd", "csrc", "indexer.hip")
+# what the scan kernel is compiled from: its source, the headers it includes and the
+# build script (flags); the traffic counters are valid only for this exact input
+SCAN_SOURCES = [os.path.join(ROOT, "kv_cache_decode_mxfp4_amd", *p) for p in (
+    ("csrc", "indexer.hip"), ("csrc", "device_common.h"), ("csrc", "launch.h"), ("build.py",))]
 CHUNK_ROWS = 1 << 18
+SCAN_EVENT_EVERY = 4
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4])
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="query rows of the oracle CPU baseline (0 = skip)")
@@ -193,8 +197,11 @@ def step_bytes(w: synth.Workload) -> int:
 
 
 def source_hash() -> str:
-    with open(SCAN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in SCAN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -290,8 +297,10 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for _ in range(args.steps):
-        step(time_scan=True)
+    # the scan's own duration comes from HIP events around it on every SCAN_EVENT_EVERY-th
+    # timed step (each event record costs the stream a few microseconds)
+    for i in range(args.steps):
+        step(time_scan=(i % SCAN_EVENT_EVERY == 0))
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)

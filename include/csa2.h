@@ -172,19 +172,19 @@ size_t csa2_topk_workspace(int64_t L, int32_t rows, int32_t k);
 /*
  * Sparse MLA attention ([N] 1: 64 heads x 512; [S]: K = V single-head MQA on
  * the 512-dim latent, top-k compressed entries plus 128 window entries).
- *   q          bf16 [B, nq, 64, 512].
+ *   q          bf16 [B, nq, 64, 512], 16-byte aligned.
  *   kv_codes   u8 [B, n_cap, 256], kv_scales u8 [B, n_cap, 32]: MXFP4 main KV.
  *   topk       int32 [B, nq, k]: entry ids; ids outside [0, n_cap) skipped.
  *   swa        u8 [B, swa_cap, 512] E4M3FN window rows; query (b, i) uses rows
  *              [max(0, swa_end[b,i] - n_win), min(swa_end[b,i], swa_cap)).
  *   softmax_scale  multiplies q . v before the softmax.
- *   out        fp32 [B, nq, 64, 512]: o_h = sum_j p_j v_j, p = softmax over the
+ *   out        fp32 [B, nq, 64, 512], 16-byte aligned: o_h = sum_j p_j v_j, p = softmax over the
  *              union of selected entries and window rows (one joint softmax);
  *              0 for an empty key set.
  *   lse        fp32 [B, nq, 64] or NULL: ln sum_j exp(l_j) (-inf if empty).
  *   ws         device workspace of csa2_sparse_attn_workspace(B, nq, k, n_win)
- *              bytes, or NULL (then the key set is not split across
- *              workgroups: correct, slower for small batches).
+ *              bytes (currently 0: every workgroup owns a slice of the output,
+ *              so nothing is combined across workgroups; NULL is accepted).
  * Dequantisation is exact in fp16; products accumulate in fp32.
  */
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq,

@@ -219,21 +219,16 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq, const uin
     REQUIRE(k == 0 || (topk && kv_codes && kv_scales), CSA2_ERR_INVALID_ARG,
             "sparse_attn: null top-k or KV cache");
     REQUIRE(swa_cap == 0 || swa != nullptr, CSA2_ERR_INVALID_ARG, "sparse_attn: null window");
-    REQUIRE(aligned(q, 16) && aligned(kv_codes, 16) && aligned(kv_scales, 4) && aligned(swa, 16),
-            CSA2_ERR_INVALID_ARG, "sparse_attn: misaligned q / kv / window pointer");
-    int32_t splits = csa2::attn_splits(queries, k, n_win);
+    REQUIRE(aligned(q, 16) && aligned(kv_codes, 16) && aligned(kv_scales, 4) && aligned(swa, 16) &&
+                aligned(out, 16),
+            CSA2_ERR_INVALID_ARG, "sparse_attn: misaligned q / kv / window / out pointer");
     const size_t need = csa2::attn_workspace(queries, k, n_win);
-    if (ws == nullptr) {
-        splits = 1;
-    } else {
-        REQUIRE(ws_bytes >= need, CSA2_ERR_WORKSPACE,
-                "sparse_attn: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-        REQUIRE(aligned(ws, 16), CSA2_ERR_INVALID_ARG, "sparse_attn: misaligned workspace");
-    }
+    REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
+            "sparse_attn: workspace of %zu bytes needed, %zu given", need, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_sparse_attn(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k,
                                            swa, swa_cap, swa_end, n_win, softmax_scale, out, lse,
-                                           ws, splits, s),
+                                           s),
                   s, "sparse_attn");
 }
 

@@ -4,332 +4,467 @@
 // 512-dim latent, top-k compressed entries plus 128 window entries).  One
 // joint softmax over both key sets; no de-duplication; no sink.
 //
-// Workgroup = 4 waves = (query row, group of 32 heads, split of the key list).
-// The key list is the k top-k slots followed by the window rows, cut into
-// tiles of 32 keys.  Per tile:
-//   1. every lane gathers its key's 128-channel slice (wave w owns channels
-//      [128w, 128w+128)), dequantises it in registers (exact in fp16) and
-//      stores it transposed to LDS (it is also V: K = V);
-//   2. S^T = K Q^T over the wave's channels (v_mfma_f32_32x32x16_f16,
-//      keys x heads); the four waves' partial sums meet in LDS and are added
-//      in a fixed order;
-//   3. online softmax per head in fp32 (exp2 domain); P is split into two
-//      fp16 terms (hi + lo) so P V keeps ~22 bits of P;
-//   4. O += P V with O = 32 heads x the wave's 128 dims in fp32 registers.
-// The S^T accumulator layout already is the A-operand layout of P for the
-// P V product once the 32 keys of a tile are taken in the order
-//   k-step u, lane half g, slot i  ->  key 16u + 8(i/4) + 4g + i%4,
-// which the B operand (V^T rows in LDS) follows.
-// With more than one split, partial (O, m, l) go to the workspace and a
-// combine kernel merges them in split order (deterministic).
+// Decomposition: one workgroup per (query row, group of 16 heads, slice of 128
+// output dims), 16 workgroups per query row, so the output needs no
+// cross-workgroup combine.  The key list (window rows first, then the top-k
+// slots) is cut into tiles of 32 keys; wave w of the 8 waves of the workgroup
+// takes every eighth tile and keeps its own online-softmax state, with no
+// barrier inside the loop.  Per tile and wave (MFMA v_mfma_f32_16x16x32_f16):
+//   S^T[32 keys x 16 heads] = K Q^T: lane l holds key l%16 of each block of 16
+//     keys and the 128 channels [128G, 128G+128) of its lane group G = l/16
+//     (k-step t: channels 128G + 8t .. +8, the same on the Q^T operand, which
+//     is read from LDS).  Keys are dequantised in registers straight into the
+//     A operand (exact in fp16); the lanes whose group G is the workgroup's
+//     output slice also store their 128 channels, row-major, to the wave's LDS
+//     tile (K = V).
+//   P^T: the S^T accumulator of lane l holds keys 4G + r (r < 4) of both
+//     blocks for head l%16, which is the B-operand layout of P^T for
+//     O^T = V^T P^T once the 32 keys of a tile take MFMA k-index 8G + i <->
+//     key 16*(i/4) + 4G + i%4.  P is split into two fp16 terms (hi + lo) so
+//     the product keeps ~22 bits of P.
+//   V^T[16 dims x 32 keys]: read from the row-major LDS tile with the gfx950
+//     transposing read ds_read_b64_tr_b16 (within each 16-lane group, lane
+//     4a + j receives element j of lanes a, a+4, a+8, a+12), two reads per
+//     MFMA, in the same key order.
+// At the end the waves' (O, max, sum) meet in LDS and are merged in wave
+// order (deterministic); every workgroup of a query row computes the same
+// scores, so the 16 workgroups agree on the normalisation.
+//
+// Loads: a wave loads the top-k indices and then the keys of kChunkTiles
+// tiles at once (with 8 waves this covers k = 512 plus the window in one
+// chunk), issued before Q is staged together with the wave's first window
+// tile, so the index -> key dependency and the Q load overlap.  Loads are
+// unconditional (clamped inside the list, masked afterwards).
 #include "device_common.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kAttnWaves = 4;
-constexpr int kTile = 32;
-constexpr int kVtStride = 36;  // halves per V^T row: 32 keys + pad (bank spread, 8-byte aligned)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((vector_size(8)));  // operand type of the LDS transposing read
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+
+#ifndef CSA2_ATTN_WAVES
+#define CSA2_ATTN_WAVES 8
+#endif
+constexpr int kAttnWaves = CSA2_ATTN_WAVES;
+constexpr int kTile = 32;                       // keys per tile (two MFMA blocks of 16)
+constexpr int kHg = 16;                         // heads per workgroup
+constexpr int kSlice = 128;                     // output dims per workgroup
+constexpr int kGroups = kHeads / kHg;           // 4 head groups
+constexpr int kSlices = kDim / kSlice;          // 4 output slices
+constexpr int kWgPerRow = kGroups * kSlices;    // 16 workgroups per query row
+constexpr int kQRow = kDim + 8;                 // halves per LDS row of Q (bank spread)
+constexpr int kVRow = kSlice + 16;              // halves per LDS row of V (288 B)
+constexpr int kChunkTiles = 2;                  // top-k tiles per wave loaded together
+constexpr int kXcds = 8;                        // MI355X dies: workgroups go round-robin
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct AttnSmem {
-    _Float16 vt[kDim * kVtStride];
-    float sx[kAttnWaves][16][kWave];
+    _Float16 q[kHg][kQRow];
+    union {
+        _Float16 v[kAttnWaves][kTile][kVRow];
+        struct {
+            float o[kAttnWaves][kHg][kSlice + 4];
+            float m[kAttnWaves][kHg];
+            float l[kAttnWaves][kHg];
+        } red;
+    } u;
 };
 
+// Raw bytes of one top-k tile for the calling lane: channels [128G, 128G+128)
+// of key l%16 of block b (64 code bytes, 8 scale bytes) and whether the key
+// is valid.
+struct MainRaw {
+    u32x4 c[2][4];
+    uint32_t s[2][2];
+    uint32_t valid;  // bit b: key of block b is valid
+};
+
+__device__ __forceinline__ half8 q_operand(const AttnSmem& sm, int head, int G, int t)
+{
+    return *reinterpret_cast<const half8*>(&sm.q[head][kSlice * G + 8 * t]);
+}
+
+__device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Online-softmax state of one wave: lane l tracks head l%16 (replicated over
+// the four lane groups, which always agree bit for bit).
+struct Online {
+    float m = -INFINITY;   // running max (log2 domain)
+    float l = 0.0f;        // running sum
+    f32x4 o[kSlice / 16];  // O^T: dims 16*db + 4G + r of the slice, head l%16
+};
+
+// Folds one tile's S^T (already scaled, -inf for invalid keys) into the state
+// and accumulates P V over the wave's LDS tile.
+__device__ __forceinline__ void fold_tile(Online& st, const f32x4 (&s)[2],
+                                          const _Float16* __restrict__ vtile, int lane)
+{
+    const int G = lane >> 4;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            tmax = fmaxf(tmax, s[b][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(st.m, tmax);
+    float p[2][4];
+    float psum = 0.0f;
+    float alpha = 1.0f;
+    if (m_new == -INFINITY) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                p[b][r] = 0.0f;
+    } else {
+        alpha = exp2f(st.m - m_new);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[b][r] = exp2f(s[b][r] - m_new);
+                psum += p[b][r];
+            }
+    }
+    psum += __shfl_xor(psum, 16, kWave);
+    psum += __shfl_xor(psum, 32, kWave);
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int db = 0; db < kSlice / 16; ++db)
+        st.o[db] *= alpha;
+
+    half8 phi, plo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float pv = p[i / 4][i % 4];
+        phi[i] = (_Float16)pv;
+        plo[i] = (_Float16)(pv - (float)phi[i]);
+    }
+    // source lane 16G + 4i' + a points at key 4G + i' (block 0) or 16 + 4G + i'
+    // (block 1), dims 16*db + 4a .. +4 of the slice
+    const int src_key = 4 * G + ((lane & 15) >> 2);
+    const int src_dim = 4 * (lane & 3);
+#pragma unroll
+    for (int db = 0; db < kSlice / 16; ++db) {
+        const _Float16* p0 = vtile + src_key * kVRow + 16 * db + src_dim;
+        const _Float16* p1 = p0 + 16 * kVRow;
+        const half4v lo =
+            __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)p0));
+        const half4v hi =
+            __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)p1));
+        const half8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.o[db] = mfma16(a, phi, st.o[db]);
+        st.o[db] = mfma16(a, plo, st.o[db]);
+    }
+}
+
+// S^T of one tile to the log2 domain, -inf for invalid keys (bit b of `valid`
+// tells whether this lane's key of block b is valid).
+__device__ __forceinline__ void scale_scores(f32x4 (&s)[2], uint32_t valid, float scale_log2,
+                                             int G)
+{
+    const uint64_t vm0 = __ballot((valid & 1u) != 0u);
+    const uint64_t vm1 = __ballot((valid & 2u) != 0u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int kk = 4 * G + r;
+        s[0][r] = ((vm0 >> kk) & 1ull) ? s[0][r] * scale_log2 : -INFINITY;
+        s[1][r] = ((vm1 >> kk) & 1ull) ? s[1][r] * scale_log2 : -INFINITY;
+    }
+}
+
 __global__ void __launch_bounds__(kAttnWaves * kWave)
-sparse_attn_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_codes,
-                   const uint8_t* __restrict__ kv_scales, int64_t n_cap, int32_t nq,
-                   const int32_t* __restrict__ topk, int32_t k, const uint8_t* __restrict__ swa,
-                   int32_t swa_cap, const int32_t* __restrict__ swa_end, int32_t n_win,
-                   float scale_log2, int32_t splits, float* __restrict__ out,
-                   float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_m,
-                   float* __restrict__ ws_l)
+sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
+                   const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
+                   int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
+                   const uint8_t* __restrict__ swa, int32_t swa_cap,
+                   const int32_t* __restrict__ swa_end, int32_t n_win, float scale_log2,
+                   float* __restrict__ out, float* __restrict__ lse)
 {
     __shared__ AttnSmem sm;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int g = lane >> 5;
-    const int col = lane & 31;
-    const int64_t qrow = blockIdx.x / (2 * splits);
-    const int hg = (blockIdx.x / splits) % 2;
-    const int sp = blockIdx.x % splits;
+    // wave index as a scalar: everything derived from it (tile lists, counts,
+    // pointer choices) stays in scalar registers and branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = lane >> 4;
+    const int key16 = lane & 15;
+
+    // the 16 workgroups of a query row share one die (and its L2): with
+    // round-robin dispatch, workgroup x runs on die x % 8
+    const int64_t x = blockIdx.x;
+    const int64_t rest = x / kXcds;
+    const int64_t qrow = kXcds * (rest / kWgPerRow) + x % kXcds;
+    const int part = (int)(rest % kWgPerRow);
+    if (qrow >= queries)
+        return;
+    const int hg = part / kSlices;     // head group
+    const int slice = part % kSlices;  // output dims [128*slice, +128)
     const int64_t b = qrow / nq;
 
+    // window rows [lo, hi) and tile counts
     int64_t end = swa_end[qrow];
     int64_t lo = end - n_win;
     lo = lo < 0 ? 0 : lo;
     int64_t hi = end < swa_cap ? end : (int64_t)swa_cap;
     hi = hi < lo ? lo : hi;
-    const int64_t n_sw = hi - lo;
-    const int64_t t_main = (k + kTile - 1) / kTile;
-    const int64_t t_all = t_main + (n_sw + kTile - 1) / kTile;
-    const int64_t t0 = sp * t_all / splits;
-    const int64_t t1 = (sp + 1) * t_all / splits;
+    const int n_sw = (int)(hi - lo);
+    const int t_sw = (n_sw + kTile - 1) / kTile;
+    const int t_main = (k + kTile - 1) / kTile;
+    // this wave's tiles: list positions wave + 8j over [window tiles, top-k tiles]
+    int m_first = (wave - t_sw) % kAttnWaves;
+    m_first = m_first < 0 ? m_first + kAttnWaves : m_first;
+    const int nm = (n_cap > 0 && m_first < t_main) ? (t_main - m_first + kAttnWaves - 1) / kAttnWaves : 0;
 
-    // B operand of S^T = K Q^T: head 32*hg + col, dims 128*wave + 64*g + 8t + i
-    half8 qb[8];
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(
-            q + (qrow * kHeads + 32 * hg + col) * kDim + 128 * wave + 64 * g);
+    // loads that have no data to fetch (no top-k tile, no window tile for this
+    // wave) read the query row instead (64 KiB, always valid) and are masked,
+    // so every load is unconditional and the load counter stays exact
+    const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + qrow * kHeads * kDim);
+    const bool have_main = nm > 0;
+    const uint8_t* kc = have_main ? kv_codes + b * n_cap * (kDim / 2) : dummy;
+    const uint8_t* ks = have_main ? kv_scales + b * n_cap * (kDim / 16) : dummy;
+    const uint8_t* sw = n_sw > 0 ? swa + b * (int64_t)swa_cap * kDim : dummy;
+    const int32_t* tk = have_main ? topk + qrow * k : reinterpret_cast<const int32_t*>(dummy);
+
+    // index of this lane's key in block bb of main tile j of this wave (-1 if
+    // none); j is clamped to the wave's last tile so the load is always valid
+    auto load_idx = [&](int j, int32_t (&e)[2]) {
+        const int jj = j < nm ? j : nm - 1;
+        const int tile = m_first + kAttnWaves * jj;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const uint4 v = src[t];
-            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qb[t][2 * i] = bf16_to_f16((uint16_t)(d[i] & 0xFFFFu));
-                qb[t][2 * i + 1] = bf16_to_f16((uint16_t)(d[i] >> 16));
-            }
+        for (int bb = 0; bb < 2; ++bb) {
+            const int slot = tile * kTile + 16 * bb + key16;
+            e[bb] = tk[have_main ? (slot < k ? slot : k - 1) : 0];
         }
-    }
-
-    const uint8_t* kc = kv_codes + b * n_cap * (kDim / 2);
-    const uint8_t* ks = kv_scales + b * n_cap * (kDim / 16);
-    const uint8_t* sw = swa + b * (int64_t)swa_cap * kDim;
-    const int32_t* tk = topk + qrow * k;
-
-    float m_run = -INFINITY;  // per head col (log2 domain)
-    float l_run = 0.0f;
-    f32x16 o[4];
+    };
+    // whether slot 16*bb + l%16 of main tile j of this wave is inside the list
+    auto in_list = [&](int j, int bb) {
+        const int jj = j < nm ? j : nm - 1;
+        return (m_first + kAttnWaves * jj) * kTile + 16 * bb + key16 < k;
+    };
+    auto load_main = [&](int j, const int32_t (&e)[2], MainRaw& R) {
+        R.valid = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-        o[c] = f32x16{};
-
-    for (int64_t tile = t0; tile < t1; ++tile) {
-        // ---- gather + dequantise this lane's key slice
-        half8 kv[8];
-        bool valid = false;
-        const int64_t slot = tile * kTile + col;
-        if (tile < t_main) {
-            int64_t e = slot < k ? (int64_t)tk[slot] : -1;
-            valid = e >= 0 && e < n_cap;
-            if (valid) {
-                const uint4* c = reinterpret_cast<const uint4*>(kc + e * (kDim / 2) + 64 * wave + 32 * g);
-                const uint4 c0 = c[0], c1 = c[1];
-                const uint32_t sc =
-                    *reinterpret_cast<const uint32_t*>(ks + e * (kDim / 16) + 8 * wave + 4 * g);
-                const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        for (int bb = 0; bb < 2; ++bb) {
+            const bool ok = have_main && in_list(j, bb) && e[bb] >= 0 && e[bb] < n_cap;
+            const int64_t ee = ok ? e[bb] : 0;
+            const u32x4* c = reinterpret_cast<const u32x4*>(kc + ee * (kDim / 2) + 64 * G);
+            const uint32_t* s = reinterpret_cast<const uint32_t*>(ks + ee * (kDim / 16) + 8 * G);
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    kv[t] = dequant8_fp4(words[t], e4m3_byte_to_f16(sc, t / 2));
-            }
-        } else {
-            const int64_t r = lo + (slot - t_main * kTile);
-            valid = r < hi;
-            if (valid) {
-                const uint4* c = reinterpret_cast<const uint4*>(sw + r * kDim + 128 * wave + 64 * g);
-#pragma unroll
-                for (int t4 = 0; t4 < 4; ++t4) {
-                    const uint4 v = c[t4];
-                    const half4v a0 = e4m3x4_to_f16(v.x), a1 = e4m3x4_to_f16(v.y);
-                    const half4v a2 = e4m3x4_to_f16(v.z), a3 = e4m3x4_to_f16(v.w);
-                    kv[2 * t4] = half8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                    kv[2 * t4 + 1] = half8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-                }
-            }
+            for (int i = 0; i < 4; ++i)
+                R.c[bb][i] = c[i];
+            R.s[bb][0] = s[0];
+            R.s[bb][1] = s[1];
+            R.valid |= ok ? (1u << bb) : 0u;
         }
-        if (!valid) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                kv[t] = half8{};
-        }
-        const uint64_t vmask = __ballot(valid);
+    };
 
-        // ---- S^T partial over this wave's channels; V^T to LDS
-        f32x16 acc = {};
+    // window tile ts of this wave: raw FP8 bytes of key l%16 of both blocks
+    auto load_swa = [&](int ts, u32x4 (&raw)[2][8], uint32_t& valid) {
+        valid = 0;
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv[t], qb[t], acc, 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int d0 = 128 * wave + 64 * g + 8 * t;
+        for (int bb = 0; bb < 2; ++bb) {
+            const int64_t r = lo + ts * kTile + 16 * bb + key16;
+            const bool ok = ts < t_sw && r < hi;
+            const int64_t rr = ok ? r : (n_sw > 0 ? lo : 0);
+            const u32x4* c = reinterpret_cast<const u32x4*>(sw + rr * kDim + kSlice * G);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                sm.vt[(d0 + i) * kVtStride + col] = kv[t][i];
+                raw[bb][i] = c[i];
+            valid |= ok ? (1u << bb) : 0u;
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            sm.sx[wave][r][lane] = acc[r];
-        __syncthreads();
+    };
 
-        // ---- full S^T (fixed order over waves), online softmax per head col
-        float s[16];
-        float tmax = -INFINITY;
+    // ---- prologue: every load of the first top-k chunk and of the first window
+    // tile is issued before Q is staged, so their latencies overlap
+    int32_t e[kChunkTiles][2];
+    MainRaw R[kChunkTiles];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float v = ((sm.sx[0][r][lane] + sm.sx[1][r][lane]) + sm.sx[2][r][lane]) +
-                            sm.sx[3][r][lane];
-            const int kr = 8 * (r / 4) + 4 * g + (r % 4);
-            s[r] = ((vmask >> kr) & 1ull) ? v * scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, s[r]);
+    for (int u = 0; u < kChunkTiles; ++u)
+        load_idx(u, e[u]);
+    // kQPer dims of one head per thread
+    constexpr int kQPer = kHg * kDim / (kAttnWaves * kWave);
+    constexpr int kThreadsPerHead = kDim / kQPer;
+    const int qh = threadIdx.x / kThreadsPerHead;
+    const int qd0 = kQPer * (threadIdx.x % kThreadsPerHead);
+    uint4 qraw[kQPer / 8];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(
+            q + (qrow * kHeads + kHg * hg + qh) * kDim + qd0);
+#pragma unroll
+        for (int i = 0; i < kQPer / 8; ++i)
+            qraw[i] = src[i];
+    }
+    u32x4 swraw[2][8];
+    uint32_t swvalid = 0;
+    load_swa(wave, swraw, swvalid);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kQPer / 8; ++i) {
+        const uint32_t d[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+        half8 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16_to_f16((uint16_t)(d[j] & 0xFFFFu));
+            v[2 * j + 1] = bf16_to_f16((uint16_t)(d[j] >> 16));
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        const float m_new = fmaxf(m_run, tmax);
-        float alpha = 1.0f;
-        float psum = 0.0f;
-        float p[16];
-        if (m_new == -INFINITY) {
+        *reinterpret_cast<half8*>(&sm.q[qh][qd0 + 8 * i]) = v;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                p[r] = 0.0f;
-        } else {
-            alpha = exp2f(m_run - m_new);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = exp2f(s[r] - m_new);
-                psum += p[r];
-            }
-        }
-        psum = psum + __shfl_xor(psum, 32, kWave);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+    for (int u = 0; u < kChunkTiles; ++u)
+        load_main(u, e[u], R[u]);
+    __syncthreads();
 
-        // ---- rescale O rows (heads) and accumulate P V
+    Online st;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float ar = __shfl(alpha, 8 * (r / 4) + 4 * g + (r % 4), kWave);
+    for (int db = 0; db < kSlice / 16; ++db)
+        st.o[db] = f32x4{};
+    _Float16* vtile = &sm.u.v[wave][0][0];
+    const bool writer = G == slice;
+
+    // ---- window tiles (FP8 rows, no scale)
+    for (int ts = wave; ts < t_sw; ts += kAttnWaves) {
+        if (ts != wave)
+            load_swa(ts, swraw, swvalid);
+        const uint32_t valid = swvalid;
+        u32x4 (&raw)[2][8] = swraw;
+        f32x4 s[2];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                o[c][r] *= ar;
-        }
-        half8 phi[2], plo[2];
+        for (int bb = 0; bb < 2; ++bb) {
+            f32x4 acc = {};
+            const bool ok = (valid >> bb) & 1u;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float pv = p[8 * u + i];
-                const _Float16 h = (_Float16)pv;
-                phi[u][i] = h;
-                plo[u][i] = (_Float16)(pv - (float)h);
+            for (int t = 0; t < 16; ++t) {
+                const uint32_t w0 = ok ? raw[bb][t / 2][2 * (t % 2)] : 0u;
+                const uint32_t w1 = ok ? raw[bb][t / 2][2 * (t % 2) + 1] : 0u;
+                const half4v x0 = e4m3x4_to_f16(w0), x1 = e4m3x4_to_f16(w1);
+                const half8 a = half8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                acc = mfma16(a, q_operand(sm, key16, G, t), acc);
+                if (writer)
+                    *reinterpret_cast<half8*>(vtile + (16 * bb + key16) * kVRow + 8 * t) = a;
             }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int dim = 128 * wave + 32 * c + col;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const _Float16* rowp = sm.vt + dim * kVtStride + 16 * u + 4 * g;
-                const half4v v0 = *reinterpret_cast<const half4v*>(rowp);
-                const half4v v1 = *reinterpret_cast<const half4v*>(rowp + 8);
-                const half8 vb = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                o[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(phi[u], vb, o[c], 0, 0, 0);
-                o[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(plo[u], vb, o[c], 0, 0, 0);
-            }
+            s[bb] = acc;
         }
-        __syncthreads();
+        scale_scores(s, valid, scale_log2, G);
+        fold_tile(st, s, vtile, lane);
     }
 
-    // ---- epilogue: rows of O are heads 8(r/4) + 4g + r%4 of the group
-    const int64_t head0 = qrow * kHeads + 32 * hg;
-    if (splits == 1) {
+    // ---- top-k tiles, a chunk of kChunkTiles at a time (all loads of a chunk in flight together)
+    auto main_tile = [&](const MainRaw& R) {
+        f32x4 s[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int hr = 8 * (r / 4) + 4 * g + (r % 4);
-            const float lr = __shfl(l_run, hr, kWave);
-            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+        for (int bb = 0; bb < 2; ++bb) {
+            f32x4 acc = {};
+            const bool ok = (R.valid >> bb) & 1u;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                out[(head0 + hr) * kDim + 128 * wave + 32 * c + col] = o[c][r] * inv;
+            for (int t = 0; t < 16; ++t) {
+                const uint32_t word = ok ? R.c[bb][t / 4][t % 4] : 0u;
+                const uint32_t sc = ok ? R.s[bb][t / 8] : 0u;
+                const half8 a = dequant8_fp4(word, e4m3_byte_to_f16(sc, (t / 2) % 4));
+                acc = mfma16(a, q_operand(sm, key16, G, t), acc);
+                if (writer)
+                    *reinterpret_cast<half8*>(vtile + (16 * bb + key16) * kVRow + 8 * t) = a;
+            }
+            s[bb] = acc;
         }
-        if (lse != nullptr && wave == 0 && lane < 32)
-            lse[head0 + col] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-    } else {
-        const int64_t part = (qrow * 2 + hg) * splits + sp;  // [Q, 2, splits] x 32 heads
+        scale_scores(s, R.valid, scale_log2, G);
+        fold_tile(st, s, vtile, lane);
+    };
+    for (int c = 0; c * kChunkTiles < nm; ++c) {
+        if (c > 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int hr = 8 * (r / 4) + 4 * g + (r % 4);
+            for (int u = 0; u < kChunkTiles; ++u)
+                load_idx(c * kChunkTiles + u, e[u]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                ws_o[(part * 32 + hr) * kDim + 128 * wave + 32 * c + col] = o[c][r];
+            for (int u = 0; u < kChunkTiles; ++u)
+                load_main(c * kChunkTiles + u, e[u], R[u]);
         }
-        if (wave == 0 && lane < 32) {
-            ws_m[part * 32 + col] = m_run;
-            ws_l[part * 32 + col] = l_run;
-        }
+#pragma unroll
+        for (int u = 0; u < kChunkTiles; ++u)
+            if (c * kChunkTiles + u < nm)
+                main_tile(R[u]);
     }
-}
 
-// Merge the per-split partials of one (query row, head): thread per output dim.
-__global__ void __launch_bounds__(256)
-attn_combine_kernel(int64_t total, int32_t splits, const float* __restrict__ ws_o,
-                    const float* __restrict__ ws_m, const float* __restrict__ ws_l,
-                    float* __restrict__ out, float* __restrict__ lse)
-{
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= total)
-        return;
-    const int64_t head = t / kDim;           // qrow * 64 + h
-    const int dim = (int)(t % kDim);
-    const int64_t qrow = head / kHeads;
-    const int h = (int)(head % kHeads);
-    const int hg = h / 32, hl = h % 32;
-    const int64_t base = (qrow * 2 + hg) * splits;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s)
-        M = fmaxf(M, ws_m[(base + s) * 32 + hl]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < splits; ++s) {
-            const float ms = ws_m[(base + s) * 32 + hl];
-            const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-            num += f * ws_o[((base + s) * 32 + hl) * kDim + dim];
-            den += f * ws_l[(base + s) * 32 + hl];
-        }
+    // ---- merge the waves in LDS (wave order), write the slice
+    __syncthreads();  // every wave is done with its V tile (aliased below)
+#pragma unroll
+    for (int db = 0; db < kSlice / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sm.u.red.o[wave][key16][16 * db + 4 * G + r] = st.o[db][r];
+    if (G == 0) {
+        sm.u.red.m[wave][key16] = st.m;
+        sm.u.red.l[wave][key16] = st.l;
     }
-    out[t] = den > 0.0f ? num / den : 0.0f;
-    if (lse != nullptr && dim == 0)
-        lse[head] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    __syncthreads();
+    {
+        constexpr int kOPer = kHg * kSlice / (kAttnWaves * kWave);  // dims per thread
+        constexpr int kThreadsPerHead = kSlice / kOPer;
+        const int t = threadIdx.x;
+        const int h = t / kThreadsPerHead;      // head within the group
+        const int d0 = kOPer * (t % kThreadsPerHead);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w)
+            M = fmaxf(M, sm.u.red.m[w][h]);
+        float f[kAttnWaves];
+        float den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+            const float mw = sm.u.red.m[w][h];
+            f[w] = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+            den += f[w] * sm.u.red.l[w][h];
+        }
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        float res[kOPer];
+#pragma unroll
+        for (int i = 0; i < kOPer; ++i) {
+            float num = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w)
+                num += f[w] * sm.u.red.o[w][h][d0 + i];
+            res[i] = num * inv;
+        }
+        float4* dst = reinterpret_cast<float4*>(
+            out + (qrow * kHeads + kHg * hg + h) * kDim + kSlice * slice + d0);
+#pragma unroll
+        for (int i = 0; i < kOPer / 4; ++i)
+            dst[i] = make_float4(res[4 * i], res[4 * i + 1], res[4 * i + 2], res[4 * i + 3]);
+        if (lse != nullptr && slice == 0 && t % kThreadsPerHead == 0)
+            lse[qrow * kHeads + kHg * hg + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    }
 }
 
 }  // namespace
 
-int32_t attn_splits(int32_t queries, int32_t k, int32_t n_win)
+size_t attn_workspace(int32_t, int32_t, int32_t)
 {
-    const int64_t tiles = (int64_t)(k + kTile - 1) / kTile + (n_win + kTile - 1) / kTile;
-    const int64_t wgs = 2ll * queries;
-    int64_t s = (512 + wgs - 1) / wgs;  // aim for >= 512 workgroups
-    const int64_t cap = (tiles + 1) / 2;  // at least two tiles per split
-    s = s > cap ? cap : s;
-    return (int32_t)(s < 1 ? 1 : s);
-}
-
-size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win)
-{
-    const int32_t s = attn_splits(queries, k, n_win);
-    if (s <= 1)
-        return 0;
-    return (size_t)queries * 2 * s * 32 * (kDim + 2) * sizeof(float);
+    return 0;
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t n_cap,
                               const int32_t* topk, int32_t k, const uint8_t* swa,
                               int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
-                              float softmax_scale, float* out, float* lse, void* ws,
-                              int32_t splits, hipStream_t stream)
+                              float softmax_scale, float* out, float* lse, hipStream_t stream)
 {
     if (queries == 0)
         return hipSuccess;
-    float* ws_o = nullptr;
-    float* ws_m = nullptr;
-    float* ws_l = nullptr;
-    if (splits > 1) {
-        const size_t parts = (size_t)queries * 2 * splits * 32;
-        ws_o = static_cast<float*>(ws);
-        ws_m = ws_o + parts * kDim;
-        ws_l = ws_m + parts;
-    }
-    const int64_t grid = (int64_t)queries * 2 * splits;
+    // rows padded to a multiple of the die count (padding workgroups exit at once)
+    const int64_t rows = ((int64_t)queries + kXcds - 1) / kXcds * kXcds;
+    const int64_t grid = rows * kWgPerRow;
     sparse_attn_kernel<<<dim3((uint32_t)grid), dim3(kAttnWaves * kWave), 0, stream>>>(
-        q, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
-        softmax_scale * kLog2e, splits, out, lse, ws_o, ws_m, ws_l);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1)
-        return e;
-    const int64_t total = (int64_t)queries * kHeads * kDim;
-    attn_combine_kernel<<<dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream>>>(
-        total, splits, ws_o, ws_m, ws_l, out, lse);
+        q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
+        softmax_scale * kLog2e, out, lse);
     return hipGetLastError();
 }
 

@@ -40,13 +40,11 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
                        const int32_t* n_valid, int32_t k, int32_t* out, void* ws,
                        hipStream_t stream);
 
-int32_t attn_splits(int32_t queries, int32_t k, int32_t n_win);
 size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win);
 hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t n_cap,
                               const int32_t* topk, int32_t k, const uint8_t* swa,
                               int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
-                              float softmax_scale, float* out, float* lse, void* ws,
-                              int32_t splits, hipStream_t stream);
+                              float softmax_scale, float* out, float* lse, hipStream_t stream);
 
 }  // namespace csa2

@@ -48,7 +48,7 @@ def test_version_and_workspace_queries():
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
     assert lib.csa2_topk_workspace(100, 1, 0) == 0
     assert lib.csa2_sparse_attn_workspace(4096, 1, 512, 128) == 0
-    assert lib.csa2_sparse_attn_workspace(16, 1, 512, 128) > 0
+    assert lib.csa2_sparse_attn_workspace(16, 1, 512, 128) == 0  # no split-K scratch
 
 
 def _status(fn, *args):
@@ -82,10 +82,10 @@ def test_host_validation_rejects_bad_arguments():
     # a long row needs a workspace
     st, msg = _status("csa2_topk", vp, None, 131072, 1, None, 512, vp, None, 0, None)
     assert st == 3 and "workspace" in msg
-    # attention workspace too small
+    # misaligned output pointer
     st, msg = _status("csa2_sparse_attn", vp, 16, 1, vp, vp, 100, vp, 512, vp, 128, vp, 128,
-                      ctypes.c_float(1.0), vp, None, vp, 8, None)
-    assert st == 3
+                      ctypes.c_float(1.0), ctypes.c_void_p(4100), None, None, 0, None)
+    assert st == 1 and "misaligned" in msg
     # misaligned query pointer
     st, msg = _status("csa2_sparse_attn", ctypes.c_void_p(18), 1, 1, vp, vp, 100, vp, 4, vp, 128,
                       vp, 128, ctypes.c_float(1.0), vp, None, None, 0, None)
