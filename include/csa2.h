@@ -66,7 +66,7 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 101. */
 int32_t csa2_version(void);
 
 /*
@@ -194,6 +194,35 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq,
                              int32_t n_win, float softmax_scale, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_workspace(int32_t B, int32_t nq, int32_t k, int32_t n_win);
+
+/*
+ * Sparse MLA attention with the output epilogue of the deployment kernel
+ * ([S] "DeepSeek-V4 model structure (7)", sequence dimension: the output is
+ * rotated back to restore relative position; [N] 4, inference side: the
+ * fused RoPE-attention-RoPE-cast kernel).  Same inputs and attention as
+ * csa2_sparse_attn; then, per query row r and head, each pair of output
+ * channels (a, b) = (o[off+2i], o[off+2i+1]), i < rope_dim/2, is rotated by
+ * minus the query position's angle:
+ *     a' = a*c + b*s,  b' = b*c - a*s   (c = rope_cos[r, i], s = rope_sin[r, i],
+ *                                        every product and sum rounded to fp32)
+ * and every channel is cast to bf16 (round to nearest even).
+ *   rope_cos, rope_sin  fp32 [B*nq, rope_dim/2]: the query's own position
+ *              (the table the query's rotary part was built with); NULL when
+ *              rope_dim == 0.  rope_offset, rope_dim even, offset + dim <= 512
+ *              (main latent: 448, 64).
+ *   out        bf16 [B, nq, 64, 512] as uint16_t bit patterns, 8-byte aligned.
+ *   lse        as csa2_sparse_attn (natural log of the softmax denominator,
+ *              the statistic a split-KV combine needs), or NULL.
+ */
+csa2_status csa2_sparse_attn_rope_bf16(const uint16_t* q, int32_t B, int32_t nq,
+                                       const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                       int64_t n_cap, const int32_t* topk, int32_t k,
+                                       const uint8_t* swa, int32_t swa_cap,
+                                       const int32_t* swa_end, int32_t n_win,
+                                       float softmax_scale, const float* rope_cos,
+                                       const float* rope_sin, int32_t rope_offset,
+                                       int32_t rope_dim, uint16_t* out, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_UNSUPPORTED",
 
 EXPORTS = ("csa2_last_error", "csa2_version", "csa2_quantize_kv", "csa2_quantize_swa",
            "csa2_index_full", "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
-           "csa2_sparse_attn", "csa2_sparse_attn_workspace")
+           "csa2_sparse_attn", "csa2_sparse_attn_workspace", "csa2_sparse_attn_rope_bf16")
 
 
 class Csa2Error(RuntimeError):
@@ -66,6 +66,9 @@ def load() -> ctypes.CDLL:
                                    vp, vp, vp, sz, vp]
     L.csa2_sparse_attn_workspace.restype = sz
     L.csa2_sparse_attn_workspace.argtypes = [i32, i32, i32, i32]
+    L.csa2_sparse_attn_rope_bf16.restype = st
+    L.csa2_sparse_attn_rope_bf16.argtypes = [vp, i32, i32, vp, vp, i64, vp, i32, vp, i32, vp, i32,
+                                             f32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -190,3 +193,20 @@ def sparse_attn(q, kv_codes, kv_scales, topk_idx, swa, swa_end, out, lse=None, n
         _p(q), B, nq, _p(kv_codes), _p(kv_scales), n_cap, _p(topk_idx), k, _p(swa),
         swa.shape[1], _p(swa_end), n_win, float(softmax_scale), _p(out), _p(lse), _p(ws),
         ws_bytes, _stream(stream)))
+
+
+def sparse_attn_rope_bf16(q, kv_codes, kv_scales, topk_idx, swa, swa_end, rope_cos, rope_sin,
+                          out, lse=None, n_win=128, softmax_scale=1.0, rope_offset=448,
+                          rope_dim=64, ws=None, stream=None):
+    """Attention with the inverse-rotary + bf16 epilogue; out is bf16 (or its uint16 bits)."""
+    q = _bf16_bits(q)
+    _dt(topk_idx, torch.int32, "topk")
+    out = _bf16_bits(out)
+    B, nq = q.shape[0], q.shape[1]
+    n_cap = kv_codes.shape[1]
+    k = topk_idx.shape[-1]
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("csa2_sparse_attn_rope_bf16", load().csa2_sparse_attn_rope_bf16(
+        _p(q), B, nq, _p(kv_codes), _p(kv_scales), n_cap, _p(topk_idx), k, _p(swa),
+        swa.shape[1], _p(swa_end), n_win, float(softmax_scale), _p(rope_cos), _p(rope_sin),
+        rope_offset, rope_dim, _p(out), _p(lse), _p(ws), ws_bytes, _stream(stream)))

@@ -62,7 +62,7 @@ const char* csa2_last_error(void)
 
 int32_t csa2_version(void)
 {
-    return 100;
+    return 101;
 }
 
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
@@ -201,35 +201,76 @@ size_t csa2_sparse_attn_workspace(int32_t B, int32_t nq, int32_t k, int32_t n_wi
     return csa2::attn_workspace(B * nq, k, n_win);
 }
 
+static csa2_status attn_common(const uint16_t* q, int32_t B, int32_t nq,
+                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t n_cap,
+                               const int32_t* topk, int32_t k, const uint8_t* swa,
+                               int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
+                               float softmax_scale, float* out, uint16_t* out_bf16,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_offset,
+                               int32_t rope_dim, float* lse, void* ws, size_t ws_bytes,
+                               void* stream, const char* name)
+{
+    REQUIRE(B >= 0 && nq >= 0 && n_cap >= 0 && k >= 0 && swa_cap >= 0 && n_win >= 0,
+            CSA2_ERR_INVALID_ARG, "%s: negative size", name);
+    REQUIRE((int64_t)B * nq <= (1ll << 24), CSA2_ERR_INVALID_ARG, "%s: too many query rows", name);
+    REQUIRE(k <= 65536 && n_win <= 65536, CSA2_ERR_UNSUPPORTED, "%s: k or n_win too large", name);
+    const int32_t queries = B * nq;
+    if (queries == 0)
+        return CSA2_OK;
+    REQUIRE(q && (out || out_bf16) && swa_end, CSA2_ERR_INVALID_ARG, "%s: null pointer", name);
+    REQUIRE(k == 0 || (topk && kv_codes && kv_scales), CSA2_ERR_INVALID_ARG,
+            "%s: null top-k or KV cache", name);
+    REQUIRE(swa_cap == 0 || swa != nullptr, CSA2_ERR_INVALID_ARG, "%s: null window", name);
+    REQUIRE(aligned(q, 16) && aligned(kv_codes, 16) && aligned(kv_scales, 4) && aligned(swa, 16) &&
+                aligned(out, 16) && aligned(out_bf16, 8),
+            CSA2_ERR_INVALID_ARG, "%s: misaligned q / kv / window / out pointer", name);
+    if (out_bf16 != nullptr) {
+        REQUIRE(rope_dim >= 0 && rope_offset >= 0 && rope_dim % 2 == 0 && rope_offset % 2 == 0 &&
+                    rope_offset + rope_dim <= csa2::kDim,
+                CSA2_ERR_INVALID_ARG, "%s: rotary range must be even and inside the 512 channels",
+                name);
+        REQUIRE(rope_dim == 0 || (rope_cos && rope_sin), CSA2_ERR_INVALID_ARG,
+                "%s: null rotary table", name);
+    }
+    const size_t need = csa2::attn_workspace(queries, k, n_win);
+    REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
+            "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_sparse_attn(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k,
+                                           swa, swa_cap, swa_end, n_win, softmax_scale, out,
+                                           out_bf16, rope_cos, rope_sin, rope_offset, rope_dim,
+                                           lse, s),
+                  s, name);
+}
+
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq, const uint8_t* kv_codes,
                              const uint8_t* kv_scales, int64_t n_cap, const int32_t* topk,
                              int32_t k, const uint8_t* swa, int32_t swa_cap,
                              const int32_t* swa_end, int32_t n_win, float softmax_scale,
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream)
 {
-    REQUIRE(B >= 0 && nq >= 0 && n_cap >= 0 && k >= 0 && swa_cap >= 0 && n_win >= 0,
-            CSA2_ERR_INVALID_ARG, "sparse_attn: negative size");
-    REQUIRE((int64_t)B * nq <= (1ll << 24), CSA2_ERR_INVALID_ARG,
-            "sparse_attn: too many query rows");
-    REQUIRE(k <= 65536 && n_win <= 65536, CSA2_ERR_UNSUPPORTED, "sparse_attn: k or n_win too large");
-    const int32_t queries = B * nq;
-    if (queries == 0)
-        return CSA2_OK;
-    REQUIRE(q && out && swa_end, CSA2_ERR_INVALID_ARG, "sparse_attn: null pointer");
-    REQUIRE(k == 0 || (topk && kv_codes && kv_scales), CSA2_ERR_INVALID_ARG,
-            "sparse_attn: null top-k or KV cache");
-    REQUIRE(swa_cap == 0 || swa != nullptr, CSA2_ERR_INVALID_ARG, "sparse_attn: null window");
-    REQUIRE(aligned(q, 16) && aligned(kv_codes, 16) && aligned(kv_scales, 4) && aligned(swa, 16) &&
-                aligned(out, 16),
-            CSA2_ERR_INVALID_ARG, "sparse_attn: misaligned q / kv / window / out pointer");
-    const size_t need = csa2::attn_workspace(queries, k, n_win);
-    REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
-            "sparse_attn: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return finish(csa2::launch_sparse_attn(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k,
-                                           swa, swa_cap, swa_end, n_win, softmax_scale, out, lse,
-                                           s),
-                  s, "sparse_attn");
+    REQUIRE(out != nullptr || (int64_t)B * nq == 0 || B < 0 || nq < 0, CSA2_ERR_INVALID_ARG,
+            "sparse_attn: null pointer");
+    return attn_common(q, B, nq, kv_codes, kv_scales, n_cap, topk, k, swa, swa_cap, swa_end,
+                       n_win, softmax_scale, out, nullptr, nullptr, nullptr, 0, 0, lse, ws,
+                       ws_bytes, stream, "sparse_attn");
+}
+
+csa2_status csa2_sparse_attn_rope_bf16(const uint16_t* q, int32_t B, int32_t nq,
+                                       const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                       int64_t n_cap, const int32_t* topk, int32_t k,
+                                       const uint8_t* swa, int32_t swa_cap,
+                                       const int32_t* swa_end, int32_t n_win,
+                                       float softmax_scale, const float* rope_cos,
+                                       const float* rope_sin, int32_t rope_offset,
+                                       int32_t rope_dim, uint16_t* out, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream)
+{
+    REQUIRE(out != nullptr || (int64_t)B * nq == 0 || B < 0 || nq < 0, CSA2_ERR_INVALID_ARG,
+            "sparse_attn_rope_bf16: null pointer");
+    return attn_common(q, B, nq, kv_codes, kv_scales, n_cap, topk, k, swa, swa_cap, swa_end,
+                       n_win, softmax_scale, nullptr, out, rope_cos, rope_sin, rope_offset,
+                       rope_dim, lse, ws, ws_bytes, stream, "sparse_attn_rope_bf16");
 }
 
 }  // extern "C"

@@ -182,13 +182,34 @@ __device__ __forceinline__ void scale_scores(f32x4 (&s)[2], uint32_t valid, floa
     }
 }
 
+// Where the merged output goes: fp32 as computed, or (kRopeBf16) inverse
+// rotary on the rotary channels followed by a bf16 cast.
+struct AttnOut {
+    float* out;            // fp32 [rows, 64, 512] (kRopeBf16 = false)
+    uint16_t* out_bf16;    // bf16 [rows, 64, 512] (kRopeBf16 = true)
+    const float* cs;       // [rows, rope_dim/2]: the query position's angles
+    const float* sn;
+    int32_t rope_off, rope_dim;
+};
+
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <bool kRopeBf16>
 __global__ void __launch_bounds__(kAttnWaves * kWave)
 sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
                    const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
                    int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
                    const uint8_t* __restrict__ swa, int32_t swa_cap,
                    const int32_t* __restrict__ swa_end, int32_t n_win, float scale_log2,
-                   float* __restrict__ out, float* __restrict__ lse)
+                   AttnOut dst_spec, float* __restrict__ lse)
 {
     __shared__ AttnSmem sm;
     const int lane = threadIdx.x & 63;
@@ -434,11 +455,37 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
                 num += f[w] * sm.u.red.o[w][h][d0 + i];
             res[i] = num * inv;
         }
-        float4* dst = reinterpret_cast<float4*>(
-            out + (qrow * kHeads + kHg * hg + h) * kDim + kSlice * slice + d0);
+        const int64_t o0 = (qrow * kHeads + kHg * hg + h) * kDim + kSlice * slice + d0;
+        if (!kRopeBf16) {
+            float4* dst = reinterpret_cast<float4*>(dst_spec.out + o0);
 #pragma unroll
-        for (int i = 0; i < kOPer / 4; ++i)
-            dst[i] = make_float4(res[4 * i], res[4 * i + 1], res[4 * i + 2], res[4 * i + 3]);
+            for (int i = 0; i < kOPer / 4; ++i)
+                dst[i] = make_float4(res[4 * i], res[4 * i + 1], res[4 * i + 2], res[4 * i + 3]);
+        } else {
+            // rotate each rotary pair (a, b) back by the query's angle:
+            // a' = a*c + b*s, b' = b*c - a*s, every product and sum rounded to fp32
+            const int half = dst_spec.rope_dim / 2;
+#pragma unroll
+            for (int i = 0; i < kOPer; i += 2) {
+                const int d = kSlice * slice + d0 + i;
+                if (d >= dst_spec.rope_off && d < dst_spec.rope_off + dst_spec.rope_dim) {
+                    const int pi = (d - dst_spec.rope_off) / 2;
+                    const float c = dst_spec.cs[qrow * half + pi];
+                    const float sn = dst_spec.sn[qrow * half + pi];
+                    const float a = res[i], bb = res[i + 1];
+                    res[i] = __fadd_rn(__fmul_rn(a, c), __fmul_rn(bb, sn));
+                    res[i + 1] = __fsub_rn(__fmul_rn(bb, c), __fmul_rn(a, sn));
+                }
+            }
+            uint32_t packed[kOPer / 2];
+#pragma unroll
+            for (int i = 0; i < kOPer / 2; ++i)
+                packed[i] = (uint32_t)bf16_rne(res[2 * i]) | ((uint32_t)bf16_rne(res[2 * i + 1]) << 16);
+            uint2* dst = reinterpret_cast<uint2*>(dst_spec.out_bf16 + o0);
+#pragma unroll
+            for (int i = 0; i < kOPer / 4; ++i)
+                dst[i] = make_uint2(packed[2 * i], packed[2 * i + 1]);
+        }
         if (lse != nullptr && slice == 0 && t % kThreadsPerHead == 0)
             lse[qrow * kHeads + kHg * hg + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
     }
@@ -455,16 +502,24 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t n_cap,
                               const int32_t* topk, int32_t k, const uint8_t* swa,
                               int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
-                              float softmax_scale, float* out, float* lse, hipStream_t stream)
+                              float softmax_scale, float* out, uint16_t* out_bf16,
+                              const float* rope_cos, const float* rope_sin, int32_t rope_off,
+                              int32_t rope_dim, float* lse, hipStream_t stream)
 {
     if (queries == 0)
         return hipSuccess;
     // rows padded to a multiple of the die count (padding workgroups exit at once)
     const int64_t rows = ((int64_t)queries + kXcds - 1) / kXcds * kXcds;
-    const int64_t grid = rows * kWgPerRow;
-    sparse_attn_kernel<<<dim3((uint32_t)grid), dim3(kAttnWaves * kWave), 0, stream>>>(
-        q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
-        softmax_scale * kLog2e, out, lse);
+    const dim3 grid((uint32_t)(rows * kWgPerRow)), block(kAttnWaves * kWave);
+    const AttnOut spec{out, out_bf16, rope_cos, rope_sin, rope_off, rope_dim};
+    if (out_bf16 == nullptr)
+        sparse_attn_kernel<false><<<grid, block, 0, stream>>>(
+            q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
+            softmax_scale * kLog2e, spec, lse);
+    else
+        sparse_attn_kernel<true><<<grid, block, 0, stream>>>(
+            q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
+            softmax_scale * kLog2e, spec, lse);
     return hipGetLastError();
 }
 

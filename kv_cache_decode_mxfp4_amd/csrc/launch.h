@@ -41,10 +41,14 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
                        hipStream_t stream);
 
 size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win);
+// out (fp32) or out_bf16 (inverse rotary on [rope_off, rope_off + rope_dim)
+// with the query's rope_cos / rope_sin, then bf16): exactly one is non-null.
 hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                               const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t n_cap,
                               const int32_t* topk, int32_t k, const uint8_t* swa,
                               int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
-                              float softmax_scale, float* out, float* lse, hipStream_t stream);
+                              float softmax_scale, float* out, uint16_t* out_bf16,
+                              const float* rope_cos, const float* rope_sin, int32_t rope_off,
+                              int32_t rope_dim, float* lse, hipStream_t stream);
 
 }  // namespace csa2

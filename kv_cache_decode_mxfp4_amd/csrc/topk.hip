@@ -348,6 +348,34 @@ group_max_kernel(const float* __restrict__ score, const int32_t* __restrict__ id
     gkey[row * ngroups + grp] = m;
 }
 
+// Group maxima for groups of 8 without an index array when rows are float4
+// aligned (L % 4 == 0, 16-byte aligned scores): lane t of the grid loads the
+// float4 of entries [4t, 4t+4) of the flattened rows, and the two lanes of a
+// group combine through a DPP swap, so every load instruction is one
+// contiguous 1 KiB.  Grid: ceil(rows * L / 4 / 256).
+__global__ void __launch_bounds__(256)
+group_max8_vec_kernel(const float* __restrict__ score, int64_t L, int64_t rows,
+                      int64_t ngroups, const int32_t* __restrict__ n_valid,
+                      uint32_t* __restrict__ gkey)
+{
+    const int64_t quads_per_row = L / 4;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t tc = t < rows * quads_per_row ? t : rows * quads_per_row - 1;
+    const int64_t row = tc / quads_per_row;
+    const int64_t pos = 4 * (tc % quads_per_row);
+    const int64_t nv = valid_prefix(n_valid, row, L);
+    const float4 f = reinterpret_cast<const float4*>(score)[tc];
+    const float v[4] = {f.x, f.y, f.z, f.w};
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (pos + j < nv && !__builtin_isnan(v[j]))
+            m = max(m, order_key(v[j]));
+    m = max(m, dpp_u32<0xB1>(0u, m));  // partner lane (xor 1): the other half of the group
+    if ((threadIdx.x & 1) == 0 && t < rows * quads_per_row)
+        gkey[row * ngroups + pos / 8] = m;
+}
+
 struct GroupSmem {
     Smem sm;
     uint32_t chosen_groups[kTopkSegment / 2];  // k <= 16384 / g with g >= 2
@@ -459,7 +487,12 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         const int32_t per_row = (int32_t)((ngroups + 255) / 256);
         uint32_t* gkey = static_cast<uint32_t*>(ws);
         const dim3 grid((uint32_t)(rows * per_row));
-        if (g == 8)
+        if (g == 8 && idx == nullptr && L % 8 == 0 &&
+            reinterpret_cast<uintptr_t>(score) % 16 == 0) {
+            const int64_t quads = (int64_t)rows * (L / 4);
+            group_max8_vec_kernel<<<dim3((uint32_t)((quads + 255) / 256)), dim3(256), 0, stream>>>(
+                score, L, rows, ngroups, n_valid, gkey);
+        } else if (g == 8)
             group_max_kernel<8><<<grid, dim3(256), 0, stream>>>(score, idx, L, g, ngroups, per_row,
                                                                 n_valid, gkey);
         else

@@ -74,6 +74,9 @@ def lib():
         L.oracle_index_scores_at.argtypes = [vp, vp, i32, i32, vp, vp, vp, i64, vp]
         L.oracle_attention.argtypes = [vp, i32, i32, vp, vp, i64, vp, i32, vp, i64, i64, i32,
                                        dbl, vp, vp]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_bf16_rne.argtypes = [dbl]
+        L.oracle_inverse_rope_bf16.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp]
         L.oracle_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -202,6 +205,31 @@ def attention(q, kv_codes, kv_scales, sel, swa, swa_end: int, n_win: int = 128,
                            _p(sel), sel.size, _p(swa), swa.shape[0], int(swa_end), n_win,
                            float(scale), _p(out), _p(lse))
     return out, lse
+
+
+def bf16_rne(x: float) -> int:
+    """bf16 bit pattern nearest to x (ties to even)."""
+    return int(lib().oracle_bf16_rne(float(x)))
+
+
+def inverse_rope_bf16(o, cos_row, sin_row, rope_off: int = 448, rope_dim: int = 64):
+    """Attention output o [H, D] (double) -> bf16 bits [H, D] after rotating the rotary
+    channels back by the query's angle (cos_row, sin_row: [rope_dim/2] fp32)."""
+    o = _c(o, np.float64)
+    Hq, Dq = o.shape
+    cs, sn = _c(cos_row, np.float32), _c(sin_row, np.float32)
+    bits = np.empty((Hq, Dq), np.uint16)
+    lib().oracle_inverse_rope_bf16(_p(o), Hq, Dq, _p(cs), _p(sn), rope_off, rope_dim, _p(bits))
+    return bits
+
+
+def attention_rope_bf16(q, kv_codes, kv_scales, sel, swa, swa_end: int, cos_row, sin_row,
+                        n_win: int = 128, scale: float = 1.0, rope_off: int = 448,
+                        rope_dim: int = 64):
+    """One query: attention, then the inverse-rotary + bf16 epilogue.  Returns
+    (bf16 bits [64,512], the double output before the epilogue, lse [64])."""
+    out, lse = attention(q, kv_codes, kv_scales, sel, swa, swa_end, n_win, scale)
+    return inverse_rope_bf16(out, cos_row, sin_row, rope_off, rope_dim), out, lse
 
 
 # ---------------------------------------------------------------- layer modes (one query)

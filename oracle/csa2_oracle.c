@@ -423,6 +423,70 @@ void oracle_attention(const uint16_t* q, int32_t H, int32_t D,
     free(v);
 }
 
+/*
+ * bf16 (1 sign, 8 exponent, 7 stored significand bits) nearest to a double,
+ * ties to the even significand; overflow to infinity, NaN to the quiet NaN
+ * 0x7FC0.  Written from the format definition: the value is split as
+ * M * 2^q with the quantum q of the binade (8 significant bits, or the fixed
+ * subnormal quantum 2^-133), M is rounded to an integer with ties to even,
+ * and the result, exactly a bf16 value, is read off its float bit pattern.
+ */
+uint16_t oracle_bf16_rne(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    const double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7F80;
+    int e;
+    frexp(a, &e);          /* a = m * 2^e, m in [0.5, 1): binade [2^(e-1), 2^e) */
+    int q = e - 8;         /* 8 significant bits */
+    if (e - 1 < -126)
+        q = -133;          /* subnormal range: fixed quantum */
+    const double M = ldexp(a, -q);          /* exact */
+    double r = floor(M);
+    const double frac = M - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))
+        r += 1.0;
+    const double v = ldexp(r, q);           /* a bf16 value, or 2^128 on overflow */
+    const float f = (float)v;               /* exact (or infinity past the bf16 range) */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/*
+ * Output epilogue of the attention ([S] sequence dimension: the output is
+ * rotated back to restore relative position; [N] 4 inference side: the fused
+ * RoPE-attention-RoPE-cast kernel).  Reading: the rotary channels of the
+ * output are rotated by minus the query position's angle, the inverse of the
+ * rotation the encoder applies to keys:  a' = a c + b s,  b' = b c - a s,
+ * for pairs (x[off+2i], x[off+2i+1]) with the query's (c_i, s_i); then every
+ * channel is rounded to bf16.  o [H, D] double in, bits [H, D] out.
+ */
+void oracle_inverse_rope_bf16(const double* o, int32_t H, int32_t D, const float* cs,
+                              const float* sn, int32_t off, int32_t rope_dim, uint16_t* bits)
+{
+    for (int32_t h = 0; h < H; ++h) {
+        const double* row = o + (int64_t)h * D;
+        for (int32_t c = 0; c < D; ++c) {
+            double v = row[c];
+            if (c >= off && c < off + rope_dim) {
+                const int32_t i = (c - off) / 2;
+                const double co = cs[i], si = sn[i];
+                if ((c - off) % 2 == 0)
+                    v = row[c] * co + row[c + 1] * si;
+                else
+                    v = row[c] * co - row[c - 1] * si;
+            }
+            bits[(int64_t)h * D + c] = oracle_bf16_rne(v);
+        }
+    }
+}
+
 /* Threads an OpenMP region of this library uses. */
 int oracle_threads(void)
 {

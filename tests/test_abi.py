@@ -25,7 +25,7 @@ def declared():
 def test_header_declares_the_five_calls():
     names = declared()
     for n in ["csa2_quantize_kv", "csa2_index_full", "csa2_index_pool", "csa2_topk",
-              "csa2_sparse_attn"]:
+              "csa2_sparse_attn", "csa2_sparse_attn_rope_bf16"]:
         assert n in names
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = L.load()
-    assert lib.csa2_version() == 100
+    assert lib.csa2_version() == 101
     assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
     assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
@@ -99,3 +99,24 @@ def test_empty_inputs_are_no_ops():
     assert _status("csa2_topk", None, None, 0, 0, None, 5, None, None, 0, None)[0] == 0
     assert _status("csa2_sparse_attn", None, 0, 1, None, None, 0, None, 0, None, 0, None, 128,
                    ctypes.c_float(1.0), None, None, None, 0, None)[0] == 0
+
+
+def _rope_attn(q=16, out=16, cos=16, sin=16, off=448, dim=64, B=1):
+    vp = ctypes.c_void_p
+    return _status("csa2_sparse_attn_rope_bf16", vp(q), B, 1, vp(16), vp(16), 100, vp(16), 4,
+                   vp(16), 128, vp(16), 128, ctypes.c_float(1.0), vp(cos), vp(sin), off, dim,
+                   vp(out), None, None, 0, None)
+
+
+def test_rope_bf16_attention_validation():
+    st, msg = _rope_attn(off=447)
+    assert st == 1 and "rotary" in msg
+    st, msg = _rope_attn(off=480, dim=64)
+    assert st == 1 and "rotary" in msg
+    st, msg = _rope_attn(cos=None)
+    assert st == 1 and "rotary table" in msg
+    st, msg = _rope_attn(out=4)
+    assert st == 1 and "misaligned" in msg
+    st, msg = _rope_attn(out=None)
+    assert st == 1
+    assert _rope_attn(B=0, out=None, cos=None, sin=None)[0] == 0

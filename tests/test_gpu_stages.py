@@ -173,7 +173,7 @@ def _topk_case(rng, rows, Lr, kind):
 
 
 @pytest.mark.parametrize("Lr,k", [(1, 1), (100, 7), (2048, 64), (16384, 2048), (16385, 512),
-                                  (40000, 512), (131072, 2048), (300000, 512), (300000, 2048),
+                                  (40000, 512), (131072, 2048), (131072, 512), (300000, 512), (300000, 2048),
                                   (50000, 6000)])
 @pytest.mark.parametrize("kind", ["random", "ties"])
 def test_topk_bit_exact(Lr, k, kind):
@@ -394,3 +394,41 @@ def test_sparse_attn_batched_kernel_many_rows():
         ro, rl = oracle.attention(q[0, i], vc, vs, sel[i], sw, int(swa_end[0, i]), 128, 1.0)
         assert max_abs(out[0, i], ro) <= ATTN_TOL, f"query {i}"
         assert max_abs(lse[0, i], rl) <= 1e-4
+
+
+def _bf16_to_f32(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def test_sparse_attn_rope_bf16_epilogue():
+    """Inverse rotary + bf16 epilogue: oracle parity within the attention tolerance plus
+    one bf16 ulp, and bit-exact agreement with the fp32 entry point's output rotated
+    and rounded with the same fp32 operations."""
+    vc, vs, sw, sel, q = _attn_case(B=3, N=3000, k=100, seed=7)
+    B = 3
+    swa_end = np.array([[128], [60], [0]], np.int32)
+    rng = np.random.default_rng(8)
+    ang = rng.uniform(-np.pi, np.pi, (B, 32))
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    out16 = torch.full((B, 1, 64, 512), 0x7777, dtype=torch.int16, device=dev())
+    lse16 = torch.empty((B, 1, 64), device=dev())
+    L.sparse_attn_rope_bf16(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end),
+                            t(cos), t(sin), out16, lse16)
+    got = out16.cpu().numpy().view(np.uint16)
+    out32, lse32 = _run_attn(q, vc, vs, sel, sw, swa_end)
+    assert np.array_equal(lse16.cpu().numpy(), lse32)
+    for b in range(B):
+        ref_bits, ref_out, ref_lse = oracle.attention_rope_bf16(
+            q[b, 0], vc[b], vs[b], sel[b, 0], sw[b], int(swa_end[b, 0]), cos[b], sin[b])
+        g, r = _bf16_to_f32(got[b, 0]), _bf16_to_f32(ref_bits)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+        assert np.all(np.abs(g - r) <= 2 * ATTN_TOL + ulp), f"seq {b}"
+        assert np.mean(got[b, 0] == ref_bits) > 0.99
+        # the same epilogue on the fp32 entry point's output, fp32 products and sums
+        o = out32[b, 0].astype(np.float32).copy()
+        a, c = o[:, 448::2].copy(), o[:, 449::2].copy()
+        co, si = cos[b][None, :], sin[b][None, :]
+        o[:, 448::2] = (a * co) + (c * si)
+        o[:, 449::2] = (c * co) - (a * si)
+        host = torch.from_numpy(o).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got[b, 0], host), f"seq {b}"
