@@ -128,12 +128,14 @@ def make_step(st, torch, L, layers):
 
     def encode_new():
         if w.decode:
-            # one row per sequence at entry N-1 of each [N]-row cache
-            L.quantize_kv(st["new_idx"], st["kc"], st["ks"], dst_row=first, dst_stride=N)
-            L.quantize_kv(st["new_kv"], st["vc"], st["vs"], st["new_cos"], st["new_sin"],
-                          synth.ROPE_OFFSET, synth.ROPE_DIM, dst_row=first, dst_stride=N)
-            L.quantize_swa(st["new_swa"], st["swa"][0], dst_row=st["new_swa_row"],
-                           dst_stride=w.swa_rows())
+            # one launch: per sequence, the main-KV and indexer-key entry N-1 of its
+            # [N]-row caches and the newest row of its window
+            L.encode_entries(st["new_kv"], st["vc"], st["vs"], st["kc"], st["ks"],
+                             idx_x=st["new_idx"], rope_cos=st["new_cos"], rope_sin=st["new_sin"],
+                             rope_offset=synth.ROPE_OFFSET, rope_dim=synth.ROPE_DIM,
+                             dst_row=first, dst_stride=N, swa_x=st["new_swa"],
+                             swa_out=st["swa"][0], swa_row=st["new_swa_row"],
+                             swa_stride=w.swa_rows())
         else:
             L.quantize_kv(st["new_idx"], st["kc"], st["ks"], dst_row=first)
             L.quantize_kv(st["new_kv"], st["vc"], st["vs"], st["new_cos"], st["new_sin"],

@@ -109,6 +109,41 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
                               int64_t dst_stride, void* stream);
 
 /*
+ * New cache entries of one step in one launch ([A] 3.3: a Full layer computes
+ * the main KV and projects the indexer key from it; [N] 2.2: indexer K is now
+ * projected from the main KV; [N] 2.3: window rows stay FP8).
+ *   rows       new compressed entries.
+ *   kv_x       fp32 [rows, 512] main latent rows -> rotary (as csa2_quantize_kv,
+ *              rope_cos / rope_sin [rows, rope_dim/2]) -> MXFP4 into kv_codes /
+ *              kv_scales, row r at kv_codes + r*kv_stride*256 and
+ *              kv_scales + r*kv_stride*32.
+ *   idx_x      fp32 [rows, 128] indexer-key rows encoded as they are (no
+ *              rotary), or NULL: then the keys are projected from the main
+ *              latent before its rotary, y = kv_x[r] . w_idx^T with
+ *   w_idx      bf16 [128, 512] (row o = output channel o), each output
+ *              channel accumulated in fp32 as four partial sums of fused
+ *              multiply-adds (channels c = 4m + j go to partial j, in
+ *              increasing c) added as (p0 + p1) + (p2 + p3), then encoded.
+ *   idx_codes, idx_scales  MXFP4 outputs, row r at + r*idx_stride*64 / *8.
+ *   idx_y      fp32 [rows, 128] receives the projection (NULL: not written;
+ *              only used when projecting).
+ *   swa_x      fp32 [swa_rows, 512] window rows -> E4M3FN (as
+ *              csa2_quantize_swa), row r at swa_out + r*swa_stride*512; NULL
+ *              when swa_rows == 0.
+ * Reading: the projection takes the latent before rotary (the rotation serves
+ * attention positions; the pages say only that the indexer key is projected
+ * from the main KV).  The encodings are bit-exact functions of their fp32
+ * inputs (the projection itself is fp32 arithmetic).
+ */
+csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* rope_cos,
+                                const float* rope_sin, int32_t rope_offset, int32_t rope_dim,
+                                uint8_t* kv_codes, uint8_t* kv_scales, int64_t kv_stride,
+                                const float* idx_x, const uint16_t* w_idx, uint8_t* idx_codes,
+                                uint8_t* idx_scales, int64_t idx_stride, float* idx_y,
+                                const float* swa_x, int32_t swa_rows, uint8_t* swa_out,
+                                int64_t swa_stride, void* stream);
+
+/*
  * Full-layer indexer scan ([N] 2.2, [A] 3.4: the first Full layer scores the
  * whole causally visible range; a block's score is the largest index score
  * of its positions).

@@ -7,10 +7,10 @@ binding (argument marshalling only); `layers` sequences the calls into the
 Full / Reindex / Reuse layer modes.
 """
 from . import _lib, layers  # noqa: F401
-from ._lib import (Csa2Error, index_full, index_pool, quantize_kv, quantize_swa,  # noqa: F401
+from ._lib import (Csa2Error, encode_entries, index_full, index_pool, quantize_kv, quantize_swa,  # noqa: F401
                    sparse_attn, sparse_attn_rope_bf16, sparse_attn_workspace, topk,
                    topk_workspace)
 
-__all__ = ["Csa2Error", "index_full", "index_pool", "quantize_kv", "quantize_swa",
+__all__ = ["Csa2Error", "encode_entries", "index_full", "index_pool", "quantize_kv", "quantize_swa",
            "sparse_attn", "sparse_attn_rope_bf16", "sparse_attn_workspace", "topk",
            "topk_workspace", "layers"]

@@ -109,6 +109,47 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
                   "quantize_swa");
 }
 
+csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* rope_cos,
+                                const float* rope_sin, int32_t rope_offset, int32_t rope_dim,
+                                uint8_t* kv_codes, uint8_t* kv_scales, int64_t kv_stride,
+                                const float* idx_x, const uint16_t* w_idx, uint8_t* idx_codes,
+                                uint8_t* idx_scales, int64_t idx_stride, float* idx_y,
+                                const float* swa_x, int32_t swa_rows, uint8_t* swa_out,
+                                int64_t swa_stride, void* stream)
+{
+    REQUIRE(rows >= 0 && swa_rows >= 0, CSA2_ERR_INVALID_ARG, "encode_entries: negative rows");
+    REQUIRE(kv_stride >= 1 && idx_stride >= 1 && swa_stride >= 1, CSA2_ERR_INVALID_ARG,
+            "encode_entries: strides must be >= 1");
+    REQUIRE(rope_dim >= 0 && rope_dim % 2 == 0 && rope_offset >= 0 && rope_offset % 2 == 0 &&
+                rope_offset + rope_dim <= csa2::kDim,
+            CSA2_ERR_INVALID_ARG, "encode_entries: rotary range [%d, %d) not even / inside 512",
+            rope_offset, rope_offset + rope_dim);
+    if (rows == 0 && swa_rows == 0)
+        return CSA2_OK;
+    if (rows > 0) {
+        REQUIRE(kv_x && kv_codes && kv_scales && idx_codes && idx_scales, CSA2_ERR_INVALID_ARG,
+                "encode_entries: null main-KV or indexer-key pointer");
+        REQUIRE(idx_x != nullptr || w_idx != nullptr, CSA2_ERR_INVALID_ARG,
+                "encode_entries: indexer keys need their own rows or a projection matrix");
+        REQUIRE(rope_dim == 0 || (rope_cos && rope_sin), CSA2_ERR_INVALID_ARG,
+                "encode_entries: rope_dim > 0 needs cos/sin tables");
+        REQUIRE(aligned(kv_x, 16) && aligned(idx_x, 16) && aligned(w_idx, 16) &&
+                    aligned(kv_codes, 8) && aligned(idx_codes, 8) && aligned(idx_y, 8),
+                CSA2_ERR_INVALID_ARG, "encode_entries: misaligned pointer");
+    }
+    if (swa_rows > 0) {
+        REQUIRE(swa_x && swa_out, CSA2_ERR_INVALID_ARG, "encode_entries: null window pointer");
+        REQUIRE(aligned(swa_x, 16) && aligned(swa_out, 4), CSA2_ERR_INVALID_ARG,
+                "encode_entries: misaligned window pointer");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_encode_entries(rows, kv_x, rope_cos, rope_sin, rope_offset,
+                                              rope_dim, kv_codes, kv_scales, kv_stride, idx_x,
+                                              w_idx, idx_codes, idx_scales, idx_stride, idx_y,
+                                              swa_x, swa_rows, swa_out, swa_stride, s),
+                  s, "encode_entries");
+}
+
 static csa2_status check_indexer(const char* fn, const uint16_t* q, const float* w,
                                  const uint8_t* k_codes, const uint8_t* k_scales, int64_t n_cap,
                                  const int32_t* n_visible, int32_t B, int32_t nq, int32_t block)

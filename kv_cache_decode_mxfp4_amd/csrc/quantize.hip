@@ -53,25 +53,14 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, float s)
            (uint32_t)(a > 5.0f * s);
 }
 
-__global__ void __launch_bounds__(256)
-quantize_kv_kernel(const float* __restrict__ x, int64_t rows, int32_t C,
-                   const float* __restrict__ cs, const float* __restrict__ sn, int32_t rope_off,
-                   int32_t rope_dim, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                   int64_t dst_stride)
+// Rotary on the pairs of one 16-channel group g of row r that fall inside
+// [rope_off, rope_off + rope_dim): a' = a*c - b*s, b' = a*s + b*c, every
+// product and sum rounded to fp32.
+__device__ __forceinline__ void rope_group(float (&v)[16], int32_t g, int64_t r,
+                                           const float* __restrict__ cs,
+                                           const float* __restrict__ sn, int32_t rope_off,
+                                           int32_t rope_dim)
 {
-    const int32_t G = C / 16;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= rows * G)
-        return;
-    const int64_t r = t / G;
-    const int32_t g = (int32_t)(t % G);
-    const float4* src = reinterpret_cast<const float4*>(x + r * C + 16 * g);
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float4 f = src[i];
-        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-    }
     const int32_t half = rope_dim / 2;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -85,23 +74,90 @@ quantize_kv_kernel(const float* __restrict__ x, int64_t rows, int32_t C,
             v[2 * p + 1] = __fadd_rn(__fmul_rn(a, si), __fmul_rn(b, co));
         }
     }
+}
+
+// E4M3 scale byte of a group whose largest magnitude is amax: RNE(amax / 6).
+__device__ __forceinline__ uint32_t group_scale(float amax)
+{
+    return e4m3_rne(__fdiv_rn(amax, 6.0f));
+}
+
+// Signed E2M1 nibble of x under scale value s (no -0 nibble; scale 0 -> 0).
+__device__ __forceinline__ uint32_t e2m1_nibble(float x, float s)
+{
+    uint32_t c = s > 0.0f ? e2m1_code(fabsf(x), s) : 0u;
+    if (c != 0u && x < 0.0f)
+        c |= 8u;
+    return c;
+}
+
+// One 16-channel group: codes (channel 2j in the low nibble of byte j) and
+// the scale byte.
+__device__ __forceinline__ uint32_t encode_group(const float (&v)[16], uint32_t (&packed)[2])
+{
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         amax = fmaxf(amax, fabsf(v[i]));
-    const uint32_t sb = e4m3_rne(__fdiv_rn(amax, 6.0f));
+    const uint32_t sb = group_scale(amax);
     const float s = e4m3_value(sb);
-    uint32_t packed[2] = {0u, 0u};
+    packed[0] = packed[1] = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        uint32_t c = s > 0.0f ? e2m1_code(fabsf(v[i]), s) : 0u;
-        if (c != 0u && v[i] < 0.0f)
-            c |= 8u;
-        packed[i / 8] |= c << (4 * (i % 8));
+    for (int i = 0; i < 16; ++i)
+        packed[i / 8] |= e2m1_nibble(v[i], s) << (4 * (i % 8));
+    return sb;
+}
+
+// Four fp32 values -> four E4M3FN bytes (RNE, saturating, sign kept).
+__device__ __forceinline__ uint32_t fp8_word(float4 f)
+{
+    const float v[4] = {f.x, f.y, f.z, f.w};
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t c = e4m3_rne(fabsf(v[i]));
+        if (__float_as_uint(v[i]) >> 31)
+            c |= 0x80u;
+        word |= c << (8 * i);
     }
+    return word;
+}
+
+// Thread t of a group-per-thread launch: group g of row r of a [rows, C] input.
+__device__ __forceinline__ void encode_row_group(const float* __restrict__ x, int64_t r,
+                                                 int32_t g, int32_t C,
+                                                 const float* __restrict__ cs,
+                                                 const float* __restrict__ sn, int32_t rope_off,
+                                                 int32_t rope_dim, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, int64_t dst_stride)
+{
+    const float4* src = reinterpret_cast<const float4*>(x + r * C + 16 * g);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 f = src[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+    rope_group(v, g, r, cs, sn, rope_off, rope_dim);
+    uint32_t packed[2];
+    const uint32_t sb = encode_group(v, packed);
     const int64_t orow = r * dst_stride;
     *reinterpret_cast<uint2*>(codes + orow * (C / 2) + 8 * g) = make_uint2(packed[0], packed[1]);
-    scales[orow * G + g] = (uint8_t)sb;
+    scales[orow * (C / 16) + g] = (uint8_t)sb;
+}
+
+__global__ void __launch_bounds__(256)
+quantize_kv_kernel(const float* __restrict__ x, int64_t rows, int32_t C,
+                   const float* __restrict__ cs, const float* __restrict__ sn, int32_t rope_off,
+                   int32_t rope_dim, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                   int64_t dst_stride)
+{
+    const int32_t G = C / 16;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= rows * G)
+        return;
+    encode_row_group(x, t / G, (int32_t)(t % G), C, cs, sn, rope_off, rope_dim, codes, scales,
+                     dst_stride);
 }
 
 // Four consecutive elements per thread; row_len % 4 == 0.
@@ -112,20 +168,105 @@ quantize_swa_kernel(const float* __restrict__ x, int64_t n, int32_t row_len,
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (4 * t >= n)
         return;
-    const float4 f = reinterpret_cast<const float4*>(x)[t];
-    const float v[4] = {f.x, f.y, f.z, f.w};
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t c = e4m3_rne(fabsf(v[i]));
-        if (__float_as_uint(v[i]) >> 31)
-            c |= 0x80u;
-        word |= c << (8 * i);
-    }
+    const uint32_t word = fp8_word(reinterpret_cast<const float4*>(x)[t]);
     const int64_t e = 4 * t;
     const int64_t r = e / row_len;
     const int64_t c = e % row_len;
     *reinterpret_cast<uint32_t*>(out + r * dst_stride * row_len + c) = word;
+}
+
+// New cache entries of one step in one launch ([A] 3.3: a Full layer computes
+// the main KV and projects the indexer key from it; [N] 2.2: the indexer key
+// is now projected from the main KV; [N] 2.3: window rows stay FP8).
+// Workgroups [0, wg_kv) encode the main-KV rows (rotary + MXFP4, one thread per
+// 16-channel group); [wg_kv, wg_kv + wg_idx) the indexer-key rows, either from
+// their own fp32 rows (one thread per group) or projected from the main
+// latent before its rotary (one wave per row: lane l computes channels 2l and
+// 2l+1 as four fixed-order partial sums of fp32 fused multiply-adds over the
+// 512 channels, added (p0 + p1) + (p2 + p3), then encodes them, the group of
+// 16 channels being 8 lanes); the rest encode the window rows.
+struct EntryJob {
+    int32_t rows;
+    const float* kv_x; const float* cs; const float* sn; int32_t rope_off, rope_dim;
+    uint8_t* kv_codes; uint8_t* kv_scales; int64_t kv_stride;
+    const float* idx_x; const uint16_t* w_idx;
+    uint8_t* idx_codes; uint8_t* idx_scales; int64_t idx_stride; float* idx_y;
+    const float* swa_x; int32_t swa_rows; uint8_t* swa_out; int64_t swa_stride;
+    int32_t wg_kv, wg_idx;  // workgroups of the first two parts
+};
+
+__device__ __forceinline__ float max8_lanes(float m)
+{
+    m = fmaxf(m, __uint_as_float(dpp_u32<0xB1>(0u, __float_as_uint(m))));
+    m = fmaxf(m, __uint_as_float(dpp_u32<0x4E>(0u, __float_as_uint(m))));
+    return fmaxf(m, __uint_as_float(dpp_u32<0x141>(0u, __float_as_uint(m))));
+}
+
+__global__ void __launch_bounds__(256)
+encode_entries_kernel(EntryJob J)
+{
+    constexpr int kKv = kDim / 16;       // 32 groups per main-KV row
+    constexpr int kIdx = kIdxDim / 16;   // 8 groups per indexer-key row
+    const int wg = blockIdx.x;
+    if (wg < J.wg_kv) {
+        const int64_t t = (int64_t)wg * 256 + threadIdx.x;
+        if (t < (int64_t)J.rows * kKv)
+            encode_row_group(J.kv_x, t / kKv, (int32_t)(t % kKv), kDim, J.cs, J.sn, J.rope_off,
+                             J.rope_dim, J.kv_codes, J.kv_scales, J.kv_stride);
+        return;
+    }
+    if (wg < J.wg_kv + J.wg_idx) {
+        const int w = wg - J.wg_kv;
+        if (J.idx_x != nullptr) {
+            const int64_t t = (int64_t)w * 256 + threadIdx.x;
+            if (t < (int64_t)J.rows * kIdx)
+                encode_row_group(J.idx_x, t / kIdx, (int32_t)(t % kIdx), kIdxDim, nullptr,
+                                 nullptr, 0, 0, J.idx_codes, J.idx_scales, J.idx_stride);
+            return;
+        }
+        // projection: one wave per row, 4 rows per workgroup
+        const int lane = threadIdx.x & 63;
+        const int64_t r = (int64_t)w * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (r >= J.rows)
+            return;
+        const float4* xr = reinterpret_cast<const float4*>(J.kv_x + r * kDim);
+        const uint4* w0 = reinterpret_cast<const uint4*>(J.w_idx + (int64_t)(2 * lane) * kDim);
+        const uint4* w1 = reinterpret_cast<const uint4*>(J.w_idx + (int64_t)(2 * lane + 1) * kDim);
+        float p0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < kDim / 8; ++j) {  // 8 channels: c = 8j + i, partial sum i % 4
+            const float4 xa = xr[2 * j], xb = xr[2 * j + 1];
+            const float xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            const uint4 a = w0[j], bw = w1[j];
+            const uint32_t da[4] = {a.x, a.y, a.z, a.w}, db[4] = {bw.x, bw.y, bw.z, bw.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float wa = __uint_as_float(i % 2 == 0 ? da[i / 2] << 16 : da[i / 2] & 0xFFFF0000u);
+                const float wb = __uint_as_float(i % 2 == 0 ? db[i / 2] << 16 : db[i / 2] & 0xFFFF0000u);
+                p0[i % 4] = __builtin_fmaf(xs[i], wa, p0[i % 4]);
+                p1[i % 4] = __builtin_fmaf(xs[i], wb, p1[i % 4]);
+            }
+        }
+        const float y0 = __fadd_rn(__fadd_rn(p0[0], p0[1]), __fadd_rn(p0[2], p0[3]));
+        const float y1 = __fadd_rn(__fadd_rn(p1[0], p1[1]), __fadd_rn(p1[2], p1[3]));
+        if (J.idx_y != nullptr)
+            *reinterpret_cast<float2*>(J.idx_y + r * kIdxDim + 2 * lane) = make_float2(y0, y1);
+        // group of 16 channels = lanes 8g .. 8g+7
+        const float amax = max8_lanes(fmaxf(fabsf(y0), fabsf(y1)));
+        const uint32_t sb = group_scale(amax);
+        const float sv = e4m3_value(sb);
+        const int64_t orow = r * J.idx_stride;
+        J.idx_codes[orow * (kIdxDim / 2) + lane] =
+            (uint8_t)(e2m1_nibble(y0, sv) | (e2m1_nibble(y1, sv) << 4));
+        if ((lane & 7) == 0)
+            J.idx_scales[orow * kIdx + lane / 8] = (uint8_t)sb;
+        return;
+    }
+    const int64_t t = (int64_t)(wg - J.wg_kv - J.wg_idx) * 256 + threadIdx.x;
+    if (4 * t >= (int64_t)J.swa_rows * kDim)
+        return;
+    const uint32_t word = fp8_word(reinterpret_cast<const float4*>(J.swa_x)[t]);
+    const int64_t r = 4 * t / kDim, c = 4 * t % kDim;
+    *reinterpret_cast<uint32_t*>(J.swa_out + r * J.swa_stride * kDim + c) = word;
 }
 
 }  // namespace
@@ -152,6 +293,29 @@ hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8
     const int64_t grid = (threads + 255) / 256;
     quantize_swa_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(x, n, row_len, out,
                                                                         dst_stride);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* cs, const float* sn,
+                                 int32_t rope_off, int32_t rope_dim, uint8_t* kv_codes,
+                                 uint8_t* kv_scales, int64_t kv_stride, const float* idx_x,
+                                 const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
+                                 int64_t idx_stride, float* idx_y, const float* swa_x,
+                                 int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
+                                 hipStream_t stream)
+{
+    EntryJob J{rows, kv_x, cs, sn, rope_off, rope_dim, kv_codes, kv_scales, kv_stride,
+               idx_x, w_idx, idx_codes, idx_scales, idx_stride, idx_y,
+               swa_x, swa_rows, swa_out, swa_stride, 0, 0};
+    J.wg_kv = (int32_t)(((int64_t)rows * (kDim / 16) + 255) / 256);
+    J.wg_idx = idx_x != nullptr ? (int32_t)(((int64_t)rows * (kIdxDim / 16) + 255) / 256)
+                                : (int32_t)((rows + 3) / 4);
+    const int64_t w_swa = ((int64_t)swa_rows * (kDim / 4) + 255) / 256;
+    const int64_t grid = (int64_t)J.wg_kv + J.wg_idx + w_swa;
+    if (grid == 0)
+        return hipSuccess;
+    encode_entries_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(J);
     return hipGetLastError();
 }
 

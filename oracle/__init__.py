@@ -74,6 +74,7 @@ def lib():
         L.oracle_index_scores_at.argtypes = [vp, vp, i32, i32, vp, vp, vp, i64, vp]
         L.oracle_attention.argtypes = [vp, i32, i32, vp, vp, i64, vp, i32, vp, i64, i64, i32,
                                        dbl, vp, vp]
+        L.oracle_project_rows.argtypes = [vp, i64, i32, vp, i32, vp]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_bf16_rne.argtypes = [dbl]
         L.oracle_inverse_rope_bf16.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp]
@@ -205,6 +206,17 @@ def attention(q, kv_codes, kv_scales, sel, swa, swa_end: int, n_win: int = 128,
                            _p(sel), sel.size, _p(swa), swa.shape[0], int(swa_end), n_win,
                            float(scale), _p(out), _p(lse))
     return out, lse
+
+
+def project_rows(x, w_bits):
+    """Indexer-key projection of new entries: x fp32 [R, D] . w bf16 bits [O, D]^T in double."""
+    x = _c(x, np.float32)
+    w_bits = _c(w_bits, np.uint16)
+    R, Dx = x.shape
+    O = w_bits.shape[0]
+    y = np.empty((R, O), np.float64)
+    lib().oracle_project_rows(_p(x), R, Dx, _p(w_bits), O, _p(y))
+    return y
 
 
 def bf16_rne(x: float) -> int:

@@ -487,6 +487,24 @@ void oracle_inverse_rope_bf16(const double* o, int32_t H, int32_t D, const float
     }
 }
 
+/*
+ * Indexer-key projection of new entries ([A] 3.3: a Full layer projects the
+ * indexer key from the main KV; [N] 2.2: indexer K is projected from the main
+ * KV): y[r, o] = sum_c x[r, c] * w[o, c], x fp32 [rows, D], w bf16 [O, D],
+ * in double.  Reading: x is the main latent before its rotary.
+ */
+void oracle_project_rows(const float* x, int64_t rows, int32_t D, const uint16_t* w, int32_t O,
+                         double* y)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t o = 0; o < O; ++o) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < D; ++c)
+                acc += (double)x[r * D + c] * bf16_value(w[(int64_t)o * D + c]);
+            y[r * O + o] = acc;
+        }
+}
+
 /* Threads an OpenMP region of this library uses. */
 int oracle_threads(void)
 {

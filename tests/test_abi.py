@@ -25,7 +25,7 @@ def declared():
 def test_header_declares_the_five_calls():
     names = declared()
     for n in ["csa2_quantize_kv", "csa2_index_full", "csa2_index_pool", "csa2_topk",
-              "csa2_sparse_attn", "csa2_sparse_attn_rope_bf16"]:
+              "csa2_sparse_attn", "csa2_sparse_attn_rope_bf16", "csa2_encode_entries"]:
         assert n in names
 
 
@@ -120,3 +120,25 @@ def test_rope_bf16_attention_validation():
     st, msg = _rope_attn(out=None)
     assert st == 1
     assert _rope_attn(B=0, out=None, cos=None, sin=None)[0] == 0
+
+
+def _entries(rows=4, kv_x=16, idx_x=16, w=None, off=448, dim=64, cos=16, swa_rows=0, swa_x=None,
+             kv_stride=1):
+    vp = ctypes.c_void_p
+    return _status("csa2_encode_entries", rows, vp(kv_x), vp(cos), vp(cos), off, dim, vp(16),
+                   vp(16), kv_stride, vp(idx_x), vp(w), vp(16), vp(16), 1, None, vp(swa_x),
+                   swa_rows, vp(16), 1, None)
+
+
+def test_encode_entries_validation():
+    st, msg = _entries(idx_x=None, w=None)
+    assert st == 1 and "projection" in msg
+    st, msg = _entries(off=447)
+    assert st == 1 and "rotary" in msg
+    st, msg = _entries(kv_x=20)
+    assert st == 1 and "misaligned" in msg
+    st, msg = _entries(swa_rows=2, swa_x=None)
+    assert st == 1 and "window" in msg
+    st, msg = _entries(kv_stride=0)
+    assert st == 1
+    assert _entries(rows=0, kv_x=None, idx_x=None, cos=None)[0] == 0

@@ -432,3 +432,61 @@ def test_sparse_attn_rope_bf16_epilogue():
         o[:, 449::2] = (c * co) - (a * si)
         host = torch.from_numpy(o).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(got[b, 0], host), f"seq {b}"
+
+
+# ------------------------------------------------------------------ new entries (one launch)
+
+def _entries_case(R, S, seed):
+    rng = np.random.default_rng(seed)
+    kv_x = synth.latent_rows(synth.key(13, 1, 0, seed), synth.key(13, 2, 0, seed), 0, R, 512)
+    cos, sin = synth.rope_rows(1000 + seed, R)
+    idx_x = rng.standard_normal((R, 128)).astype(np.float32)
+    swa_x = synth.latent_rows(synth.key(13, 3, 0, seed), synth.key(13, 4, 0, seed), 0, S, 512)
+    return kv_x, cos, sin, idx_x, swa_x
+
+
+def _entries_buffers(n_rows, n_swa):
+    z = lambda *sh: torch.full(sh, 0xA5, dtype=torch.uint8, device=dev())
+    return z(n_rows, 256), z(n_rows, 32), z(n_rows, 64), z(n_rows, 8), z(n_swa, 512)
+
+
+@pytest.mark.parametrize("R,S,project", [(1, 1, False), (16, 16, False), (37, 5, False),
+                                         (0, 3, False), (1, 0, True), (16, 16, True),
+                                         (37, 0, True)])
+def test_encode_entries_one_launch(R, S, project):
+    kv_x, cos, sin, idx_x, swa_x = _entries_case(R, S, seed=R + 3 * S + project)
+    stride, row0, swa_stride, swa_row0 = 3, 2, 2, 1
+    n_rows, n_swa = row0 + max(R - 1, 0) * stride + 2, swa_row0 + max(S - 1, 0) * swa_stride + 2
+    kc, ks, ic, isc, sw = _entries_buffers(n_rows, n_swa)
+    rng = np.random.default_rng(R)
+    w_bits = torch.from_numpy((rng.standard_normal((128, 512)) / np.sqrt(512)).astype(np.float32)).to(
+        torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    y = torch.full((max(R, 1), 128), np.nan, device=dev()) if project else None
+    L.encode_entries(t(kv_x), kc, ks, ic, isc, idx_x=None if project else t(idx_x),
+                     w_idx=t(w_bits, torch.uint16) if project else None,
+                     rope_cos=t(cos), rope_sin=t(sin), rope_offset=448, rope_dim=64,
+                     dst_row=row0, dst_stride=stride, idx_y=y,
+                     swa_x=t(swa_x) if S else None, swa_out=sw if S else None,
+                     swa_row=swa_row0, swa_stride=swa_stride)
+    kc, ks, ic, isc, sw = (a.cpu().numpy() for a in (kc, ks, ic, isc, sw))
+    rows = row0 + stride * np.arange(R)
+    other = np.setdiff1d(np.arange(n_rows), rows)
+    if R:
+        ref_c, ref_s = oracle.quantize_rows(kv_x, cos, sin, 448, 64)
+        assert np.array_equal(kc[rows], ref_c) and np.array_equal(ks[rows], ref_s)
+        if project:
+            yg = y.cpu().numpy()[:R]
+            yo = oracle.project_rows(kv_x, w_bits)
+            wd = (w_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            bound = 130 * 2.0 ** -24 * (np.abs(kv_x).astype(np.float64) @ np.abs(wd).T)
+            assert np.all(np.abs(yg - yo) <= bound)
+            ref_ic, ref_is = oracle.quantize_rows(yg.astype(np.float32))  # the kernel's own fp32 keys
+        else:
+            ref_ic, ref_is = oracle.quantize_rows(idx_x)
+        assert np.array_equal(ic[rows], ref_ic) and np.array_equal(isc[rows], ref_is)
+    for a in (kc, ks, ic, isc):
+        assert np.all(a[other] == 0xA5)
+    if S:
+        srows = swa_row0 + swa_stride * np.arange(S)
+        assert np.array_equal(sw[srows], oracle.encode_fp8(swa_x))
+        assert np.all(sw[np.setdiff1d(np.arange(n_swa), srows)] == 0xA5)
