@@ -36,10 +36,11 @@ METRIC = "CSA2 decode queries/sec per layer at 1M ctx; achieved HBM TB/s vs peak
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 PEAK_F16 = 2.5e15  # MI355X dense fp16 MFMA, flop/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_full_scan_1M_b16_traffic.txt")
-# what the scan kernel is compiled from: its source, the headers it includes and the
-# build script (flags); the traffic counters are valid only for this exact input
+# what the scan kernel is compiled from: its source, the device headers it includes
+# and the build script (flags); the traffic counters are valid only for this exact
+# input (launch.h holds only host launcher declarations)
 SCAN_SOURCES = [os.path.join(ROOT, "kv_cache_decode_mxfp4_amd", *p) for p in (
-    ("csrc", "indexer.hip"), ("csrc", "device_common.h"), ("csrc", "launch.h"), ("build.py",))]
+    ("csrc", "indexer.hip"), ("csrc", "device_common.h"), ("csrc", "dims.h"), ("build.py",))]
 CHUNK_ROWS = 1 << 18
 SCAN_EVENT_EVERY = 4
 

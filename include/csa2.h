@@ -115,8 +115,12 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
  *   rows       new compressed entries.
  *   kv_x       fp32 [rows, 512] main latent rows -> rotary (as csa2_quantize_kv,
  *              rope_cos / rope_sin [rows, rope_dim/2]) -> MXFP4 into kv_codes /
- *              kv_scales, row r at kv_codes + r*kv_stride*256 and
- *              kv_scales + r*kv_stride*32.
+ *              kv_scales, row r at cache row d = kv_dst[r] (kv_codes + d*256,
+ *              kv_scales + d*32), or d = r*kv_stride when kv_dst is NULL.
+ *   kv_dst     int64 [rows] or NULL: per-entry destination rows (each
+ *              sequence's own append position: b*n_cap + n_b); rows whose
+ *              d is outside [0, kv_cap) are skipped.  The indexer-key row r
+ *              goes to the same d.
  *   idx_x      fp32 [rows, 128] indexer-key rows encoded as they are (no
  *              rotary), or NULL: then the keys are projected from the main
  *              latent before its rotary, y = kv_x[r] . w_idx^T with
@@ -124,12 +128,21 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
  *              channel accumulated in fp32 as four partial sums of fused
  *              multiply-adds (channels c = 4m + j go to partial j, in
  *              increasing c) added as (p0 + p1) + (p2 + p3), then encoded.
- *   idx_codes, idx_scales  MXFP4 outputs, row r at + r*idx_stride*64 / *8.
+ *   idx_codes, idx_scales  MXFP4 outputs, row d at + d*64 / d*8 (d as above,
+ *              with idx_stride in place of kv_stride when kv_dst is NULL).
  *   idx_y      fp32 [rows, 128] receives the projection (NULL: not written;
  *              only used when projecting).
  *   swa_x      fp32 [swa_rows, 512] window rows -> E4M3FN (as
- *              csa2_quantize_swa), row r at swa_out + r*swa_stride*512; NULL
- *              when swa_rows == 0.
+ *              csa2_quantize_swa), row r at swa_out + d*512 with d = swa_dst[r]
+ *              (skipped outside [0, swa_cap)) or r*swa_stride; NULL when
+ *              swa_rows == 0.  Window ring ([S], state cache: the window
+ *              segment of the last 128 tokens is overwritten in place, one per
+ *              sequence and layer; [N] 2.4: a miss replays only the last n_win
+ *              tokens): token p of sequence b goes to d = b*n_win + p % n_win,
+ *              and attention reads the ring with swa_cap = n_win and
+ *              swa_end = min(p + 1, n_win) (the joint softmax does not depend
+ *              on row order).  Replaying the last n_win tokens of a prompt is
+ *              the same call with their rows and ring slots.
  * Reading: the projection takes the latent before rotary (the rotation serves
  * attention positions; the pages say only that the indexer key is projected
  * from the main KV).  The encodings are bit-exact functions of their fp32
@@ -138,10 +151,11 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
 csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* rope_cos,
                                 const float* rope_sin, int32_t rope_offset, int32_t rope_dim,
                                 uint8_t* kv_codes, uint8_t* kv_scales, int64_t kv_stride,
-                                const float* idx_x, const uint16_t* w_idx, uint8_t* idx_codes,
-                                uint8_t* idx_scales, int64_t idx_stride, float* idx_y,
-                                const float* swa_x, int32_t swa_rows, uint8_t* swa_out,
-                                int64_t swa_stride, void* stream);
+                                const int64_t* kv_dst, int64_t kv_cap, const float* idx_x,
+                                const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
+                                int64_t idx_stride, float* idx_y, const float* swa_x,
+                                int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
+                                const int64_t* swa_dst, int64_t swa_cap, void* stream);
 
 /*
  * Full-layer indexer scan ([N] 2.2, [A] 3.4: the first Full layer scores the

@@ -68,8 +68,8 @@ def load() -> ctypes.CDLL:
     L.csa2_sparse_attn_workspace.restype = sz
     L.csa2_sparse_attn_workspace.argtypes = [i32, i32, i32, i32]
     L.csa2_encode_entries.restype = st
-    L.csa2_encode_entries.argtypes = [i32, vp, vp, vp, i32, i32, vp, vp, i64, vp, vp, vp, vp, i64,
-                                      vp, vp, i32, vp, i64, vp]
+    L.csa2_encode_entries.argtypes = [i32, vp, vp, vp, i32, i32, vp, vp, i64, vp, i64, vp, vp, vp,
+                                      vp, i64, vp, vp, i32, vp, i64, vp, i64, vp]
     L.csa2_sparse_attn_rope_bf16.restype = st
     L.csa2_sparse_attn_rope_bf16.argtypes = [vp, i32, i32, vp, vp, i64, vp, i32, vp, i32, vp, i32,
                                              f32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
@@ -145,17 +145,25 @@ def quantize_swa(x, out, row_len=512, dst_row=0, dst_stride=1, stream=None):
 
 def encode_entries(kv_x, kv_codes, kv_scales, idx_codes, idx_scales, idx_x=None, w_idx=None,
                    rope_cos=None, rope_sin=None, rope_offset=0, rope_dim=0, dst_row=0, dst_stride=1,
-                   idx_y=None, swa_x=None, swa_out=None, swa_row=0, swa_stride=1, stream=None):
+                   kv_dst=None, idx_y=None, swa_x=None, swa_out=None, swa_row=0, swa_stride=1,
+                   swa_dst=None, stream=None):
     """One launch for a step's new entries: main-KV rows kv_x [rows, 512] and indexer-key
     rows (idx_x [rows, 128], or projected from kv_x by w_idx bf16 [128, 512]) into rows
-    dst_row + r*dst_stride of the flat caches; window rows swa_x [n, 512] into rows
-    swa_row + r*swa_stride of swa_out."""
+    dst_row + r*dst_stride of the flat caches (or rows kv_dst[r], int64); window rows
+    swa_x [n, 512] into rows swa_row + r*swa_stride of swa_out (or rows swa_dst[r], e.g.
+    ring slots)."""
     _dt(kv_x, torch.float32, "kv_x")
     rows = kv_x.shape[0]
     for t_, n_, rb in ((kv_codes, "kv_codes", 256), (kv_scales, "kv_scales", 32),
                        (idx_codes, "idx_codes", 64), (idx_scales, "idx_scales", 8)):
         _dt(t_, torch.uint8, n_)
-        _rows_fit(t_, rb, dst_row, dst_stride, rows, n_)
+        if kv_dst is None:
+            _rows_fit(t_, rb, dst_row, dst_stride, rows, n_)
+    kv_cap = min(kv_codes.numel() // 256, kv_scales.numel() // 32, idx_codes.numel() // 64,
+                 idx_scales.numel() // 8)
+    if kv_dst is not None:
+        _dt(kv_dst, torch.int64, "kv_dst")
+        dst_row = 0
     if idx_x is not None:
         _dt(idx_x, torch.float32, "idx_x")
     if w_idx is not None:
@@ -165,14 +173,19 @@ def encode_entries(kv_x, kv_codes, kv_scales, idx_codes, idx_scales, idx_x=None,
         _dt(swa_x, torch.float32, "swa_x")
         _dt(swa_out, torch.uint8, "swa_out")
         n_sw = swa_x.shape[0]
-        _rows_fit(swa_out, 512, swa_row, swa_stride, n_sw, "swa_out")
+        if swa_dst is None:
+            _rows_fit(swa_out, 512, swa_row, swa_stride, n_sw, "swa_out")
+        else:
+            _dt(swa_dst, torch.int64, "swa_dst")
+            swa_row = 0
+    swa_cap = swa_out.numel() // 512 if swa_out is not None else 0
     _check("csa2_encode_entries", load().csa2_encode_entries(
         rows, _p(kv_x), _p(rope_cos), _p(rope_sin), rope_offset, rope_dim,
-        _p(kv_codes) + dst_row * 256, _p(kv_scales) + dst_row * 32, dst_stride,
-        _p(idx_x), _p(w_idx), _p(idx_codes) + dst_row * 64, _p(idx_scales) + dst_row * 8,
-        dst_stride, _p(idx_y), _p(swa_x), n_sw,
+        _p(kv_codes) + dst_row * 256, _p(kv_scales) + dst_row * 32, dst_stride, _p(kv_dst),
+        kv_cap, _p(idx_x), _p(w_idx), _p(idx_codes) + dst_row * 64,
+        _p(idx_scales) + dst_row * 8, dst_stride, _p(idx_y), _p(swa_x), n_sw,
         (_p(swa_out) + swa_row * 512) if swa_out is not None else None, swa_stride,
-        _stream(stream)))
+        _p(swa_dst), swa_cap, _stream(stream)))
 
 
 def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block=8, stream=None):

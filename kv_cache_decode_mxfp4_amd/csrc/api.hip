@@ -112,14 +112,18 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
 csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* rope_cos,
                                 const float* rope_sin, int32_t rope_offset, int32_t rope_dim,
                                 uint8_t* kv_codes, uint8_t* kv_scales, int64_t kv_stride,
-                                const float* idx_x, const uint16_t* w_idx, uint8_t* idx_codes,
-                                uint8_t* idx_scales, int64_t idx_stride, float* idx_y,
-                                const float* swa_x, int32_t swa_rows, uint8_t* swa_out,
-                                int64_t swa_stride, void* stream)
+                                const int64_t* kv_dst, int64_t kv_cap, const float* idx_x,
+                                const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
+                                int64_t idx_stride, float* idx_y, const float* swa_x,
+                                int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
+                                const int64_t* swa_dst, int64_t swa_cap, void* stream)
 {
     REQUIRE(rows >= 0 && swa_rows >= 0, CSA2_ERR_INVALID_ARG, "encode_entries: negative rows");
     REQUIRE(kv_stride >= 1 && idx_stride >= 1 && swa_stride >= 1, CSA2_ERR_INVALID_ARG,
             "encode_entries: strides must be >= 1");
+    REQUIRE(kv_cap >= 0 && swa_cap >= 0, CSA2_ERR_INVALID_ARG, "encode_entries: negative capacity");
+    REQUIRE(aligned(kv_dst, 8) && aligned(swa_dst, 8), CSA2_ERR_INVALID_ARG,
+            "encode_entries: misaligned destination index array");
     REQUIRE(rope_dim >= 0 && rope_dim % 2 == 0 && rope_offset >= 0 && rope_offset % 2 == 0 &&
                 rope_offset + rope_dim <= csa2::kDim,
             CSA2_ERR_INVALID_ARG, "encode_entries: rotary range [%d, %d) not even / inside 512",
@@ -144,9 +148,10 @@ csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* ro
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_encode_entries(rows, kv_x, rope_cos, rope_sin, rope_offset,
-                                              rope_dim, kv_codes, kv_scales, kv_stride, idx_x,
-                                              w_idx, idx_codes, idx_scales, idx_stride, idx_y,
-                                              swa_x, swa_rows, swa_out, swa_stride, s),
+                                              rope_dim, kv_codes, kv_scales, kv_stride, kv_dst,
+                                              kv_cap, idx_x, w_idx, idx_codes, idx_scales,
+                                              idx_stride, idx_y, swa_x, swa_rows, swa_out,
+                                              swa_stride, swa_dst, swa_cap, s),
                   s, "encode_entries");
 }
 

@@ -36,6 +36,7 @@
 // tile, so the index -> key dependency and the Q load overlap.  Loads are
 // unconditional (clamped inside the list, masked afterwards).
 #include "device_common.h"
+#include "launch.h"
 
 namespace csa2 {
 namespace {

@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "launch.h"
+#include "dims.h"
 
 namespace csa2 {
 

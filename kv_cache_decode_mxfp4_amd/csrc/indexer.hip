@@ -22,6 +22,7 @@
 //   exact for every value within 2^28 of that maximum; the head weight absorbs
 //   the inverse power, so the score is unchanged.
 #include "device_common.h"
+#include "launch.h"
 
 namespace csa2 {
 namespace {

@@ -7,16 +7,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
-namespace csa2 {
+#include "dims.h"
 
-constexpr int kIdxHeads = 32;
-constexpr int kIdxDim = 128;
-constexpr int kHeads = 64;
-constexpr int kDim = 512;
-constexpr int kGroup = 16;
-constexpr int kBlock = 8;
-constexpr int kTopkSegment = 16384;  // elements one top-k workgroup holds
-constexpr int kTopkMaxK = 8192;
+namespace csa2 {
 
 hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, const float* cs,
                               const float* sn, int32_t rope_off, int32_t rope_dim, uint8_t* codes,
@@ -31,11 +24,12 @@ hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8
 // the fp32 projection), and the FP8 window rows.
 hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* cs, const float* sn,
                                  int32_t rope_off, int32_t rope_dim, uint8_t* kv_codes,
-                                 uint8_t* kv_scales, int64_t kv_stride, const float* idx_x,
-                                 const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
-                                 int64_t idx_stride, float* idx_y, const float* swa_x,
-                                 int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
-                                 hipStream_t stream);
+                                 uint8_t* kv_scales, int64_t kv_stride, const int64_t* kv_dst,
+                                 int64_t kv_cap, const float* idx_x, const uint16_t* w_idx,
+                                 uint8_t* idx_codes, uint8_t* idx_scales, int64_t idx_stride,
+                                 float* idx_y, const float* swa_x, int32_t swa_rows,
+                                 uint8_t* swa_out, int64_t swa_stride, const int64_t* swa_dst,
+                                 int64_t swa_cap, hipStream_t stream);
 
 hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,

@@ -6,6 +6,7 @@
 //   - FP8 E4M3FN window rows ([N] 2.3: window KV kept in FP8).
 // One thread per 16-channel group; memory-bound and tiny per decode step.
 #include "device_common.h"
+#include "launch.h"
 
 // Every product and sum of the encoders rounds on its own (the library is built
 // with -ffp-contract=off): contracting the rotary a*c - b*s into a fused
@@ -129,7 +130,7 @@ __device__ __forceinline__ void encode_row_group(const float* __restrict__ x, in
                                                  const float* __restrict__ cs,
                                                  const float* __restrict__ sn, int32_t rope_off,
                                                  int32_t rope_dim, uint8_t* __restrict__ codes,
-                                                 uint8_t* __restrict__ scales, int64_t dst_stride)
+                                                 uint8_t* __restrict__ scales, int64_t orow)
 {
     const float4* src = reinterpret_cast<const float4*>(x + r * C + 16 * g);
     float v[16];
@@ -141,7 +142,6 @@ __device__ __forceinline__ void encode_row_group(const float* __restrict__ x, in
     rope_group(v, g, r, cs, sn, rope_off, rope_dim);
     uint32_t packed[2];
     const uint32_t sb = encode_group(v, packed);
-    const int64_t orow = r * dst_stride;
     *reinterpret_cast<uint2*>(codes + orow * (C / 2) + 8 * g) = make_uint2(packed[0], packed[1]);
     scales[orow * (C / 16) + g] = (uint8_t)sb;
 }
@@ -157,7 +157,7 @@ quantize_kv_kernel(const float* __restrict__ x, int64_t rows, int32_t C,
     if (t >= rows * G)
         return;
     encode_row_group(x, t / G, (int32_t)(t % G), C, cs, sn, rope_off, rope_dim, codes, scales,
-                     dst_stride);
+                     (t / G) * dst_stride);
 }
 
 // Four consecutive elements per thread; row_len % 4 == 0.
@@ -184,16 +184,34 @@ quantize_swa_kernel(const float* __restrict__ x, int64_t n, int32_t row_len,
 // latent before its rotary (one wave per row: lane l computes channels 2l and
 // 2l+1 as four fixed-order partial sums of fp32 fused multiply-adds over the
 // 512 channels, added (p0 + p1) + (p2 + p3), then encodes them, the group of
-// 16 channels being 8 lanes); the rest encode the window rows.
+// 16 channels being 8 lanes); the rest encode the window rows.  Row r of the
+// caches goes to row kv_dst[r] (else r * stride) and window row r to row
+// swa_dst[r] (else r * swa_stride): with per-sequence positions that is each
+// sequence's own append position, and for the window a ring slot.
 struct EntryJob {
     int32_t rows;
     const float* kv_x; const float* cs; const float* sn; int32_t rope_off, rope_dim;
     uint8_t* kv_codes; uint8_t* kv_scales; int64_t kv_stride;
+    const int64_t* kv_dst;   // per-row destination row of the caches, or null (r * stride)
+    int64_t kv_cap;          // rows of the caches (destinations outside are skipped)
     const float* idx_x; const uint16_t* w_idx;
     uint8_t* idx_codes; uint8_t* idx_scales; int64_t idx_stride; float* idx_y;
     const float* swa_x; int32_t swa_rows; uint8_t* swa_out; int64_t swa_stride;
+    const int64_t* swa_dst;  // per-row destination row of the window buffer, or null
+    int64_t swa_cap;         // rows of the window buffer
     int32_t wg_kv, wg_idx;  // workgroups of the first two parts
 };
+
+// Destination row of input row r: dst[r] (-1 when outside [0, cap): skipped)
+// or r * stride.
+__device__ __forceinline__ int64_t dst_row(const int64_t* __restrict__ dst, int64_t r,
+                                           int64_t stride, int64_t cap)
+{
+    if (dst == nullptr)
+        return r * stride;
+    const int64_t d = dst[r];
+    return d >= 0 && d < cap ? d : -1;
+}
 
 __device__ __forceinline__ float max8_lanes(float m)
 {
@@ -210,18 +228,26 @@ encode_entries_kernel(EntryJob J)
     const int wg = blockIdx.x;
     if (wg < J.wg_kv) {
         const int64_t t = (int64_t)wg * 256 + threadIdx.x;
-        if (t < (int64_t)J.rows * kKv)
-            encode_row_group(J.kv_x, t / kKv, (int32_t)(t % kKv), kDim, J.cs, J.sn, J.rope_off,
-                             J.rope_dim, J.kv_codes, J.kv_scales, J.kv_stride);
+        if (t < (int64_t)J.rows * kKv) {
+            const int64_t r = t / kKv;
+            const int64_t o = dst_row(J.kv_dst, r, J.kv_stride, J.kv_cap);
+            if (o >= 0)
+                encode_row_group(J.kv_x, r, (int32_t)(t % kKv), kDim, J.cs, J.sn, J.rope_off,
+                                 J.rope_dim, J.kv_codes, J.kv_scales, o);
+        }
         return;
     }
     if (wg < J.wg_kv + J.wg_idx) {
         const int w = wg - J.wg_kv;
         if (J.idx_x != nullptr) {
             const int64_t t = (int64_t)w * 256 + threadIdx.x;
-            if (t < (int64_t)J.rows * kIdx)
-                encode_row_group(J.idx_x, t / kIdx, (int32_t)(t % kIdx), kIdxDim, nullptr,
-                                 nullptr, 0, 0, J.idx_codes, J.idx_scales, J.idx_stride);
+            if (t < (int64_t)J.rows * kIdx) {
+                const int64_t r = t / kIdx;
+                const int64_t o = dst_row(J.kv_dst, r, J.idx_stride, J.kv_cap);
+                if (o >= 0)
+                    encode_row_group(J.idx_x, r, (int32_t)(t % kIdx), kIdxDim, nullptr, nullptr,
+                                     0, 0, J.idx_codes, J.idx_scales, o);
+            }
             return;
         }
         // projection: one wave per row, 4 rows per workgroup
@@ -254,7 +280,9 @@ encode_entries_kernel(EntryJob J)
         const float amax = max8_lanes(fmaxf(fabsf(y0), fabsf(y1)));
         const uint32_t sb = group_scale(amax);
         const float sv = e4m3_value(sb);
-        const int64_t orow = r * J.idx_stride;
+        const int64_t orow = dst_row(J.kv_dst, r, J.idx_stride, J.kv_cap);
+        if (orow < 0)
+            return;
         J.idx_codes[orow * (kIdxDim / 2) + lane] =
             (uint8_t)(e2m1_nibble(y0, sv) | (e2m1_nibble(y1, sv) << 4));
         if ((lane & 7) == 0)
@@ -266,7 +294,9 @@ encode_entries_kernel(EntryJob J)
         return;
     const uint32_t word = fp8_word(reinterpret_cast<const float4*>(J.swa_x)[t]);
     const int64_t r = 4 * t / kDim, c = 4 * t % kDim;
-    *reinterpret_cast<uint32_t*>(J.swa_out + r * J.swa_stride * kDim + c) = word;
+    const int64_t o = dst_row(J.swa_dst, r, J.swa_stride, J.swa_cap);
+    if (o >= 0)
+        *reinterpret_cast<uint32_t*>(J.swa_out + o * kDim + c) = word;
 }
 
 }  // namespace
@@ -299,15 +329,16 @@ hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8
 
 hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* cs, const float* sn,
                                  int32_t rope_off, int32_t rope_dim, uint8_t* kv_codes,
-                                 uint8_t* kv_scales, int64_t kv_stride, const float* idx_x,
-                                 const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
-                                 int64_t idx_stride, float* idx_y, const float* swa_x,
-                                 int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
-                                 hipStream_t stream)
+                                 uint8_t* kv_scales, int64_t kv_stride, const int64_t* kv_dst,
+                                 int64_t kv_cap, const float* idx_x, const uint16_t* w_idx,
+                                 uint8_t* idx_codes, uint8_t* idx_scales, int64_t idx_stride,
+                                 float* idx_y, const float* swa_x, int32_t swa_rows,
+                                 uint8_t* swa_out, int64_t swa_stride, const int64_t* swa_dst,
+                                 int64_t swa_cap, hipStream_t stream)
 {
-    EntryJob J{rows, kv_x, cs, sn, rope_off, rope_dim, kv_codes, kv_scales, kv_stride,
-               idx_x, w_idx, idx_codes, idx_scales, idx_stride, idx_y,
-               swa_x, swa_rows, swa_out, swa_stride, 0, 0};
+    EntryJob J{rows, kv_x, cs, sn, rope_off, rope_dim, kv_codes, kv_scales, kv_stride, kv_dst,
+               kv_cap, idx_x, w_idx, idx_codes, idx_scales, idx_stride, idx_y,
+               swa_x, swa_rows, swa_out, swa_stride, swa_dst, swa_cap, 0, 0};
     J.wg_kv = (int32_t)(((int64_t)rows * (kDim / 16) + 255) / 256);
     J.wg_idx = idx_x != nullptr ? (int32_t)(((int64_t)rows * (kIdxDim / 16) + 255) / 256)
                                 : (int32_t)((rows + 3) / 4);

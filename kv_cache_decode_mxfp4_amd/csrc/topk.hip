@@ -25,6 +25,7 @@
 //     candidates (the global top-k is a subset of their union, and the
 //     candidate lists keep position order) until one segment remains.
 #include "device_common.h"
+#include "launch.h"
 
 namespace csa2 {
 namespace {

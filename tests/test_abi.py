@@ -123,11 +123,11 @@ def test_rope_bf16_attention_validation():
 
 
 def _entries(rows=4, kv_x=16, idx_x=16, w=None, off=448, dim=64, cos=16, swa_rows=0, swa_x=None,
-             kv_stride=1):
+             kv_stride=1, dst=None):
     vp = ctypes.c_void_p
     return _status("csa2_encode_entries", rows, vp(kv_x), vp(cos), vp(cos), off, dim, vp(16),
-                   vp(16), kv_stride, vp(idx_x), vp(w), vp(16), vp(16), 1, None, vp(swa_x),
-                   swa_rows, vp(16), 1, None)
+                   vp(16), kv_stride, None, 0, vp(idx_x), vp(w), vp(16), vp(16), 1, None,
+                   vp(swa_x), swa_rows, vp(16), 1, vp(dst), 10, None)
 
 
 def test_encode_entries_validation():
@@ -141,4 +141,6 @@ def test_encode_entries_validation():
     assert st == 1 and "window" in msg
     st, msg = _entries(kv_stride=0)
     assert st == 1
+    st, msg = _entries(dst=12)
+    assert st == 1 and "destination" in msg
     assert _entries(rows=0, kv_x=None, idx_x=None, cos=None)[0] == 0

@@ -490,3 +490,56 @@ def test_encode_entries_one_launch(R, S, project):
         srows = swa_row0 + swa_stride * np.arange(S)
         assert np.array_equal(sw[srows], oracle.encode_fp8(swa_x))
         assert np.all(sw[np.setdiff1d(np.arange(n_swa), srows)] == 0xA5)
+
+
+def test_encode_entries_per_sequence_destinations_and_ring():
+    """Sequences at different positions: each appends its entry at its own cache row and
+    its window row at ring slot p % 128; destinations outside the buffers are skipped."""
+    R, n_cap, ring = 6, 40, 128
+    kv_x, cos, sin, idx_x, swa_x = _entries_case(R, R, seed=11)
+    pos = np.array([5, 127, 128, 300, 39, 7], np.int64)       # token positions
+    n_b = np.array([3, 39, 0, 17, 39, 2], np.int64)           # append positions in the caches
+    kv_dst = np.arange(R) * n_cap + n_b
+    kv_dst[5] = R * n_cap + 3                                 # outside: skipped
+    swa_dst = np.arange(R) * ring + pos % ring
+    swa_dst[4] = -1                                           # skipped
+    kc, ks, ic, isc, sw = _entries_buffers(R * n_cap, R * ring)
+    L.encode_entries(t(kv_x), kc, ks, ic, isc, idx_x=t(idx_x), rope_cos=t(cos), rope_sin=t(sin),
+                     rope_offset=448, rope_dim=64, kv_dst=t(kv_dst), swa_x=t(swa_x), swa_out=sw,
+                     swa_dst=t(swa_dst))
+    kc, ks, ic, isc, sw = (a.cpu().numpy() for a in (kc, ks, ic, isc, sw))
+    ref_c, ref_s = oracle.quantize_rows(kv_x, cos, sin, 448, 64)
+    ref_ic, ref_is = oracle.quantize_rows(idx_x)
+    ok = np.arange(5)
+    assert np.array_equal(kc[kv_dst[ok]], ref_c[ok]) and np.array_equal(ks[kv_dst[ok]], ref_s[ok])
+    assert np.array_equal(ic[kv_dst[ok]], ref_ic[ok]) and np.array_equal(isc[kv_dst[ok]], ref_is[ok])
+    untouched = np.setdiff1d(np.arange(R * n_cap), kv_dst[ok])
+    assert all(np.all(a[untouched] == 0xA5) for a in (kc, ks, ic, isc))
+    sok = np.array([0, 1, 2, 3, 5])
+    assert np.array_equal(sw[swa_dst[sok]], oracle.encode_fp8(swa_x)[sok])
+    assert np.all(sw[np.setdiff1d(np.arange(R * ring), swa_dst[sok])] == 0xA5)
+
+
+@pytest.mark.parametrize("P", [50, 300])
+def test_window_ring_replay_matches_linear_window(P):
+    """Bounded replay of a prompt's last 128 tokens into the ring (slot p % 128) gives the
+    same attention as a linear window holding the same tokens (joint softmax: row order
+    does not matter), and both match the oracle."""
+    vc, vs, sw_unused, sel, q = _attn_case(B=1, N=2000, k=64, seed=13)
+    toks = synth.latent_rows(synth.key(14, 1, 0, P), synth.key(14, 2, 0, P), 0, P, 512)
+    lo = max(0, P - 128)
+    # linear window: every token row, attention over [P-128, P)
+    lin = torch.zeros((1, P, 512), dtype=torch.uint8, device=dev())
+    L.quantize_swa(t(toks), lin)
+    # ring: replay only the last 128 tokens into slots p % 128
+    ring = torch.zeros((1, 128, 512), dtype=torch.uint8, device=dev())
+    p = np.arange(lo, P, dtype=np.int64)
+    L.encode_entries(t(np.zeros((0, 512), np.float32)), *_entries_buffers(1, 1)[:4],
+                     idx_x=t(np.zeros((0, 128), np.float32)), swa_x=t(toks[lo:]), swa_out=ring,
+                     swa_dst=t(p % 128))
+    o_lin, l_lin = _run_attn(q, vc, vs, sel, lin.cpu().numpy(), np.array([[P]], np.int32))
+    o_ring, l_ring = _run_attn(q, vc, vs, sel, ring.cpu().numpy(),
+                               np.array([[min(P, 128)]], np.int32))
+    assert max_abs(o_ring, o_lin) <= 1e-5 and max_abs(l_ring, l_lin) <= 1e-5
+    ro, rl = oracle.attention(q[0, 0], vc[0], vs[0], sel[0, 0], lin.cpu().numpy()[0], P, 128)
+    assert max_abs(o_ring[0, 0], ro) <= ATTN_TOL and max_abs(l_ring[0, 0], rl) <= 1e-4
