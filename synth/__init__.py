@@ -133,7 +133,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 @dataclass
 class Workload:
-    """One of the five synthetic CSA2 workloads.
+    """One of the six synthetic CSA2 workloads.
 
     B sequences, nq queries each, n_cap compressed entries per sequence of which
     n_visible[b, i] are visible to query i; k = top-k, nb = pool blocks (0 = no
@@ -214,6 +214,10 @@ WORKLOADS = {
                 B=16, nq=1, n_cap=1048576, k=512, nb=2048),
     4: Workload(4, "encoder CSA2 chunked prefill (m=2), 4096 tokens of 131072, 65536 entries",
                 B=1, nq=4096, n_cap=65536, k=512, nb=0, m=2, tokens=131072, chunk=4096),
+    5: Workload(5, "decoder CSA2 chunked prefill (m=1) Full->Reindex with a 2048-block pool "
+                   "per token, 1024 tokens of 65536",
+                B=1, nq=1024, n_cap=65536, k=512, nb=2048, m=1, tokens=65536, chunk=1024,
+                layers=("full", "reindex")),
 }
 
 

@@ -148,3 +148,40 @@ def test_prefill_chunk_causal():
         ro, rl = oracle_attention(c, 0, i, 0, o_top[0, i])
         assert max_abs(out[0, i], ro) <= ATTN_TOL, f"query {i}"
     print(f"[case] prefill: near-tie swaps {swaps}", flush=True)
+
+
+def test_decoder_prefill_with_pool():
+    """Decoder chunked prefill (m = 1): every token of the chunk builds its own pool of
+    2048 blocks under its causal limit (Full) and a Reindex layer rescores that pool."""
+    w = synth.scaled(W[5], tokens=40000, chunk=64, nq=64, n_cap=40000)
+    print(f"[case] decoder prefill tokens={w.tokens} chunk={w.chunk} n_cap={w.n_cap}", flush=True)
+    c = build_case(w)
+    d = gpu_encode(c)
+    assert_encodings_equal(c, d)
+    T, k, nb = w.nq, w.k, w.nb
+    buf = layers.Buffers.create(1, T, w.n_cap, k, nb, w.n_win)
+    layers.full_indexer(buf, d["q_idx"][0], d["w_idx"][0], d["kc"], d["ks"], d["n_vis"], d["n_blk"],
+                        k, nb)
+    g_pool = buf.pool.cpu().numpy()[0].copy()
+    g_top0 = buf.topk.cpu().numpy()[0].copy()
+    layers.reindex_indexer(buf, d["q_idx"][1], d["w_idx"][1], d["kc"], d["ks"], d["n_vis"],
+                           buf.pool, k)
+    g_top1 = buf.topk.cpu().numpy()[0].copy()
+    layers.attention(buf, d["q_main"][1], d["vc"], d["vs"], buf.topk, d["swa"][1], d["swa_end"])
+    g_out1 = buf.out.cpu().numpy()[0]
+    nv = w.n_visible()[0]
+    swaps = 0
+    for i in range(T):
+        full = oracle_full(c, 0, i)
+        assert full["topk"].max() < nv[i] and full["pool"].max() < (nv[i] + 7) // 8
+        swaps += check_set(g_pool[i], full["pool"], lambda j: full["block_max"][j], f"pool {i}")
+        swaps += check_set(g_top0[i], full["topk"], lambda j: full["scores"][j], f"top-k {i}")
+        if np.array_equal(g_pool[i], full["pool"]):
+            ri = oracle.reindex_layer(c.q_idx[1][0, i], c.w_idx[1][0, i], c.o_kc[0], c.o_ks[0],
+                                      int(nv[i]), full["pool"], k)
+            sc = dict(zip(ri["pool_pos"].tolist(), ri["pool_scores"].tolist()))
+            swaps += check_set(g_top1[i], ri["topk"], lambda j: sc[j], f"reindex {i}")
+            if (i % 8 == 0 or i == T - 1) and np.array_equal(g_top1[i], ri["topk"]):
+                ro, _ = oracle_attention(c, 0, i, 1, ri["topk"])
+                assert max_abs(g_out1[i], ro) <= ATTN_TOL, f"attention query {i}"
+    print(f"[case] decoder prefill: near-tie swaps {swaps}", flush=True)

@@ -117,3 +117,7 @@ def test_fullsize_cfg2_group_of_four():
 def test_fullsize_cfg4_prefill():
     _run(synth.WORKLOADS[4], sample_seqs=[0],
          sample_queries=list(range(0, 4096, 256)) + [1, 2047, 4095])
+
+
+def test_fullsize_cfg5_decoder_prefill_with_pool():
+    _run(synth.WORKLOADS[5], sample_seqs=[0], sample_queries=[0, 1, 511, 1023])

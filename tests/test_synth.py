@@ -42,3 +42,12 @@ def test_workload_visibility_and_windows():
     assert w.new_entries() == (63488, 2048)
     d = synth.WORKLOADS[3]
     assert d.n_visible().shape == (16, 1) and d.new_entries() == (1048575, 1)
+
+
+def test_decoder_prefill_visibility():
+    # m = 1: entry j is token j; token t of the chunk sees entries [0, t + 1)
+    w = synth.WORKLOADS[5]
+    nv = w.n_visible()[0]
+    assert nv[0] == 65536 - 1024 + 1 and nv[-1] == 65536 and np.all(np.diff(nv) == 1)
+    assert w.new_entries() == (64512, 1024) and w.swa_rows() == 127 + 1024
+    assert w.layers == ("full", "reindex") and w.nb == 2048
