@@ -55,6 +55,12 @@ def parse():
                     help="query rows of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--kv-production", choices=["rows", "project"], default="rows",
+                    help="indexer key of each new entry: its own synthetic row (default), or "
+                         "projected from the new main-KV latent by a bf16 [128, 512] matrix")
+    ap.add_argument("--attn-out", choices=["fp32", "bf16"], default="fp32",
+                    help="attention output: fp32 (default), or rotated back by the query's "
+                         "position and cast to bf16 in the kernel epilogue")
     return ap.parse_args()
 
 
@@ -110,13 +116,28 @@ def build_device(w: synth.Workload, torch, L):
     st["new_sin"] = torch.from_numpy(np.tile(sin, (B, 1))).to(dev)
     new_tok = w.chunk if not w.decode else 1
     st["new_swa_row"] = w.swa_rows() - new_tok
+    # per-sequence destinations of the new rows (each sequence's own append position and
+    # its window slot; the decode window is the ring slot of the newest token)
+    st["kv_dst"] = torch.from_numpy((np.arange(B, dtype=np.int64)[:, None] * N + first +
+                                     np.arange(count)[None, :]).reshape(-1)).to(dev)
+    st["swa_dst"] = torch.from_numpy((np.arange(B, dtype=np.int64)[:, None] * w.swa_rows() +
+                                      st["new_swa_row"] + np.arange(new_tok)[None, :])
+                                     .reshape(-1)).to(dev)
+    st["w_proj"] = torch.from_numpy(synth.w_proj(w)).to(dev)
+    # rotary angles of each query row's own position (its last visible entry), for the
+    # bf16 output epilogue
+    qpos = (w.n_visible().reshape(-1).astype(np.int64) - 1)
+    p0 = int(qpos.min())
+    qc, qs = synth.rope_rows(p0, int(qpos.max()) - p0 + 1)
+    st["q_cos"] = torch.from_numpy(np.ascontiguousarray(qc[qpos - p0])).to(dev)
+    st["q_sin"] = torch.from_numpy(np.ascontiguousarray(qs[qpos - p0])).to(dev)
     st["new_swa"] = torch.from_numpy(np.concatenate(
         [synth.swa_rows(w, 0, b, st["new_swa_row"], new_tok) for b in range(B)])).to(dev)
     torch.cuda.synchronize()
     return st
 
 
-def make_step(st, torch, L, layers):
+def make_step(st, torch, L, layers, kv_production="rows", attn_out="fp32"):
     """The timed step: one layer group of the workload over the whole batch."""
     w = st["w"]
     B, nq, N = w.B, w.nq, w.n_cap
@@ -130,18 +151,28 @@ def make_step(st, torch, L, layers):
     def encode_new():
         if w.decode:
             # one launch: per sequence, the main-KV and indexer-key entry N-1 of its
-            # [N]-row caches and the newest row of its window
+            # [N]-row caches and the newest (ring) row of its window
+            project = kv_production == "project"
             L.encode_entries(st["new_kv"], st["vc"], st["vs"], st["kc"], st["ks"],
-                             idx_x=st["new_idx"], rope_cos=st["new_cos"], rope_sin=st["new_sin"],
+                             idx_x=None if project else st["new_idx"],
+                             w_idx=st["w_proj"] if project else None,
+                             rope_cos=st["new_cos"], rope_sin=st["new_sin"],
                              rope_offset=synth.ROPE_OFFSET, rope_dim=synth.ROPE_DIM,
-                             dst_row=first, dst_stride=N, swa_x=st["new_swa"],
-                             swa_out=st["swa"][0], swa_row=st["new_swa_row"],
-                             swa_stride=w.swa_rows())
+                             kv_dst=st["kv_dst"], swa_x=st["new_swa"], swa_out=st["swa"][0],
+                             swa_dst=st["swa_dst"])
         else:
             L.quantize_kv(st["new_idx"], st["kc"], st["ks"], dst_row=first)
             L.quantize_kv(st["new_kv"], st["vc"], st["vs"], st["new_cos"], st["new_sin"],
                           synth.ROPE_OFFSET, synth.ROPE_DIM, dst_row=first)
             L.quantize_swa(st["new_swa"], st["swa"][0], dst_row=st["new_swa_row"])
+
+    out16 = (torch.empty(B, nq, 64, 512, dtype=torch.int16, device=buf.out.device)
+             if attn_out == "bf16" else None)
+
+    def attn(layer):
+        layers.attention(buf, st["q_main"][layer], st["vc"], st["vs"], buf.topk, st["swa"][layer],
+                         st["swa_end"], w.n_win, out_bf16=out16, rope_cos=st["q_cos"],
+                         rope_sin=st["q_sin"])
 
     def step(time_scan=False):
         encode_new()
@@ -156,14 +187,12 @@ def make_step(st, torch, L, layers):
         L.index_pool(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], buf.sel_blocks,
                      st["n_vis"], buf.pool_score, buf.pool_idx)
         L.topk(buf.pool_score, w.k, buf.topk, idx=buf.pool_idx, ws=buf.ws_topk)
-        layers.attention(buf, st["q_main"][0], st["vc"], st["vs"], buf.topk, st["swa"][0],
-                         st["swa_end"], w.n_win)
+        attn(0)
         if "reindex" in w.layers:
             layers.reindex_indexer(buf, st["q_idx"][1], st["w_idx"][1], st["kc"], st["ks"],
                                    st["n_vis"], buf.pool, w.k)
             for layer in range(1, len(w.layers)):
-                layers.attention(buf, st["q_main"][layer], st["vc"], st["vs"], buf.topk,
-                                 st["swa"][layer], st["swa_end"], w.n_win)
+                attn(layer)
 
     return step, scan_events
 
@@ -282,7 +311,7 @@ def main():
     w = synth.WORKLOADS[args.config]
     log(f"workload: {w.name}")
     st = build_device(w, torch, L)
-    step, scan_events = make_step(st, torch, L, layers)
+    step, scan_events = make_step(st, torch, L, layers, args.kv_production, args.attn_out)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -341,7 +370,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "queries_per_seq": w.nq, "n_cap": w.n_cap,
                    "topk": w.k, "pool_blocks": w.nb, "block": w.block, "n_win": w.n_win,
-                   "indexer": "32x128", "attention": "64x512", "layers": list(w.layers)},
+                   "indexer": "32x128", "attention": "64x512", "layers": list(w.layers),
+                   "kv_production": args.kv_production, "attn_out": args.attn_out},
         "roofline": roof,
     }
     if w.decode:

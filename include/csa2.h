@@ -124,10 +124,11 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
  *   idx_x      fp32 [rows, 128] indexer-key rows encoded as they are (no
  *              rotary), or NULL: then the keys are projected from the main
  *              latent before its rotary, y = kv_x[r] . w_idx^T with
- *   w_idx      bf16 [128, 512] (row o = output channel o), each output
- *              channel accumulated in fp32 as four partial sums of fused
- *              multiply-adds (channels c = 4m + j go to partial j, in
- *              increasing c) added as (p0 + p1) + (p2 + p3), then encoded.
+ *   w_idx      bf16 [128, 512] (row o = output channel o).  Each output
+ *              channel is accumulated in fp32: per quarter Q of the 512
+ *              channels, four partial sums of fused multiply-adds (channel c
+ *              to partial c % 4, in increasing c) added as (p0 + p1) + (p2 + p3);
+ *              then the quarters as (Q0 + Q1) + (Q2 + Q3); then encoded.
  *   idx_codes, idx_scales  MXFP4 outputs, row d at + d*64 / d*8 (d as above,
  *              with idx_stride in place of kv_stride when kv_dst is NULL).
  *   idx_y      fp32 [rows, 128] receives the projection (NULL: not written;

@@ -181,9 +181,11 @@ quantize_swa_kernel(const float* __restrict__ x, int64_t n, int32_t row_len,
 // Workgroups [0, wg_kv) encode the main-KV rows (rotary + MXFP4, one thread per
 // 16-channel group); [wg_kv, wg_kv + wg_idx) the indexer-key rows, either from
 // their own fp32 rows (one thread per group) or projected from the main
-// latent before its rotary (one wave per row: lane l computes channels 2l and
-// 2l+1 as four fixed-order partial sums of fp32 fused multiply-adds over the
-// 512 channels, added (p0 + p1) + (p2 + p3), then encodes them, the group of
+// latent before its rotary (one workgroup per row: wave q sums channels
+// [128q, 128q+128) for every output in four fixed-order partial sums of fp32
+// fused multiply-adds (channel c to partial c % 4, in increasing c), adds
+// them (p0 + p1) + (p2 + p3), the four quarters are added (q0 + q1) + (q2 + q3),
+// and wave 0 encodes the row, lane l holding channels 2l and 2l+1, a group of
 // 16 channels being 8 lanes); the rest encode the window rows.  Row r of the
 // caches goes to row kv_dst[r] (else r * stride) and window row r to row
 // swa_dst[r] (else r * swa_stride): with per-sequence positions that is each
@@ -225,6 +227,7 @@ encode_entries_kernel(EntryJob J)
 {
     constexpr int kKv = kDim / 16;       // 32 groups per main-KV row
     constexpr int kIdx = kIdxDim / 16;   // 8 groups per indexer-key row
+    constexpr int kSlice4 = kDim / 4;    // projection channels per wave
     const int wg = blockIdx.x;
     if (wg < J.wg_kv) {
         const int64_t t = (int64_t)wg * 256 + threadIdx.x;
@@ -250,30 +253,54 @@ encode_entries_kernel(EntryJob J)
             }
             return;
         }
-        // projection: one wave per row, 4 rows per workgroup
+        // projection: one workgroup per row; wave q sums channels [128q, 128q+128) for
+        // every output (lane l: outputs 2l, 2l+1), loads one 16-channel step ahead
+        __shared__ float part[4][kIdxDim];
         const int lane = threadIdx.x & 63;
-        const int64_t r = (int64_t)w * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        if (r >= J.rows)
-            return;
-        const float4* xr = reinterpret_cast<const float4*>(J.kv_x + r * kDim);
-        const uint4* w0 = reinterpret_cast<const uint4*>(J.w_idx + (int64_t)(2 * lane) * kDim);
-        const uint4* w1 = reinterpret_cast<const uint4*>(J.w_idx + (int64_t)(2 * lane + 1) * kDim);
+        const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int64_t r = w;
+        const float4* xr = reinterpret_cast<const float4*>(J.kv_x + r * kDim + kSlice4 * q);
+        const uint4* w0 = reinterpret_cast<const uint4*>(J.w_idx + (int64_t)(2 * lane) * kDim +
+                                                         kSlice4 * q);
+        const uint4* w1 = reinterpret_cast<const uint4*>(J.w_idx + (int64_t)(2 * lane + 1) * kDim +
+                                                         kSlice4 * q);
         float p0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int j = 0; j < kDim / 8; ++j) {  // 8 channels: c = 8j + i, partial sum i % 4
-            const float4 xa = xr[2 * j], xb = xr[2 * j + 1];
-            const float xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-            const uint4 a = w0[j], bw = w1[j];
-            const uint32_t da[4] = {a.x, a.y, a.z, a.w}, db[4] = {bw.x, bw.y, bw.z, bw.w};
+        float4 xa[4];
+        uint4 wa[2], wb[2];
+        auto load = [&](int j) {  // channels 16j .. 16j+15 of the quarter
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float wa = __uint_as_float(i % 2 == 0 ? da[i / 2] << 16 : da[i / 2] & 0xFFFF0000u);
-                const float wb = __uint_as_float(i % 2 == 0 ? db[i / 2] << 16 : db[i / 2] & 0xFFFF0000u);
-                p0[i % 4] = __builtin_fmaf(xs[i], wa, p0[i % 4]);
-                p1[i % 4] = __builtin_fmaf(xs[i], wb, p1[i % 4]);
+            for (int i = 0; i < 4; ++i)
+                xa[i] = xr[4 * j + i];
+            wa[0] = w0[2 * j]; wa[1] = w0[2 * j + 1];
+            wb[0] = w1[2 * j]; wb[1] = w1[2 * j + 1];
+        };
+        load(0);
+#pragma unroll
+        for (int j = 0; j < kSlice4 / 16; ++j) {
+            const float xs[16] = {xa[0].x, xa[0].y, xa[0].z, xa[0].w, xa[1].x, xa[1].y, xa[1].z,
+                                  xa[1].w, xa[2].x, xa[2].y, xa[2].z, xa[2].w, xa[3].x, xa[3].y,
+                                  xa[3].z, xa[3].w};
+            const uint32_t da[8] = {wa[0].x, wa[0].y, wa[0].z, wa[0].w, wa[1].x, wa[1].y, wa[1].z, wa[1].w};
+            const uint32_t db[8] = {wb[0].x, wb[0].y, wb[0].z, wb[0].w, wb[1].x, wb[1].y, wb[1].z, wb[1].w};
+            if (j + 1 < kSlice4 / 16)
+                load(j + 1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float fa = __uint_as_float(i % 2 == 0 ? da[i / 2] << 16 : da[i / 2] & 0xFFFF0000u);
+                const float fb = __uint_as_float(i % 2 == 0 ? db[i / 2] << 16 : db[i / 2] & 0xFFFF0000u);
+                p0[i % 4] = __builtin_fmaf(xs[i], fa, p0[i % 4]);
+                p1[i % 4] = __builtin_fmaf(xs[i], fb, p1[i % 4]);
             }
         }
-        const float y0 = __fadd_rn(__fadd_rn(p0[0], p0[1]), __fadd_rn(p0[2], p0[3]));
-        const float y1 = __fadd_rn(__fadd_rn(p1[0], p1[1]), __fadd_rn(p1[2], p1[3]));
+        part[q][2 * lane] = __fadd_rn(__fadd_rn(p0[0], p0[1]), __fadd_rn(p0[2], p0[3]));
+        part[q][2 * lane + 1] = __fadd_rn(__fadd_rn(p1[0], p1[1]), __fadd_rn(p1[2], p1[3]));
+        __syncthreads();
+        if (q != 0)
+            return;
+        const float y0 = __fadd_rn(__fadd_rn(part[0][2 * lane], part[1][2 * lane]),
+                                   __fadd_rn(part[2][2 * lane], part[3][2 * lane]));
+        const float y1 = __fadd_rn(__fadd_rn(part[0][2 * lane + 1], part[1][2 * lane + 1]),
+                                   __fadd_rn(part[2][2 * lane + 1], part[3][2 * lane + 1]));
         if (J.idx_y != nullptr)
             *reinterpret_cast<float2*>(J.idx_y + r * kIdxDim + 2 * lane) = make_float2(y0, y1);
         // group of 16 channels = lanes 8g .. 8g+7
@@ -341,7 +368,7 @@ hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* c
                swa_x, swa_rows, swa_out, swa_stride, swa_dst, swa_cap, 0, 0};
     J.wg_kv = (int32_t)(((int64_t)rows * (kDim / 16) + 255) / 256);
     J.wg_idx = idx_x != nullptr ? (int32_t)(((int64_t)rows * (kIdxDim / 16) + 255) / 256)
-                                : (int32_t)((rows + 3) / 4);
+                                : rows;
     const int64_t w_swa = ((int64_t)swa_rows * (kDim / 4) + 255) / 256;
     const int64_t grid = (int64_t)J.wg_kv + J.wg_idx + w_swa;
     if (grid == 0)

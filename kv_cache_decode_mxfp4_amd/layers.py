@@ -114,7 +114,14 @@ def reindex_indexer(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, po
 
 
 def attention(buf: Buffers, q, kv_codes, kv_scales, topk, swa, swa_end, n_win: int = 128,
-              scale: float = 1.0, stream=None):
-    """Sparse MLA attention of one layer (every mode ends with it)."""
-    _lib.sparse_attn(q, kv_codes, kv_scales, topk, swa, swa_end, buf.out, buf.lse, n_win=n_win,
-                     softmax_scale=scale, ws=buf.ws_attn, stream=stream)
+              scale: float = 1.0, stream=None, out_bf16=None, rope_cos=None, rope_sin=None):
+    """Sparse MLA attention of one layer (every mode ends with it).  With out_bf16 (and the
+    query rows' rope_cos / rope_sin) the output is rotated back and cast to bf16 there
+    instead of written as fp32 to buf.out."""
+    if out_bf16 is None:
+        _lib.sparse_attn(q, kv_codes, kv_scales, topk, swa, swa_end, buf.out, buf.lse,
+                         n_win=n_win, softmax_scale=scale, ws=buf.ws_attn, stream=stream)
+    else:
+        _lib.sparse_attn_rope_bf16(q, kv_codes, kv_scales, topk, swa, swa_end, rope_cos, rope_sin,
+                                   out_bf16, buf.lse, n_win=n_win, softmax_scale=scale,
+                                   ws=buf.ws_attn, stream=stream)

@@ -33,6 +33,7 @@ TAG_SWA_OUT = 5
 TAG_Q_IDX = 6
 TAG_W_IDX = 7
 TAG_Q_MAIN = 8
+TAG_W_PROJ = 9
 
 SEED = 0
 P_OUTLIER = 1e-3
@@ -264,6 +265,14 @@ def w_idx(w: Workload, layer: int, B: int | None = None) -> np.ndarray:
     for b in range(B):
         out[b] = uniform_f32(key(w.config, TAG_W_IDX, layer, b), 0, n)
     return out.reshape(B, w.nq, w.h_idx)
+
+
+def w_proj(w: Workload) -> np.ndarray:
+    """Indexer-key projection of the main latent, bf16 bits [128, 512], N(0, 1/512), so a
+    projected key of an RMS-normalised latent row has unit variance per channel like the
+    synthetic indexer keys."""
+    return normal_bf16(key(w.config, TAG_W_PROJ, 0, 0), 0, w.d_idx * w.d,
+                       1.0 / np.sqrt(w.d)).reshape(w.d_idx, w.d)
 
 
 def q_main(w: Workload, layer: int, B: int | None = None) -> np.ndarray:
