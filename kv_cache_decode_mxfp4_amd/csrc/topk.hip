@@ -9,8 +9,10 @@
 // registers, 16 per thread (slot i of thread t is element 1024*i + t, so loads
 // are coalesced and position order is slot-major).  The k-th largest key is
 // found by an adaptive-range radix select: each pass histograms the live key
-// range [lo, hi] into at most 8192 equal LDS bins and keeps the bin holding the
-// k-th key, shrinking the span by at least 2^13 (three passes at most).  One
+// range [lo, hi] into at most 4096 equal LDS bins and keeps the bin holding the
+// k-th key, shrinking the span by at least 2^12 (three passes at most; 4096
+// bins, 4 per thread, keep a pass's prefix step short — measured faster than
+// 8192 or 2048 on score-like data).  One
 // ballot round then gives every chosen entry its output offset:
 //   offset = (#greater before it) + min(#equal before it, #equal to take).
 //
@@ -33,8 +35,12 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kPer = kTopkSegment / kThreads;  // 16
 constexpr int kNumWaves = kThreads / kWave;    // 16
-constexpr int kBinBits = 13;
-constexpr int kBins = 1 << kBinBits;           // 8192 bins, 8 per thread
+#ifndef CSA2_TOPK_BIN_BITS
+#define CSA2_TOPK_BIN_BITS 12
+#endif
+constexpr int kBinBits = CSA2_TOPK_BIN_BITS;
+constexpr int kBins = 1 << kBinBits;           // radix bins per pass
+constexpr int kBpt = kBins / kThreads;         // bins per thread
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -110,13 +116,13 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
             if (key[i] >= lo && key[i] <= hi)
                 atomicAdd(&sm.hist[buf][(key[i] - lo) >> shift], 1u);
         __syncthreads();
-        // thread t owns bins 8t .. 8t+7
-        uint32_t c[8], mine = 0;
+        // thread t owns bins kBpt*t .. kBpt*t + kBpt - 1
+        uint32_t c[kBpt], mine = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            c[j] = sm.hist[buf][8 * tid + j];
+        for (int j = 0; j < kBpt; ++j) {
+            c[j] = sm.hist[buf][kBpt * tid + j];
             mine += c[j];
-            sm.hist[buf ^ 1][8 * tid + j] = 0u;  // clear the buffer of the next pass
+            sm.hist[buf ^ 1][kBpt * tid + j] = 0u;  // clear the buffer of the next pass
         }
         const uint32_t incl = wave_prefix_sum(mine, lane);
         if (lane == kWave - 1)
@@ -129,11 +135,11 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
             before += i < wave ? v : 0u;
             all += v;
         }
-        uint32_t above = all - (before + incl);  // keys in bins above 8t+7
+        uint32_t above = all - (before + incl);  // keys in bins above this thread's
 #pragma unroll
-        for (int j = 7; j >= 0; --j) {
+        for (int j = kBpt - 1; j >= 0; --j) {
             if (above < need && above + c[j] >= need) {
-                sm.bcast[buf][0] = 8u * tid + j;
+                sm.bcast[buf][0] = (uint32_t)(kBpt * tid + j);
                 sm.bcast[buf][1] = above;
             }
             above += c[j];
