@@ -100,7 +100,8 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
         lo = min(lo, sm.wave_a[1][i]);
         hi = max(hi, sm.wave_a[2][i]);
     }
-    __syncthreads();
+    // no barrier here: wave_a is next written after the first pass's barrier (or
+    // in the next call, after place()'s barriers), when every wave has read it
     Pick pk{0u, 0u};
     if (total <= k)
         return pk;
