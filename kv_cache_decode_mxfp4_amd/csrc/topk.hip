@@ -12,7 +12,10 @@
 // range [lo, hi] into at most 4096 equal LDS bins and keeps the bin holding the
 // k-th key, shrinking the span by at least 2^12 (three passes at most; 4096
 // bins, 4 per thread, keep a pass's prefix step short — measured faster than
-// 8192 or 2048 on score-like data).  One
+// 8192 or 2048 on score-like data).  Once the chosen bin holds at most 64
+// keys (on score-like data, after the first pass) they are gathered into LDS
+// and one wave ranks them against each other instead of running another
+// pass, whose cost is the same per key however few keys are live.  One
 // ballot round then gives every chosen entry its output offset:
 //   offset = (#greater before it) + min(#equal before it, #equal to take).
 //
@@ -60,8 +63,11 @@ struct Smem {
     uint32_t part_gt[kPer * kNumWaves];
     uint32_t part_eq[kPer * kNumWaves];
     uint32_t wave_a[3][kNumWaves];
-    uint32_t bcast[2][2];
+    uint32_t bcast[2][3];
     uint32_t totals[2];
+    uint32_t few_n;             // keys appended to few_key
+    uint32_t few_key[kWave];    // the keys of a small chosen bin
+    uint32_t few_pick[2];       // (threshold, keys equal to it to take)
 };
 
 struct Pick {
@@ -90,6 +96,8 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
         sm.wave_a[1][wave] = lo;
         sm.wave_a[2][wave] = hi;
     }
+    if (tid == 0)
+        sm.few_n = 0u;
     __syncthreads();
     uint32_t total = 0;
     lo = 0xFFFFFFFFu;
@@ -105,17 +113,20 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
     Pick pk{0u, 0u};
     if (total <= k)
         return pk;
-    uint32_t need = k;
+    uint32_t need = k, live = total;  // live: keys inside [lo, hi]
     // invariant: the threshold is the need-th largest key inside [lo, hi]
     for (int pass = 0; pass < 4 && hi != lo; ++pass) {
         const int buf = pass & 1;
         const uint32_t span = hi - lo;
         const int bits = 32 - __builtin_clz(span);
         const int shift = bits > kBinBits ? bits - kBinBits : 0;
+        // key - lo wraps above span for keys below lo (the invalid key 0 too)
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (key[i] >= lo && key[i] <= hi)
-                atomicAdd(&sm.hist[buf][(key[i] - lo) >> shift], 1u);
+        for (int i = 0; i < kPer; ++i) {
+            const uint32_t d = key[i] - lo;
+            if (d <= span)
+                atomicAdd(&sm.hist[buf][d >> shift], 1u);
+        }
         __syncthreads();
         // thread t owns bins kBpt*t .. kBpt*t + kBpt - 1
         uint32_t c[kBpt], mine = 0;
@@ -142,31 +153,114 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
             if (above < need && above + c[j] >= need) {
                 sm.bcast[buf][0] = (uint32_t)(kBpt * tid + j);
                 sm.bcast[buf][1] = above;
+                sm.bcast[buf][2] = c[j];
             }
             above += c[j];
         }
         __syncthreads();
         const uint32_t bin = sm.bcast[buf][0];
+        const uint32_t in_bin = sm.bcast[buf][2];
         need -= sm.bcast[buf][1];
+        live = in_bin;
         lo = lo + (bin << shift);
         const uint64_t top = (uint64_t)lo + ((1ull << shift) - 1ull);
         hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+        if (in_bin <= (uint32_t)kWave && hi != lo) {
+            // Few keys left in [lo, hi]: gather them and rank them in one wave
+            // instead of another histogram pass.
+            const uint32_t width = hi - lo;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+                if (key[i] - lo <= width) {
+                    const uint32_t p = atomicAdd(&sm.few_n, 1u);
+                    if (p < (uint32_t)kWave)
+                        sm.few_key[p] = key[i];
+                }
+            __syncthreads();
+            if (wave == 0) {
+                const uint32_t v = lane < (int)in_bin ? sm.few_key[lane] : 0u;
+                uint32_t gt = 0, eq = 0;
+                for (uint32_t j = 0; j < in_bin; ++j) {
+                    const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)j);
+                    gt += u > v ? 1u : 0u;
+                    eq += u == v ? 1u : 0u;
+                }
+                // the need-th largest of the gathered keys: gt < need <= gt + eq
+                if (lane < (int)in_bin && gt < need && need <= gt + eq) {
+                    // when every key equal to v is taken, "above v - 1" says the same
+                    const bool all = need == gt + eq;
+                    sm.few_pick[0] = all ? v - 1u : v;
+                    sm.few_pick[1] = all ? 0u : need - gt;
+                }
+            }
+            __syncthreads();
+            pk.T = sm.few_pick[0];
+            pk.need = sm.few_pick[1];
+            return pk;
+        }
     }
-    pk.T = lo;
-    pk.need = need;
+    // every key left equals lo
+    pk.T = need == live ? lo - 1u : lo;
+    pk.need = need == live ? 0u : need;
     return pk;
 }
 
+// Exclusive scan, in position order, of the 256 (slot, wave) counts part[] in
+// place by one wave (4 per lane); returns the total on every lane.
+__device__ __forceinline__ uint32_t scan_parts(uint32_t* part, int lane)
+{
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        c[j] = part[4 * lane + j];
+        sum += c[j];
+    }
+    const uint32_t incl = wave_prefix_sum(sum, lane);
+    uint32_t run = incl - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        part[4 * lane + j] = run;
+        run += c[j];
+    }
+    return (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+}
+
 // Marks the chosen slots and their output offsets (position order); returns
-// how many were chosen.
+// how many were chosen.  pk.need == 0 (every key equal to the threshold is
+// taken, or there is none) needs only the "above" ballots.
 __device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPer],
                           uint32_t (&off)[kPer], Smem& sm, int lane, int wave)
 {
+    if (pk.need == 0u) {
+        uint32_t gt_below[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const uint64_t bg = __ballot(key[i] > pk.T);
+            gt_below[i] = lanes_below(bg, lane);
+            if (lane == 0)
+                sm.part_gt[i * kNumWaves + wave] = (uint32_t)__popcll(bg);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const uint32_t all = scan_parts(sm.part_gt, lane);
+            if (lane == 0)
+                sm.totals[0] = all;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            take[i] = key[i] > pk.T;
+            off[i] = sm.part_gt[i * kNumWaves + wave] + gt_below[i];
+        }
+        const uint32_t n_gt = sm.totals[0];
+        __syncthreads();
+        return n_gt;
+    }
     uint32_t gt_below[kPer], eq_below[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const uint64_t bg = __ballot(key[i] > pk.T);
-        const uint64_t be = __ballot(pk.T != 0u && key[i] == pk.T);
+        const uint64_t be = __ballot(key[i] == pk.T);
         gt_below[i] = lanes_below(bg, lane);
         eq_below[i] = lanes_below(be, lane);
         if (lane == 0) {
@@ -176,31 +270,16 @@ __device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPe
     }
     __syncthreads();
     if (wave < 2) {
-        // exclusive scan of 256 (slot, wave) counts in position order, 4 per lane
-        uint32_t* part = wave == 0 ? sm.part_gt : sm.part_eq;
-        uint32_t c[4], sum = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            c[j] = part[4 * lane + j];
-            sum += c[j];
-        }
-        const uint32_t incl = wave_prefix_sum(sum, lane);
-        uint32_t run = incl - sum;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            part[4 * lane + j] = run;
-            run += c[j];
-        }
-        if (lane == kWave - 1)
-            sm.totals[wave] = incl;
+        const uint32_t all = scan_parts(wave == 0 ? sm.part_gt : sm.part_eq, lane);
+        if (lane == 0)
+            sm.totals[wave] = all;
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const uint32_t gt_before = sm.part_gt[i * kNumWaves + wave] + gt_below[i];
         const uint32_t eq_before = sm.part_eq[i * kNumWaves + wave] + eq_below[i];
-        const bool eq = pk.T != 0u && key[i] == pk.T;
-        take[i] = key[i] > pk.T || (eq && eq_before < pk.need);
+        take[i] = key[i] > pk.T || (key[i] == pk.T && eq_before < pk.need);
         off[i] = gt_before + (eq_before < pk.need ? eq_before : pk.need);
     }
     const uint32_t n_gt = sm.totals[0], n_eq = sm.totals[1];

@@ -159,13 +159,20 @@ def test_quantize_swa_bit_exact():
 
 # ------------------------------------------------------------------ top-k
 
-def _topk_case(rng, rows, Lr, kind):
+def _topk_case(rng, rows, Lr, kind, k=1):
     if kind == "ties":
         s = np.round(rng.standard_normal((rows, Lr)), 1).astype(np.float32)
     elif kind == "allequal":
         s = np.zeros((rows, Lr), np.float32)
     else:
         s = rng.standard_normal((rows, Lr)).astype(np.float32) * 10
+        if kind == "near_ties":
+            # eight equal scores straddling rank k-1 of the full row: the bin that
+            # holds the k-th key is small but not all of its equal keys are taken
+            for r in range(rows):
+                o = np.argsort(-s[r], kind="stable")
+                a = max(0, min(k, Lr) - 4)
+                s[r, o[a:a + 8]] = s[r, o[a]]
     s[:, ::97] = -0.0
     s[:, 5::211] = np.nan
     s[:, 7::301] = -np.inf
@@ -175,11 +182,11 @@ def _topk_case(rng, rows, Lr, kind):
 @pytest.mark.parametrize("Lr,k", [(1, 1), (100, 7), (2048, 64), (16384, 2048), (16385, 512),
                                   (40000, 512), (131072, 2048), (131072, 512), (300000, 512), (300000, 2048),
                                   (50000, 6000)])
-@pytest.mark.parametrize("kind", ["random", "ties"])
+@pytest.mark.parametrize("kind", ["random", "ties", "near_ties"])
 def test_topk_bit_exact(Lr, k, kind):
     rng = np.random.default_rng(Lr + k)
     rows = 3
-    s = _topk_case(rng, rows, Lr, kind)
+    s = _topk_case(rng, rows, Lr, kind, k)
     n_valid = np.array([Lr, max(0, Lr - 13), min(Lr, k // 2)], np.int32)
     out = torch.empty(rows, k, dtype=torch.int32, device=dev())
     ws_n = L.topk_workspace(Lr, rows, k)
