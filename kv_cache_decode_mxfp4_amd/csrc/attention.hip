@@ -4,37 +4,51 @@
 // 512-dim latent, top-k compressed entries plus 128 window entries).  One
 // joint softmax over both key sets; no de-duplication; no sink.
 //
-// Decomposition: one workgroup per (query row, group of 16 heads, slice of 128
-// output dims), 16 workgroups per query row, so the output needs no
-// cross-workgroup combine.  The key list (window rows first, then the top-k
-// slots) is cut into tiles of 32 keys; wave w of the 8 waves of the workgroup
-// takes every eighth tile and keeps its own online-softmax state, with no
-// barrier inside the loop.  Per tile and wave (MFMA v_mfma_f32_16x16x32_f16):
+// Two decompositions of the same computation, picked by the number of query
+// rows (both: tiles of 32 keys, MFMA v_mfma_f32_16x16x32_f16, keys dequantised
+// exactly to fp16 straight into the MFMA operand and stored row-major to an
+// LDS tile (K = V), online softmax in the log2 domain, P split into two fp16
+// terms (hi + lo) so P V keeps ~22 bits of P):
+//
+// Spread (few rows, decode: 16 rows fill the 256 CUs): one workgroup per
+// (query row, group of 16 heads, slice of 128 output dims), 16 workgroups per
+// row, so a row's work is spread over 16 CUs and nothing is combined across
+// workgroups.  Each workgroup scores its 16 heads against the full 512
+// channels of every key (the four slices of a head group repeat that work, the
+// price of the spread).  Wave w of 8 takes every eighth tile and keeps its own
+// softmax state, with no barrier inside the loop; the waves meet in LDS at the
+// end and are merged in wave order.
 //   S^T[32 keys x 16 heads] = K Q^T: lane l holds key l%16 of each block of 16
 //     keys and the 128 channels [128G, 128G+128) of its lane group G = l/16
-//     (k-step t: channels 128G + 8t .. +8, the same on the Q^T operand, which
-//     is read from LDS).  Keys are dequantised in registers straight into the
-//     A operand (exact in fp16); the lanes whose group G is the workgroup's
-//     output slice also store their 128 channels, row-major, to the wave's LDS
-//     tile (K = V).
+//     (k-step t: channels 128G + 8t .. +8, the same on the Q^T operand, read
+//     from LDS); the lanes whose G is the output slice also store their 128
+//     channels to the wave's LDS tile.
+//
+// Grouped (many rows, prefill): one workgroup per (query row, group of 16
+// heads), 4 workgroups per row; the four waves walk the same tiles and wave w
+// owns the channels [128w, 128w+128): it dequantises only those channels of
+// each key, forms the partial scores over them and accumulates the output for
+// those 128 dims, so each key is dequantised once per head group and no score
+// or output is computed twice (about a quarter of the spread form's
+// dequantisation and half its MFMA work per row).
+//   partial S^T over the wave's channels: lane l holds key l%16 and the 32
+//     channels [128w + 32G, +32) (k-step t: 128w + 32G + 8t .. +8; the Q^T
+//     operand stays in registers); the four partials meet in LDS (one barrier
+//     per tile) and every wave adds them in wave order, so all four hold
+//     bit-identical scores and softmax state.
+//
+// Common to both:
 //   P^T: the S^T accumulator of lane l holds keys 4G + r (r < 4) of both
 //     blocks for head l%16, which is the B-operand layout of P^T for
 //     O^T = V^T P^T once the 32 keys of a tile take MFMA k-index 8G + i <->
-//     key 16*(i/4) + 4G + i%4.  P is split into two fp16 terms (hi + lo) so
-//     the product keeps ~22 bits of P.
+//     key 16*(i/4) + 4G + i%4;
 //   V^T[16 dims x 32 keys]: read from the row-major LDS tile with the gfx950
 //     transposing read ds_read_b64_tr_b16 (within each 16-lane group, lane
 //     4a + j receives element j of lanes a, a+4, a+8, a+12), two reads per
-//     MFMA, in the same key order.
-// At the end the waves' (O, max, sum) meet in LDS and are merged in wave
-// order (deterministic); every workgroup of a query row computes the same
-// scores, so the 16 workgroups agree on the normalisation.
-//
-// Loads: a wave loads the top-k indices and then the keys of kChunkTiles
-// tiles at once (with 8 waves this covers k = 512 plus the window in one
-// chunk), issued before Q is staged together with the wave's first window
-// tile, so the index -> key dependency and the Q load overlap.  Loads are
-// unconditional (clamped inside the list, masked afterwards).
+//     MFMA, in the same key order;
+//   loads are unconditional (clamped inside the list or pointed at the query
+//     row, masked afterwards), so the load counter stays exact; the top-k
+//     indices are loaded ahead of the keys they address.
 #include "device_common.h"
 #include "launch.h"
 
@@ -45,48 +59,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __fp16 fp16x4 __attribute__((vector_size(8)));  // operand type of the LDS transposing read
 typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
 
-#ifndef CSA2_ATTN_WAVES
-#define CSA2_ATTN_WAVES 8
-#endif
-constexpr int kAttnWaves = CSA2_ATTN_WAVES;
 constexpr int kTile = 32;                       // keys per tile (two MFMA blocks of 16)
 constexpr int kHg = 16;                         // heads per workgroup
-constexpr int kSlice = 128;                     // output dims per workgroup
 constexpr int kGroups = kHeads / kHg;           // 4 head groups
-constexpr int kSlices = kDim / kSlice;          // 4 output slices
-constexpr int kWgPerRow = kGroups * kSlices;    // 16 workgroups per query row
-constexpr int kQRow = kDim + 8;                 // halves per LDS row of Q (bank spread)
+constexpr int kSlice = 128;                     // channels / output dims per slice
+constexpr int kSlices = kDim / kSlice;          // 4 slices
 constexpr int kVRow = kSlice + 16;              // halves per LDS row of V (288 B)
-constexpr int kChunkTiles = 2;                  // top-k tiles per wave loaded together
 constexpr int kXcds = 8;                        // MI355X dies: workgroups go round-robin
+constexpr int kCus = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-struct AttnSmem {
-    _Float16 q[kHg][kQRow];
-    union {
-        _Float16 v[kAttnWaves][kTile][kVRow];
-        struct {
-            float o[kAttnWaves][kHg][kSlice + 4];
-            float m[kAttnWaves][kHg];
-            float l[kAttnWaves][kHg];
-        } red;
-    } u;
-};
-
-// Raw bytes of one top-k tile for the calling lane: channels [128G, 128G+128)
-// of key l%16 of block b (64 code bytes, 8 scale bytes) and whether the key
-// is valid.
-struct MainRaw {
-    u32x4 c[2][4];
-    uint32_t s[2][2];
-    uint32_t valid;  // bit b: key of block b is valid
-};
-
-__device__ __forceinline__ half8 q_operand(const AttnSmem& sm, int head, int G, int t)
-{
-    return *reinterpret_cast<const half8*>(&sm.q[head][kSlice * G + 8 * t]);
-}
 
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
 {
@@ -98,7 +80,7 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
 struct Online {
     float m = -INFINITY;   // running max (log2 domain)
     float l = 0.0f;        // running sum
-    f32x4 o[kSlice / 16];  // O^T: dims 16*db + 4G + r of the slice, head l%16
+    f32x4 o[kSlice / 16];  // O^T: dims 16*db + 4G + r of the wave's slice, head l%16
 };
 
 // Folds one tile's S^T (already scaled, -inf for invalid keys) into the state
@@ -183,8 +165,8 @@ __device__ __forceinline__ void scale_scores(f32x4 (&s)[2], uint32_t valid, floa
     }
 }
 
-// Where the merged output goes: fp32 as computed, or (kRopeBf16) inverse
-// rotary on the rotary channels followed by a bf16 cast.
+// Where the output goes: fp32 as computed, or (kRopeBf16) inverse rotary on
+// the rotary channels followed by a bf16 cast.
 struct AttnOut {
     float* out;            // fp32 [rows, 64, 512] (kRopeBf16 = false)
     uint16_t* out_bf16;    // bf16 [rows, 64, 512] (kRopeBf16 = true)
@@ -203,16 +185,49 @@ __device__ __forceinline__ uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+// ============================================================== spread form
+
+constexpr int kSpreadWaves = 8;
+constexpr int kSpreadWgPerRow = kGroups * kSlices;  // 16 workgroups per query row
+constexpr int kQRow = kDim + 8;                     // halves per LDS row of Q (bank spread)
+constexpr int kChunkTiles = 2;                      // top-k tiles per wave loaded together
+
+struct SpreadSmem {
+    _Float16 q[kHg][kQRow];
+    union {
+        _Float16 v[kSpreadWaves][kTile][kVRow];
+        struct {
+            float o[kSpreadWaves][kHg][kSlice + 4];
+            float m[kSpreadWaves][kHg];
+            float l[kSpreadWaves][kHg];
+        } red;
+    } u;
+};
+
+// Raw bytes of one top-k tile for the calling lane: channels [128G, 128G+128)
+// of key l%16 of block b (64 code bytes, 8 scale bytes) and whether the key
+// is valid.
+struct MainRaw {
+    u32x4 c[2][4];
+    uint32_t s[2][2];
+    uint32_t valid;  // bit b: key of block b is valid
+};
+
+__device__ __forceinline__ half8 q_operand(const SpreadSmem& sm, int head, int G, int t)
+{
+    return *reinterpret_cast<const half8*>(&sm.q[head][kSlice * G + 8 * t]);
+}
+
 template <bool kRopeBf16>
-__global__ void __launch_bounds__(kAttnWaves * kWave)
-sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
+__global__ void __launch_bounds__(kSpreadWaves * kWave)
+attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
                    const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
                    int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
                    const uint8_t* __restrict__ swa, int32_t swa_cap,
                    const int32_t* __restrict__ swa_end, int32_t n_win, float scale_log2,
                    AttnOut dst_spec, float* __restrict__ lse)
 {
-    __shared__ AttnSmem sm;
+    __shared__ SpreadSmem sm;
     const int lane = threadIdx.x & 63;
     // wave index as a scalar: everything derived from it (tile lists, counts,
     // pointer choices) stays in scalar registers and branches
@@ -224,8 +239,8 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     // round-robin dispatch, workgroup x runs on die x % 8
     const int64_t x = blockIdx.x;
     const int64_t rest = x / kXcds;
-    const int64_t qrow = kXcds * (rest / kWgPerRow) + x % kXcds;
-    const int part = (int)(rest % kWgPerRow);
+    const int64_t qrow = kXcds * (rest / kSpreadWgPerRow) + x % kXcds;
+    const int part = (int)(rest % kSpreadWgPerRow);
     if (qrow >= queries)
         return;
     const int hg = part / kSlices;     // head group
@@ -242,9 +257,9 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     const int t_sw = (n_sw + kTile - 1) / kTile;
     const int t_main = (k + kTile - 1) / kTile;
     // this wave's tiles: list positions wave + 8j over [window tiles, top-k tiles]
-    int m_first = (wave - t_sw) % kAttnWaves;
-    m_first = m_first < 0 ? m_first + kAttnWaves : m_first;
-    const int nm = (n_cap > 0 && m_first < t_main) ? (t_main - m_first + kAttnWaves - 1) / kAttnWaves : 0;
+    int m_first = (wave - t_sw) % kSpreadWaves;
+    m_first = m_first < 0 ? m_first + kSpreadWaves : m_first;
+    const int nm = (n_cap > 0 && m_first < t_main) ? (t_main - m_first + kSpreadWaves - 1) / kSpreadWaves : 0;
 
     // loads that have no data to fetch (no top-k tile, no window tile for this
     // wave) read the query row instead (64 KiB, always valid) and are masked,
@@ -260,7 +275,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     // none); j is clamped to the wave's last tile so the load is always valid
     auto load_idx = [&](int j, int32_t (&e)[2]) {
         const int jj = j < nm ? j : nm - 1;
-        const int tile = m_first + kAttnWaves * jj;
+        const int tile = m_first + kSpreadWaves * jj;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
             const int slot = tile * kTile + 16 * bb + key16;
@@ -270,7 +285,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     // whether slot 16*bb + l%16 of main tile j of this wave is inside the list
     auto in_list = [&](int j, int bb) {
         const int jj = j < nm ? j : nm - 1;
-        return (m_first + kAttnWaves * jj) * kTile + 16 * bb + key16 < k;
+        return (m_first + kSpreadWaves * jj) * kTile + 16 * bb + key16 < k;
     };
     auto load_main = [&](int j, const int32_t (&e)[2], MainRaw& R) {
         R.valid = 0;
@@ -313,7 +328,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     for (int u = 0; u < kChunkTiles; ++u)
         load_idx(u, e[u]);
     // kQPer dims of one head per thread
-    constexpr int kQPer = kHg * kDim / (kAttnWaves * kWave);
+    constexpr int kQPer = kHg * kDim / (kSpreadWaves * kWave);
     constexpr int kThreadsPerHead = kDim / kQPer;
     const int qh = threadIdx.x / kThreadsPerHead;
     const int qd0 = kQPer * (threadIdx.x % kThreadsPerHead);
@@ -354,7 +369,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     const bool writer = G == slice;
 
     // ---- window tiles (FP8 rows, no scale)
-    for (int ts = wave; ts < t_sw; ts += kAttnWaves) {
+    for (int ts = wave; ts < t_sw; ts += kSpreadWaves) {
         if (ts != wave)
             load_swa(ts, swraw, swvalid);
         const uint32_t valid = swvalid;
@@ -429,19 +444,19 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     }
     __syncthreads();
     {
-        constexpr int kOPer = kHg * kSlice / (kAttnWaves * kWave);  // dims per thread
+        constexpr int kOPer = kHg * kSlice / (kSpreadWaves * kWave);  // dims per thread
         constexpr int kThreadsPerHead = kSlice / kOPer;
         const int t = threadIdx.x;
         const int h = t / kThreadsPerHead;      // head within the group
         const int d0 = kOPer * (t % kThreadsPerHead);
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w)
+        for (int w = 0; w < kSpreadWaves; ++w)
             M = fmaxf(M, sm.u.red.m[w][h]);
-        float f[kAttnWaves];
+        float f[kSpreadWaves];
         float den = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
+        for (int w = 0; w < kSpreadWaves; ++w) {
             const float mw = sm.u.red.m[w][h];
             f[w] = mw == -INFINITY ? 0.0f : exp2f(mw - M);
             den += f[w] * sm.u.red.l[w][h];
@@ -452,7 +467,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
         for (int i = 0; i < kOPer; ++i) {
             float num = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w)
+            for (int w = 0; w < kSpreadWaves; ++w)
                 num += f[w] * sm.u.red.o[w][h][d0 + i];
             res[i] = num * inv;
         }
@@ -492,6 +507,268 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int32_t queries,
     }
 }
 
+// ============================================================= grouped form
+
+constexpr int kGroupWaves = kSlices;            // one wave per 128-channel slice
+constexpr int kGroupWgPerRow = kGroups;         // 4 workgroups per query row
+constexpr int kDepth = 3;                       // tiles in flight per wave
+
+struct GroupSmem {
+    _Float16 v[kGroupWaves][kTile][kVRow];          // each wave's V tile (its 128 dims)
+    float part[2][kGroupWaves][kWave * 8];          // partial S^T per wave, double-buffered
+};
+
+// Raw bytes of one tile for the calling lane, for key l%16 of block b:
+// top-k tile: a = the 16 code bytes of channels [128w + 32G, +32), s = the 16
+// scale bytes that hold this wave's slice; window tile: a, s = the 32 E4M3
+// bytes of those channels.
+struct TileRaw {
+    u32x4 a[2], s[2];
+    uint32_t valid;  // bit b: key of block b is valid
+};
+
+// Partial S^T of one tile over the wave's 128 channels (block bb in s[bb]);
+// the dequantised keys also go to the wave's LDS tile.  kMain: MXFP4 top-k
+// keys, else E4M3 window rows.
+template <bool kMain>
+__device__ __forceinline__ void tile_scores(const TileRaw& R, const half8 (&qop)[4],
+                                            _Float16* __restrict__ vtile, int slice, int G,
+                                            int key16, f32x4 (&s)[2])
+{
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        f32x4 acc = {};
+        const bool ok = (R.valid >> bb) & 1u;
+        // scale bytes of this lane's 32 channels: dword 2(w%2) + G/2 of the 16
+        // loaded, bytes 2(G%2) and 2(G%2)+1
+        const uint32_t sdw = (slice & 1) ? (G >= 2 ? R.s[bb][3] : R.s[bb][2])
+                                        : (G >= 2 ? R.s[bb][1] : R.s[bb][0]);
+        const uint32_t sc = ok ? sdw >> (16 * (G & 1)) : 0u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            half8 a;
+            if (kMain) {
+                const uint32_t word = ok ? R.a[bb][t] : 0u;
+                a = dequant8_fp4(word, e4m3_byte_to_f16(sc, t / 2));
+            } else {
+                const u32x4 src = t < 2 ? R.a[bb] : R.s[bb];
+                const uint32_t w0 = ok ? src[2 * (t % 2)] : 0u;
+                const uint32_t w1 = ok ? src[2 * (t % 2) + 1] : 0u;
+                const half4v x0 = e4m3x4_to_f16(w0), x1 = e4m3x4_to_f16(w1);
+                a = half8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            }
+            acc = mfma16(a, qop[t], acc);
+            *reinterpret_cast<half8*>(vtile + (16 * bb + key16) * kVRow + 32 * G + 8 * t) = a;
+        }
+        s[bb] = acc;
+    }
+}
+
+// Writes this lane's outputs (head `head`, dims 128*slice + 16db + 4G + r) as
+// o * inv, through the epilogue of kRopeBf16.
+template <bool kRopeBf16>
+__device__ __forceinline__ void emit(const f32x4 (&o)[kSlice / 16], float inv, int64_t qrow,
+                                     int head, int slice, int G, const AttnOut& dst)
+{
+    const int64_t base = (qrow * kHeads + head) * kDim + kSlice * slice + 4 * G;
+#pragma unroll
+    for (int db = 0; db < kSlice / 16; ++db) {
+        float res[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            res[r] = o[db][r] * inv;
+        if (!kRopeBf16) {
+            *reinterpret_cast<float4*>(dst.out + base + 16 * db) =
+                make_float4(res[0], res[1], res[2], res[3]);
+        } else {
+            // rotate each rotary pair (a, b) back by the query's angle:
+            // a' = a*c + b*s, b' = b*c - a*s, every product and sum rounded to fp32
+            const int half = dst.rope_dim / 2;
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const int d = kSlice * slice + 16 * db + 4 * G + i;
+                if (d >= dst.rope_off && d < dst.rope_off + dst.rope_dim) {
+                    const int pi = (d - dst.rope_off) / 2;
+                    const float c = dst.cs[qrow * half + pi];
+                    const float sn = dst.sn[qrow * half + pi];
+                    const float a = res[i], bb = res[i + 1];
+                    res[i] = __fadd_rn(__fmul_rn(a, c), __fmul_rn(bb, sn));
+                    res[i + 1] = __fsub_rn(__fmul_rn(bb, c), __fmul_rn(a, sn));
+                }
+            }
+            const uint32_t p0 = (uint32_t)bf16_rne(res[0]) | ((uint32_t)bf16_rne(res[1]) << 16);
+            const uint32_t p1 = (uint32_t)bf16_rne(res[2]) | ((uint32_t)bf16_rne(res[3]) << 16);
+            *reinterpret_cast<uint2*>(dst.out_bf16 + base + 16 * db) = make_uint2(p0, p1);
+        }
+    }
+}
+
+template <bool kRopeBf16>
+__global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(3)))
+attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
+                  const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
+                  int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
+                  const uint8_t* __restrict__ swa, int32_t swa_cap,
+                  const int32_t* __restrict__ swa_end, int32_t n_win, float scale_log2,
+                  AttnOut dst_spec, float* __restrict__ lse)
+{
+    __shared__ GroupSmem sm;
+    const int lane = threadIdx.x & 63;
+    // the wave's slice as a scalar: everything derived from it (pointers,
+    // offsets) stays in scalar registers
+    const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = lane >> 4;
+    const int key16 = lane & 15;
+
+    // the 4 workgroups of a query row share one die (and its L2, which then
+    // serves the keys to every head group): with round-robin dispatch,
+    // workgroup x runs on die x % 8
+    const int64_t x = blockIdx.x;
+    const int64_t rest = x / kXcds;
+    const int64_t qrow = kXcds * (rest / kGroupWgPerRow) + x % kXcds;
+    const int hg = (int)(rest % kGroupWgPerRow);
+    if (qrow >= queries)
+        return;
+    const int64_t b = qrow / nq;
+    const int head = kHg * hg + key16;  // head of this lane's score column
+
+    // tile list: top-k tiles [0, t_main), then window tiles
+    const int t_main = n_cap > 0 ? (k + kTile - 1) / kTile : 0;
+
+    // loads with no data to fetch read the query row (64 KiB, always valid)
+    // and are masked, so every load is unconditional
+    const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + qrow * kHeads * kDim);
+    const uint8_t* kc = t_main > 0 ? kv_codes + b * n_cap * (kDim / 2) : dummy;
+    const uint8_t* ks = t_main > 0 ? kv_scales + b * n_cap * (kDim / 16) : dummy;
+    const int32_t* tk = t_main > 0 ? topk + qrow * k : reinterpret_cast<const int32_t*>(dummy);
+
+    // top-k index of this lane's key in block bb of tile p (any valid slot
+    // when p is not a top-k tile)
+    auto load_idx = [&](int p, int32_t (&e)[2]) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int slot = p * kTile + 16 * bb + key16;
+            e[bb] = tk[t_main > 0 ? (slot < k ? slot : k - 1) : 0];
+        }
+    };
+
+    int32_t eidx[kDepth][2];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u)
+        load_idx(u, eidx[u]);
+    // Q^T operand: head l%16 of the group, channels [128w + 32G, +32), bf16 -> fp16
+    uint4 qraw[4];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(
+            q + (qrow * kHeads + head) * kDim + kSlice * slice + 32 * G);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            qraw[t] = src[t];
+    }
+
+    // window rows [lo, hi)
+    const int64_t end = swa_end[qrow];
+    int64_t lo = end - n_win;
+    lo = lo < 0 ? 0 : lo;
+    int64_t hi = end < swa_cap ? end : (int64_t)swa_cap;
+    hi = hi < lo ? lo : hi;
+    const int n_sw = (int)(hi - lo);
+    const int t_sw = (n_sw + kTile - 1) / kTile;
+    const uint8_t* sw = n_sw > 0 ? swa + b * (int64_t)swa_cap * kDim : dummy;
+    const int n_tiles = t_main + t_sw;
+
+    // raw bytes of tile p; tiles past the list load valid rows and are
+    // masked.  Both kinds' addresses are formed and one is selected, so the
+    // loads stay outside any branch.
+    auto load_tile = [&](int p, const int32_t (&e)[2], TileRaw& R) {
+        const bool is_main = p < t_main;
+        const int tw = p - t_main;
+        R.valid = 0;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int slot = p * kTile + 16 * bb + key16;
+            const bool ok_m = slot < k && e[bb] >= 0 && e[bb] < n_cap;
+            const int64_t ee = ok_m ? e[bb] : 0;
+            const int64_t r = lo + (int64_t)tw * kTile + 16 * bb + key16;
+            const bool ok_w = tw >= 0 && tw < t_sw && r < hi;
+            const int64_t rr = ok_w ? r : (n_sw > 0 ? lo : 0);
+            const uint8_t* pm = kc + ee * (kDim / 2) + 64 * slice + 16 * G;
+            const uint8_t* pw = sw + rr * kDim + kSlice * slice + 32 * G;
+            const uint8_t* pa = is_main ? pm : pw;
+            const uint8_t* ps = is_main ? ks + ee * (kDim / 16) + 16 * (slice / 2) : pw + 16;
+            R.a[bb] = *reinterpret_cast<const u32x4*>(pa);
+            R.s[bb] = *reinterpret_cast<const u32x4*>(ps);
+            R.valid |= (is_main ? ok_m : ok_w) ? (1u << bb) : 0u;
+        }
+    };
+
+    TileRaw ring[kDepth];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u)
+        load_tile(u, eidx[u], ring[u]);
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u)
+        load_idx(u + kDepth, eidx[u]);
+
+    half8 qop[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t d[4] = {qraw[t].x, qraw[t].y, qraw[t].z, qraw[t].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qop[t][2 * i] = bf16_to_f16((uint16_t)(d[i] & 0xFFFFu));
+            qop[t][2 * i + 1] = bf16_to_f16((uint16_t)(d[i] >> 16));
+        }
+    }
+
+    Online st;
+#pragma unroll
+    for (int db = 0; db < kSlice / 16; ++db)
+        st.o[db] = f32x4{};
+    _Float16* vtile = &sm.v[slice][0][0];
+
+    // slot u of the ring holds tile p0 + u; after use it is refilled with tile
+    // p + kDepth, and its index slot with the indices of tile p + 2*kDepth
+    for (int p0 = 0; p0 < n_tiles; p0 += kDepth) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            const int p = p0 + u;
+            if (p < n_tiles) {  // the same for every wave: the barrier below is uniform
+                f32x4 s[2];
+                if (p < t_main)
+                    tile_scores<true>(ring[u], qop, vtile, slice, G, key16, s);
+                else
+                    tile_scores<false>(ring[u], qop, vtile, slice, G, key16, s);
+                // the four partial scores meet in LDS; every wave adds them in
+                // wave order (bit-identical in every wave)
+                float* mine = &sm.part[p & 1][slice][8 * lane];
+                *reinterpret_cast<f32x4*>(mine) = s[0];
+                *reinterpret_cast<f32x4*>(mine + 4) = s[1];
+                __syncthreads();
+                const float* all = &sm.part[p & 1][0][8 * lane];
+                f32x4 tot0 = *reinterpret_cast<const f32x4*>(all);
+                f32x4 tot1 = *reinterpret_cast<const f32x4*>(all + 4);
+#pragma unroll
+                for (int w = 1; w < kGroupWaves; ++w) {
+                    tot0 += *reinterpret_cast<const f32x4*>(all + w * kWave * 8);
+                    tot1 += *reinterpret_cast<const f32x4*>(all + w * kWave * 8 + 4);
+                }
+                s[0] = tot0;
+                s[1] = tot1;
+                scale_scores(s, ring[u].valid, scale_log2, G);
+                fold_tile(st, s, vtile, lane);
+            }
+            load_tile(p + kDepth, eidx[u], ring[u]);
+            load_idx(p + 2 * kDepth, eidx[u]);
+        }
+    }
+
+    const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    emit<kRopeBf16>(st.o, inv, qrow, head, slice, G, dst_spec);
+    if (lse != nullptr && slice == 0 && G == 0)
+        lse[qrow * kHeads + head] = st.l > 0.0f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
+}
+
 }  // namespace
 
 size_t attn_workspace(int32_t, int32_t, int32_t)
@@ -511,16 +788,32 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
         return hipSuccess;
     // rows padded to a multiple of the die count (padding workgroups exit at once)
     const int64_t rows = ((int64_t)queries + kXcds - 1) / kXcds * kXcds;
-    const dim3 grid((uint32_t)(rows * kWgPerRow)), block(kAttnWaves * kWave);
     const AttnOut spec{out, out_bf16, rope_cos, rope_sin, rope_off, rope_dim};
-    if (out_bf16 == nullptr)
-        sparse_attn_kernel<false><<<grid, block, 0, stream>>>(
-            q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
-            softmax_scale * kLog2e, spec, lse);
-    else
-        sparse_attn_kernel<true><<<grid, block, 0, stream>>>(
-            q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
-            softmax_scale * kLog2e, spec, lse);
+    const float scale_log2 = softmax_scale * kLog2e;
+    // the spread form while its 16 workgroups per row fit on the CUs at once
+    // (one round, the latency of one row); beyond that the grouped form, with
+    // a quarter of the work per row, has the higher throughput
+    if (rows * kSpreadWgPerRow <= kCus) {
+        const dim3 grid((uint32_t)(rows * kSpreadWgPerRow)), block(kSpreadWaves * kWave);
+        if (out_bf16 == nullptr)
+            attn_spread_kernel<false><<<grid, block, 0, stream>>>(
+                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
+                n_win, scale_log2, spec, lse);
+        else
+            attn_spread_kernel<true><<<grid, block, 0, stream>>>(
+                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
+                n_win, scale_log2, spec, lse);
+    } else {
+        const dim3 grid((uint32_t)(rows * kGroupWgPerRow)), block(kGroupWaves * kWave);
+        if (out_bf16 == nullptr)
+            attn_group_kernel<false><<<grid, block, 0, stream>>>(
+                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
+                n_win, scale_log2, spec, lse);
+        else
+            attn_group_kernel<true><<<grid, block, 0, stream>>>(
+                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
+                n_win, scale_log2, spec, lse);
+    }
     return hipGetLastError();
 }
 

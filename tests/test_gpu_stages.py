@@ -381,7 +381,8 @@ def test_sparse_attn_k_not_multiple_of_tile_and_large_k():
 
 
 def test_sparse_attn_batched_kernel_many_rows():
-    """More than 256 query rows take the batched kernel (one workgroup per 32 heads)."""
+    """300 query rows of one sequence (the grouped form: one workgroup per 16 heads,
+    channels split over the waves), sampled rows against the oracle."""
     N, nq, k, cap = 3000, 300, 96, 500
     x = synth.latent_rows(synth.key(13, 2), synth.key(13, 3), 0, N, 512)
     cos, sin = synth.rope_rows(0, N)
@@ -403,6 +404,92 @@ def test_sparse_attn_batched_kernel_many_rows():
         assert max_abs(lse[0, i], rl) <= 1e-4
 
 
+def _grouped_case(seed=21):
+    """24 query rows (3 sequences x 8 queries): more rows than the spread form serves, so
+    the grouped form runs.  Row r mixes top-k padding and window shapes by r % 6: plain,
+    padded (-1 and out-of-range ids), window only, empty, window past the ring capacity,
+    short window; k = 100 leaves a ragged last tile."""
+    B, nq, N, k, cap = 3, 8, 2000, 100, 160
+    rng = np.random.default_rng(seed)
+    vc, vs, sw = [], [], []
+    for b in range(B):
+        x = synth.latent_rows(synth.key(15, 2, 0, b), synth.key(15, 3, 0, b), 0, N, 512)
+        cos, sin = synth.rope_rows(0, N)
+        c, sc = oracle.quantize_rows(x, cos, sin, 448, 64)
+        vc.append(c)
+        vs.append(sc)
+        sw.append(oracle.encode_fp8(synth.latent_rows(synth.key(15, 4, 0, b),
+                                                      synth.key(15, 5, 0, b), 0, cap, 512)))
+    sel = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(B * nq)])
+    sel = sel.astype(np.int32).reshape(B, nq, k)
+    ends = np.array([128, 150, 140, 0, 200, 40], np.int32)
+    swa_end = np.zeros((B, nq), np.int32)
+    for r in range(B * nq):
+        b, i = divmod(r, nq)
+        kind = r % 6
+        swa_end[b, i] = ends[kind]
+        if kind == 1:
+            sel[b, i, ::7] = -1
+            sel[b, i, 3] = 10 ** 6
+        elif kind in (2, 3):
+            sel[b, i] = -1
+    q = synth.normal_bf16(synth.key(15, 8), 0, B * nq * 64 * 512, 1 / np.sqrt(512))
+    return np.stack(vc), np.stack(vs), np.stack(sw), sel, q.reshape(B, nq, 64, 512), swa_end
+
+
+def test_sparse_attn_grouped_form_matches_oracle():
+    vc, vs, sw, sel, q, swa_end = _grouped_case()
+    B, nq = q.shape[:2]
+    out = torch.full((B, nq, 64, 512), 777.0, device=dev())
+    lse = torch.full((B, nq, 64), 777.0, device=dev())
+    L.sparse_attn(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end), out, lse,
+                  softmax_scale=0.8)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for i in range(nq):
+            ro, rl = oracle.attention(q[b, i], vc[b], vs[b], sel[b, i], sw[b],
+                                      int(swa_end[b, i]), 128, 0.8)
+            assert max_abs(out[b, i], ro) <= ATTN_TOL, f"row {b},{i}"
+            if np.all(np.isinf(rl)):
+                assert np.all(np.isneginf(lse[b, i])) and np.all(out[b, i] == 0)
+            else:
+                assert max_abs(lse[b, i], rl) <= 1e-4, f"row {b},{i}"
+
+
+def test_sparse_attn_grouped_form_rope_bf16():
+    """The bf16 epilogue in the grouped form: oracle parity and bit-exact agreement with
+    the grouped fp32 output rotated and rounded on the host."""
+    vc, vs, sw, sel, q, swa_end = _grouped_case(seed=22)
+    B, nq = q.shape[:2]
+    rng = np.random.default_rng(23)
+    ang = rng.uniform(-np.pi, np.pi, (B * nq, 32))
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    out16 = torch.full((B, nq, 64, 512), 0x7777, dtype=torch.int16, device=dev())
+    lse16 = torch.empty((B, nq, 64), device=dev())
+    L.sparse_attn_rope_bf16(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end),
+                            t(cos), t(sin), out16, lse16)
+    out32 = torch.empty((B, nq, 64, 512), device=dev())
+    lse32 = torch.empty((B, nq, 64), device=dev())
+    L.sparse_attn(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end), out32, lse32)
+    got = out16.cpu().numpy().view(np.uint16)
+    out32 = out32.cpu().numpy()
+    assert np.array_equal(lse16.cpu().numpy(), lse32.cpu().numpy())
+    for r in range(B * nq):
+        b, i = divmod(r, nq)
+        ref_bits, _, _ = oracle.attention_rope_bf16(
+            q[b, i], vc[b], vs[b], sel[b, i], sw[b], int(swa_end[b, i]), cos[r], sin[r])
+        g, ref = _bf16_to_f32(got[b, i]), _bf16_to_f32(ref_bits)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert np.all(np.abs(g - ref) <= 2 * ATTN_TOL + ulp), f"row {r}"
+        o = out32[b, i].astype(np.float32).copy()
+        a, c = o[:, 448::2].copy(), o[:, 449::2].copy()
+        co, si = cos[r][None, :], sin[r][None, :]
+        o[:, 448::2] = (a * co) + (c * si)
+        o[:, 449::2] = (c * co) - (a * si)
+        host = torch.from_numpy(o).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got[b, i], host), f"row {r}"
+
+
 def _bf16_to_f32(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
@@ -419,8 +506,11 @@ def test_sparse_attn_rope_bf16_epilogue():
     cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
     out16 = torch.full((B, 1, 64, 512), 0x7777, dtype=torch.int16, device=dev())
     lse16 = torch.empty((B, 1, 64), device=dev())
+    # the same key split as _run_attn's fp32 call, so both sum in the same order
+    ws = torch.empty(max(L.sparse_attn_workspace(B, 1, sel.shape[-1], 128), 16),
+                     dtype=torch.uint8, device=dev())
     L.sparse_attn_rope_bf16(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end),
-                            t(cos), t(sin), out16, lse16)
+                            t(cos), t(sin), out16, lse16, ws=ws)
     got = out16.cpu().numpy().view(np.uint16)
     out32, lse32 = _run_attn(q, vc, vs, sel, sw, swa_end)
     assert np.array_equal(lse16.cpu().numpy(), lse32)
