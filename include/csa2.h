@@ -232,9 +232,14 @@ size_t csa2_topk_workspace(int64_t L, int32_t rows, int32_t k);
  *              union of selected entries and window rows (one joint softmax);
  *              0 for an empty key set.
  *   lse        fp32 [B, nq, 64] or NULL: ln sum_j exp(l_j) (-inf if empty).
- *   ws         device workspace of csa2_sparse_attn_workspace(B, nq, k, n_win)
- *              bytes (currently 0: every workgroup owns a slice of the output,
- *              so nothing is combined across workgroups; NULL is accepted).
+ *   ws         device workspace, 16-byte aligned, contents arbitrary, or NULL.
+ *              With csa2_sparse_attn_workspace(B, nq, k, n_win) bytes (non-zero
+ *              only for few query rows) each row's keys are split over several
+ *              workgroups whose partial results are merged by a second launch;
+ *              with NULL or fewer bytes the call still completes, with one
+ *              workgroup per (row, 16 heads, 128 output dims) instead.  The
+ *              result is deterministic for a given choice; the two differ only
+ *              in fp32 rounding order.
  * Dequantisation is exact in fp16; products accumulate in fp32.
  */
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq,

@@ -278,14 +278,13 @@ static csa2_status attn_common(const uint16_t* q, int32_t B, int32_t nq,
         REQUIRE(rope_dim == 0 || (rope_cos && rope_sin), CSA2_ERR_INVALID_ARG,
                 "%s: null rotary table", name);
     }
-    const size_t need = csa2::attn_workspace(queries, k, n_win);
-    REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
-            "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+    REQUIRE(ws == nullptr || aligned(ws, 16), CSA2_ERR_INVALID_ARG, "%s: misaligned workspace",
+            name);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_sparse_attn(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k,
                                            swa, swa_cap, swa_end, n_win, softmax_scale, out,
                                            out_bf16, rope_cos, rope_sin, rope_offset, rope_dim,
-                                           lse, s),
+                                           lse, ws, ws_bytes, s),
                   s, name);
 }
 

@@ -247,18 +247,11 @@ attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
     const int slice = part % kSlices;  // output dims [128*slice, +128)
     const int64_t b = qrow / nq;
 
-    // window rows [lo, hi) and tile counts
-    int64_t end = swa_end[qrow];
-    int64_t lo = end - n_win;
-    lo = lo < 0 ? 0 : lo;
-    int64_t hi = end < swa_cap ? end : (int64_t)swa_cap;
-    hi = hi < lo ? lo : hi;
-    const int n_sw = (int)(hi - lo);
-    const int t_sw = (n_sw + kTile - 1) / kTile;
+    // this wave's tiles: list positions wave + 8j over [top-k tiles, window
+    // tiles]; the top-k part does not depend on the window, so the index loads
+    // go out before the window's end is known
     const int t_main = (k + kTile - 1) / kTile;
-    // this wave's tiles: list positions wave + 8j over [window tiles, top-k tiles]
-    int m_first = (wave - t_sw) % kSpreadWaves;
-    m_first = m_first < 0 ? m_first + kSpreadWaves : m_first;
+    const int m_first = wave;
     const int nm = (n_cap > 0 && m_first < t_main) ? (t_main - m_first + kSpreadWaves - 1) / kSpreadWaves : 0;
 
     // loads that have no data to fetch (no top-k tile, no window tile for this
@@ -268,7 +261,6 @@ attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
     const bool have_main = nm > 0;
     const uint8_t* kc = have_main ? kv_codes + b * n_cap * (kDim / 2) : dummy;
     const uint8_t* ks = have_main ? kv_scales + b * n_cap * (kDim / 16) : dummy;
-    const uint8_t* sw = n_sw > 0 ? swa + b * (int64_t)swa_cap * kDim : dummy;
     const int32_t* tk = have_main ? topk + qrow * k : reinterpret_cast<const int32_t*>(dummy);
 
     // index of this lane's key in block bb of main tile j of this wave (-1 if
@@ -304,22 +296,6 @@ attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
         }
     };
 
-    // window tile ts of this wave: raw FP8 bytes of key l%16 of both blocks
-    auto load_swa = [&](int ts, u32x4 (&raw)[2][8], uint32_t& valid) {
-        valid = 0;
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int64_t r = lo + ts * kTile + 16 * bb + key16;
-            const bool ok = ts < t_sw && r < hi;
-            const int64_t rr = ok ? r : (n_sw > 0 ? lo : 0);
-            const u32x4* c = reinterpret_cast<const u32x4*>(sw + rr * kDim + kSlice * G);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                raw[bb][i] = c[i];
-            valid |= ok ? (1u << bb) : 0u;
-        }
-    };
-
     // ---- prologue: every load of the first top-k chunk and of the first window
     // tile is issued before Q is staged, so their latencies overlap
     int32_t e[kChunkTiles][2];
@@ -340,9 +316,34 @@ attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
         for (int i = 0; i < kQPer / 8; ++i)
             qraw[i] = src[i];
     }
+    // window rows [lo, hi); this wave's window tiles are sw_first + 8j
+    const int64_t end = swa_end[qrow];
+    int64_t lo = end - n_win;
+    lo = lo < 0 ? 0 : lo;
+    int64_t hi = end < swa_cap ? end : (int64_t)swa_cap;
+    hi = hi < lo ? lo : hi;
+    const int n_sw = (int)(hi - lo);
+    const int t_sw = (n_sw + kTile - 1) / kTile;
+    const int sw_first = ((wave - t_main) % kSpreadWaves + kSpreadWaves) % kSpreadWaves;
+    const uint8_t* sw = n_sw > 0 ? swa + b * (int64_t)swa_cap * kDim : dummy;
+    // window tile ts of this wave: raw FP8 bytes of key l%16 of both blocks
+    auto load_swa = [&](int ts, u32x4 (&raw)[2][8], uint32_t& valid) {
+        valid = 0;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int64_t r = lo + ts * kTile + 16 * bb + key16;
+            const bool ok = ts < t_sw && r < hi;
+            const int64_t rr = ok ? r : (n_sw > 0 ? lo : 0);
+            const u32x4* c = reinterpret_cast<const u32x4*>(sw + rr * kDim + kSlice * G);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                raw[bb][i] = c[i];
+            valid |= ok ? (1u << bb) : 0u;
+        }
+    };
     u32x4 swraw[2][8];
     uint32_t swvalid = 0;
-    load_swa(wave, swraw, swvalid);
+    load_swa(sw_first, swraw, swvalid);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kQPer / 8; ++i) {
@@ -369,8 +370,8 @@ attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
     const bool writer = G == slice;
 
     // ---- window tiles (FP8 rows, no scale)
-    for (int ts = wave; ts < t_sw; ts += kSpreadWaves) {
-        if (ts != wave)
+    for (int ts = sw_first; ts < t_sw; ts += kSpreadWaves) {
+        if (ts != sw_first)
             load_swa(ts, swraw, swvalid);
         const uint32_t valid = swvalid;
         u32x4 (&raw)[2][8] = swraw;
@@ -510,8 +511,16 @@ attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
 // ============================================================= grouped form
 
 constexpr int kGroupWaves = kSlices;            // one wave per 128-channel slice
-constexpr int kGroupWgPerRow = kGroups;         // 4 workgroups per query row
-constexpr int kDepth = 3;                       // tiles in flight per wave
+#ifndef CSA2_ATTN_DEPTH
+#define CSA2_ATTN_DEPTH 3
+#endif
+constexpr int kDepth = CSA2_ATTN_DEPTH;          // tiles in flight per wave
+#ifndef CSA2_ATTN_SPLIT_WGS
+#define CSA2_ATTN_SPLIT_WGS 256
+#endif
+constexpr int64_t kSplitWgs = CSA2_ATTN_SPLIT_WGS;  // workgroup budget of the key splits
+constexpr int kMaxSplits = 8;                   // key splits per (row, head group)
+constexpr int kPartFloats = kHg * kDim + 2 * kHg;  // one split's O [16][512], max, sum
 
 struct GroupSmem {
     _Float16 v[kGroupWaves][kTile][kVRow];          // each wave's V tile (its 128 dims)
@@ -610,7 +619,8 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                   int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
                   const uint8_t* __restrict__ swa, int32_t swa_cap,
                   const int32_t* __restrict__ swa_end, int32_t n_win, float scale_log2,
-                  AttnOut dst_spec, float* __restrict__ lse)
+                  int32_t splits, float* __restrict__ part, AttnOut dst_spec,
+                  float* __restrict__ lse)
 {
     __shared__ GroupSmem sm;
     const int lane = threadIdx.x & 63;
@@ -620,20 +630,24 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     const int G = lane >> 4;
     const int key16 = lane & 15;
 
-    // the 4 workgroups of a query row share one die (and its L2, which then
-    // serves the keys to every head group): with round-robin dispatch,
-    // workgroup x runs on die x % 8
+    // the workgroups of a query row (4 head groups x splits) share one die
+    // (and its L2, which then serves the keys to every head group): with
+    // round-robin dispatch, workgroup x runs on die x % 8
+    const int wg_per_row = kGroups * splits;
     const int64_t x = blockIdx.x;
     const int64_t rest = x / kXcds;
-    const int64_t qrow = kXcds * (rest / kGroupWgPerRow) + x % kXcds;
-    const int hg = (int)(rest % kGroupWgPerRow);
+    const int64_t qrow = kXcds * (rest / wg_per_row) + x % kXcds;
+    const int hg = (int)(rest % wg_per_row) % kGroups;
+    const int split = (int)(rest % wg_per_row) / kGroups;
     if (qrow >= queries)
         return;
     const int64_t b = qrow / nq;
     const int head = kHg * hg + key16;  // head of this lane's score column
 
-    // tile list: top-k tiles [0, t_main), then window tiles
+    // tile list: top-k tiles [0, t_main), then window tiles; this workgroup
+    // takes the list positions split + splits * j
     const int t_main = n_cap > 0 ? (k + kTile - 1) / kTile : 0;
+    auto pos = [&](int j) { return split + splits * j; };
 
     // loads with no data to fetch read the query row (64 KiB, always valid)
     // and are masked, so every load is unconditional
@@ -655,7 +669,7 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     int32_t eidx[kDepth][2];
 #pragma unroll
     for (int u = 0; u < kDepth; ++u)
-        load_idx(u, eidx[u]);
+        load_idx(pos(u), eidx[u]);
     // Q^T operand: head l%16 of the group, channels [128w + 32G, +32), bf16 -> fp16
     uint4 qraw[4];
     {
@@ -676,6 +690,7 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     const int t_sw = (n_sw + kTile - 1) / kTile;
     const uint8_t* sw = n_sw > 0 ? swa + b * (int64_t)swa_cap * kDim : dummy;
     const int n_tiles = t_main + t_sw;
+    const int n_j = split < n_tiles ? (n_tiles - split + splits - 1) / splits : 0;
 
     // raw bytes of tile p; tiles past the list load valid rows and are
     // masked.  Both kinds' addresses are formed and one is selected, so the
@@ -705,10 +720,10 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     TileRaw ring[kDepth];
 #pragma unroll
     for (int u = 0; u < kDepth; ++u)
-        load_tile(u, eidx[u], ring[u]);
+        load_tile(pos(u), eidx[u], ring[u]);
 #pragma unroll
     for (int u = 0; u < kDepth; ++u)
-        load_idx(u + kDepth, eidx[u]);
+        load_idx(pos(u + kDepth), eidx[u]);
 
     half8 qop[4];
 #pragma unroll
@@ -727,13 +742,15 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
         st.o[db] = f32x4{};
     _Float16* vtile = &sm.v[slice][0][0];
 
-    // slot u of the ring holds tile p0 + u; after use it is refilled with tile
-    // p + kDepth, and its index slot with the indices of tile p + 2*kDepth
-    for (int p0 = 0; p0 < n_tiles; p0 += kDepth) {
+    // slot u of the ring holds the tile of step j0 + u; after use it is refilled
+    // with the tile of step j + kDepth, and its index slot with the indices of
+    // step j + 2*kDepth
+    for (int j0 = 0; j0 < n_j; j0 += kDepth) {
 #pragma unroll
         for (int u = 0; u < kDepth; ++u) {
-            const int p = p0 + u;
-            if (p < n_tiles) {  // the same for every wave: the barrier below is uniform
+            const int j = j0 + u;
+            const int p = pos(j);
+            if (j < n_j) {  // the same for every wave: the barrier below is uniform
                 f32x4 s[2];
                 if (p < t_main)
                     tile_scores<true>(ring[u], qop, vtile, slice, G, key16, s);
@@ -741,11 +758,11 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                     tile_scores<false>(ring[u], qop, vtile, slice, G, key16, s);
                 // the four partial scores meet in LDS; every wave adds them in
                 // wave order (bit-identical in every wave)
-                float* mine = &sm.part[p & 1][slice][8 * lane];
+                float* mine = &sm.part[j & 1][slice][8 * lane];
                 *reinterpret_cast<f32x4*>(mine) = s[0];
                 *reinterpret_cast<f32x4*>(mine + 4) = s[1];
                 __syncthreads();
-                const float* all = &sm.part[p & 1][0][8 * lane];
+                const float* all = &sm.part[j & 1][0][8 * lane];
                 f32x4 tot0 = *reinterpret_cast<const f32x4*>(all);
                 f32x4 tot1 = *reinterpret_cast<const f32x4*>(all + 4);
 #pragma unroll
@@ -758,22 +775,129 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                 scale_scores(s, ring[u].valid, scale_log2, G);
                 fold_tile(st, s, vtile, lane);
             }
-            load_tile(p + kDepth, eidx[u], ring[u]);
-            load_idx(p + 2 * kDepth, eidx[u]);
+            load_tile(pos(j + kDepth), eidx[u], ring[u]);
+            load_idx(pos(j + 2 * kDepth), eidx[u]);
         }
     }
 
-    const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
-    emit<kRopeBf16>(st.o, inv, qrow, head, slice, G, dst_spec);
-    if (lse != nullptr && slice == 0 && G == 0)
-        lse[qrow * kHeads + head] = st.l > 0.0f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
+    if (splits == 1) {
+        const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+        emit<kRopeBf16>(st.o, inv, qrow, head, slice, G, dst_spec);
+        if (lse != nullptr && slice == 0 && G == 0)
+            lse[qrow * kHeads + head] = st.l > 0.0f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
+        return;
+    }
+    // this split's unnormalised (O, max, sum) for attn_merge_kernel
+    float* mine = part + ((qrow * kGroups + hg) * splits + split) * kPartFloats;
+#pragma unroll
+    for (int db = 0; db < kSlice / 16; ++db)
+        *reinterpret_cast<f32x4*>(mine + key16 * kDim + kSlice * slice + 16 * db + 4 * G) = st.o[db];
+    if (slice == 0 && G == 0) {
+        mine[kHg * kDim + key16] = st.m;
+        mine[kHg * kDim + kHg + key16] = st.l;
+    }
+}
+
+// Merge of the key splits of attn_group_kernel: one workgroup per (query row,
+// head group, 128-dim slice); thread t takes head t/16 and the 8 dims
+// 8*(t%16) .. +8 of the slice.  The splits are combined in split order
+// (deterministic), then written through the epilogue.
+template <bool kRopeBf16>
+__global__ void __launch_bounds__(256)
+attn_merge_kernel(const float* __restrict__ part, int32_t splits, int32_t queries,
+                  AttnOut dst, float* __restrict__ lse)
+{
+    // the same die as the workgroups that wrote the partials of the row
+    const int64_t x = blockIdx.x;
+    const int64_t rest = x / kXcds;
+    const int64_t qrow = kXcds * (rest / (kGroups * kSlices)) + x % kXcds;
+    const int hg = (int)(rest % (kGroups * kSlices)) / kSlices;
+    const int slice = (int)(rest % (kGroups * kSlices)) % kSlices;
+    if (qrow >= queries)
+        return;
+    const int h = threadIdx.x / 16;
+    const int d0 = kSlice * slice + 8 * (threadIdx.x % 16);
+    const float* p0 = part + (qrow * kGroups + hg) * splits * kPartFloats;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s)
+        M = fmaxf(M, p0[s * kPartFloats + kHg * kDim + h]);
+    float den = 0.0f;
+    float num[8] = {};
+    for (int s = 0; s < splits; ++s) {
+        const float* ps = p0 + s * kPartFloats;
+        const float ms = ps[kHg * kDim + h];
+        const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+        den += f * ps[kHg * kDim + kHg + h];
+        const float4 a = *reinterpret_cast<const float4*>(ps + h * kDim + d0);
+        const float4 c = *reinterpret_cast<const float4*>(ps + h * kDim + d0 + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            num[i] += f * v[i];
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    float res[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        res[i] = num[i] * inv;
+    const int head = kHg * hg + h;
+    const int64_t o0 = (qrow * kHeads + head) * kDim + d0;
+    if (!kRopeBf16) {
+        float4* o = reinterpret_cast<float4*>(dst.out + o0);
+        o[0] = make_float4(res[0], res[1], res[2], res[3]);
+        o[1] = make_float4(res[4], res[5], res[6], res[7]);
+    } else {
+        // rotate each rotary pair (a, b) back by the query's angle:
+        // a' = a*c + b*s, b' = b*c - a*s, every product and sum rounded to fp32
+        const int half = dst.rope_dim / 2;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            const int d = d0 + i;
+            if (d >= dst.rope_off && d < dst.rope_off + dst.rope_dim) {
+                const int pi = (d - dst.rope_off) / 2;
+                const float c = dst.cs[qrow * half + pi];
+                const float sn = dst.sn[qrow * half + pi];
+                const float a = res[i], bb = res[i + 1];
+                res[i] = __fadd_rn(__fmul_rn(a, c), __fmul_rn(bb, sn));
+                res[i + 1] = __fsub_rn(__fmul_rn(bb, c), __fmul_rn(a, sn));
+            }
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)bf16_rne(res[2 * i]) | ((uint32_t)bf16_rne(res[2 * i + 1]) << 16);
+        uint2* o = reinterpret_cast<uint2*>(dst.out_bf16 + o0);
+        o[0] = make_uint2(w[0], w[1]);
+        o[1] = make_uint2(w[2], w[3]);
+    }
+    if (lse != nullptr && slice == 0 && threadIdx.x % 16 == 0)
+        lse[qrow * kHeads + head] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+int64_t padded_rows(int32_t queries)
+{
+    return ((int64_t)queries + kXcds - 1) / kXcds * kXcds;
+}
+
+// Key splits of the grouped form for few query rows: enough workgroups to
+// cover the CUs once, at least two tiles per split; 1 when the rows alone
+// fill the CUs.
+int32_t attn_splits(int32_t queries, int32_t k, int32_t n_win)
+{
+    const int64_t groups = padded_rows(queries) * kGroups;
+    const int64_t tiles = ((int64_t)k + kTile - 1) / kTile + ((int64_t)n_win + kTile - 1) / kTile;
+    int32_t s = 1;
+    while (s < kMaxSplits && groups * s * 2 <= kSplitWgs && tiles >= 4 * s)
+        s *= 2;
+    return s;
 }
 
 }  // namespace
 
-size_t attn_workspace(int32_t, int32_t, int32_t)
+size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win)
 {
-    return 0;
+    const int32_t s = attn_splits(queries, k, n_win);
+    return s > 1 ? (size_t)padded_rows(queries) * kGroups * s * kPartFloats * sizeof(float) : 0;
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
@@ -782,18 +906,37 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                               int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
                               float softmax_scale, float* out, uint16_t* out_bf16,
                               const float* rope_cos, const float* rope_sin, int32_t rope_off,
-                              int32_t rope_dim, float* lse, hipStream_t stream)
+                              int32_t rope_dim, float* lse, void* ws, size_t ws_bytes,
+                              hipStream_t stream)
 {
     if (queries == 0)
         return hipSuccess;
     // rows padded to a multiple of the die count (padding workgroups exit at once)
-    const int64_t rows = ((int64_t)queries + kXcds - 1) / kXcds * kXcds;
+    const int64_t rows = padded_rows(queries);
     const AttnOut spec{out, out_bf16, rope_cos, rope_sin, rope_off, rope_dim};
     const float scale_log2 = softmax_scale * kLog2e;
-    // the spread form while its 16 workgroups per row fit on the CUs at once
-    // (one round, the latency of one row); beyond that the grouped form, with
-    // a quarter of the work per row, has the higher throughput
-    if (rows * kSpreadWgPerRow <= kCus) {
+    const size_t need = attn_workspace(queries, k, n_win);
+    if (need > 0 && ws != nullptr && ws_bytes >= need) {
+        // few rows: the grouped form with each row's keys split over workgroups,
+        // then the merge of the splits (a second launch: the kernel boundary
+        // orders the partials, with no cache maintenance inside the kernels)
+        const int32_t splits = attn_splits(queries, k, n_win);
+        float* part = static_cast<float*>(ws);
+        const dim3 grid((uint32_t)(rows * kGroups * splits)), block(kGroupWaves * kWave);
+        attn_group_kernel<false><<<grid, block, 0, stream>>>(
+            q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
+            scale_log2, splits, part, spec, lse);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        const dim3 mgrid((uint32_t)(rows * kGroups * kSlices)), mblock(256);
+        if (out_bf16 == nullptr)
+            attn_merge_kernel<false><<<mgrid, mblock, 0, stream>>>(part, splits, queries, spec, lse);
+        else
+            attn_merge_kernel<true><<<mgrid, mblock, 0, stream>>>(part, splits, queries, spec, lse);
+    } else if (rows * kSpreadWgPerRow <= kCus) {
+        // few rows and no workspace: the spread form (one round of 16
+        // workgroups per row, nothing to combine)
         const dim3 grid((uint32_t)(rows * kSpreadWgPerRow)), block(kSpreadWaves * kWave);
         if (out_bf16 == nullptr)
             attn_spread_kernel<false><<<grid, block, 0, stream>>>(
@@ -804,15 +947,15 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, spec, lse);
     } else {
-        const dim3 grid((uint32_t)(rows * kGroupWgPerRow)), block(kGroupWaves * kWave);
+        const dim3 grid((uint32_t)(rows * kGroups)), block(kGroupWaves * kWave);
         if (out_bf16 == nullptr)
             attn_group_kernel<false><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
-                n_win, scale_log2, spec, lse);
+                n_win, scale_log2, 1, nullptr, spec, lse);
         else
             attn_group_kernel<true><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
-                n_win, scale_log2, spec, lse);
+                n_win, scale_log2, 1, nullptr, spec, lse);
     }
     return hipGetLastError();
 }

@@ -46,6 +46,7 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
                        const int32_t* n_valid, int32_t k, int32_t* out, void* ws,
                        hipStream_t stream);
 
+// Bytes of the key-split partials for few query rows (0: no split).
 size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win);
 // out (fp32) or out_bf16 (inverse rotary on [rope_off, rope_off + rope_dim)
 // with the query's rope_cos / rope_sin, then bf16): exactly one is non-null.
@@ -55,6 +56,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                               int32_t swa_cap, const int32_t* swa_end, int32_t n_win,
                               float softmax_scale, float* out, uint16_t* out_bf16,
                               const float* rope_cos, const float* rope_sin, int32_t rope_off,
-                              int32_t rope_dim, float* lse, hipStream_t stream);
+                              int32_t rope_dim, float* lse, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 }  // namespace csa2

@@ -47,8 +47,10 @@ def test_version_and_workspace_queries():
     assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
     assert lib.csa2_topk_workspace(100, 1, 0) == 0
-    assert lib.csa2_sparse_attn_workspace(4096, 1, 512, 128) == 0
-    assert lib.csa2_sparse_attn_workspace(16, 1, 512, 128) == 0  # no split-K scratch
+    assert lib.csa2_sparse_attn_workspace(4096, 1, 512, 128) == 0  # rows fill the CUs
+    # 16 rows: 4 key splits per (row, 16 heads), each an O [16, 512] plus max and sum
+    assert lib.csa2_sparse_attn_workspace(16, 1, 512, 128) == 16 * 4 * 4 * (16 * 512 + 32) * 4
+    assert lib.csa2_sparse_attn_workspace(1, 1, 512, 128) == 8 * 4 * 8 * (16 * 512 + 32) * 4
 
 
 def _status(fn, *args):
