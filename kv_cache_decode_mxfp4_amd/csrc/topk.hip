@@ -469,14 +469,17 @@ struct GroupSmem {
 };
 
 // Grouped select for one row from its group maxima gkey[row, 0..ngroups)
-// (ngroups <= 16384, g * k <= 16384).  Grid: rows.
+// (ngroups <= 16384, g * k <= 16384).  Grid: rows.  kG: the group size when
+// known at compile time (8: L up to 131072 with k <= 2048), else 0.
+template <int kG>
 __global__ void __launch_bounds__(kThreads)
 topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
-                    int32_t g, int64_t ngroups, const uint32_t* __restrict__ gkey,
+                    int32_t g_runtime, int64_t ngroups, const uint32_t* __restrict__ gkey,
                     const int32_t* __restrict__ n_valid, int32_t k, int32_t* __restrict__ out)
 {
     __shared__ GroupSmem gs;
     Smem& sm = gs.sm;
+    const uint32_t g = kG > 0 ? (uint32_t)kG : (uint32_t)g_runtime;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -508,21 +511,33 @@ topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__
         sm.hist[0][b] = 0u;
     __syncthreads();
     const uint32_t n_chosen = chosen < (uint32_t)k ? chosen : (uint32_t)k;
-    // candidate c*g + r is entry r of the c-th chosen group: position order
+    // candidate c*g + r is entry r of the c-th chosen group: position order.
+    // Every group id is read first, then every score (clamped, masked), so the
+    // loads of all 16 slots are in flight together.
+    uint32_t cg[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const uint32_t c = (uint32_t)(kThreads * i + tid) / g;
+        cg[i] = gs.chosen_groups[c < n_chosen ? c : 0u];
+    }
     float f[kPer];
     int64_t pos[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const uint32_t e = (uint32_t)(kThreads * i + tid);
-        const uint32_t c = e / (uint32_t)g;
-        pos[i] = -1;
-        if (c < n_chosen) {
-            const int64_t p = (int64_t)gs.chosen_groups[c] * g + e % (uint32_t)g;
-            pos[i] = p < nv ? p : -1;
-        }
-        const int64_t pl = pos[i] >= 0 ? pos[i] : 0;
-        f[i] = srow[pl];
-        id[i] = irow != nullptr ? irow[pl] : (int32_t)pl;
+        const uint32_t c = e / g;
+        const int64_t p = (int64_t)cg[i] * g + (e - c * g);
+        pos[i] = c < n_chosen && p < nv ? p : -1;
+        f[i] = srow[pos[i] >= 0 ? pos[i] : 0];
+    }
+    if (irow != nullptr) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            id[i] = irow[pos[i] >= 0 ? pos[i] : 0];
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            id[i] = (int32_t)pos[i];
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -588,8 +603,12 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        topk_grouped_kernel<<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
-            score, idx, L, g, ngroups, gkey, n_valid, k, out);
+        if (g == 8)
+            topk_grouped_kernel<8><<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
+                score, idx, L, g, ngroups, gkey, n_valid, k, out);
+        else
+            topk_grouped_kernel<0><<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
+                score, idx, L, g, ngroups, gkey, n_valid, k, out);
         return hipGetLastError();
     }
     const size_t half = topk_workspace(L, rows, k) / 2;
