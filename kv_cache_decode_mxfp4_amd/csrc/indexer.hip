@@ -295,26 +295,30 @@ index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const int half = lane >> 5;
     const int64_t slots = (int64_t)n_blocks * kBlock;
 
-    const uint8_t* kc = codes + b * n_cap * (kIdxDim / 2);
-    const uint8_t* ks = scales + b * n_cap * (kIdxDim / 16);
+    // with nothing visible the loads read the query row instead (8 KiB, always
+    // valid) and are masked: every load below is unconditional, so all of a
+    // wave's loads are in flight together
+    const uint8_t* qrow_bytes = reinterpret_cast<const uint8_t*>(q + row * (kIdxHeads * kIdxDim));
+    const uint8_t* kc = n_vis > 0 ? codes + b * n_cap * (kIdxDim / 2) : qrow_bytes;
+    const uint8_t* ks = n_vis > 0 ? scales + b * n_cap * (kIdxDim / 16) : qrow_bytes;
     const int32_t* blk = blocks + row * n_blocks;
 
     const int64_t first = ((int64_t)part * kWaves + wave) * kPoolTilesPerWave * kTileEntries;
-    // gather every tile of this wave first, then score: all loads in flight at once
+    // every block id of this wave's tiles first, then every key
+    int32_t bl[kPoolTilesPerWave];
+#pragma unroll
+    for (int i = 0; i < kPoolTilesPerWave; ++i) {
+        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        bl[i] = blk[(slot < slots ? slot : slots - 1) / kBlock];
+    }
     int64_t pos[kPoolTilesPerWave];
     KeyTile K[kPoolTilesPerWave];
 #pragma unroll
     for (int i = 0; i < kPoolTilesPerWave; ++i) {
         const int64_t slot = first + i * kTileEntries + (lane & 31);
-        pos[i] = -1;
-        if (slot < slots) {
-            const int32_t bl = blk[slot / kBlock];
-            const int64_t p = (int64_t)bl * kBlock + slot % kBlock;
-            pos[i] = (bl >= 0 && p < n_vis) ? p : -1;
-        }
-        K[i] = KeyTile{};
-        if (pos[i] >= 0)
-            load_key(kc, ks, pos[i], half, K[i]);
+        const int64_t p = (int64_t)bl[i] * kBlock + slot % kBlock;
+        pos[i] = (slot < slots && bl[i] >= 0 && p < n_vis) ? p : -1;
+        load_key(kc, ks, pos[i] >= 0 ? pos[i] : 0, half, K[i]);
     }
     QueryOperand Q;  // loaded while the gathers are in flight
     load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
