@@ -818,22 +818,34 @@ attn_merge_kernel(const float* __restrict__ part, int32_t splits, int32_t querie
     const int h = threadIdx.x / 16;
     const int d0 = kSlice * slice + 8 * (threadIdx.x % 16);
     const float* p0 = part + (qrow * kGroups + hg) * splits * kPartFloats;
+    // every split's (max, sum, 8 outputs) is loaded first (slots past `splits`
+    // repeat the last split and are ignored), then combined in split order
+    float ms[kMaxSplits], ls[kMaxSplits];
+    float4 va[kMaxSplits], vb[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        const float* ps = p0 + (s < splits ? s : splits - 1) * kPartFloats;
+        ms[s] = ps[kHg * kDim + h];
+        ls[s] = ps[kHg * kDim + kHg + h];
+        va[s] = *reinterpret_cast<const float4*>(ps + h * kDim + d0);
+        vb[s] = *reinterpret_cast<const float4*>(ps + h * kDim + d0 + 4);
+    }
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s)
-        M = fmaxf(M, p0[s * kPartFloats + kHg * kDim + h]);
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        M = s < splits ? fmaxf(M, ms[s]) : M;
     float den = 0.0f;
     float num[8] = {};
-    for (int s = 0; s < splits; ++s) {
-        const float* ps = p0 + s * kPartFloats;
-        const float ms = ps[kHg * kDim + h];
-        const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-        den += f * ps[kHg * kDim + kHg + h];
-        const float4 a = *reinterpret_cast<const float4*>(ps + h * kDim + d0);
-        const float4 c = *reinterpret_cast<const float4*>(ps + h * kDim + d0 + 4);
-        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            num[i] += f * v[i];
+    for (int s = 0; s < kMaxSplits; ++s) {
+        if (s < splits) {
+            const float f = ms[s] == -INFINITY ? 0.0f : exp2f(ms[s] - M);
+            den += f * ls[s];
+            const float v[8] = {va[s].x, va[s].y, va[s].z, va[s].w, vb[s].x, vb[s].y, vb[s].z, vb[s].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                num[i] += f * v[i];
+        }
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     float res[8];
