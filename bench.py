@@ -79,7 +79,7 @@ def build_device(w: synth.Workload, torch, L):
     dev = torch.device("cuda:0")
     B, N = w.B, w.n_cap
     st = {"w": w}
-    st["kc"] = torch.empty(B, N, 64, dtype=torch.uint8, device=dev)
+    st["kc"] = L.key_codes_empty(B * N, device=dev)  # tiled indexer-key codes
     st["ks"] = torch.empty(B, N, 8, dtype=torch.uint8, device=dev)
     st["vc"] = torch.empty(B, N, 256, dtype=torch.uint8, device=dev)
     st["vs"] = torch.empty(B, N, 32, dtype=torch.uint8, device=dev)
@@ -90,7 +90,7 @@ def build_device(w: synth.Workload, torch, L):
         cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
         for b in range(B):
             kx = torch.from_numpy(synth.idx_k_rows(w, b, r0, n)).to(dev)
-            L.quantize_kv(kx, st["kc"][b], st["ks"][b], dst_row=r0)
+            L.quantize_kv(kx, st["kc"], st["ks"], dst_row=b * N + r0)
             vx = torch.from_numpy(synth.kv_rows(w, b, r0, n)).to(dev)
             L.quantize_kv(vx, st["vc"][b], st["vs"][b], cos_d, sin_d, synth.ROPE_OFFSET,
                           synth.ROPE_DIM, dst_row=r0)

@@ -29,7 +29,8 @@
  *   Reuse    csa2_sparse_attn with the latest top-k.
  *
  * Conventions for every call:
- *   - All tensors are row-major and contiguous.  Every data pointer is a
+ *   - All tensors are row-major and contiguous, except the indexer-key code
+ *     cache (key-tile layout, see csa2_quantize_kv).  Every data pointer is a
  *     DEVICE pointer, allocated and owned by the caller; the library never
  *     allocates, frees or synchronises, and keeps no state between calls.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
@@ -66,7 +67,7 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Library ABI version (major * 100 + minor): 101. */
+/* Library ABI version (major * 100 + minor): 102. */
 int32_t csa2_version(void);
 
 /*
@@ -80,13 +81,20 @@ int32_t csa2_version(void);
  *             product and sum rounded to fp32 (no fused multiply-add).
  *             rope_offset and rope_dim must be even, rope_offset + rope_dim
  *             <= channels.  Main KV: offset 448, dim 64.
- *   codes     u8 output; row r goes to codes + r*dst_stride*channels/2
- *             (channel 2j in the low nibble of byte j, 2j+1 in the high one).
- *   scales    u8 output; row r goes to scales + r*dst_stride*channels/16
- *             (byte g scales channels [16g, 16g+16)).
+ *   codes     u8 output; row r is written as row d = dst_row + r*dst_stride
+ *             of the code array (channel 2j in the low nibble of byte j, 2j+1
+ *             in the high one).  channels != 128: row-major, byte j of row d
+ *             at codes + d*channels/2 + j.  channels == 128 (indexer keys):
+ *             the KEY-TILE LAYOUT of the indexer-key cache, byte j of row d at
+ *               codes + (d/32)*2048 + (j/16)*512 + (d%32)*16 + j%16
+ *             (tiles of 32 rows, each stored as four 512-byte planes of
+ *             16-byte chunks); the array must hold whole tiles.
+ *   scales    u8 output, row-major in both cases: row d at scales +
+ *             d*channels/16 (byte g scales channels [16g, 16g+16)).
+ *   dst_row   >= 0: output row of input row 0.
  *   dst_stride  >= 1: distance in rows between consecutive output rows (1 =
  *             contiguous; n_cap = one new row per sequence of a [B, n_cap]
- *             cache).
+ *             cache, with dst_row = its position in sequence 0).
  * Encoding per group: scale = E4M3 round-to-nearest-even of max|x|/6,
  * saturating at 448; code = nearest E2M1 value of |x|/scale, ties to the even
  * code, saturating at 6; scale 0 gives code 0; sign only on non-zero codes.
@@ -95,8 +103,8 @@ int32_t csa2_version(void);
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
                              const float* rope_cos, const float* rope_sin,
                              int32_t rope_offset, int32_t rope_dim,
-                             uint8_t* codes, uint8_t* scales, int64_t dst_stride,
-                             void* stream);
+                             uint8_t* codes, uint8_t* scales, int64_t dst_row,
+                             int64_t dst_stride, void* stream);
 
 /*
  * FP8 encoder of sliding-window KV rows ([N] 2.3: the window KV stays in FP8).
@@ -116,7 +124,8 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
  *   kv_x       fp32 [rows, 512] main latent rows -> rotary (as csa2_quantize_kv,
  *              rope_cos / rope_sin [rows, rope_dim/2]) -> MXFP4 into kv_codes /
  *              kv_scales, row r at cache row d = kv_dst[r] (kv_codes + d*256,
- *              kv_scales + d*32), or d = r*kv_stride when kv_dst is NULL.
+ *              kv_scales + d*32), or d = dst_row + r*kv_stride when kv_dst is
+ *              NULL.
  *   kv_dst     int64 [rows] or NULL: per-entry destination rows (each
  *              sequence's own append position: b*n_cap + n_b); rows whose
  *              d is outside [0, kv_cap) are skipped.  The indexer-key row r
@@ -129,8 +138,11 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
  *              channels, four partial sums of fused multiply-adds (channel c
  *              to partial c % 4, in increasing c) added as (p0 + p1) + (p2 + p3);
  *              then the quarters as (Q0 + Q1) + (Q2 + Q3); then encoded.
- *   idx_codes, idx_scales  MXFP4 outputs, row d at + d*64 / d*8 (d as above,
- *              with idx_stride in place of kv_stride when kv_dst is NULL).
+ *   idx_codes, idx_scales  MXFP4 outputs for row d (d as above, with
+ *              idx_stride in place of kv_stride when kv_dst is NULL): codes
+ *              in the key-tile layout of csa2_quantize_kv (channels 128),
+ *              scales at idx_scales + d*8.  kv_cap counts rows of both
+ *              caches; idx_codes must hold ceil(kv_cap/32) tiles of 2048 B.
  *   idx_y      fp32 [rows, 128] receives the projection (NULL: not written;
  *              only used when projecting).
  *   swa_x      fp32 [swa_rows, 512] window rows -> E4M3FN (as
@@ -152,11 +164,12 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
 csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* rope_cos,
                                 const float* rope_sin, int32_t rope_offset, int32_t rope_dim,
                                 uint8_t* kv_codes, uint8_t* kv_scales, int64_t kv_stride,
-                                const int64_t* kv_dst, int64_t kv_cap, const float* idx_x,
-                                const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
-                                int64_t idx_stride, float* idx_y, const float* swa_x,
-                                int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
-                                const int64_t* swa_dst, int64_t swa_cap, void* stream);
+                                const int64_t* kv_dst, int64_t dst_row, int64_t kv_cap,
+                                const float* idx_x, const uint16_t* w_idx, uint8_t* idx_codes,
+                                uint8_t* idx_scales, int64_t idx_stride, float* idx_y,
+                                const float* swa_x, int32_t swa_rows, uint8_t* swa_out,
+                                int64_t swa_stride, const int64_t* swa_dst, int64_t swa_cap,
+                                void* stream);
 
 /*
  * Full-layer indexer scan ([N] 2.2, [A] 3.4: the first Full layer scores the
@@ -164,8 +177,12 @@ csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* ro
  * of its positions).
  *   q          bf16 [B, nq, 32, 128] indexer queries.
  *   w          fp32 [B, nq, 32] per-head weights.
- *   k_codes    u8 [B, n_cap, 64], k_scales u8 [B, n_cap, 8]: MXFP4 indexer
- *              keys (shared by every query of a sequence).
+ *   k_codes    MXFP4 indexer-key codes of the [B, n_cap] cache in the key-tile
+ *              layout (csa2_quantize_kv, channels 128): entry j of sequence b
+ *              is row f = b*n_cap + j, in tile f/32; the array holds
+ *              ceil(B*n_cap/32) tiles of 2048 B (16-byte aligned).
+ *   k_scales   u8 [B, n_cap, 8] row-major scales (shared by every query of a
+ *              sequence, like the codes).
  *   n_visible  int32 [B, nq]: query (b, i) sees entries [0, min(n_visible, n_cap)).
  *   block      positions per block (8).
  *   block_max  fp32 [B, nq, ceil(n_cap/block)]: block beta of query (b,i)

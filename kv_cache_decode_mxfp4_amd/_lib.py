@@ -51,7 +51,7 @@ def load() -> ctypes.CDLL:
     L.csa2_version.restype = i32
     L.csa2_version.argtypes = []
     L.csa2_quantize_kv.restype = st
-    L.csa2_quantize_kv.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, vp, i64, vp]
+    L.csa2_quantize_kv.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, vp, i64, i64, vp]
     L.csa2_quantize_swa.restype = st
     L.csa2_quantize_swa.argtypes = [vp, i64, i32, vp, i64, vp]
     L.csa2_index_full.restype = st
@@ -68,8 +68,8 @@ def load() -> ctypes.CDLL:
     L.csa2_sparse_attn_workspace.restype = sz
     L.csa2_sparse_attn_workspace.argtypes = [i32, i32, i32, i32]
     L.csa2_encode_entries.restype = st
-    L.csa2_encode_entries.argtypes = [i32, vp, vp, vp, i32, i32, vp, vp, i64, vp, i64, vp, vp, vp,
-                                      vp, i64, vp, vp, i32, vp, i64, vp, i64, vp]
+    L.csa2_encode_entries.argtypes = [i32, vp, vp, vp, i32, i32, vp, vp, i64, vp, i64, i64, vp,
+                                      vp, vp, vp, i64, vp, vp, i32, vp, i64, vp, i64, vp]
     L.csa2_sparse_attn_rope_bf16.restype = st
     L.csa2_sparse_attn_rope_bf16.argtypes = [vp, i32, i32, vp, vp, i64, vp, i32, vp, i32, vp, i32,
                                              f32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
@@ -112,25 +112,44 @@ def _bf16_bits(t):
     raise TypeError(f"expected bfloat16 (or its uint16 bits), got {t.dtype}")
 
 
-def _rows_fit(t, row_bytes, dst_row, dst_stride, rows, name):
+KEY_TILE = 32            # entries per tile of the indexer-key code cache
+KEY_TILE_BYTES = 2048    # 32 entries x 64 code bytes
+
+
+def key_code_bytes(rows: int) -> int:
+    """Bytes of an indexer-key code array holding `rows` entries (whole tiles of 32).
+
+    Layout (include/csa2.h, csa2_quantize_kv with 128 channels): byte j of entry f at
+    (f // 32) * 2048 + (j // 16) * 512 + (f % 32) * 16 + j % 16."""
+    return -(-rows // KEY_TILE) * KEY_TILE_BYTES
+
+
+def key_codes_empty(rows: int, device="cuda") -> torch.Tensor:
+    """Uninitialised indexer-key code array for `rows` entries ([tiles, 2048] uint8)."""
+    return torch.empty(key_code_bytes(rows) // KEY_TILE_BYTES, KEY_TILE_BYTES, dtype=torch.uint8,
+                       device=device)
+
+
+def _rows_fit(t, row_bytes, dst_row, dst_stride, rows, name, tiled=False):
     last = dst_row + (rows - 1) * dst_stride + 1 if rows else 0
-    if dst_row < 0 or last * row_bytes > t.numel():
+    need = key_code_bytes(last) if tiled else last * row_bytes
+    if dst_row < 0 or need > t.numel():
         raise ValueError(f"{name}: rows do not fit the destination")
 
 
 def quantize_kv(x, codes, scales, rope_cos=None, rope_sin=None, rope_offset=0, rope_dim=0,
                 dst_row=0, dst_stride=1, stream=None):
-    """Encode x [rows, C] into rows dst_row + r*dst_stride of the flat code/scale caches."""
+    """Encode x [rows, C] into rows dst_row + r*dst_stride of the flat code/scale caches
+    (C = 128: codes in the key-tile layout of the indexer-key cache)."""
     _dt(x, torch.float32, "x")
     _dt(codes, torch.uint8, "codes")
     _dt(scales, torch.uint8, "scales")
     rows, C = x.shape
-    _rows_fit(codes, C // 2, dst_row, dst_stride, rows, "codes")
+    _rows_fit(codes, C // 2, dst_row, dst_stride, rows, "codes", tiled=(C == 128))
     _rows_fit(scales, C // 16, dst_row, dst_stride, rows, "scales")
     _check("csa2_quantize_kv", load().csa2_quantize_kv(
         _p(x), rows, C, _p(rope_cos), _p(rope_sin), rope_offset, rope_dim,
-        _p(codes) + dst_row * (C // 2), _p(scales) + dst_row * (C // 16), dst_stride,
-        _stream(stream)))
+        _p(codes), _p(scales), dst_row, dst_stride, _stream(stream)))
 
 
 def quantize_swa(x, out, row_len=512, dst_row=0, dst_stride=1, stream=None):
@@ -158,9 +177,9 @@ def encode_entries(kv_x, kv_codes, kv_scales, idx_codes, idx_scales, idx_x=None,
                        (idx_codes, "idx_codes", 64), (idx_scales, "idx_scales", 8)):
         _dt(t_, torch.uint8, n_)
         if kv_dst is None:
-            _rows_fit(t_, rb, dst_row, dst_stride, rows, n_)
-    kv_cap = min(kv_codes.numel() // 256, kv_scales.numel() // 32, idx_codes.numel() // 64,
-                 idx_scales.numel() // 8)
+            _rows_fit(t_, rb, dst_row, dst_stride, rows, n_, tiled=(n_ == "idx_codes"))
+    kv_cap = min(kv_codes.numel() // 256, kv_scales.numel() // 32,
+                 idx_codes.numel() // KEY_TILE_BYTES * KEY_TILE, idx_scales.numel() // 8)
     if kv_dst is not None:
         _dt(kv_dst, torch.int64, "kv_dst")
         dst_row = 0
@@ -181,11 +200,24 @@ def encode_entries(kv_x, kv_codes, kv_scales, idx_codes, idx_scales, idx_x=None,
     swa_cap = swa_out.numel() // 512 if swa_out is not None else 0
     _check("csa2_encode_entries", load().csa2_encode_entries(
         rows, _p(kv_x), _p(rope_cos), _p(rope_sin), rope_offset, rope_dim,
-        _p(kv_codes) + dst_row * 256, _p(kv_scales) + dst_row * 32, dst_stride, _p(kv_dst),
-        kv_cap, _p(idx_x), _p(w_idx), _p(idx_codes) + dst_row * 64,
-        _p(idx_scales) + dst_row * 8, dst_stride, _p(idx_y), _p(swa_x), n_sw,
+        _p(kv_codes), _p(kv_scales), dst_stride, _p(kv_dst), dst_row,
+        kv_cap, _p(idx_x), _p(w_idx), _p(idx_codes),
+        _p(idx_scales), dst_stride, _p(idx_y), _p(swa_x), n_sw,
         (_p(swa_out) + swa_row * 512) if swa_out is not None else None, swa_stride,
         _p(swa_dst), swa_cap, _stream(stream)))
+
+
+def _key_cache_rows(k_codes, k_scales, B) -> int:
+    """n_cap of a [B, n_cap] indexer-key cache: scales [B, n_cap, 8] row-major, codes in
+    whole key tiles for the B * n_cap entries."""
+    _dt(k_codes, torch.uint8, "k_codes")
+    _dt(k_scales, torch.uint8, "k_scales")
+    if k_scales.dim() != 3 or k_scales.shape[0] != B or k_scales.shape[2] != 8:
+        raise ValueError(f"k_scales: expected [{B}, n_cap, 8], got {tuple(k_scales.shape)}")
+    n_cap = k_scales.shape[1]
+    if k_codes.numel() < key_code_bytes(B * n_cap):
+        raise ValueError(f"k_codes: {k_codes.numel()} bytes cannot hold {B * n_cap} key entries")
+    return n_cap
 
 
 def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block=8, stream=None):
@@ -193,7 +225,7 @@ def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block
     _dt(w, torch.float32, "w")
     _dt(n_visible, torch.int32, "n_visible")
     B, nq = q.shape[0], q.shape[1]
-    n_cap = k_codes.shape[1]
+    n_cap = _key_cache_rows(k_codes, k_scales, B)
     _check("csa2_index_full", load().csa2_index_full(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block,
         _p(block_max), _p(scores), _stream(stream)))
@@ -204,7 +236,7 @@ def index_pool(q, w, k_codes, k_scales, blocks, n_visible, pool_score, pool_idx,
     q = _bf16_bits(q)
     _dt(blocks, torch.int32, "blocks")
     B, nq = q.shape[0], q.shape[1]
-    n_cap = k_codes.shape[1]
+    n_cap = _key_cache_rows(k_codes, k_scales, B)
     _check("csa2_index_pool", load().csa2_index_pool(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(blocks), blocks.shape[-1], block,
         _p(n_visible), B, nq, _p(pool_score), _p(pool_idx), _stream(stream)))

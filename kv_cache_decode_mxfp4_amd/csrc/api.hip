@@ -62,15 +62,16 @@ const char* csa2_last_error(void)
 
 int32_t csa2_version(void)
 {
-    return 101;
+    return 102;
 }
 
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
                              const float* rope_cos, const float* rope_sin, int32_t rope_offset,
                              int32_t rope_dim, uint8_t* codes, uint8_t* scales,
-                             int64_t dst_stride, void* stream)
+                             int64_t dst_row, int64_t dst_stride, void* stream)
 {
     REQUIRE(rows >= 0, CSA2_ERR_INVALID_ARG, "quantize_kv: rows < 0");
+    REQUIRE(dst_row >= 0, CSA2_ERR_INVALID_ARG, "quantize_kv: dst_row < 0");
     REQUIRE(channels > 0 && channels % 16 == 0 && channels <= 4096, CSA2_ERR_UNSUPPORTED,
             "quantize_kv: channels must be a positive multiple of 16 up to 4096 (got %d)",
             channels);
@@ -88,7 +89,7 @@ csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
             "quantize_kv: x must be 16-byte and codes 8-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_quantize_kv(x, rows, channels, rope_cos, rope_sin, rope_offset,
-                                           rope_dim, codes, scales, dst_stride, s),
+                                           rope_dim, codes, scales, dst_row, dst_stride, s),
                   s, "quantize_kv");
 }
 
@@ -112,13 +113,15 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
 csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* rope_cos,
                                 const float* rope_sin, int32_t rope_offset, int32_t rope_dim,
                                 uint8_t* kv_codes, uint8_t* kv_scales, int64_t kv_stride,
-                                const int64_t* kv_dst, int64_t kv_cap, const float* idx_x,
-                                const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
-                                int64_t idx_stride, float* idx_y, const float* swa_x,
-                                int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
-                                const int64_t* swa_dst, int64_t swa_cap, void* stream)
+                                const int64_t* kv_dst, int64_t dst_row, int64_t kv_cap,
+                                const float* idx_x, const uint16_t* w_idx, uint8_t* idx_codes,
+                                uint8_t* idx_scales, int64_t idx_stride, float* idx_y,
+                                const float* swa_x, int32_t swa_rows, uint8_t* swa_out,
+                                int64_t swa_stride, const int64_t* swa_dst, int64_t swa_cap,
+                                void* stream)
 {
     REQUIRE(rows >= 0 && swa_rows >= 0, CSA2_ERR_INVALID_ARG, "encode_entries: negative rows");
+    REQUIRE(dst_row >= 0, CSA2_ERR_INVALID_ARG, "encode_entries: dst_row < 0");
     REQUIRE(kv_stride >= 1 && idx_stride >= 1 && swa_stride >= 1, CSA2_ERR_INVALID_ARG,
             "encode_entries: strides must be >= 1");
     REQUIRE(kv_cap >= 0 && swa_cap >= 0, CSA2_ERR_INVALID_ARG, "encode_entries: negative capacity");
@@ -149,7 +152,7 @@ csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* ro
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_encode_entries(rows, kv_x, rope_cos, rope_sin, rope_offset,
                                               rope_dim, kv_codes, kv_scales, kv_stride, kv_dst,
-                                              kv_cap, idx_x, w_idx, idx_codes, idx_scales,
+                                              dst_row, kv_cap, idx_x, w_idx, idx_codes, idx_scales,
                                               idx_stride, idx_y, swa_x, swa_rows, swa_out,
                                               swa_stride, swa_dst, swa_cap, s),
                   s, "encode_entries");

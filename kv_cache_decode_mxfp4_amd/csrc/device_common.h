@@ -21,6 +21,14 @@ constexpr int kWave = 64;
 
 // --------------------------------------------------------------- formats
 
+// Byte offset of code byte c (< 64) of indexer-key entry f in the tiled key
+// cache (layout in dims.h).
+__device__ __forceinline__ int64_t key_code_offset(int64_t f, int c)
+{
+    return (f >> 5) * kKeyTileBytes + (c >> 4) * kKeyPlane + (f & 31) * 16 + (c & 15);
+}
+
+
 // 8 E2M1 codes (one dword, channel 2j in the low nibble of byte j) times the
 // scale s -> 8 fp16 values in channel order.  The hardware converter applies
 // only the exponent of its fp32 scale, so it runs with 1.0 and the E4M3 scale

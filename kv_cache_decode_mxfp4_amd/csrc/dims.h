@@ -14,4 +14,15 @@ constexpr int kBlock = 8;
 constexpr int kTopkSegment = 16384;  // elements one top-k workgroup holds
 constexpr int kTopkMaxK = 8192;
 
+// Indexer-key code cache layout: tiles of 32 consecutive entries (flat entry
+// index f = b * n_cap + j), each tile 2048 bytes stored as four planes of
+// 16-byte chunks: byte c of entry f sits at
+//   (f / 32) * 2048 + (c / 16) * 512 + (f % 32) * 16 + c % 16,
+// so the 32 entries' chunk p form one contiguous 512-byte plane.  A scan
+// lane that owns one entry and reads 16 bytes then makes every load
+// instruction of a wave cover whole cache lines.
+constexpr int kKeyTile = 32;
+constexpr int kKeyPlane = kKeyTile * 16;        // 512
+constexpr int kKeyTileBytes = kKeyTile * kIdxDim / 2;  // 2048
+
 }  // namespace csa2

@@ -14,8 +14,9 @@
 //   A = q   [32 heads x 16 channels per k-step], B = k^T [16 channels x 32
 //   entries], D [32 heads x 32 entries] in fp32.  Lane l owns entry l%32 and
 //   the channel half h = l/32: k-step t covers channels 64h + 8t .. +8 on both
-//   operands, so a lane reads 32 contiguous code bytes and one dword of
-//   scales per entry.  Keys are dequantised in registers (exact in fp16, the
+//   operands, so a lane reads code bytes [32h, 32h + 32) of its entry (chunks
+//   2h and 2h + 1 of the tiled key layout: each load instruction of the wave
+//   reads two whole 512-byte planes) and one dword of scales.  Keys are dequantised in registers (exact in fp16, the
 //   E4M3-per-16 scale is not gfx950's E8M0-per-32 MX scale, so the scaled MFMA
 //   cannot take it).  Each query head is pre-multiplied by a power of two that
 //   brings its largest |q| to [2^14, 2^15), which keeps the bf16 -> fp16 cast
@@ -104,30 +105,34 @@ struct KeyTile {
     uint32_t sc;    // scale bytes [4h, 4h+4)
 };
 
+// Key of flat entry f (tiled codes, row-major scales), channel half `half`.
 __device__ __forceinline__ void load_key(const uint8_t* __restrict__ codes,
-                                         const uint8_t* __restrict__ scales, int64_t entry,
+                                         const uint8_t* __restrict__ scales, int64_t f,
                                          int half, KeyTile& K)
 {
-    const u32x4* c = reinterpret_cast<const u32x4*>(codes + entry * (kIdxDim / 2) + 32 * half);
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(scales + entry * (kIdxDim / 16) + 4 * half);
+    const u32x4* c = reinterpret_cast<const u32x4*>(codes + key_code_offset(f, 32 * half));
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(scales + f * (kIdxDim / 16) + 4 * half);
 #if CSA2_SCAN_NONTEMPORAL
     // streamed once: do not keep the keys in the caches
     K.c0 = __builtin_nontemporal_load(c);
-    K.c1 = __builtin_nontemporal_load(c + 1);
+    K.c1 = __builtin_nontemporal_load(c + kKeyPlane / 16);
     K.sc = __builtin_nontemporal_load(sp);
 #else
     K.c0 = c[0];
-    K.c1 = c[1];
+    K.c1 = c[kKeyPlane / 16];
     K.sc = *sp;
 #endif
 }
 
 // Keys of one chunk, read with raw buffer loads: the descriptors hold the
-// chunk's base addresses and its visible size in bytes (scalar registers), a
-// lane keeps one 32-bit offset per array, and the hardware range check turns
-// every load past the visible size into zeros.  Tile offsets are added to
-// the vector offset, which the range check covers.  Loads are non-temporal
-// (the keys are streamed once).
+// chunk's base addresses and sizes in bytes (scalar registers), a lane keeps
+// one 32-bit offset per array, and the hardware range check turns every load
+// past the size into zeros.  The scale descriptor ends at the last visible
+// entry; the code descriptor starts at the key tile holding the chunk's first
+// entry f0 and ends with the tile holding its last visible entry (entries of
+// that tile past the visible end are read and masked).  Tile offsets are
+// added to the vector offset, which the range check covers.  Loads are
+// non-temporal (the keys are streamed once).
 struct ChunkKeys {
     __amdgpu_buffer_rsrc_t codes, scales;
     int32_t vc, vs;  // byte offsets of the lane's entry and half in tile 0
@@ -136,29 +141,36 @@ struct ChunkKeys {
 constexpr int kBufferConfig = 0x00020000;  // raw (untyped) buffer, 32-bit data
 constexpr int kNonTemporal = 2;
 
+// f0: flat index of the chunk's first entry; entries: visible entries of the
+// chunk; entry: the lane's entry relative to f0 in tile 0 (32 * wave plus
+// lane % 32).
 __device__ __forceinline__ ChunkKeys chunk_keys(const uint8_t* codes, const uint8_t* scales,
-                                                int64_t start, int32_t entries, int entry,
+                                                int64_t f0, int32_t entries, int entry,
                                                 int half)
 {
     ChunkKeys C;
+    const int64_t t0 = f0 >> 5;                                // key tile of f0
+    const int64_t t_end = (f0 + entries + kKeyTile - 1) >> 5;  // past the last visible tile
     C.codes = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(codes + start * (kIdxDim / 2)), 0, entries * (kIdxDim / 2),
-        kBufferConfig);
+        const_cast<uint8_t*>(codes + t0 * kKeyTileBytes), 0,
+        (int32_t)((t_end - t0) * kKeyTileBytes), kBufferConfig);
     C.scales = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(scales + start * (kIdxDim / 16)), 0, entries * (kIdxDim / 16),
+        const_cast<uint8_t*>(scales + f0 * (kIdxDim / 16)), 0, entries * (kIdxDim / 16),
         kBufferConfig);
-    C.vc = entry * (kIdxDim / 2) + 32 * half;
+    const int e = (int)(f0 & 31) + entry;  // the lane's entry counted from tile t0's first
+    C.vc = (e >> 5) * kKeyTileBytes + 2 * half * kKeyPlane + (e & 31) * 16;
     C.vs = entry * (kIdxDim / 16) + 4 * half;
     return C;
 }
 
-// Tile whose entries start `first_entry` entries after the lane's tile-0 entry.
+// Tile whose entries start `first_entry` (a multiple of 32) entries after the
+// lane's tile-0 entry.
 __device__ __forceinline__ void load_key(const ChunkKeys& C, int32_t first_entry, KeyTile& K)
 {
     const int32_t oc = C.vc + first_entry * (kIdxDim / 2);
     const int32_t os = C.vs + first_entry * (kIdxDim / 16);
     K.c0 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc, 0, kNonTemporal);
-    K.c1 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc + 16, 0, kNonTemporal);
+    K.c1 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc + kKeyPlane, 0, kNonTemporal);
     K.sc = __builtin_amdgcn_raw_buffer_load_b32(C.scales, os, 0, kNonTemporal);
 }
 
@@ -231,9 +243,7 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const int half = lane >> 5;
     const int entry0 = kTileEntries * wave + (lane & 31);  // lane's entry in tile 0
 
-    const ChunkKeys C = chunk_keys(codes + b * n_cap * (kIdxDim / 2),
-                                   scales + b * n_cap * (kIdxDim / 16), start, n_here, entry0,
-                                   half);
+    const ChunkKeys C = chunk_keys(codes, scales, b * n_cap + start, n_here, entry0, half);
     KeyTile ring[kPrefetch];
 #pragma unroll
     for (int p = 0; p < kPrefetch; ++p)
@@ -296,11 +306,13 @@ index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const int64_t slots = (int64_t)n_blocks * kBlock;
 
     // with nothing visible the loads read the query row instead (8 KiB, always
-    // valid) and are masked: every load below is unconditional, so all of a
-    // wave's loads are in flight together
+    // valid: entry 0 of the tiled layout lies in its first 1552 bytes) and are
+    // masked: every load below is unconditional, so all of a wave's loads are
+    // in flight together
     const uint8_t* qrow_bytes = reinterpret_cast<const uint8_t*>(q + row * (kIdxHeads * kIdxDim));
-    const uint8_t* kc = n_vis > 0 ? codes + b * n_cap * (kIdxDim / 2) : qrow_bytes;
-    const uint8_t* ks = n_vis > 0 ? scales + b * n_cap * (kIdxDim / 16) : qrow_bytes;
+    const uint8_t* kc = n_vis > 0 ? codes : qrow_bytes;
+    const uint8_t* ks = n_vis > 0 ? scales : qrow_bytes;
+    const int64_t f_seq = n_vis > 0 ? b * n_cap : 0;  // flat index of the sequence's entry 0
     const int32_t* blk = blocks + row * n_blocks;
 
     const int64_t first = ((int64_t)part * kWaves + wave) * kPoolTilesPerWave * kTileEntries;
@@ -318,7 +330,7 @@ index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
         const int64_t slot = first + i * kTileEntries + (lane & 31);
         const int64_t p = (int64_t)bl[i] * kBlock + slot % kBlock;
         pos[i] = (slot < slots && bl[i] >= 0 && p < n_vis) ? p : -1;
-        load_key(kc, ks, pos[i] >= 0 ? pos[i] : 0, half, K[i]);
+        load_key(kc, ks, f_seq + (pos[i] >= 0 ? pos[i] : 0), half, K[i]);
     }
     QueryOperand Q;  // loaded while the gathers are in flight
     load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);

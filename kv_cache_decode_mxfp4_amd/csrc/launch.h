@@ -13,7 +13,8 @@ namespace csa2 {
 
 hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, const float* cs,
                               const float* sn, int32_t rope_off, int32_t rope_dim, uint8_t* codes,
-                              uint8_t* scales, int64_t dst_stride, hipStream_t stream);
+                              uint8_t* scales, int64_t dst_row, int64_t dst_stride,
+                              hipStream_t stream);
 
 hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_t* out,
                                int64_t dst_stride, hipStream_t stream);
@@ -25,11 +26,11 @@ hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8
 hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* cs, const float* sn,
                                  int32_t rope_off, int32_t rope_dim, uint8_t* kv_codes,
                                  uint8_t* kv_scales, int64_t kv_stride, const int64_t* kv_dst,
-                                 int64_t kv_cap, const float* idx_x, const uint16_t* w_idx,
-                                 uint8_t* idx_codes, uint8_t* idx_scales, int64_t idx_stride,
-                                 float* idx_y, const float* swa_x, int32_t swa_rows,
-                                 uint8_t* swa_out, int64_t swa_stride, const int64_t* swa_dst,
-                                 int64_t swa_cap, hipStream_t stream);
+                                 int64_t dst_row, int64_t kv_cap, const float* idx_x,
+                                 const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
+                                 int64_t idx_stride, float* idx_y, const float* swa_x,
+                                 int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
+                                 const int64_t* swa_dst, int64_t swa_cap, hipStream_t stream);
 
 hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,

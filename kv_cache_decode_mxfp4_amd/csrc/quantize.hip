@@ -124,7 +124,9 @@ __device__ __forceinline__ uint32_t fp8_word(float4 f)
     return word;
 }
 
-// Thread t of a group-per-thread launch: group g of row r of a [rows, C] input.
+// Thread t of a group-per-thread launch: group g of row r of a [rows, C] input,
+// written to row orow of the outputs: row-major codes, or the tiled
+// indexer-key layout when C is the indexer-key width.
 __device__ __forceinline__ void encode_row_group(const float* __restrict__ x, int64_t r,
                                                  int32_t g, int32_t C,
                                                  const float* __restrict__ cs,
@@ -142,7 +144,9 @@ __device__ __forceinline__ void encode_row_group(const float* __restrict__ x, in
     rope_group(v, g, r, cs, sn, rope_off, rope_dim);
     uint32_t packed[2];
     const uint32_t sb = encode_group(v, packed);
-    *reinterpret_cast<uint2*>(codes + orow * (C / 2) + 8 * g) = make_uint2(packed[0], packed[1]);
+    // bytes [8g, 8g + 8) of the row: one aligned 8-byte store in either layout
+    const int64_t co = C == kIdxDim ? key_code_offset(orow, 8 * g) : orow * (C / 2) + 8 * g;
+    *reinterpret_cast<uint2*>(codes + co) = make_uint2(packed[0], packed[1]);
     scales[orow * (C / 16) + g] = (uint8_t)sb;
 }
 
@@ -150,14 +154,14 @@ __global__ void __launch_bounds__(256)
 quantize_kv_kernel(const float* __restrict__ x, int64_t rows, int32_t C,
                    const float* __restrict__ cs, const float* __restrict__ sn, int32_t rope_off,
                    int32_t rope_dim, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                   int64_t dst_stride)
+                   int64_t dst_row, int64_t dst_stride)
 {
     const int32_t G = C / 16;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= rows * G)
         return;
     encode_row_group(x, t / G, (int32_t)(t % G), C, cs, sn, rope_off, rope_dim, codes, scales,
-                     (t / G) * dst_stride);
+                     dst_row + (t / G) * dst_stride);
 }
 
 // Four consecutive elements per thread; row_len % 4 == 0.
@@ -189,12 +193,15 @@ quantize_swa_kernel(const float* __restrict__ x, int64_t n, int32_t row_len,
 // 16 channels being 8 lanes); the rest encode the window rows.  Row r of the
 // caches goes to row kv_dst[r] (else r * stride) and window row r to row
 // swa_dst[r] (else r * swa_stride): with per-sequence positions that is each
-// sequence's own append position, and for the window a ring slot.
+// sequence's own append position, and for the window a ring slot.  Without
+// kv_dst, cache row r goes to dst0 + r * stride.  Indexer-key codes use the
+// tiled key layout.
 struct EntryJob {
     int32_t rows;
     const float* kv_x; const float* cs; const float* sn; int32_t rope_off, rope_dim;
     uint8_t* kv_codes; uint8_t* kv_scales; int64_t kv_stride;
-    const int64_t* kv_dst;   // per-row destination row of the caches, or null (r * stride)
+    const int64_t* kv_dst;   // per-row destination row of the caches, or null
+    int64_t dst0;            // without kv_dst: row r goes to dst0 + r * stride
     int64_t kv_cap;          // rows of the caches (destinations outside are skipped)
     const float* idx_x; const uint16_t* w_idx;
     uint8_t* idx_codes; uint8_t* idx_scales; int64_t idx_stride; float* idx_y;
@@ -205,12 +212,12 @@ struct EntryJob {
 };
 
 // Destination row of input row r: dst[r] (-1 when outside [0, cap): skipped)
-// or r * stride.
-__device__ __forceinline__ int64_t dst_row(const int64_t* __restrict__ dst, int64_t r,
-                                           int64_t stride, int64_t cap)
+// or dst0 + r * stride.
+__device__ __forceinline__ int64_t dst_row(const int64_t* __restrict__ dst, int64_t dst0,
+                                           int64_t r, int64_t stride, int64_t cap)
 {
     if (dst == nullptr)
-        return r * stride;
+        return dst0 + r * stride;
     const int64_t d = dst[r];
     return d >= 0 && d < cap ? d : -1;
 }
@@ -233,7 +240,7 @@ encode_entries_kernel(EntryJob J)
         const int64_t t = (int64_t)wg * 256 + threadIdx.x;
         if (t < (int64_t)J.rows * kKv) {
             const int64_t r = t / kKv;
-            const int64_t o = dst_row(J.kv_dst, r, J.kv_stride, J.kv_cap);
+            const int64_t o = dst_row(J.kv_dst, J.dst0, r, J.kv_stride, J.kv_cap);
             if (o >= 0)
                 encode_row_group(J.kv_x, r, (int32_t)(t % kKv), kDim, J.cs, J.sn, J.rope_off,
                                  J.rope_dim, J.kv_codes, J.kv_scales, o);
@@ -246,7 +253,7 @@ encode_entries_kernel(EntryJob J)
             const int64_t t = (int64_t)w * 256 + threadIdx.x;
             if (t < (int64_t)J.rows * kIdx) {
                 const int64_t r = t / kIdx;
-                const int64_t o = dst_row(J.kv_dst, r, J.idx_stride, J.kv_cap);
+                const int64_t o = dst_row(J.kv_dst, J.dst0, r, J.idx_stride, J.kv_cap);
                 if (o >= 0)
                     encode_row_group(J.idx_x, r, (int32_t)(t % kIdx), kIdxDim, nullptr, nullptr,
                                      0, 0, J.idx_codes, J.idx_scales, o);
@@ -307,10 +314,10 @@ encode_entries_kernel(EntryJob J)
         const float amax = max8_lanes(fmaxf(fabsf(y0), fabsf(y1)));
         const uint32_t sb = group_scale(amax);
         const float sv = e4m3_value(sb);
-        const int64_t orow = dst_row(J.kv_dst, r, J.idx_stride, J.kv_cap);
+        const int64_t orow = dst_row(J.kv_dst, J.dst0, r, J.idx_stride, J.kv_cap);
         if (orow < 0)
             return;
-        J.idx_codes[orow * (kIdxDim / 2) + lane] =
+        J.idx_codes[key_code_offset(orow, lane)] =
             (uint8_t)(e2m1_nibble(y0, sv) | (e2m1_nibble(y1, sv) << 4));
         if ((lane & 7) == 0)
             J.idx_scales[orow * kIdx + lane / 8] = (uint8_t)sb;
@@ -321,7 +328,7 @@ encode_entries_kernel(EntryJob J)
         return;
     const uint32_t word = fp8_word(reinterpret_cast<const float4*>(J.swa_x)[t]);
     const int64_t r = 4 * t / kDim, c = 4 * t % kDim;
-    const int64_t o = dst_row(J.swa_dst, r, J.swa_stride, J.swa_cap);
+    const int64_t o = dst_row(J.swa_dst, 0, r, J.swa_stride, J.swa_cap);
     if (o >= 0)
         *reinterpret_cast<uint32_t*>(J.swa_out + o * kDim + c) = word;
 }
@@ -330,14 +337,15 @@ encode_entries_kernel(EntryJob J)
 
 hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, const float* cs,
                               const float* sn, int32_t rope_off, int32_t rope_dim, uint8_t* codes,
-                              uint8_t* scales, int64_t dst_stride, hipStream_t stream)
+                              uint8_t* scales, int64_t dst_row, int64_t dst_stride,
+                              hipStream_t stream)
 {
     const int64_t threads = rows * (channels / 16);
     if (threads == 0)
         return hipSuccess;
     const int64_t grid = (threads + 255) / 256;
     quantize_kv_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
-        x, rows, channels, cs, sn, rope_off, rope_dim, codes, scales, dst_stride);
+        x, rows, channels, cs, sn, rope_off, rope_dim, codes, scales, dst_row, dst_stride);
     return hipGetLastError();
 }
 
@@ -357,14 +365,14 @@ hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8
 hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* cs, const float* sn,
                                  int32_t rope_off, int32_t rope_dim, uint8_t* kv_codes,
                                  uint8_t* kv_scales, int64_t kv_stride, const int64_t* kv_dst,
-                                 int64_t kv_cap, const float* idx_x, const uint16_t* w_idx,
-                                 uint8_t* idx_codes, uint8_t* idx_scales, int64_t idx_stride,
-                                 float* idx_y, const float* swa_x, int32_t swa_rows,
-                                 uint8_t* swa_out, int64_t swa_stride, const int64_t* swa_dst,
-                                 int64_t swa_cap, hipStream_t stream)
+                                 int64_t dst_row, int64_t kv_cap, const float* idx_x,
+                                 const uint16_t* w_idx, uint8_t* idx_codes, uint8_t* idx_scales,
+                                 int64_t idx_stride, float* idx_y, const float* swa_x,
+                                 int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
+                                 const int64_t* swa_dst, int64_t swa_cap, hipStream_t stream)
 {
     EntryJob J{rows, kv_x, cs, sn, rope_off, rope_dim, kv_codes, kv_scales, kv_stride, kv_dst,
-               kv_cap, idx_x, w_idx, idx_codes, idx_scales, idx_stride, idx_y,
+               dst_row, kv_cap, idx_x, w_idx, idx_codes, idx_scales, idx_stride, idx_y,
                swa_x, swa_rows, swa_out, swa_stride, swa_dst, swa_cap, 0, 0};
     J.wg_kv = (int32_t)(((int64_t)rows * (kDim / 16) + 255) / 256);
     J.wg_idx = idx_x != nullptr ? (int32_t)(((int64_t)rows * (kIdxDim / 16) + 255) / 256)

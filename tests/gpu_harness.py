@@ -28,6 +28,38 @@ def dev():
     return torch.device("cuda:0")
 
 
+# The GPU's indexer-key code cache is tiled (include/csa2.h, csa2_quantize_kv with 128
+# channels): byte j of entry f at (f // 32) * 2048 + (j // 16) * 512 + (f % 32) * 16 + j % 16.
+# The oracle keeps plain [rows, 64] rows; these two permutations convert between them.
+
+def tile_keys(codes: np.ndarray) -> np.ndarray:
+    """Row-major key codes [..., rows, 64] (leading dims flattened in order) -> the tiled
+    byte array of whole 32-entry tiles [tiles, 2048], padding entries zero."""
+    flat = np.ascontiguousarray(codes).reshape(-1, 64)
+    n = flat.shape[0]
+    tiles = -(-n // 32)
+    pad = np.zeros((tiles * 32, 64), np.uint8)
+    pad[:n] = flat
+    # [tile, entry, chunk, byte] -> [tile, chunk, entry, byte]
+    return np.ascontiguousarray(pad.reshape(tiles, 32, 4, 16).transpose(0, 2, 1, 3)).reshape(tiles, 2048)
+
+
+def seq_keys(tiled: torch.Tensor, b: int, n_cap: int) -> np.ndarray:
+    """Row-major codes [n_cap, 64] of sequence b of a tiled [B, n_cap] key cache (copies
+    only that sequence's tiles to the host)."""
+    flat = tiled.reshape(-1)
+    t0, t1 = (b * n_cap) // 32, -(-((b + 1) * n_cap) // 32)
+    rows = untile_keys(flat[t0 * 2048:t1 * 2048], (t1 - t0) * 32)
+    return rows[b * n_cap - t0 * 32:][:n_cap]
+
+
+def untile_keys(tiled, rows: int) -> np.ndarray:
+    """Inverse of tile_keys: the first `rows` entries as row-major [rows, 64]."""
+    a = tiled.cpu().numpy() if isinstance(tiled, torch.Tensor) else np.asarray(tiled)
+    a = a.reshape(-1, 4, 32, 16).transpose(0, 2, 1, 3).reshape(-1, 64)
+    return np.ascontiguousarray(a[:rows])
+
+
 @dataclass
 class Case:
     w: synth.Workload
@@ -85,13 +117,13 @@ def gpu_encode(c: Case) -> dict:
     w = c.w
     B, N = w.B, w.n_cap
     d = {}
-    d["kc"] = torch.empty(B, N, 64, dtype=torch.uint8, device=dev())
+    d["kc"] = _lib.key_codes_empty(B * N, device=dev())
     d["ks"] = torch.empty(B, N, 8, dtype=torch.uint8, device=dev())
     d["vc"] = torch.empty(B, N, 256, dtype=torch.uint8, device=dev())
     d["vs"] = torch.empty(B, N, 32, dtype=torch.uint8, device=dev())
     cos, sin = t(c.cos), t(c.sin)
     for b in range(B):
-        _lib.quantize_kv(t(c.idx_x[b]), d["kc"][b], d["ks"][b])
+        _lib.quantize_kv(t(c.idx_x[b]), d["kc"], d["ks"], dst_row=b * N)
         _lib.quantize_kv(t(c.kv_x[b]), d["vc"][b], d["vs"][b], cos, sin, synth.ROPE_OFFSET,
                          synth.ROPE_DIM)
     d["swa"] = []
@@ -110,7 +142,9 @@ def gpu_encode(c: Case) -> dict:
 
 
 def assert_encodings_equal(c: Case, d: dict):
-    assert np.array_equal(d["kc"].cpu().numpy(), c.o_kc), "indexer key codes differ"
+    B, N = c.w.B, c.w.n_cap
+    assert np.array_equal(untile_keys(d["kc"], B * N).reshape(B, N, 64), c.o_kc), \
+        "indexer key codes differ"
     assert np.array_equal(d["ks"].cpu().numpy(), c.o_ks), "indexer key scales differ"
     assert np.array_equal(d["vc"].cpu().numpy(), c.o_vc), "main KV codes differ"
     assert np.array_equal(d["vs"].cpu().numpy(), c.o_vs), "main KV scales differ"

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = L.load()
-    assert lib.csa2_version() == 101
+    assert lib.csa2_version() == 102
     assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
     assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
@@ -62,14 +62,17 @@ def _status(fn, *args):
 def test_host_validation_rejects_bad_arguments():
     vp = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     # channels not a multiple of 16
-    st, msg = _status("csa2_quantize_kv", vp, 4, 15, None, None, 0, 0, vp, vp, 1, None)
+    st, msg = _status("csa2_quantize_kv", vp, 4, 15, None, None, 0, 0, vp, vp, 0, 1, None)
     assert st == 2 and "channels" in msg
     # rotary range outside the row
-    st, msg = _status("csa2_quantize_kv", vp, 4, 512, vp, vp, 480, 64, vp, vp, 1, None)
+    st, msg = _status("csa2_quantize_kv", vp, 4, 512, vp, vp, 480, 64, vp, vp, 0, 1, None)
     assert st == 1 and "rotary" in msg
     # null pointers with work to do
-    st, _ = _status("csa2_quantize_kv", None, 4, 512, None, None, 0, 0, None, None, 1, None)
+    st, _ = _status("csa2_quantize_kv", None, 4, 512, None, None, 0, 0, None, None, 0, 1, None)
     assert st == 1
+    # negative destination row
+    st, msg = _status("csa2_quantize_kv", vp, 4, 128, None, None, 0, 0, vp, vp, -1, 1, None)
+    assert st == 1 and "dst_row" in msg
     # unsupported block size
     st, msg = _status("csa2_index_full", vp, vp, vp, vp, 100, vp, 1, 1, 4, vp, None, None)
     assert st == 2 and "block" in msg
@@ -95,7 +98,8 @@ def test_host_validation_rejects_bad_arguments():
 
 
 def test_empty_inputs_are_no_ops():
-    assert _status("csa2_quantize_kv", None, 0, 512, None, None, 0, 0, None, None, 1, None)[0] == 0
+    assert _status("csa2_quantize_kv", None, 0, 512, None, None, 0, 0, None, None, 0, 1,
+                   None)[0] == 0
     assert _status("csa2_index_full", None, None, None, None, 0, None, 0, 1, 8, None, None,
                    None)[0] == 0
     assert _status("csa2_topk", None, None, 0, 0, None, 5, None, None, 0, None)[0] == 0
@@ -125,10 +129,10 @@ def test_rope_bf16_attention_validation():
 
 
 def _entries(rows=4, kv_x=16, idx_x=16, w=None, off=448, dim=64, cos=16, swa_rows=0, swa_x=None,
-             kv_stride=1, dst=None):
+             kv_stride=1, dst=None, dst_row=0):
     vp = ctypes.c_void_p
     return _status("csa2_encode_entries", rows, vp(kv_x), vp(cos), vp(cos), off, dim, vp(16),
-                   vp(16), kv_stride, None, 0, vp(idx_x), vp(w), vp(16), vp(16), 1, None,
+                   vp(16), kv_stride, None, dst_row, 0, vp(idx_x), vp(w), vp(16), vp(16), 1, None,
                    vp(swa_x), swa_rows, vp(16), 1, vp(dst), 10, None)
 
 
@@ -145,4 +149,25 @@ def test_encode_entries_validation():
     assert st == 1
     st, msg = _entries(dst=12)
     assert st == 1 and "destination" in msg
+    st, msg = _entries(dst_row=-2)
+    assert st == 1 and "dst_row" in msg
     assert _entries(rows=0, kv_x=None, idx_x=None, cos=None)[0] == 0
+
+
+def test_key_tile_helpers_follow_the_documented_layout():
+    """The tests' row <-> key-tile permutations place byte j of entry f at
+    (f // 32) * 2048 + (j // 16) * 512 + (f % 32) * 16 + j % 16 and invert each other."""
+    import numpy as np
+    from gpu_harness import tile_keys, untile_keys
+    rng = np.random.default_rng(3)
+    rows = 77
+    codes = rng.integers(0, 256, (rows, 64), dtype=np.uint8)
+    tiled = tile_keys(codes)
+    assert tiled.shape == (3, 2048)
+    flat = tiled.reshape(-1)
+    for f in range(rows):
+        for j in range(64):
+            assert flat[(f // 32) * 2048 + (j // 16) * 512 + (f % 32) * 16 + j % 16] == codes[f, j]
+    assert np.array_equal(untile_keys(tiled, rows), codes)
+    assert not untile_keys(tiled, 96)[rows:].any()  # padding entries are zero
+    assert L.key_code_bytes(rows) == 3 * 2048 and L.key_code_bytes(64) == 2 * 2048

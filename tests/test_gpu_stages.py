@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import synth
-from gpu_harness import (ATTN_TOL, cdiv, check_set, dev, finite_close, max_abs, t)
+from gpu_harness import (ATTN_TOL, cdiv, check_set, dev, finite_close, max_abs, t, tile_keys,
+                         untile_keys)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +58,9 @@ def test_quantize_kv_bit_exact(kind):
             np.zeros((4, 128)), -np.zeros((4, 128)), rng.standard_normal((8, 128)) * 1e-40,
         ]).astype(np.float32)
     C = x.shape[1]
-    codes = torch.empty(x.shape[0], C // 2, dtype=torch.uint8, device=dev())
+    # 128 channels: the indexer-key cache's tiled code layout
+    codes = (L.key_codes_empty(x.shape[0], device=dev()) if C == 128 else
+             torch.empty(x.shape[0], C // 2, dtype=torch.uint8, device=dev()))
     scales = torch.empty(x.shape[0], C // 16, dtype=torch.uint8, device=dev())
     if cos is None:
         L.quantize_kv(t(x), codes, scales)
@@ -65,8 +68,32 @@ def test_quantize_kv_bit_exact(kind):
     else:
         L.quantize_kv(t(x), codes, scales, t(cos), t(sin), 448, 64)
         ref = oracle.quantize_rows(x, cos, sin, 448, 64)
-    assert np.array_equal(codes.cpu().numpy(), ref[0])
+    got = untile_keys(codes, x.shape[0]) if C == 128 else codes.cpu().numpy()
+    assert np.array_equal(got, ref[0])
     assert np.array_equal(scales.cpu().numpy(), ref[1])
+
+
+def test_quantize_kv_key_tiles_strided_rows():
+    """Indexer-key rows at rows dst_row + r*dst_stride of a tiled code array: every
+    row lands in its tile slot and nothing else is written."""
+    rng = np.random.default_rng(9)
+    R, row0, stride, cap = 23, 5, 3, 100
+    x = rng.standard_normal((R, 128)).astype(np.float32)
+    codes = torch.full((L.key_code_bytes(cap),), 0x5A, dtype=torch.uint8, device=dev())
+    scales = torch.full((cap, 8), 0x5A, dtype=torch.uint8, device=dev())
+    L.quantize_kv(t(x), codes, scales, dst_row=row0, dst_stride=stride)
+    rc, rs = oracle.quantize_rows(x)
+    rows = row0 + stride * np.arange(R)
+    got_c = untile_keys(codes, L.key_code_bytes(cap) // 64)
+    got_s = scales.cpu().numpy()
+    assert np.array_equal(got_c[rows], rc) and np.array_equal(got_s[rows], rs)
+    other = np.setdiff1d(np.arange(got_c.shape[0]), rows)
+    assert np.all(got_c[other] == 0x5A)
+    assert np.all(got_s[np.setdiff1d(np.arange(cap), rows)] == 0x5A)
+    # the tiled placement itself: entry f, byte j at (f//32)*2048 + (j//16)*512 + (f%32)*16 + j%16
+    raw = codes.cpu().numpy()
+    f, j = rows[7], 37
+    assert raw[(f // 32) * 2048 + (j // 16) * 512 + (f % 32) * 16 + j % 16] == rc[7, j]
 
 
 def _rotary_tie_rows(n, seed=21):
@@ -129,10 +156,9 @@ def test_quantize_kv_strided_append():
     codes = torch.zeros(B, n_cap, 256, dtype=torch.uint8, device=dev())
     scales = torch.zeros(B, n_cap, 32, dtype=torch.uint8, device=dev())
     xd, cd, sd = t(x), t(cos), t(sin)
-    # rows go to row n_cap-1 of every sequence: base pointer of that row, stride n_cap
+    # rows go to row n_cap-1 of every sequence: dst_row n_cap-1, stride n_cap
     st = L.load().csa2_quantize_kv(xd.data_ptr(), B, 512, cd.data_ptr(), sd.data_ptr(), 448, 64,
-                                   codes.data_ptr() + (n_cap - 1) * 256,
-                                   scales.data_ptr() + (n_cap - 1) * 32, n_cap,
+                                   codes.data_ptr(), scales.data_ptr(), n_cap - 1, n_cap,
                                    torch.cuda.current_stream().cuda_stream)
     assert st == 0
     torch.cuda.synchronize()
@@ -235,7 +261,7 @@ def test_index_full_scores_and_block_max_match_oracle():
     nblk = cdiv(N, 8)
     bm = torch.full((B, 1, nblk), 12345.0, device=dev())
     sc = torch.full((B, 1, N), 12345.0, device=dev())
-    L.index_full(t(q, torch.uint16), t(w), t(kc), t(ks), t(nv), bm, sc)
+    L.index_full(t(q, torch.uint16), t(w), t(tile_keys(kc)), t(ks), t(nv), bm, sc)
     bm, sc = bm.cpu().numpy(), sc.cpu().numpy()
     for b in range(B):
         n = int(nv[b, 0])
@@ -263,9 +289,9 @@ def test_index_full_long_chunks_ragged_rows():
     nblk = cdiv(N, 8)
     bm = torch.full((1, nq, nblk), 12345.0, device=dev())
     sc = torch.full((1, nq, N), 12345.0, device=dev())
-    L.index_full(t(q, torch.uint16), t(w), t(kc[None]), t(ks[None]), t(nv), bm, sc)
+    L.index_full(t(q, torch.uint16), t(w), t(tile_keys(kc)), t(ks[None]), t(nv), bm, sc)
     bm2 = torch.full((1, nq, nblk), 12345.0, device=dev())
-    L.index_full(t(q, torch.uint16), t(w), t(kc[None]), t(ks[None]), t(nv), bm2)
+    L.index_full(t(q, torch.uint16), t(w), t(tile_keys(kc)), t(ks[None]), t(nv), bm2)
     bm, sc, bm2 = bm.cpu().numpy()[0], sc.cpu().numpy()[0], bm2.cpu().numpy()[0]
     assert np.array_equal(bm, bm2)  # with and without the score output
     for i in list(range(len(edges))) + [100, 311, 511]:
@@ -284,7 +310,7 @@ def test_index_pool_scores_bit_identical_to_scan():
     B, N = kc.shape[0], kc.shape[1]
     sc = torch.zeros((B, 1, N), device=dev())
     bm = torch.zeros((B, 1, cdiv(N, 8)), device=dev())
-    L.index_full(t(q, torch.uint16), t(w), t(kc), t(ks), t(nv), bm, sc)
+    L.index_full(t(q, torch.uint16), t(w), t(tile_keys(kc)), t(ks), t(nv), bm, sc)
     rng = np.random.default_rng(2)
     nb = 300
     blocks = np.sort(rng.choice(cdiv(N, 8), (B, 1, nb), replace=True), axis=-1).astype(np.int32)
@@ -292,7 +318,7 @@ def test_index_pool_scores_bit_identical_to_scan():
     blocks[0, 0, -6] = cdiv(N, 8) - 1  # partial last block
     ps = torch.empty(B, 1, nb * 8, device=dev())
     pi = torch.empty(B, 1, nb * 8, dtype=torch.int32, device=dev())
-    L.index_pool(t(q, torch.uint16), t(w), t(kc), t(ks), t(blocks), t(nv), ps, pi)
+    L.index_pool(t(q, torch.uint16), t(w), t(tile_keys(kc)), t(ks), t(blocks), t(nv), ps, pi)
     ps, pi, sc = ps.cpu().numpy(), pi.cpu().numpy(), sc.cpu().numpy()
     for b in range(B):
         pos = oracle.pool_positions(blocks[b, 0], 8, int(nv[b, 0]))
@@ -543,8 +569,16 @@ def _entries_case(R, S, seed):
 
 
 def _entries_buffers(n_rows, n_swa):
+    """Caches filled with 0xA5; the indexer-key codes in whole key tiles."""
     z = lambda *sh: torch.full(sh, 0xA5, dtype=torch.uint8, device=dev())
-    return z(n_rows, 256), z(n_rows, 32), z(n_rows, 64), z(n_rows, 8), z(n_swa, 512)
+    return (z(n_rows, 256), z(n_rows, 32), z(L.key_code_bytes(n_rows)), z(n_rows, 8),
+            z(n_swa, 512))
+
+
+def _host_caches(kc, ks, ic, isc, sw, n_rows):
+    """Host copies, the key codes untiled to [n_rows, 64]."""
+    return (kc.cpu().numpy(), ks.cpu().numpy(), untile_keys(ic, n_rows), isc.cpu().numpy(),
+            sw.cpu().numpy())
 
 
 @pytest.mark.parametrize("R,S,project", [(1, 1, False), (16, 16, False), (37, 5, False),
@@ -565,7 +599,10 @@ def test_encode_entries_one_launch(R, S, project):
                      dst_row=row0, dst_stride=stride, idx_y=y,
                      swa_x=t(swa_x) if S else None, swa_out=sw if S else None,
                      swa_row=swa_row0, swa_stride=swa_stride)
-    kc, ks, ic, isc, sw = (a.cpu().numpy() for a in (kc, ks, ic, isc, sw))
+    padded = L.key_code_bytes(n_rows) // 64
+    tail = untile_keys(ic, padded)[n_rows:]
+    assert np.all(tail == 0xA5)  # the padding rows of the last key tile are untouched
+    kc, ks, ic, isc, sw = _host_caches(kc, ks, ic, isc, sw, n_rows)
     rows = row0 + stride * np.arange(R)
     other = np.setdiff1d(np.arange(n_rows), rows)
     if R:
@@ -604,7 +641,7 @@ def test_encode_entries_per_sequence_destinations_and_ring():
     L.encode_entries(t(kv_x), kc, ks, ic, isc, idx_x=t(idx_x), rope_cos=t(cos), rope_sin=t(sin),
                      rope_offset=448, rope_dim=64, kv_dst=t(kv_dst), swa_x=t(swa_x), swa_out=sw,
                      swa_dst=t(swa_dst))
-    kc, ks, ic, isc, sw = (a.cpu().numpy() for a in (kc, ks, ic, isc, sw))
+    kc, ks, ic, isc, sw = _host_caches(kc, ks, ic, isc, sw, R * n_cap)
     ref_c, ref_s = oracle.quantize_rows(kv_x, cos, sin, 448, 64)
     ref_ic, ref_is = oracle.quantize_rows(idx_x)
     ok = np.arange(5)
