@@ -12,7 +12,7 @@ One step = one Full layer at decode for the whole batch: encode the new
 token's main-KV, indexer-key and window rows; block scan over every entry;
 pool select (top-2048 blocks); pool rescoring; top-512; sparse attention.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--cpu-sample 4]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--cpu-sample 16]
 
 Prints one JSON line.  Only one GPU is supported (--gpus above 1 exits).
 The default warm-up (300 steps, about 90 ms at the default workload) is
@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--cpu-sample", type=int, default=4,
+    ap.add_argument("--cpu-sample", type=int, default=16,
                     help="query rows of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
