@@ -42,6 +42,12 @@ constexpr int kGroupEntries = kPrefetch * kStep;  // entries per prefetch round
 // query once and keeps its prefetch ring running over a long range.
 constexpr int kMaxChunk = 16384;
 constexpr int64_t kScanTargetWorkgroups = 1024;
+// Query rows per sequence from which the scan pairs rows (prefill shapes);
+// decode (one row per sequence) streams its keys from HBM, one row each.
+#ifndef CSA2_SCAN_PAIR_MIN_ROWS
+#define CSA2_SCAN_PAIR_MIN_ROWS 2
+#endif
+constexpr int32_t kPairMinRows = CSA2_SCAN_PAIR_MIN_ROWS;
 #ifndef CSA2_SCAN_NONTEMPORAL
 #define CSA2_SCAN_NONTEMPORAL 1
 #endif
@@ -174,17 +180,10 @@ __device__ __forceinline__ void load_key(const ChunkKeys& C, int32_t first_entry
     K.sc = __builtin_amdgcn_raw_buffer_load_b32(C.scales, os, 0, kNonTemporal);
 }
 
-// Score of the lane's entry (both lanes of an entry return the same value).
-__device__ __forceinline__ float score_entry(const QueryOperand& Q, const KeyTile& K)
+// Weighted ReLU head sum of one query's accumulators (both lanes of an entry
+// return the same value).
+__device__ __forceinline__ float head_sum(const QueryOperand& Q, const f32x16& acc)
 {
-    const uint32_t words[8] = {K.c0[0], K.c0[1], K.c0[2], K.c0[3], K.c1[0], K.c1[1], K.c1[2], K.c1[3]};
-    f32x16 acc = {};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const _Float16 s = e4m3_byte_to_f16(K.sc, t / 2);
-        const half8 b = dequant8_fp4(words[t], s);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q.a[t], b, acc, 0, 0, 0);
-    }
     // max(0, x) as a signed-integer max of the bit pattern: one instruction,
     // the same value as fmaxf for every non-NaN x (-0 and negatives give +0)
     float part = 0.0f;
@@ -198,6 +197,39 @@ __device__ __forceinline__ float score_entry(const QueryOperand& Q, const KeyTil
     const auto pair = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                        __float_as_uint(part), false, false);
     return __uint_as_float(pair[0]) + __uint_as_float(pair[1]);
+}
+
+// Score of the lane's entry (both lanes of an entry return the same value).
+__device__ __forceinline__ float score_entry(const QueryOperand& Q, const KeyTile& K)
+{
+    const uint32_t words[8] = {K.c0[0], K.c0[1], K.c0[2], K.c0[3], K.c1[0], K.c1[1], K.c1[2], K.c1[3]};
+    f32x16 acc = {};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const _Float16 s = e4m3_byte_to_f16(K.sc, t / 2);
+        const half8 b = dequant8_fp4(words[t], s);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q.a[t], b, acc, 0, 0, 0);
+    }
+    return head_sum(Q, acc);
+}
+
+// Scores of the lane's entry for two queries: the key is dequantised once and
+// feeds both MFMA chains; each chain is the one score_entry runs (same operands,
+// same order), so both scores are bit-identical to score_entry's.
+__device__ __forceinline__ void score_entry2(const QueryOperand& Q0, const QueryOperand& Q1,
+                                             const KeyTile& K, float& s0, float& s1)
+{
+    const uint32_t words[8] = {K.c0[0], K.c0[1], K.c0[2], K.c0[3], K.c1[0], K.c1[1], K.c1[2], K.c1[3]};
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const _Float16 s = e4m3_byte_to_f16(K.sc, t / 2);
+        const half8 b = dequant8_fp4(words[t], s);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q0.a[t], b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q1.a[t], b, acc1, 0, 0, 0);
+    }
+    s0 = head_sum(Q0, acc0);
+    s1 = head_sum(Q1, acc1);
 }
 
 // Maximum over the 8 lanes of each aligned group of 8 (DPP: swap neighbours,
@@ -285,6 +317,107 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
         dst[t] = sblk[t];
 }
 
+// Full-range scan of two query rows of one sequence (rows 2p and 2p + 1 of
+// its nq; the second is absent when nq is odd): the many-row (prefill) form.
+// Each key tile is loaded and dequantised once for both rows, which halves
+// the dequantisation per score, the VALU work that bounds the one-row scan
+// when its keys come from the caches rather than HBM.  Same chunking, key
+// ring, masking and outputs per row as index_full_kernel; a row whose visible
+// range ends before the chunk writes nothing for it.  Two waves per SIMD (the
+// two queries' operands and accumulators take twice the registers).
+template <bool kScores>
+__global__ void __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+index_full_pair_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                       const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                       int64_t n_cap, const int32_t* __restrict__ n_visible, int32_t nq,
+                       int32_t pairs_per_seq, int32_t chunk, int32_t chunks_per_pair,
+                       int64_t nblk_cap, float* __restrict__ block_max,
+                       float* __restrict__ scores)
+{
+    __shared__ float sblk[2][kMaxChunk / kBlock];
+
+    const int64_t pair = blockIdx.x / chunks_per_pair;
+    const int64_t b = pair / pairs_per_seq;
+    const int64_t i0 = 2 * (pair % pairs_per_seq);
+    const bool two = i0 + 1 < nq;
+    const int64_t row0 = b * nq + i0;
+    const int64_t row1 = two ? row0 + 1 : row0;
+    int64_t nv0 = n_visible[row0];
+    nv0 = nv0 < 0 ? 0 : (nv0 > n_cap ? n_cap : nv0);
+    int64_t nv1 = two ? (int64_t)n_visible[row1] : 0;
+    nv1 = nv1 < 0 ? 0 : (nv1 > n_cap ? n_cap : nv1);
+    const int64_t start = (int64_t)(blockIdx.x % chunks_per_pair) * chunk;
+    const int64_t nv_max = nv0 > nv1 ? nv0 : nv1;
+    if (start >= nv_max)
+        return;
+    auto here = [&](int64_t nv) {
+        return (int32_t)(nv <= start ? 0 : (nv - start < chunk ? nv - start : chunk));
+    };
+    const int32_t n_here0 = here(nv0), n_here1 = here(nv1);
+    const int32_t n_here = n_here0 > n_here1 ? n_here0 : n_here1;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int entry0 = kTileEntries * wave + (lane & 31);
+
+    const ChunkKeys C = chunk_keys(codes, scales, b * n_cap + start, n_here, entry0, half);
+    KeyTile ring[kPrefetch];
+#pragma unroll
+    for (int p = 0; p < kPrefetch; ++p)
+        load_key(C, p * kStep, ring[p]);
+    __builtin_amdgcn_sched_barrier(0);
+    QueryOperand Q0, Q1;
+    load_query(q + row0 * (kIdxHeads * kIdxDim), w + row0 * kIdxHeads, lane, Q0);
+    load_query(q + row1 * (kIdxHeads * kIdxDim), w + row1 * kIdxHeads, lane, Q1);
+
+    const bool writer = lane < 32 && (lane & 7) == 0;
+    const int blk0 = entry0 / kBlock;
+    const int groups = (n_here + kGroupEntries - 1) / kGroupEntries;
+    auto finish = [&](int i, float s0, float s1) {
+        const int e = entry0 + i * kStep;
+        s0 = e < n_here0 ? s0 : -INFINITY;
+        s1 = e < n_here1 ? s1 : -INFINITY;
+        if (kScores && lane < 32) {
+            if (e < n_here0)
+                scores[row0 * n_cap + start + e] = s0;
+            if (e < n_here1)
+                scores[row1 * n_cap + start + e] = s1;
+        }
+        const float m0 = max8(s0);
+        const float m1 = max8(s1);
+        if (writer) {
+            sblk[0][blk0 + i * (kStep / kBlock)] = m0;
+            sblk[1][blk0 + i * (kStep / kBlock)] = m1;
+        }
+    };
+    for (int g = 0; g < groups - 1; ++g) {
+#pragma unroll
+        for (int p = 0; p < kPrefetch; ++p) {
+            const int i = g * kPrefetch + p;
+            float s0, s1;
+            score_entry2(Q0, Q1, ring[p], s0, s1);
+            load_key(C, (i + kPrefetch) * kStep, ring[p]);
+            finish(i, s0, s1);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < kPrefetch; ++p) {
+        const int i = (groups - 1) * kPrefetch + p;
+        float s0, s1;
+        score_entry2(Q0, Q1, ring[p], s0, s1);
+        finish(i, s0, s1);
+    }
+    __syncthreads();
+    const int nb0 = (n_here0 + kBlock - 1) / kBlock;
+    const int nb1 = (n_here1 + kBlock - 1) / kBlock;
+    float* dst0 = block_max + row0 * nblk_cap + start / kBlock;
+    float* dst1 = block_max + row1 * nblk_cap + start / kBlock;
+    for (int t = threadIdx.x; t < nb0; t += kWaves * kWave)
+        dst0[t] = sblk[0][t];
+    for (int t = threadIdx.x; t < nb1; t += kWaves * kWave)
+        dst1[t] = sblk[1][t];
+}
+
 // Pool scan: score the positions of a list of blocks (4 blocks per tile).
 constexpr int kPoolTilesPerWave = 4;
 
@@ -354,6 +487,29 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
                              int32_t B, int32_t nq, float* block_max, float* scores,
                              hipStream_t stream)
 {
+    const int64_t nblk_cap = (n_cap + kBlock - 1) / kBlock;
+    if (nq >= kPairMinRows) {
+        // many rows per sequence (prefill): two rows per workgroup
+        const int32_t pairs_per_seq = (nq + 1) / 2;
+        const int64_t pairs = (int64_t)B * pairs_per_seq;
+        int32_t chunk = kMaxChunk;
+        while (chunk > kGroupEntries &&
+               pairs * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
+            chunk /= 2;
+        const int64_t chunks = (n_cap + chunk - 1) / chunk;
+        const int64_t grid = pairs * chunks;
+        if (grid == 0)
+            return hipSuccess;
+        if (scores != nullptr)
+            index_full_pair_kernel<true><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
+                q, w, k_codes, k_scales, n_cap, n_visible, nq, pairs_per_seq, chunk,
+                (int32_t)chunks, nblk_cap, block_max, scores);
+        else
+            index_full_pair_kernel<false><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
+                q, w, k_codes, k_scales, n_cap, n_visible, nq, pairs_per_seq, chunk,
+                (int32_t)chunks, nblk_cap, block_max, nullptr);
+        return hipGetLastError();
+    }
     const int64_t rows = (int64_t)B * nq;
     int32_t chunk = kMaxChunk;
     while (chunk > kGroupEntries && rows * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
@@ -362,7 +518,6 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
     const int64_t grid = rows * chunks;
     if (grid == 0)
         return hipSuccess;
-    const int64_t nblk_cap = (n_cap + kBlock - 1) / kBlock;
     if (scores != nullptr)
         index_full_kernel<true><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
             q, w, k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,

@@ -328,6 +328,46 @@ def test_index_pool_scores_bit_identical_to_scan():
         assert np.all(np.isneginf(ps[b, 0][~ok]))
 
 
+def test_paired_scan_bit_identical_to_one_row_scan_and_pool():
+    """Several query rows of one sequence take the paired scan (two rows per workgroup,
+    one dequantisation per key): every score and block maximum must equal, bit for bit,
+    the one-row scan of the same row and the pool scan of the same positions; an odd
+    row count leaves one row unpaired, and rows see different causal lengths."""
+    N, nq = 5003, 5
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((N, 128)).astype(np.float32)
+    kc, ks = oracle.quantize_rows(x)
+    kct, kst = t(tile_keys(kc)), t(ks[None])
+    q = synth.normal_bf16(synth.key(11, 10, 0, 0), 0, nq * 4096, 1 / np.sqrt(128)).reshape(1, nq, 32, 128)
+    w = synth.uniform_f32(synth.key(11, 11, 0, 0), 0, nq * 32).reshape(1, nq, 32)
+    nv = np.array([[N, N - 1, 700, 0, 4099]], np.int32)
+    nblk = cdiv(N, 8)
+    sc = torch.full((1, nq, N), 12345.0, device=dev())
+    bm = torch.full((1, nq, nblk), 12345.0, device=dev())
+    L.index_full(t(q, torch.uint16), t(w), kct, kst, t(nv), bm, sc)
+    sc, bm = sc.cpu().numpy()[0], bm.cpu().numpy()[0]
+    blocks = np.sort(rng.choice(nblk, (1, nq, 64), replace=False), axis=-1).astype(np.int32)
+    ps = torch.empty(1, nq, 64 * 8, device=dev())
+    pi = torch.empty(1, nq, 64 * 8, dtype=torch.int32, device=dev())
+    L.index_pool(t(q, torch.uint16), t(w), kct, kst, t(blocks), t(nv), ps, pi)
+    ps, pi = ps.cpu().numpy()[0], pi.cpu().numpy()[0]
+    for i in range(nq):
+        n = int(nv[0, i])
+        s1 = torch.full((1, 1, N), 12345.0, device=dev())
+        b1 = torch.full((1, 1, nblk), 12345.0, device=dev())
+        L.index_full(t(q[:, i:i + 1], torch.uint16), t(w[:, i:i + 1]), kct, kst,
+                     t(nv[:, i:i + 1]), b1, s1)
+        assert np.array_equal(sc[i], s1.cpu().numpy()[0, 0]), f"row {i}: scores differ"
+        assert np.array_equal(bm[i], b1.cpu().numpy()[0, 0]), f"row {i}: block maxima differ"
+        if n:
+            ref = oracle.index_scores(q[0, i], w[0, i], kc, ks, n)
+            ok, err = finite_close(sc[i, :n], ref)
+            assert ok, f"row {i}: max err {err}"
+        ok = pi[i] >= 0
+        assert np.array_equal(pi[i], oracle.pool_positions(blocks[0, i], 8, n))
+        assert np.array_equal(ps[i][ok], sc[i][pi[i][ok]])
+
+
 # ------------------------------------------------------------------ attention
 
 def _attn_case(B=2, N=3000, k=100, swa_cap=160, seed=3):
