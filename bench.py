@@ -178,16 +178,38 @@ def make_step(st, torch, L, layers, kv_production="rows", attn_out="fp32"):
                          st["swa_end"], w.n_win, out_bf16=out16, rope_cos=st["q_cos"],
                          rope_sin=st["q_sin"])
 
+    def event_pair():
+        # created (by one record) before use: the library's scan dispatch records them
+        pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in pair:
+            e.record()
+        return pair
+
+    spare_events = []
+
+    def prepare_scan_events(n):
+        spare_events.extend(event_pair() for _ in range(n))
+        torch.cuda.synchronize()
+
     def step(time_scan=False):
         encode_new()
+        evs = None
         if time_scan:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        L.index_full(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], st["n_vis"], buf.block_max)
-        if time_scan:
-            e1.record()
-            scan_events.append((e0, e1))
-        layers.select_blocks(buf, n_blk, w.k, w.nb)
+            evs = spare_events.pop() if spare_events else event_pair()
+            scan_events.append(evs)
+        if w.nb >= w.k:
+            # scan + pool select in one call (the scan also writes the select's group
+            # maxima); the scan kernel's own dispatch records the timing events
+            L.index_full_pool(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], st["n_vis"],
+                              buf.block_max, buf.pool, ws=buf.ws_topk, scan_events=evs)
+        else:
+            if evs:
+                evs[0].record()
+            L.index_full(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], st["n_vis"],
+                         buf.block_max)
+            if evs:
+                evs[1].record()
+            layers.select_blocks(buf, n_blk, w.k, w.nb)
         L.index_pool(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], buf.sel_blocks,
                      st["n_vis"], buf.pool_score, buf.pool_idx)
         L.topk(buf.pool_score, w.k, buf.topk, idx=buf.pool_idx, ws=buf.ws_topk)
@@ -198,15 +220,26 @@ def make_step(st, torch, L, layers, kv_production="rows", attn_out="fp32"):
             for layer in range(1, len(w.layers)):
                 attn(layer)
 
+    step.prepare_scan_events = prepare_scan_events
     return step, scan_events
 
 
 def scan_bytes(w: synth.Workload) -> int:
-    """Algorithmic bytes of one index_full launch at decode: every visible indexer key of
-    the query's own sequence (64 B codes + 8 B scales), the query (32x128 bf16) and
-    weights (32 fp32), the block maxima written (fp32 per 8 entries)."""
+    """Algorithmic bytes of one scan launch at decode: every visible indexer key of the
+    query's own sequence (64 B codes + 8 B scales), the query (32x128 bf16) and weights
+    (32 fp32), the block maxima written (fp32 per 8 entries) and, when the scan feeds the
+    pool select in the same call with groups of g blocks, one uint32 group key per g
+    blocks of the row."""
     nv = w.n_visible().astype(np.int64)
-    return int(nv.sum()) * 72 + w.B * w.nq * (32 * 128 * 2 + 32 * 4) + int(((nv + 7) // 8).sum()) * 4
+    nblk_cap = (w.n_cap + 7) // 8
+    b = int(nv.sum()) * 72 + w.B * w.nq * (32 * 128 * 2 + 32 * 4) + int(((nv + 7) // 8).sum()) * 4
+    # the select's group size over a row of nblk_cap block maxima (0: no groups); the scan
+    # writes the group keys when it is a power of two dividing 64
+    g = -(-nblk_cap // 16384) if nblk_cap > 16384 else 0
+    g = g if g * w.nb <= 16384 else 0
+    if w.nb >= w.k and w.nb > 0 and g > 0 and 64 % g == 0:
+        b += w.B * w.nq * (-(-nblk_cap // g)) * 4
+    return b
 
 
 def scan_flops(w: synth.Workload) -> int:
@@ -329,12 +362,13 @@ def main():
     torch.cuda.synchronize()
     log("warm")
     scan_events.clear()
+    step.prepare_scan_events((args.steps + SCAN_EVENT_EVERY - 1) // SCAN_EVENT_EVERY)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    # the scan's own duration comes from HIP events around it on every SCAN_EVENT_EVERY-th
-    # timed step (each event record costs the stream a few microseconds)
+    # the scan's own duration: HIP events that the scan kernel's dispatch records (through
+    # the library call) on every SCAN_EVENT_EVERY-th timed step
     for i in range(args.steps):
         step(time_scan=(i % SCAN_EVENT_EVERY == 0))
     t_end.record()

@@ -19,6 +19,7 @@
  *
  * Layer call sequences (one query row per (sequence, query)):
  *   Full     csa2_index_full -> csa2_topk(block maxima, nb) = pool
+ *            (or both in one call: csa2_index_full_pool)
  *            -> csa2_index_pool(own query, pool) -> csa2_topk(k) = top-k
  *            -> csa2_sparse_attn.
  *            When the pool has fewer than k blocks (or there is no pool, as
@@ -67,7 +68,7 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Library ABI version (major * 100 + minor): 102. */
+/* Library ABI version (major * 100 + minor): 103. */
 int32_t csa2_version(void);
 
 /*
@@ -198,6 +199,36 @@ csa2_status csa2_index_full(const uint16_t* q, const float* w,
                             const uint8_t* k_codes, const uint8_t* k_scales, int64_t n_cap,
                             const int32_t* n_visible, int32_t B, int32_t nq, int32_t block,
                             float* block_max, float* scores, void* stream);
+
+/*
+ * Full-layer scan and pool select in one call ([N] 2.2, [A] 3.4: the Full
+ * layer scores the whole visible range and keeps the nb blocks with the
+ * largest block scores as the pool).  Same arguments and block_max output as
+ * csa2_index_full (no per-entry scores), plus
+ *   nb         pool blocks per query row, 1 <= nb <= 8192.
+ *   pool       int32 [B, nq, nb]: the chosen block ids in ascending order,
+ *              -1 padded -- exactly csa2_topk(block_max, L = ceil(n_cap/8),
+ *              rows = B*nq, n_valid = ceil(n_visible/8), k = nb).
+ *   ws, ws_bytes  device workspace of at least
+ *              csa2_index_full_pool_workspace(n_cap, B*nq, nb) bytes (8-byte
+ *              aligned; any contents): the same as that csa2_topk call needs.
+ *   scan_start, scan_stop  hipEvent_t (created by the caller) or NULL: the
+ *              scan kernel's dispatch records them at its start and end, so
+ *              hipEventElapsedTime gives the scan's own duration inside the
+ *              call (the benchmark's roofline).  No other effect.
+ * When the select groups blocks (rows of more than 16384 blocks) in groups
+ * that align with the scan's chunks, the scan writes the group maxima into
+ * the workspace itself, which saves the select's pass over the block maxima.
+ * Errors as csa2_index_full and csa2_topk (CSA2_ERR_WORKSPACE when ws_bytes
+ * is too small).
+ */
+size_t      csa2_index_full_pool_workspace(int64_t n_cap, int32_t rows, int32_t nb);
+csa2_status csa2_index_full_pool(const uint16_t* q, const float* w,
+                                 const uint8_t* k_codes, const uint8_t* k_scales, int64_t n_cap,
+                                 const int32_t* n_visible, int32_t B, int32_t nq, int32_t block,
+                                 int32_t nb, float* block_max, int32_t* pool, void* ws,
+                                 size_t ws_bytes, void* scan_start, void* scan_stop,
+                                 void* stream);
 
 /*
  * Indexer scoring restricted to a pool of blocks ([N] 2.2, [A] 3.4: Reindex

@@ -20,7 +20,8 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_UNSUPPORTED",
           3: "CSA2_ERR_WORKSPACE", 4: "CSA2_ERR_LAUNCH"}
 
 EXPORTS = ("csa2_last_error", "csa2_version", "csa2_quantize_kv", "csa2_quantize_swa",
-           "csa2_index_full", "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
+           "csa2_index_full", "csa2_index_full_pool", "csa2_index_full_pool_workspace",
+           "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
            "csa2_sparse_attn", "csa2_sparse_attn_workspace", "csa2_sparse_attn_rope_bf16",
            "csa2_encode_entries")
 
@@ -56,6 +57,11 @@ def load() -> ctypes.CDLL:
     L.csa2_quantize_swa.argtypes = [vp, i64, i32, vp, i64, vp]
     L.csa2_index_full.restype = st
     L.csa2_index_full.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, i32, vp, vp, vp]
+    L.csa2_index_full_pool.restype = st
+    L.csa2_index_full_pool.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, sz,
+                                       vp, vp, vp]
+    L.csa2_index_full_pool_workspace.restype = sz
+    L.csa2_index_full_pool_workspace.argtypes = [i64, i32, i32]
     L.csa2_index_pool.restype = st
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i32, i32, vp, vp, vp]
     L.csa2_topk.restype = st
@@ -229,6 +235,30 @@ def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block
     _check("csa2_index_full", load().csa2_index_full(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block,
         _p(block_max), _p(scores), _stream(stream)))
+
+
+def index_full_pool_workspace(n_cap, rows, nb) -> int:
+    return int(load().csa2_index_full_pool_workspace(n_cap, rows, nb))
+
+
+def index_full_pool(q, w, k_codes, k_scales, n_visible, block_max, pool, ws=None, block=8,
+                    scan_events=None, stream=None):
+    """Full-layer scan and pool select in one call: block_max as index_full, pool [B, nq, nb]
+    = the nb best blocks in ascending order (what topk over block_max returns).
+    scan_events: optional (start, stop) torch.cuda.Event pair (timing enabled, already
+    created by one record) that the scan kernel's dispatch records."""
+    q = _bf16_bits(q)
+    _dt(w, torch.float32, "w")
+    _dt(n_visible, torch.int32, "n_visible")
+    _dt(pool, torch.int32, "pool")
+    B, nq = q.shape[0], q.shape[1]
+    n_cap = _key_cache_rows(k_codes, k_scales, B)
+    nb = pool.shape[-1]
+    _check("csa2_index_full_pool", load().csa2_index_full_pool(
+        _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block, nb,
+        _p(block_max), _p(pool), _p(ws), ws.numel() if ws is not None else 0,
+        scan_events[0].cuda_event if scan_events else None,
+        scan_events[1].cuda_event if scan_events else None, _stream(stream)))
 
 
 def index_pool(q, w, k_codes, k_scales, blocks, n_visible, pool_score, pool_idx, block=8,

@@ -62,7 +62,7 @@ const char* csa2_last_error(void)
 
 int32_t csa2_version(void)
 {
-    return 102;
+    return 103;
 }
 
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
@@ -190,8 +190,58 @@ csa2_status csa2_index_full(const uint16_t* q, const float* w, const uint8_t* k_
     REQUIRE(block_max != nullptr, CSA2_ERR_INVALID_ARG, "index_full: null block_max");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq,
-                                          block_max, scores, s),
+                                          block_max, scores, nullptr, 0, nullptr, nullptr, s),
                   s, "index_full");
+}
+
+size_t csa2_index_full_pool_workspace(int64_t n_cap, int32_t rows, int32_t nb)
+{
+    if (n_cap < 0 || rows < 0 || nb < 1)
+        return 0;
+    return csa2::topk_workspace((n_cap + csa2::kBlock - 1) / csa2::kBlock, rows, nb);
+}
+
+csa2_status csa2_index_full_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                                 const uint8_t* k_scales, int64_t n_cap,
+                                 const int32_t* n_visible, int32_t B, int32_t nq, int32_t block,
+                                 int32_t nb, float* block_max, int32_t* pool, void* ws,
+                                 size_t ws_bytes, void* scan_start, void* scan_stop,
+                                 void* stream)
+{
+    csa2_status st = check_indexer("index_full_pool", q, w, k_codes, k_scales, n_cap, n_visible,
+                                   B, nq, block);
+    if (st != CSA2_OK)
+        return st;
+    REQUIRE(nb >= 1 && nb <= csa2::kTopkMaxK, CSA2_ERR_UNSUPPORTED,
+            "index_full_pool: nb must be in [1, %d]", csa2::kTopkMaxK);
+    const int64_t rows = (int64_t)B * nq;
+    const int64_t L = (n_cap + csa2::kBlock - 1) / csa2::kBlock;
+    REQUIRE(rows * ((L + csa2::kTopkSegment - 1) / csa2::kTopkSegment) <= (1ll << 31) - 1,
+            CSA2_ERR_INVALID_ARG, "index_full_pool: too many segments");
+    if (rows == 0)
+        return CSA2_OK;
+    REQUIRE(block_max != nullptr && pool != nullptr, CSA2_ERR_INVALID_ARG,
+            "index_full_pool: null block_max or pool");
+    const size_t need = csa2::topk_workspace(L, (int32_t)rows, nb);
+    REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
+            "index_full_pool: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    REQUIRE(aligned(ws, 8), CSA2_ERR_INVALID_ARG,
+            "index_full_pool: workspace must be 8-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the scan writes the block select's group maxima itself when the groups
+    // align with its chunks (group size dividing 64 blocks)
+    const int32_t g = csa2::topk_group_size(L, nb);
+    const bool fused = g > 0 && 64 % g == 0 && n_cap > 0;  // g in {1, 2, 4, 8, ...}: a power of two
+    hipError_t e = hipSuccess;
+    if (n_cap > 0)
+        e = csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq, block_max,
+                                    nullptr, fused ? static_cast<uint32_t*>(ws) : nullptr,
+                                    fused ? g : 0, static_cast<hipEvent_t>(scan_start),
+                                    static_cast<hipEvent_t>(scan_stop), s);
+    if (e == hipSuccess)
+        e = csa2::launch_topk(block_max, nullptr, L, (int32_t)rows, n_visible, csa2::kBlock, nb,
+                              pool, ws, fused, s);
+    return finish(e, s, "index_full_pool");
 }
 
 csa2_status csa2_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
@@ -240,7 +290,8 @@ csa2_status csa2_topk(const float* score, const int32_t* idx, int64_t L, int32_t
             "topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
     REQUIRE(aligned(ws, 8), CSA2_ERR_INVALID_ARG, "topk: workspace must be 8-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return finish(csa2::launch_topk(score, idx, L, rows, n_valid, k, out, ws, s), s, "topk");
+    return finish(csa2::launch_topk(score, idx, L, rows, n_valid, 1, k, out, ws, false, s), s,
+                  "topk");
 }
 
 size_t csa2_sparse_attn_workspace(int32_t B, int32_t nq, int32_t k, int32_t n_win)

@@ -520,6 +520,10 @@ constexpr int kDepth = CSA2_ATTN_DEPTH;          // tiles in flight per wave
 #endif
 constexpr int64_t kSplitWgs = CSA2_ATTN_SPLIT_WGS;  // workgroup budget of the key splits
 constexpr int kMaxSplits = 8;                   // key splits per (row, head group)
+#ifndef CSA2_ATTN_MIN_SPLIT_TILES
+#define CSA2_ATTN_MIN_SPLIT_TILES 2
+#endif
+constexpr int kMinSplitTiles = CSA2_ATTN_MIN_SPLIT_TILES;  // fewest key tiles per split
 constexpr int kPartFloats = kHg * kDim + 2 * kHg;  // one split's O [16][512], max, sum
 
 struct GroupSmem {
@@ -899,7 +903,7 @@ int32_t attn_splits(int32_t queries, int32_t k, int32_t n_win)
     const int64_t groups = padded_rows(queries) * kGroups;
     const int64_t tiles = ((int64_t)k + kTile - 1) / kTile + ((int64_t)n_win + kTile - 1) / kTile;
     int32_t s = 1;
-    while (s < kMaxSplits && groups * s * 2 <= kSplitWgs && tiles >= 4 * s)
+    while (s < kMaxSplits && groups * s * 2 <= kSplitWgs && tiles >= kMinSplitTiles * 2 * s)
         s *= 2;
     return s;
 }

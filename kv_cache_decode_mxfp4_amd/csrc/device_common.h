@@ -21,6 +21,16 @@ constexpr int kWave = 64;
 
 // --------------------------------------------------------------- formats
 
+// Selection order of a score as an unsigned key: larger score <=> larger key,
+// -0 ranks as +0; key 0 is below every score and marks "no entry".
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u)
+        u = 0u;  // -0 ranks as +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Byte offset of code byte c (< 64) of indexer-key entry f in the tiled key
 // cache (layout in dims.h).
 __device__ __forceinline__ int64_t key_code_offset(int64_t f, int c)

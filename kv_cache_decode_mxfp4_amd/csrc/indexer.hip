@@ -22,6 +22,8 @@
 //   brings its largest |q| to [2^14, 2^15), which keeps the bf16 -> fp16 cast
 //   exact for every value within 2^28 of that maximum; the head weight absorbs
 //   the inverse power, so the score is unchanged.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -241,6 +243,39 @@ __device__ __forceinline__ float max8(float s)
     return fmaxf(m, __uint_as_float(dpp_u32<0x141>(0u, __float_as_uint(m))));
 }
 
+// Group keys of one row's chunk for the block select (after the scan loop):
+// group t of the chunk -- blocks [t*g, t*g + g) of the chunk, g = 1 << gshift,
+// of which [0, nb_here) are visible and held in sblk -- gets the order key of
+// its largest non-NaN block maximum, 0 if it has none: what the block
+// select's group-maxima pass computes from the block maxima.  Row `row` of
+// gkey has ngroups groups; the chunk starts at entry `start` (a multiple of
+// 512 entries, so its first group is whole for g <= 64).
+__device__ __attribute__((noinline)) void write_group_keys(const float* sblk, int nb_here,
+                                                           int64_t row, int64_t start,
+                                                           int32_t chunk, int32_t gshift,
+                                                           int64_t ngroups,
+                                                           uint32_t* __restrict__ gkey)
+{
+    const int64_t g0 = (start / kBlock) >> gshift;
+    const int64_t left = ngroups - g0;
+    const int per = (chunk / kBlock) >> gshift;
+    const int groups_here = (int)(left < per ? (left < 0 ? 0 : left) : per);
+    uint32_t* gk = gkey + row * ngroups + g0;
+    const int g = 1 << gshift;
+    for (int t = threadIdx.x; t < groups_here; t += kWaves * kWave) {
+        uint32_t m = 0u;
+        for (int r = 0; r < g; ++r) {
+            const int blk = t * g + r;
+            if (blk < nb_here) {
+                const float f = sblk[blk];
+                if (!__builtin_isnan(f))
+                    m = max(m, order_key(f));
+            }
+        }
+        gk[t] = m;
+    }
+}
+
 // Full-range scan: one workgroup scans `chunk` entries of one query row and
 // writes the maxima of the blocks of 8 it covers (and, with kScores, every
 // score).  Wave w scores tiles start + 32*(w + kWaves*i).
@@ -258,7 +293,8 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                   const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                   int64_t n_cap, const int32_t* __restrict__ n_visible, int32_t nq,
                   int32_t chunk, int32_t chunks_per_query, int64_t nblk_cap,
-                  float* __restrict__ block_max, float* __restrict__ scores)
+                  float* __restrict__ block_max, float* __restrict__ scores,
+                  uint32_t* __restrict__ gkey, int32_t gshift, int64_t ngroups)
 {
     __shared__ float sblk[kMaxChunk / kBlock];
 
@@ -267,8 +303,11 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     int64_t n_vis = n_visible[row];
     n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
     const int64_t start = (int64_t)(blockIdx.x % chunks_per_query) * chunk;
-    if (start >= n_vis)
+    if (start >= n_vis) {
+        if (gkey != nullptr)
+            write_group_keys(sblk, 0, row, start, chunk, gshift, ngroups, gkey);
         return;
+    }
     const int32_t n_here = (int32_t)(n_vis - start < chunk ? n_vis - start : chunk);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -315,6 +354,8 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     float* dst = block_max + row * nblk_cap + start / kBlock;
     for (int t = threadIdx.x; t < nb_here; t += kWaves * kWave)
         dst[t] = sblk[t];
+    if (gkey != nullptr)
+        write_group_keys(sblk, nb_here, row, start, chunk, gshift, ngroups, gkey);
 }
 
 // Full-range scan of two query rows of one sequence (rows 2p and 2p + 1 of
@@ -332,7 +373,8 @@ index_full_pair_kernel(const uint16_t* __restrict__ q, const float* __restrict__
                        int64_t n_cap, const int32_t* __restrict__ n_visible, int32_t nq,
                        int32_t pairs_per_seq, int32_t chunk, int32_t chunks_per_pair,
                        int64_t nblk_cap, float* __restrict__ block_max,
-                       float* __restrict__ scores)
+                       float* __restrict__ scores, uint32_t* __restrict__ gkey, int32_t gshift,
+                       int64_t ngroups)
 {
     __shared__ float sblk[2][kMaxChunk / kBlock];
 
@@ -348,8 +390,14 @@ index_full_pair_kernel(const uint16_t* __restrict__ q, const float* __restrict__
     nv1 = nv1 < 0 ? 0 : (nv1 > n_cap ? n_cap : nv1);
     const int64_t start = (int64_t)(blockIdx.x % chunks_per_pair) * chunk;
     const int64_t nv_max = nv0 > nv1 ? nv0 : nv1;
-    if (start >= nv_max)
+    if (start >= nv_max) {
+        if (gkey != nullptr) {
+            write_group_keys(sblk[0], 0, row0, start, chunk, gshift, ngroups, gkey);
+            if (two)
+                write_group_keys(sblk[1], 0, row1, start, chunk, gshift, ngroups, gkey);
+        }
         return;
+    }
     auto here = [&](int64_t nv) {
         return (int32_t)(nv <= start ? 0 : (nv - start < chunk ? nv - start : chunk));
     };
@@ -416,10 +464,18 @@ index_full_pair_kernel(const uint16_t* __restrict__ q, const float* __restrict__
         dst0[t] = sblk[0][t];
     for (int t = threadIdx.x; t < nb1; t += kWaves * kWave)
         dst1[t] = sblk[1][t];
+    if (gkey != nullptr) {
+        write_group_keys(sblk[0], nb0, row0, start, chunk, gshift, ngroups, gkey);
+        if (two)
+            write_group_keys(sblk[1], nb1, row1, start, chunk, gshift, ngroups, gkey);
+    }
 }
 
 // Pool scan: score the positions of a list of blocks (4 blocks per tile).
-constexpr int kPoolTilesPerWave = 4;
+#ifndef CSA2_POOL_TILES_PER_WAVE
+#define CSA2_POOL_TILES_PER_WAVE 4
+#endif
+constexpr int kPoolTilesPerWave = CSA2_POOL_TILES_PER_WAVE;
 
 __global__ void __launch_bounds__(kWaves * kWave)
 index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
@@ -480,14 +536,40 @@ index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     }
 }
 
+template <typename T>
+struct same_type {
+    using type = T;
+};
+
+// Launch of a scan kernel; with timing events, through hipExtLaunchKernel so
+// that the dispatch itself records them at the kernel's start and end.
+template <typename... P>
+hipError_t launch_scan(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                       hipEvent_t ev_start, hipEvent_t ev_stop,
+                       typename same_type<P>::type... args)
+{
+    if (ev_start != nullptr || ev_stop != nullptr) {
+        void* a[] = {static_cast<void*>(&args)...};
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, a, 0, stream,
+                                  ev_start, ev_stop, 0);
+    }
+    kernel<<<grid, block, 0, stream>>>(args...);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
                              int32_t B, int32_t nq, float* block_max, float* scores,
-                             hipStream_t stream)
+                             uint32_t* group_keys, int32_t group, hipEvent_t ev_start,
+                             hipEvent_t ev_stop, hipStream_t stream)
 {
     const int64_t nblk_cap = (n_cap + kBlock - 1) / kBlock;
+    int32_t gshift = 0;  // group = 1 << gshift (a power of two dividing 64)
+    while (group_keys != nullptr && (1 << gshift) < group)
+        ++gshift;
+    const int64_t ngroups = (nblk_cap + (1 << gshift) - 1) >> gshift;
     if (nq >= kPairMinRows) {
         // many rows per sequence (prefill): two rows per workgroup
         const int32_t pairs_per_seq = (nq + 1) / 2;
@@ -500,15 +582,12 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
         const int64_t grid = pairs * chunks;
         if (grid == 0)
             return hipSuccess;
-        if (scores != nullptr)
-            index_full_pair_kernel<true><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
-                q, w, k_codes, k_scales, n_cap, n_visible, nq, pairs_per_seq, chunk,
-                (int32_t)chunks, nblk_cap, block_max, scores);
-        else
-            index_full_pair_kernel<false><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
-                q, w, k_codes, k_scales, n_cap, n_visible, nq, pairs_per_seq, chunk,
-                (int32_t)chunks, nblk_cap, block_max, nullptr);
-        return hipGetLastError();
+        return launch_scan(scores != nullptr ? index_full_pair_kernel<true>
+                                             : index_full_pair_kernel<false>,
+                           dim3((uint32_t)grid), dim3(kWaves * kWave), stream, ev_start, ev_stop,
+                           reinterpret_cast<const uint16_t*>(q), w, k_codes, k_scales, n_cap,
+                           n_visible, nq, pairs_per_seq, chunk, (int32_t)chunks, nblk_cap,
+                           block_max, scores, group_keys, gshift, ngroups);
     }
     const int64_t rows = (int64_t)B * nq;
     int32_t chunk = kMaxChunk;
@@ -518,15 +597,10 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
     const int64_t grid = rows * chunks;
     if (grid == 0)
         return hipSuccess;
-    if (scores != nullptr)
-        index_full_kernel<true><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
-            q, w, k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,
-            block_max, scores);
-    else
-        index_full_kernel<false><<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
-            q, w, k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,
-            block_max, nullptr);
-    return hipGetLastError();
+    return launch_scan(scores != nullptr ? index_full_kernel<true> : index_full_kernel<false>,
+                       dim3((uint32_t)grid), dim3(kWaves * kWave), stream, ev_start, ev_stop, q, w,
+                       k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,
+                       block_max, scores, group_keys, gshift, ngroups);
 }
 
 hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,

@@ -32,10 +32,16 @@ hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* c
                                  int32_t swa_rows, uint8_t* swa_out, int64_t swa_stride,
                                  const int64_t* swa_dst, int64_t swa_cap, hipStream_t stream);
 
+// group_keys (or null): also write the selection order key of the maximum of
+// every group of `group` consecutive blocks, [B*nq, ceil(ceil(n_cap/8)/group)]
+// (0 for groups with no visible block); group must be a power of two <= 64.
+// ev_start / ev_stop (or null): HIP events the scan kernel's dispatch records
+// at its start and end.
 hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
                              int32_t B, int32_t nq, float* block_max, float* scores,
-                             hipStream_t stream);
+                             uint32_t* group_keys, int32_t group, hipEvent_t ev_start,
+                             hipEvent_t ev_stop, hipStream_t stream);
 
 hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
@@ -43,9 +49,16 @@ hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k
                              float* pool_score, int32_t* pool_idx, hipStream_t stream);
 
 size_t topk_workspace(int64_t L, int32_t rows, int32_t k);
+// Group size of the grouped select for a row of L keys and k winners (0: the
+// direct or segment path); its group maxima live at the front of the workspace
+// as uint32 order keys [rows, ceil(L / g)].
+int32_t topk_group_size(int64_t L, int32_t k);
+// n_valid[row] / valid_div (rounded up) is the row's valid prefix (valid_div 8:
+// visible entries -> visible blocks).  group_keys_ready: the workspace already
+// holds the group maxima (written by the scan), so they are not recomputed.
 hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_t rows,
-                       const int32_t* n_valid, int32_t k, int32_t* out, void* ws,
-                       hipStream_t stream);
+                       const int32_t* n_valid, int32_t valid_div, int32_t k, int32_t* out,
+                       void* ws, bool group_keys_ready, hipStream_t stream);
 
 // Bytes of the key-split partials for few query rows (0: no split).
 size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win);

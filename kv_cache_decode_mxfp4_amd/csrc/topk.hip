@@ -45,14 +45,6 @@ constexpr int kBinBits = CSA2_TOPK_BIN_BITS;
 constexpr int kBins = 1 << kBinBits;           // radix bins per pass
 constexpr int kBpt = kBins / kThreads;         // bins per thread
 
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u)
-        u = 0u;  // -0 ranks as +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __device__ __forceinline__ float key_value(uint32_t k)
 {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -337,13 +329,16 @@ __device__ __forceinline__ void load_slots(const float* __restrict__ srow,
     }
 }
 
+// Valid prefix of a row: ceil(n_valid[row] / div) clamped to [0, L] (div = 8
+// turns a count of visible entries into a count of visible blocks), or L.
 __device__ __forceinline__ int64_t valid_prefix(const int32_t* __restrict__ n_valid, int64_t row,
-                                                int64_t L)
+                                                int64_t L, int32_t div)
 {
     if (n_valid == nullptr)
         return L;
-    const int64_t nv = n_valid[row];
-    return nv < 0 ? 0 : (nv > L ? L : nv);
+    int64_t nv = n_valid[row];
+    nv = nv < 0 ? 0 : (nv + div - 1) / div;
+    return nv > L ? L : nv;
 }
 
 // Direct select within segments of up to 16384 entries.  Grid: rows * nseg.
@@ -352,7 +347,8 @@ __device__ __forceinline__ int64_t valid_prefix(const int32_t* __restrict__ n_va
 // pairs in position order, padded with index -1.
 __global__ void __launch_bounds__(kThreads)
 topk_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
-            int64_t seg_len, int32_t nseg, const int32_t* __restrict__ n_valid, int32_t k,
+            int64_t seg_len, int32_t nseg, const int32_t* __restrict__ n_valid,
+            int32_t valid_div, int32_t k,
             int32_t* __restrict__ out, float* __restrict__ cand_score,
             int32_t* __restrict__ cand_idx)
 {
@@ -362,7 +358,7 @@ topk_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, in
     const int wave = tid >> 6;
     const int64_t row = blockIdx.x / nseg;
     const int64_t seg = blockIdx.x % nseg;
-    const int64_t nv = valid_prefix(n_valid, row, L);
+    const int64_t nv = valid_prefix(n_valid, row, L, valid_div);
     const int64_t seg_start = seg * seg_len;
     const int64_t seg_end = seg_start + seg_len < nv ? seg_start + seg_len : nv;
     for (int b = tid; b < kBins; b += kThreads)
@@ -396,14 +392,15 @@ template <int G>
 __global__ void __launch_bounds__(256)
 group_max_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
                  int32_t g_runtime, int64_t ngroups, int32_t wgs_per_row,
-                 const int32_t* __restrict__ n_valid, uint32_t* __restrict__ gkey)
+                 const int32_t* __restrict__ n_valid, int32_t valid_div,
+                 uint32_t* __restrict__ gkey)
 {
     const int g = G > 0 ? G : g_runtime;
     const int64_t row = blockIdx.x / wgs_per_row;
     const int64_t grp = (int64_t)(blockIdx.x % wgs_per_row) * 256 + threadIdx.x;
     if (grp >= ngroups)
         return;
-    const int64_t nv = valid_prefix(n_valid, row, L);
+    const int64_t nv = valid_prefix(n_valid, row, L, valid_div);
     const float* srow = score + row * L;
     const int32_t* irow = idx != nullptr ? idx + row * L : nullptr;
     uint32_t m = 0u;
@@ -442,7 +439,7 @@ group_max_kernel(const float* __restrict__ score, const int32_t* __restrict__ id
 // contiguous 1 KiB.  Grid: ceil(rows * L / 4 / 256).
 __global__ void __launch_bounds__(256)
 group_max8_vec_kernel(const float* __restrict__ score, int64_t L, int64_t rows,
-                      int64_t ngroups, const int32_t* __restrict__ n_valid,
+                      int64_t ngroups, const int32_t* __restrict__ n_valid, int32_t valid_div,
                       uint32_t* __restrict__ gkey)
 {
     const int64_t quads_per_row = L / 4;
@@ -450,7 +447,7 @@ group_max8_vec_kernel(const float* __restrict__ score, int64_t L, int64_t rows,
     const int64_t tc = t < rows * quads_per_row ? t : rows * quads_per_row - 1;
     const int64_t row = tc / quads_per_row;
     const int64_t pos = 4 * (tc % quads_per_row);
-    const int64_t nv = valid_prefix(n_valid, row, L);
+    const int64_t nv = valid_prefix(n_valid, row, L, valid_div);
     const float4 f = reinterpret_cast<const float4*>(score)[tc];
     const float v[4] = {f.x, f.y, f.z, f.w};
     uint32_t m = 0u;
@@ -475,7 +472,8 @@ template <int kG>
 __global__ void __launch_bounds__(kThreads)
 topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
                     int32_t g_runtime, int64_t ngroups, const uint32_t* __restrict__ gkey,
-                    const int32_t* __restrict__ n_valid, int32_t k, int32_t* __restrict__ out)
+                    const int32_t* __restrict__ n_valid, int32_t valid_div, int32_t k,
+                    int32_t* __restrict__ out)
 {
     __shared__ GroupSmem gs;
     Smem& sm = gs.sm;
@@ -484,7 +482,7 @@ topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t row = blockIdx.x;
-    const int64_t nv = valid_prefix(n_valid, row, L);
+    const int64_t nv = valid_prefix(n_valid, row, L, valid_div);
     const float* srow = score + row * L;
     const int32_t* irow = idx != nullptr ? idx + row * L : nullptr;
     for (int b = tid; b < kBins; b += kThreads)
@@ -577,9 +575,14 @@ size_t topk_workspace(int64_t L, int32_t rows, int32_t k)
     return 2ull * (size_t)rows * (size_t)segments(L) * (size_t)k * (sizeof(float) + sizeof(int32_t));
 }
 
+int32_t topk_group_size(int64_t L, int32_t k)
+{
+    return group_size(L, k);
+}
+
 hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_t rows,
-                       const int32_t* n_valid, int32_t k, int32_t* out, void* ws,
-                       hipStream_t stream)
+                       const int32_t* n_valid, int32_t valid_div, int32_t k, int32_t* out,
+                       void* ws, bool group_keys_ready, hipStream_t stream)
 {
     if (rows == 0)
         return hipSuccess;
@@ -589,26 +592,28 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         const int32_t per_row = (int32_t)((ngroups + 255) / 256);
         uint32_t* gkey = static_cast<uint32_t*>(ws);
         const dim3 grid((uint32_t)(rows * per_row));
-        if (g == 8 && idx == nullptr && L % 8 == 0 &&
-            reinterpret_cast<uintptr_t>(score) % 16 == 0) {
+        if (group_keys_ready) {
+            // the scan already wrote the group maxima into the workspace
+        } else if (g == 8 && idx == nullptr && L % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(score) % 16 == 0) {
             const int64_t quads = (int64_t)rows * (L / 4);
             group_max8_vec_kernel<<<dim3((uint32_t)((quads + 255) / 256)), dim3(256), 0, stream>>>(
-                score, L, rows, ngroups, n_valid, gkey);
+                score, L, rows, ngroups, n_valid, valid_div, gkey);
         } else if (g == 8)
             group_max_kernel<8><<<grid, dim3(256), 0, stream>>>(score, idx, L, g, ngroups, per_row,
-                                                                n_valid, gkey);
+                                                                n_valid, valid_div, gkey);
         else
             group_max_kernel<0><<<grid, dim3(256), 0, stream>>>(score, idx, L, g, ngroups, per_row,
-                                                                n_valid, gkey);
+                                                                n_valid, valid_div, gkey);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
         if (g == 8)
             topk_grouped_kernel<8><<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
-                score, idx, L, g, ngroups, gkey, n_valid, k, out);
+                score, idx, L, g, ngroups, gkey, n_valid, valid_div, k, out);
         else
             topk_grouped_kernel<0><<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
-                score, idx, L, g, ngroups, gkey, n_valid, k, out);
+                score, idx, L, g, ngroups, gkey, n_valid, valid_div, k, out);
         return hipGetLastError();
     }
     const size_t half = topk_workspace(L, rows, k) / 2;
@@ -620,7 +625,7 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         float* cs = reinterpret_cast<float*>(bufs[flip]);
         int32_t* ci = reinterpret_cast<int32_t*>(bufs[flip] + n * sizeof(float));
         topk_kernel<<<dim3((uint32_t)(rows * nseg)), dim3(kThreads), 0, stream>>>(
-            score, idx, L, kTopkSegment, (int32_t)nseg, n_valid, k, nullptr, cs, ci);
+            score, idx, L, kTopkSegment, (int32_t)nseg, n_valid, valid_div, k, nullptr, cs, ci);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -631,7 +636,7 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         flip ^= 1;
     }
     topk_kernel<<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
-        score, idx, L, L, 1, n_valid, k, out, nullptr, nullptr);
+        score, idx, L, L, 1, n_valid, valid_div, k, out, nullptr, nullptr);
     return hipGetLastError();
 }
 

@@ -89,10 +89,18 @@ def select_blocks(buf: Buffers, n_blocks_valid: torch.Tensor, k: int, nb: int, s
 
 def full_indexer(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, n_blocks_valid,
                  k: int, nb: int, scores=None, stream=None):
-    """Full layer indexer: block scan, pool, top-k.  Leaves buf.pool and buf.topk."""
-    _lib.index_full(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, scores=scores,
-                    stream=stream)
-    select_blocks(buf, n_blocks_valid, k, nb, stream=stream)
+    """Full layer indexer: block scan, pool, top-k.  Leaves buf.pool and buf.topk.
+
+    With a pool of at least k blocks (and no per-entry scores asked for) the scan and
+    the pool select are one library call, whose scan also writes the select's group
+    maxima."""
+    if nb >= k and nb > 0 and scores is None:
+        _lib.index_full_pool(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, buf.pool,
+                             ws=buf.ws_topk, stream=stream)
+    else:
+        _lib.index_full(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, scores=scores,
+                        stream=stream)
+        select_blocks(buf, n_blocks_valid, k, nb, stream=stream)
     _lib.index_pool(q_idx, w_idx, k_codes, k_scales, buf.sel_blocks, n_visible, buf.pool_score,
                     buf.pool_idx, stream=stream)
     _lib.topk(buf.pool_score, k, buf.topk, idx=buf.pool_idx, ws=buf.ws_topk, stream=stream)

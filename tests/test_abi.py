@@ -24,8 +24,9 @@ def declared():
 
 def test_header_declares_the_five_calls():
     names = declared()
-    for n in ["csa2_quantize_kv", "csa2_index_full", "csa2_index_pool", "csa2_topk",
-              "csa2_sparse_attn", "csa2_sparse_attn_rope_bf16", "csa2_encode_entries"]:
+    for n in ["csa2_quantize_kv", "csa2_index_full", "csa2_index_full_pool", "csa2_index_pool",
+              "csa2_topk", "csa2_sparse_attn", "csa2_sparse_attn_rope_bf16",
+              "csa2_encode_entries"]:
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = L.load()
-    assert lib.csa2_version() == 102
+    assert lib.csa2_version() == 103
     assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
     assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
@@ -171,3 +172,22 @@ def test_key_tile_helpers_follow_the_documented_layout():
     assert np.array_equal(untile_keys(tiled, rows), codes)
     assert not untile_keys(tiled, 96)[rows:].any()  # padding entries are zero
     assert L.key_code_bytes(rows) == 3 * 2048 and L.key_code_bytes(64) == 2 * 2048
+
+
+def test_index_full_pool_validation():
+    vp = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    args = lambda nb, ws_bytes, block=8: ("csa2_index_full_pool", vp, vp, vp, vp, 1 << 20, vp, 16,
+                                          1, block, nb, vp, vp, vp, ws_bytes, None, None, None)
+    st, msg = _status(*args(0, 1 << 30))
+    assert st == 2 and "nb" in msg
+    st, msg = _status(*args(9000, 1 << 30))
+    assert st == 2
+    st, msg = _status(*args(2048, 1 << 30, block=4))
+    assert st == 2 and "block" in msg
+    need = L.index_full_pool_workspace(1 << 20, 16, 2048)
+    assert need == L.topk_workspace(1 << 17, 16, 2048) and need > 0
+    st, msg = _status(*args(2048, need - 1))
+    assert st == 3 and "workspace" in msg
+    # nothing to do: no rows
+    assert _status("csa2_index_full_pool", None, None, None, None, 100, None, 0, 1, 8, 64, None,
+                   None, None, 0, None, None, None)[0] == 0

@@ -368,6 +368,58 @@ def test_paired_scan_bit_identical_to_one_row_scan_and_pool():
         assert np.array_equal(ps[i][ok], sc[i][pi[i][ok]])
 
 
+@pytest.mark.parametrize("B,nq,n_cap,nb,nvis", [
+    (1, 1, 1 << 20, 2048, [1 << 20]),                      # groups of 8 blocks
+    (2, 1, 1 << 20, 2048, [(1 << 20) - 5000, 300001]),     # chunks past the end, partial groups
+    (1, 2, 1 << 20, 2048, [1 << 20, 999999]),              # paired rows write group keys too
+    (1, 1, 1 << 20, 512, [654321]),                        # groups of 8, k = 512
+    (2, 1, 140003, 2048, [140003, 70001]),                 # groups of 2
+    (1, 3, 300000, 2048, [300000, 299999, 5]),             # groups of 3: the select's own pass
+    (2, 1, 65536, 2048, [70000, 100]),                     # one segment: direct select
+    (1, 1, 2048, 2048, [0]),                               # nothing visible
+])
+def test_index_full_pool_matches_scan_then_topk(B, nq, n_cap, nb, nvis):
+    """csa2_index_full_pool returns exactly csa2_index_full's block maxima and
+    csa2_topk's selection over them (n_valid = ceil(n_visible / 8)), whether the scan
+    writes the select's group maxima itself or the select computes them."""
+    print(f"[case] B={B} nq={nq} n_cap={n_cap} nb={nb} nvis={nvis}", flush=True)
+    g = torch.Generator(device=dev())
+    g.manual_seed(n_cap + nb)
+    kc = torch.randint(0, 256, (L.key_code_bytes(B * n_cap),), dtype=torch.uint8, device=dev(),
+                       generator=g)
+    ks = (torch.randint(0, 256, (B, n_cap, 8), dtype=torch.uint8, device=dev(), generator=g)
+          & 0x77) | 0x30  # finite E4M3 scales
+    q = synth.normal_bf16(synth.key(11, 12, 0, 0), 0, B * nq * 4096, 1 / np.sqrt(128)).reshape(B, nq, 32, 128)
+    w = synth.uniform_f32(synth.key(11, 13, 0, 0), 0, B * nq * 32).reshape(B, nq, 32)
+    nv = np.array(nvis, np.int32).reshape(B, nq)
+    nblk = cdiv(n_cap, 8)
+    ws_n = max(L.index_full_pool_workspace(n_cap, B * nq, nb), 8)
+    assert ws_n >= L.topk_workspace(nblk, B * nq, nb)
+    bm1 = torch.full((B, nq, nblk), 777.0, device=dev())
+    pool1 = torch.full((B, nq, nb), -7, dtype=torch.int32, device=dev())
+    ws = torch.full((ws_n,), 0xC3, dtype=torch.uint8, device=dev())  # stale contents
+    evs = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in evs:
+        e.record()  # created before the library records them
+    L.index_full_pool(t(q, torch.uint16), t(w), kc, ks, t(nv), bm1, pool1, ws=ws, scan_events=evs)
+    torch.cuda.synchronize()
+    if max(nvis) > 0:  # the scan's dispatch recorded both events
+        assert evs[0].elapsed_time(evs[1]) > 0.0
+    bm2 = torch.full((B, nq, nblk), 777.0, device=dev())
+    L.index_full(t(q, torch.uint16), t(w), kc, ks, t(nv), bm2)
+    pool2 = torch.full((B, nq, nb), -7, dtype=torch.int32, device=dev())
+    nblk_valid = t(((np.maximum(nv.astype(np.int64), 0) + 7) // 8).astype(np.int32))
+    L.topk(bm2, nb, pool2, n_valid=nblk_valid, ws=torch.empty(ws_n, dtype=torch.uint8, device=dev()))
+    bm1, bm2 = bm1.cpu().numpy(), bm2.cpu().numpy()
+    assert np.array_equal(bm1, bm2)
+    p1, p2 = pool1.cpu().numpy(), pool2.cpu().numpy()
+    assert np.array_equal(p1, p2)
+    for r in range(B * nq):  # a valid pool: ascending ids of visible blocks, -1 padded
+        row = p1.reshape(B * nq, nb)[r]
+        n_ok = min(nb, cdiv(max(int(nv.reshape(-1)[r]), 0), 8))
+        assert np.all(np.diff(row[:n_ok]) > 0) and np.all(row[n_ok:] == -1)
+
+
 # ------------------------------------------------------------------ attention
 
 def _attn_case(B=2, N=3000, k=100, swa_cap=160, seed=3):
