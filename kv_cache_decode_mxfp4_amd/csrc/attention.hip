@@ -512,7 +512,7 @@ attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
 
 constexpr int kGroupWaves = kSlices;            // one wave per 128-channel slice
 #ifndef CSA2_ATTN_DEPTH
-#define CSA2_ATTN_DEPTH 3
+#define CSA2_ATTN_DEPTH 2
 #endif
 constexpr int kDepth = CSA2_ATTN_DEPTH;          // tiles in flight per wave
 #ifndef CSA2_ATTN_SPLIT_WGS
@@ -616,8 +616,13 @@ __device__ __forceinline__ void emit(const f32x4 (&o)[kSlice / 16], float inv, i
     }
 }
 
+#ifndef CSA2_ATTN_WAVES_PER_EU
+#define CSA2_ATTN_WAVES_PER_EU 3
+#endif
+
 template <bool kRopeBf16>
-__global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(kGroupWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(CSA2_ATTN_WAVES_PER_EU)))
 attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                   const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
                   int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
