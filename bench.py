@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cold-steps", type=int, default=50,
+                    help="steps timed one by one after a 512 MiB cache-evicting write each "
+                         "(median / p10 / p90 reported beside value; 0 = skip)")
     ap.add_argument("--cpu-sample", type=int, default=16,
                     help="query rows of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -292,6 +295,30 @@ def measured_traffic():
         return None
 
 
+FLUSH_BYTES = 512 << 20  # twice the 256 MB last-level cache (MALL) of the MI355X
+
+
+def cold_steps(step, n, torch):
+    """Steps timed one by one (HIP events around each), each after writing a 512 MiB scratch
+    buffer, so no step finds the previous one's data in the L2s or the MALL.  Reported
+    beside the contract's warm, back-to-back figure."""
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    times = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    t = np.array(times)
+    return {"steps": n, "flush_bytes": FLUSH_BYTES, "median_ms": round(float(np.median(t)), 4),
+            "p10_ms": round(float(np.percentile(t, 10)), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4)}
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
 def cpu_baseline(w: synth.Workload, rows: int):
@@ -374,6 +401,7 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
+    cold = cold_steps(step, args.cold_steps, torch) if args.cold_steps > 0 else None
     ms_step = ms_total / args.steps
     scan_ms = float(np.mean([a.elapsed_time(b) for a, b in scan_events]))
     rows = w.B * w.nq
@@ -414,6 +442,8 @@ def main():
     }
     if w.decode:
         out["step_tbps"] = round(step_bytes(w) / (ms_step / 1e3) / 1e12, 3)
+    if cold is not None:
+        out["cold"] = cold
     if args.cpu_sample > 0 and args.config in (1, 3):
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     print(json.dumps(out), flush=True)
