@@ -472,8 +472,11 @@ index_full_pair_kernel(const uint16_t* __restrict__ q, const float* __restrict__
 }
 
 // Pool scan: score the positions of a list of blocks (4 blocks per tile).
+// 8 tiles per wave: the most gathers in flight that still keep 3 waves per SIMD
+// (168 VGPRs); measured 15-22 % faster than 4 on the prefill pool scans and
+// equal on the decode one
 #ifndef CSA2_POOL_TILES_PER_WAVE
-#define CSA2_POOL_TILES_PER_WAVE 4
+#define CSA2_POOL_TILES_PER_WAVE 8
 #endif
 constexpr int kPoolTilesPerWave = CSA2_POOL_TILES_PER_WAVE;
 
