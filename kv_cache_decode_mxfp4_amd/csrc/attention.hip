@@ -528,7 +528,10 @@ constexpr int kPartFloats = kHg * kDim + 2 * kHg;  // one split's O [16][512], m
 
 struct GroupSmem {
     _Float16 v[kGroupWaves][kTile][kVRow];          // each wave's V tile (its 128 dims)
-    float part[2][kGroupWaves][kWave * 8];          // partial S^T per wave, double-buffered
+    // partial S^T per wave, double-buffered: [buffer][wave][key block][lane], so
+    // each lane's 16-byte store and load is contiguous with its neighbours'
+    // (a 32-byte lane stride made lanes l and l + 8 share banks)
+    f32x4 part[2][kGroupWaves][2][kWave];
 };
 
 // Raw bytes of one tile for the calling lane, for key l%16 of block b:
@@ -767,17 +770,15 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                     tile_scores<false>(ring[u], qop, vtile, slice, G, key16, s);
                 // the four partial scores meet in LDS; every wave adds them in
                 // wave order (bit-identical in every wave)
-                float* mine = &sm.part[j & 1][slice][8 * lane];
-                *reinterpret_cast<f32x4*>(mine) = s[0];
-                *reinterpret_cast<f32x4*>(mine + 4) = s[1];
+                sm.part[j & 1][slice][0][lane] = s[0];
+                sm.part[j & 1][slice][1][lane] = s[1];
                 __syncthreads();
-                const float* all = &sm.part[j & 1][0][8 * lane];
-                f32x4 tot0 = *reinterpret_cast<const f32x4*>(all);
-                f32x4 tot1 = *reinterpret_cast<const f32x4*>(all + 4);
+                f32x4 tot0 = sm.part[j & 1][0][0][lane];
+                f32x4 tot1 = sm.part[j & 1][0][1][lane];
 #pragma unroll
                 for (int w = 1; w < kGroupWaves; ++w) {
-                    tot0 += *reinterpret_cast<const f32x4*>(all + w * kWave * 8);
-                    tot1 += *reinterpret_cast<const f32x4*>(all + w * kWave * 8 + 4);
+                    tot0 += sm.part[j & 1][w][0][lane];
+                    tot1 += sm.part[j & 1][w][1][lane];
                 }
                 s[0] = tot0;
                 s[1] = tot1;
