@@ -537,10 +537,15 @@ topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__
         for (int i = 0; i < kPer; ++i)
             id[i] = (int32_t)pos[i];
     }
+    // A candidate below v, the k-th largest group key, cannot win: each of the
+    // k chosen groups holds an entry >= v, so k entries rank above it.  Dropping
+    // those candidates (ties at v stay) narrows the second search's range.
+    const uint32_t keep = pk.need > 0u ? pk.T : pk.T + 1u;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const bool ok = pos[i] >= 0 && id[i] >= 0 && !__builtin_isnan(f[i]);
-        key[i] = ok ? order_key(f[i]) : 0u;
+        const uint32_t kk = ok ? order_key(f[i]) : 0u;
+        key[i] = kk >= keep ? kk : 0u;
         id[i] = pos[i] >= 0 ? id[i] : -1;
     }
     pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
