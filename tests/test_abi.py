@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -191,3 +192,12 @@ def test_index_full_pool_validation():
     # nothing to do: no rows
     assert _status("csa2_index_full_pool", None, None, None, None, 100, None, 0, 1, 8, 64, None,
                    None, None, 0, None, None, None)[0] == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on exactly one GPU: --gpus above 1 exits with a message (before any
+    GPU work)."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
