@@ -351,10 +351,35 @@ def cpu_baseline(w: synth.Workload, rows: int):
         full = oracle.full_layer(qi[b, i], wi[b, i], kc, ks, int(nv[b, i]), w.k, w.nb, w.block)
         oracle.attention(qm[b, i], vc, vs, full["topk"], sw, int(se[b, i]), w.n_win, 1.0)
     dt = time.perf_counter() - t0
-    return {"value": round(len(sample) / dt, 4), "unit": "queries/s", "cores": oracle.threads(),
+    cores = oracle.threads()
+    # the same Full-layer step of the first row on one thread
+    b, i = sample[0]
+    kc, ks, vc, vs, sw = enc[b]
+    oracle.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.quantize_rows(new_idx[b])
+        oracle.quantize_rows(new_kv[b], ncos, nsin, synth.ROPE_OFFSET, synth.ROPE_DIM)
+        full = oracle.full_layer(qi[b, i], wi[b, i], kc, ks, int(nv[b, i]), w.k, w.nb, w.block)
+        oracle.attention(qm[b, i], vc, vs, full["topk"], sw, int(se[b, i]), w.n_win, 1.0)
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_threads(0)
+    return {"value": round(len(sample) / dt, 4), "unit": "queries/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{len(sample)} query rows ({len(seqs)} sequences) of the same workload, "
-                      f"full Full-layer step per row, {dt:.1f} s wall"}
+                      f"full Full-layer step per row, {dt:.1f} s wall",
+            "single_thread_value": round(1.0 / dt1, 4), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------ main

@@ -79,6 +79,8 @@ def lib():
         L.oracle_bf16_rne.argtypes = [dbl]
         L.oracle_inverse_rope_bf16.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp]
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -93,6 +95,12 @@ def _p(a):
 
 def threads() -> int:
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results do not depend on it);
+    n < 1 restores the default."""
+    lib().oracle_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- formats

@@ -505,6 +505,20 @@ void oracle_project_rows(const float* x, int64_t rows, int32_t D, const uint16_t
         }
 }
 
+/* Sets the threads of the library's OpenMP regions (timing harness only; the
+ * results do not depend on it).  n < 1 restores the runtime's default. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    static int deflt = 0;
+    if (deflt == 0)
+        deflt = omp_get_max_threads();
+    omp_set_num_threads(n >= 1 ? n : deflt);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads an OpenMP region of this library uses. */
 int oracle_threads(void)
 {
