@@ -194,7 +194,17 @@ def make_step(st, torch, L, layers, kv_production="rows", attn_out="fp32"):
         spare_events.extend(event_pair() for _ in range(n))
         torch.cuda.synchronize()
 
+    layer_events = []  # per sampled step of a multi-layer group: events at layer boundaries
+
+    def mark(evl):
+        if evl is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            evl.append(e)
+
     def step(time_scan=False):
+        evl = [] if time_scan and len(w.layers) > 1 else None
+        mark(evl)
         encode_new()
         evs = None
         if time_scan:
@@ -217,13 +227,18 @@ def make_step(st, torch, L, layers, kv_production="rows", attn_out="fp32"):
                      st["n_vis"], buf.pool_score, buf.pool_idx)
         L.topk(buf.pool_score, w.k, buf.topk, idx=buf.pool_idx, ws=buf.ws_topk)
         attn(0)
+        mark(evl)
         if "reindex" in w.layers:
             layers.reindex_indexer(buf, st["q_idx"][1], st["w_idx"][1], st["kc"], st["ks"],
                                    st["n_vis"], buf.pool, w.k)
             for layer in range(1, len(w.layers)):
                 attn(layer)
+                mark(evl)
+        if evl is not None:
+            layer_events.append(evl)
 
     step.prepare_scan_events = prepare_scan_events
+    step.layer_events = layer_events
     return step, scan_events
 
 
@@ -414,6 +429,7 @@ def main():
     torch.cuda.synchronize()
     log("warm")
     scan_events.clear()
+    step.layer_events.clear()
     step.prepare_scan_events((args.steps + SCAN_EVENT_EVERY - 1) // SCAN_EVENT_EVERY)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -439,6 +455,8 @@ def main():
                 "traffic": measured_traffic() if args.config == 3 else None,
                 "kernel": "index_full_kernel", "kernel_ms": round(scan_ms, 4),
                 "algorithmic_bytes": sb}
+        if roof["traffic"]:
+            roof["traffic_GBps"] = round(roof["traffic"] / (scan_ms / 1e3) / 1e9, 1)
     else:
         fl = scan_flops(w)
         achieved = fl / (scan_ms / 1e3)
@@ -467,6 +485,12 @@ def main():
     }
     if w.decode:
         out["step_tbps"] = round(step_bytes(w) / (ms_step / 1e3) / 1e12, 3)
+    if step.layer_events:
+        # each layer of the group: Full (encode .. its attention), Reindex (pool rescoring,
+        # top-k, attention), Reuse (attention), from events on the sampled steps
+        per = np.array([[a.elapsed_time(b) for a, b in zip(ev[:-1], ev[1:])]
+                        for ev in step.layer_events])
+        out["layers_ms"] = [[name, round(float(v), 4)] for name, v in zip(w.layers, per.mean(0))]
     if cold is not None:
         out["cold"] = cold
     if args.cpu_sample > 0 and args.config in (1, 3):
