@@ -208,7 +208,8 @@ csa2_status csa2_index_full(const uint16_t* q, const float* w,
  *   nb         pool blocks per query row, 1 <= nb <= 8192.
  *   pool       int32 [B, nq, nb]: the chosen block ids in ascending order,
  *              -1 padded -- exactly csa2_topk(block_max, L = ceil(n_cap/8),
- *              rows = B*nq, n_valid = ceil(n_visible/8), k = nb).
+ *              rows = B*nq, n_valid = ceil(n_visible/8), k = nb).  With
+ *              n_cap == 0 it is all -1 and block_max may be NULL.
  *   ws, ws_bytes  device workspace of at least
  *              csa2_index_full_pool_workspace(n_cap, B*nq, nb) bytes (8-byte
  *              aligned; any contents): the same as that csa2_topk call needs.

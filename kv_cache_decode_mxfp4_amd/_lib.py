@@ -8,6 +8,7 @@ happens in the library's HIP kernels; a missing library raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -280,7 +281,7 @@ def topk(score, k, out, idx=None, n_valid=None, ws=None, stream=None):
     _dt(score, torch.float32, "score")
     _dt(out, torch.int32, "out")
     L = score.shape[-1]
-    rows = score.numel() // L if L else 0
+    rows = math.prod(score.shape[:-1])  # also for L == 0 (every row then all -1)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("csa2_topk", load().csa2_topk(
         _p(score), _p(idx), L, rows, _p(n_valid), k, _p(out), _p(ws), ws_bytes,

@@ -220,7 +220,9 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w, const uint8_
             CSA2_ERR_INVALID_ARG, "index_full_pool: too many segments");
     if (rows == 0)
         return CSA2_OK;
-    REQUIRE(block_max != nullptr && pool != nullptr, CSA2_ERR_INVALID_ARG,
+    // an empty cache has no block maxima to write (block_max may be null); the
+    // pool is then all -1
+    REQUIRE(pool != nullptr && (n_cap == 0 || block_max != nullptr), CSA2_ERR_INVALID_ARG,
             "index_full_pool: null block_max or pool");
     const size_t need = csa2::topk_workspace(L, (int32_t)rows, nb);
     REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,

@@ -377,6 +377,7 @@ def test_paired_scan_bit_identical_to_one_row_scan_and_pool():
     (1, 3, 300000, 2048, [300000, 299999, 5]),             # groups of 3: the select's own pass
     (2, 1, 65536, 2048, [70000, 100]),                     # one segment: direct select
     (1, 1, 2048, 2048, [0]),                               # nothing visible
+    (1, 1, 0, 64, [5]),                                    # empty cache: no blocks
 ])
 def test_index_full_pool_matches_scan_then_topk(B, nq, n_cap, nb, nvis):
     """csa2_index_full_pool returns exactly csa2_index_full's block maxima and
@@ -416,7 +417,7 @@ def test_index_full_pool_matches_scan_then_topk(B, nq, n_cap, nb, nvis):
     assert np.array_equal(p1, p2)
     for r in range(B * nq):  # a valid pool: ascending ids of visible blocks, -1 padded
         row = p1.reshape(B * nq, nb)[r]
-        n_ok = min(nb, cdiv(max(int(nv.reshape(-1)[r]), 0), 8))
+        n_ok = min(nb, cdiv(min(max(int(nv.reshape(-1)[r]), 0), n_cap), 8))
         assert np.all(np.diff(row[:n_ok]) > 0) and np.all(row[n_ok:] == -1)
 
 
