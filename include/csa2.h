@@ -272,7 +272,8 @@ size_t csa2_topk_workspace(int64_t L, int32_t rows, int32_t k);
  * Sparse MLA attention ([N] 1: 64 heads x 512; [S]: K = V single-head MQA on
  * the 512-dim latent, top-k compressed entries plus 128 window entries).
  *   q          bf16 [B, nq, 64, 512], 16-byte aligned.
- *   kv_codes   u8 [B, n_cap, 256], kv_scales u8 [B, n_cap, 32]: MXFP4 main KV.
+ *   kv_codes   u8 [B, n_cap, 256], kv_scales u8 [B, n_cap, 32]: MXFP4 main KV
+ *              (NULL allowed when n_cap == 0: no compressed entries yet).
  *   topk       int32 [B, nq, k]: entry ids; ids outside [0, n_cap) skipped.
  *   swa        u8 [B, swa_cap, 512] E4M3FN window rows; query (b, i) uses rows
  *              [max(0, swa_end[b,i] - n_win), min(swa_end[b,i], swa_cap)).

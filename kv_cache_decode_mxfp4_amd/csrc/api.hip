@@ -320,7 +320,9 @@ static csa2_status attn_common(const uint16_t* q, int32_t B, int32_t nq,
     if (queries == 0)
         return CSA2_OK;
     REQUIRE(q && (out || out_bf16) && swa_end, CSA2_ERR_INVALID_ARG, "%s: null pointer", name);
-    REQUIRE(k == 0 || (topk && kv_codes && kv_scales), CSA2_ERR_INVALID_ARG,
+    // an empty main cache (n_cap == 0) may come as null pointers: every top-k
+    // index is then out of range and skipped, and the kernels never read it
+    REQUIRE(k == 0 || (topk && (n_cap == 0 || (kv_codes && kv_scales))), CSA2_ERR_INVALID_ARG,
             "%s: null top-k or KV cache", name);
     REQUIRE(swa_cap == 0 || swa != nullptr, CSA2_ERR_INVALID_ARG, "%s: null window", name);
     REQUIRE(aligned(q, 16) && aligned(kv_codes, 16) && aligned(kv_scales, 4) && aligned(swa, 16) &&

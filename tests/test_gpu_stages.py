@@ -328,44 +328,54 @@ def test_index_pool_scores_bit_identical_to_scan():
         assert np.all(np.isneginf(ps[b, 0][~ok]))
 
 
-def test_paired_scan_bit_identical_to_one_row_scan_and_pool():
+@pytest.mark.parametrize("B", [1, 2])
+def test_paired_scan_bit_identical_to_one_row_scan_and_pool(B):
     """Several query rows of one sequence take the paired scan (two rows per workgroup,
     one dequantisation per key): every score and block maximum must equal, bit for bit,
     the one-row scan of the same row and the pool scan of the same positions; an odd
-    row count leaves one row unpaired, and rows see different causal lengths."""
+    row count leaves one row unpaired, and rows see different causal lengths.  With two
+    sequences of 5003 entries the second sequence starts inside a key tile."""
     N, nq = 5003, 5
     rng = np.random.default_rng(6)
-    x = rng.standard_normal((N, 128)).astype(np.float32)
-    kc, ks = oracle.quantize_rows(x)
-    kct, kst = t(tile_keys(kc)), t(ks[None])
-    q = synth.normal_bf16(synth.key(11, 10, 0, 0), 0, nq * 4096, 1 / np.sqrt(128)).reshape(1, nq, 32, 128)
-    w = synth.uniform_f32(synth.key(11, 11, 0, 0), 0, nq * 32).reshape(1, nq, 32)
-    nv = np.array([[N, N - 1, 700, 0, 4099]], np.int32)
+    x = rng.standard_normal((B, N, 128)).astype(np.float32)
+    enc = [oracle.quantize_rows(x[b]) for b in range(B)]
+    kc = np.stack([e[0] for e in enc])
+    ks = np.stack([e[1] for e in enc])
+    kct, kst = t(tile_keys(kc)), t(ks)
+    q = synth.normal_bf16(synth.key(11, 10, 0, 0), 0, B * nq * 4096, 1 / np.sqrt(128)).reshape(B, nq, 32, 128)
+    w = synth.uniform_f32(synth.key(11, 11, 0, 0), 0, B * nq * 32).reshape(B, nq, 32)
+    nv = np.array([[N, N - 1, 700, 0, 4099], [4097, N, 1, 33, N - 31]], np.int32)[:B]
     nblk = cdiv(N, 8)
-    sc = torch.full((1, nq, N), 12345.0, device=dev())
-    bm = torch.full((1, nq, nblk), 12345.0, device=dev())
+    sc = torch.full((B, nq, N), 12345.0, device=dev())
+    bm = torch.full((B, nq, nblk), 12345.0, device=dev())
     L.index_full(t(q, torch.uint16), t(w), kct, kst, t(nv), bm, sc)
-    sc, bm = sc.cpu().numpy()[0], bm.cpu().numpy()[0]
-    blocks = np.sort(rng.choice(nblk, (1, nq, 64), replace=False), axis=-1).astype(np.int32)
-    ps = torch.empty(1, nq, 64 * 8, device=dev())
-    pi = torch.empty(1, nq, 64 * 8, dtype=torch.int32, device=dev())
+    sc, bm = sc.cpu().numpy(), bm.cpu().numpy()
+    blocks = np.sort(np.stack([rng.choice(nblk, (nq, 64), replace=False) for _ in range(B)]),
+                     axis=-1).astype(np.int32)
+    ps = torch.empty(B, nq, 64 * 8, device=dev())
+    pi = torch.empty(B, nq, 64 * 8, dtype=torch.int32, device=dev())
     L.index_pool(t(q, torch.uint16), t(w), kct, kst, t(blocks), t(nv), ps, pi)
-    ps, pi = ps.cpu().numpy()[0], pi.cpu().numpy()[0]
-    for i in range(nq):
-        n = int(nv[0, i])
-        s1 = torch.full((1, 1, N), 12345.0, device=dev())
-        b1 = torch.full((1, 1, nblk), 12345.0, device=dev())
-        L.index_full(t(q[:, i:i + 1], torch.uint16), t(w[:, i:i + 1]), kct, kst,
-                     t(nv[:, i:i + 1]), b1, s1)
-        assert np.array_equal(sc[i], s1.cpu().numpy()[0, 0]), f"row {i}: scores differ"
-        assert np.array_equal(bm[i], b1.cpu().numpy()[0, 0]), f"row {i}: block maxima differ"
-        if n:
-            ref = oracle.index_scores(q[0, i], w[0, i], kc, ks, n)
-            ok, err = finite_close(sc[i, :n], ref)
-            assert ok, f"row {i}: max err {err}"
-        ok = pi[i] >= 0
-        assert np.array_equal(pi[i], oracle.pool_positions(blocks[0, i], 8, n))
-        assert np.array_equal(ps[i][ok], sc[i][pi[i][ok]])
+    ps, pi = ps.cpu().numpy(), pi.cpu().numpy()
+    for b in range(B):
+        for i in range(nq):
+            n = int(nv[b, i])
+            # the same row through the one-row scan: a one-row batch per sequence
+            qb = np.zeros((B, 1, 32, 128), np.uint16)
+            wb = np.zeros((B, 1, 32), np.float32)
+            nb1 = np.zeros((B, 1), np.int32)
+            qb[b, 0], wb[b, 0], nb1[b, 0] = q[b, i], w[b, i], n
+            s1 = torch.full((B, 1, N), 12345.0, device=dev())
+            b1 = torch.full((B, 1, nblk), 12345.0, device=dev())
+            L.index_full(t(qb, torch.uint16), t(wb), kct, kst, t(nb1), b1, s1)
+            assert np.array_equal(sc[b, i], s1.cpu().numpy()[b, 0]), f"seq {b} row {i}: scores"
+            assert np.array_equal(bm[b, i], b1.cpu().numpy()[b, 0]), f"seq {b} row {i}: maxima"
+            if n:
+                ref = oracle.index_scores(q[b, i], w[b, i], kc[b], ks[b], n)
+                ok, err = finite_close(sc[b, i, :n], ref)
+                assert ok, f"seq {b} row {i}: max err {err}"
+            ok = pi[b, i] >= 0
+            assert np.array_equal(pi[b, i], oracle.pool_positions(blocks[b, i], 8, n))
+            assert np.array_equal(ps[b, i][ok], sc[b, i][pi[b, i][ok]])
 
 
 @pytest.mark.parametrize("B,nq,n_cap,nb,nvis", [
@@ -439,6 +449,30 @@ def _attn_case(B=2, N=3000, k=100, swa_cap=160, seed=3):
         q.append(synth.normal_bf16(synth.key(12, 8, 0, b), 0, 64 * 512, 1 / np.sqrt(512)))
     return (np.stack(vc), np.stack(vs), np.stack(sw), np.stack(sel)[:, None],
             np.stack(q).reshape(B, 1, 64, 512))
+
+
+def test_topk_of_empty_rows_is_all_padding():
+    """Rows of length 0 (an empty cache has no blocks) select nothing: -1 everywhere."""
+    out = torch.full((3, 5), 7, dtype=torch.int32, device=dev())
+    L.topk(torch.empty((3, 0), device=dev()), 5, out)
+    assert np.all(out.cpu().numpy() == -1)
+
+
+@pytest.mark.parametrize("use_ws", [True, False])
+def test_attention_with_empty_main_cache_is_window_only(use_ws):
+    """No compressed entries yet (n_cap = 0, every top-k index -1): the softmax runs over
+    the window rows alone, as the oracle's attention over an empty selected set."""
+    _, _, sw, _, q = _attn_case(B=2, N=64, k=16, seed=17)
+    B = q.shape[0]
+    vc = np.zeros((B, 0, 256), np.uint8)
+    vs = np.zeros((B, 0, 32), np.uint8)
+    sel = np.full((B, 1, 16), -1, np.int32)
+    swa_end = np.array([[128], [37]], np.int32)
+    out, lse = _run_attn(q, vc, vs, sel, sw, swa_end, use_ws=use_ws)
+    for b in range(B):
+        ref, ref_lse = oracle.attention(q[b, 0], vc[b], vs[b], sel[b, 0], sw[b], int(swa_end[b, 0]))
+        assert max_abs(out[b, 0], ref) <= ATTN_TOL
+        assert max_abs(lse[b, 0], ref_lse) <= 1e-4
 
 
 def _run_attn(q, vc, vs, sel, sw, swa_end, n_win=128, scale=1.0, use_ws=True):
