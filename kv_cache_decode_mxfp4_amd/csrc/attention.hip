@@ -526,12 +526,14 @@ constexpr int kMaxSplits = 8;                   // key splits per (row, head gro
 constexpr int kMinSplitTiles = CSA2_ATTN_MIN_SPLIT_TILES;  // fewest key tiles per split
 constexpr int kPartFloats = kHg * kDim + 2 * kHg;  // one split's O [16][512], max, sum
 
+template <int kHgW>
 struct GroupSmem {
     _Float16 v[kGroupWaves][kTile][kVRow];          // each wave's V tile (its 128 dims)
-    // partial S^T per wave, double-buffered: [buffer][wave][key block][lane], so
-    // each lane's 16-byte store and load is contiguous with its neighbours'
-    // (a 32-byte lane stride made lanes l and l + 8 share banks)
-    f32x4 part[2][kGroupWaves][2][kWave];
+    // partial S^T per head group and wave, double-buffered: [buffer][head
+    // group][wave][key block][lane], so each lane's 16-byte store and load is
+    // contiguous with its neighbours' (a 32-byte lane stride made lanes l and
+    // l + 8 share banks)
+    f32x4 part[2][kHgW][kGroupWaves][2][kWave];
 };
 
 // Raw bytes of one tile for the calling lane, for key l%16 of block b:
@@ -546,14 +548,17 @@ struct TileRaw {
 // Partial S^T of one tile over the wave's 128 channels (block bb in s[bb]);
 // the dequantised keys also go to the wave's LDS tile.  kMain: MXFP4 top-k
 // keys, else E4M3 window rows.
-template <bool kMain>
-__device__ __forceinline__ void tile_scores(const TileRaw& R, const half8 (&qop)[4],
+template <bool kMain, int kHgW>
+__device__ __forceinline__ void tile_scores(const TileRaw& R, const half8 (&qop)[kHgW][4],
                                             _Float16* __restrict__ vtile, int slice, int G,
-                                            int key16, f32x4 (&s)[2])
+                                            int key16, f32x4 (&s)[kHgW][2])
 {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-        f32x4 acc = {};
+        f32x4 acc[kHgW];
+#pragma unroll
+        for (int h = 0; h < kHgW; ++h)
+            acc[h] = f32x4{};
         const bool ok = (R.valid >> bb) & 1u;
         // scale bytes of this lane's 32 channels: dword 2(w%2) + G/2 of the 16
         // loaded, bytes 2(G%2) and 2(G%2)+1
@@ -573,10 +578,14 @@ __device__ __forceinline__ void tile_scores(const TileRaw& R, const half8 (&qop)
                 const half4v x0 = e4m3x4_to_f16(w0), x1 = e4m3x4_to_f16(w1);
                 a = half8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             }
-            acc = mfma16(a, qop[t], acc);
+#pragma unroll
+            for (int h = 0; h < kHgW; ++h)
+                acc[h] = mfma16(a, qop[h][t], acc[h]);
             *reinterpret_cast<half8*>(vtile + (16 * bb + key16) * kVRow + 32 * G + 8 * t) = a;
         }
-        s[bb] = acc;
+#pragma unroll
+        for (int h = 0; h < kHgW; ++h)
+            s[h][bb] = acc[h];
     }
 }
 
@@ -622,10 +631,18 @@ __device__ __forceinline__ void emit(const f32x4 (&o)[kSlice / 16], float inv, i
 #ifndef CSA2_ATTN_WAVES_PER_EU
 #define CSA2_ATTN_WAVES_PER_EU 3
 #endif
+#ifndef CSA2_ATTN_ROWS_HG_PER_WG
+#define CSA2_ATTN_ROWS_HG_PER_WG 2
+#endif
 
-template <bool kRopeBf16>
+// kHgW head groups per workgroup: 1 for the key-split (few rows) form; 2 for
+// many rows, where each dequantised key then serves 32 heads (half the
+// dequantisation and key fetches per head) at two waves per SIMD.  Every head
+// group runs exactly the one-group sequence of operations, so outputs are
+// bit-identical either way.
+template <bool kRopeBf16, int kHgW>
 __global__ void __launch_bounds__(kGroupWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(CSA2_ATTN_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kHgW == 1 ? CSA2_ATTN_WAVES_PER_EU : 2)))
 attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                   const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
                   int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
@@ -634,7 +651,7 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                   int32_t splits, float* __restrict__ part, AttnOut dst_spec,
                   float* __restrict__ lse)
 {
-    __shared__ GroupSmem sm;
+    __shared__ GroupSmem<kHgW> sm;
     const int lane = threadIdx.x & 63;
     // the wave's slice as a scalar: everything derived from it (pointers,
     // offsets) stays in scalar registers
@@ -645,16 +662,17 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     // the workgroups of a query row (4 head groups x splits) share one die
     // (and its L2, which then serves the keys to every head group): with
     // round-robin dispatch, workgroup x runs on die x % 8
-    const int wg_per_row = kGroups * splits;
+    constexpr int kWgGroups = kGroups / kHgW;  // workgroups per row and split
+    const int wg_per_row = kWgGroups * splits;
     const int64_t x = blockIdx.x;
     const int64_t rest = x / kXcds;
     const int64_t qrow = kXcds * (rest / wg_per_row) + x % kXcds;
-    const int hg = (int)(rest % wg_per_row) % kGroups;
-    const int split = (int)(rest % wg_per_row) / kGroups;
+    const int hg0 = ((int)(rest % wg_per_row) % kWgGroups) * kHgW;  // first head group
+    const int split = (int)(rest % wg_per_row) / kWgGroups;
     if (qrow >= queries)
         return;
     const int64_t b = qrow / nq;
-    const int head = kHg * hg + key16;  // head of this lane's score column
+    // head of this lane's score column in head group hg0 + h: kHg * (hg0 + h) + key16
 
     // tile list: top-k tiles [0, t_main), then window tiles; this workgroup
     // takes the list positions split + splits * j
@@ -682,14 +700,15 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
 #pragma unroll
     for (int u = 0; u < kDepth; ++u)
         load_idx(pos(u), eidx[u]);
-    // Q^T operand: head l%16 of the group, channels [128w + 32G, +32), bf16 -> fp16
-    uint4 qraw[4];
-    {
+    // Q^T operand: head l%16 of each group, channels [128w + 32G, +32), bf16 -> fp16
+    uint4 qraw[kHgW][4];
+#pragma unroll
+    for (int h = 0; h < kHgW; ++h) {
         const uint4* src = reinterpret_cast<const uint4*>(
-            q + (qrow * kHeads + head) * kDim + kSlice * slice + 32 * G);
+            q + (qrow * kHeads + kHg * (hg0 + h) + key16) * kDim + kSlice * slice + 32 * G);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            qraw[t] = src[t];
+            qraw[h][t] = src[t];
     }
 
     // window rows [lo, hi)
@@ -737,21 +756,25 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     for (int u = 0; u < kDepth; ++u)
         load_idx(pos(u + kDepth), eidx[u]);
 
-    half8 qop[4];
+    half8 qop[kHgW][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint32_t d[4] = {qraw[t].x, qraw[t].y, qraw[t].z, qraw[t].w};
+    for (int h = 0; h < kHgW; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qop[t][2 * i] = bf16_to_f16((uint16_t)(d[i] & 0xFFFFu));
-            qop[t][2 * i + 1] = bf16_to_f16((uint16_t)(d[i] >> 16));
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t d[4] = {qraw[h][t].x, qraw[h][t].y, qraw[h][t].z, qraw[h][t].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qop[h][t][2 * i] = bf16_to_f16((uint16_t)(d[i] & 0xFFFFu));
+                qop[h][t][2 * i + 1] = bf16_to_f16((uint16_t)(d[i] >> 16));
+            }
         }
-    }
 
-    Online st;
+    Online st[kHgW];
 #pragma unroll
-    for (int db = 0; db < kSlice / 16; ++db)
-        st.o[db] = f32x4{};
+    for (int h = 0; h < kHgW; ++h)
+#pragma unroll
+        for (int db = 0; db < kSlice / 16; ++db)
+            st[h].o[db] = f32x4{};
     _Float16* vtile = &sm.v[slice][0][0];
 
     // slot u of the ring holds the tile of step j0 + u; after use it is refilled
@@ -763,27 +786,33 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
             const int j = j0 + u;
             const int p = pos(j);
             if (j < n_j) {  // the same for every wave: the barrier below is uniform
-                f32x4 s[2];
+                f32x4 s[kHgW][2];
                 if (p < t_main)
-                    tile_scores<true>(ring[u], qop, vtile, slice, G, key16, s);
+                    tile_scores<true, kHgW>(ring[u], qop, vtile, slice, G, key16, s);
                 else
-                    tile_scores<false>(ring[u], qop, vtile, slice, G, key16, s);
-                // the four partial scores meet in LDS; every wave adds them in
-                // wave order (bit-identical in every wave)
-                sm.part[j & 1][slice][0][lane] = s[0];
-                sm.part[j & 1][slice][1][lane] = s[1];
-                __syncthreads();
-                f32x4 tot0 = sm.part[j & 1][0][0][lane];
-                f32x4 tot1 = sm.part[j & 1][0][1][lane];
+                    tile_scores<false, kHgW>(ring[u], qop, vtile, slice, G, key16, s);
+                // the four partial scores of each head group meet in LDS; every
+                // wave adds them in wave order (bit-identical in every wave)
 #pragma unroll
-                for (int w = 1; w < kGroupWaves; ++w) {
-                    tot0 += sm.part[j & 1][w][0][lane];
-                    tot1 += sm.part[j & 1][w][1][lane];
+                for (int h = 0; h < kHgW; ++h) {
+                    sm.part[j & 1][h][slice][0][lane] = s[h][0];
+                    sm.part[j & 1][h][slice][1][lane] = s[h][1];
                 }
-                s[0] = tot0;
-                s[1] = tot1;
-                scale_scores(s, ring[u].valid, scale_log2, G);
-                fold_tile(st, s, vtile, lane);
+                __syncthreads();
+#pragma unroll
+                for (int h = 0; h < kHgW; ++h) {
+                    f32x4 tot0 = sm.part[j & 1][h][0][0][lane];
+                    f32x4 tot1 = sm.part[j & 1][h][0][1][lane];
+#pragma unroll
+                    for (int w = 1; w < kGroupWaves; ++w) {
+                        tot0 += sm.part[j & 1][h][w][0][lane];
+                        tot1 += sm.part[j & 1][h][w][1][lane];
+                    }
+                    s[h][0] = tot0;
+                    s[h][1] = tot1;
+                    scale_scores(s[h], ring[u].valid, scale_log2, G);
+                    fold_tile(st[h], s[h], vtile, lane);
+                }
             }
             load_tile(pos(j + kDepth), eidx[u], ring[u]);
             load_idx(pos(j + 2 * kDepth), eidx[u]);
@@ -791,20 +820,29 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     }
 
     if (splits == 1) {
-        const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
-        emit<kRopeBf16>(st.o, inv, qrow, head, slice, G, dst_spec);
-        if (lse != nullptr && slice == 0 && G == 0)
-            lse[qrow * kHeads + head] = st.l > 0.0f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
+#pragma unroll
+        for (int h = 0; h < kHgW; ++h) {
+            const int head = kHg * (hg0 + h) + key16;
+            const float inv = st[h].l > 0.0f ? 1.0f / st[h].l : 0.0f;
+            emit<kRopeBf16>(st[h].o, inv, qrow, head, slice, G, dst_spec);
+            if (lse != nullptr && slice == 0 && G == 0)
+                lse[qrow * kHeads + head] =
+                    st[h].l > 0.0f ? (st[h].m + log2f(st[h].l)) * kLn2 : -INFINITY;
+        }
         return;
     }
     // this split's unnormalised (O, max, sum) for attn_merge_kernel
-    float* mine = part + ((qrow * kGroups + hg) * splits + split) * kPartFloats;
 #pragma unroll
-    for (int db = 0; db < kSlice / 16; ++db)
-        *reinterpret_cast<f32x4*>(mine + key16 * kDim + kSlice * slice + 16 * db + 4 * G) = st.o[db];
-    if (slice == 0 && G == 0) {
-        mine[kHg * kDim + key16] = st.m;
-        mine[kHg * kDim + kHg + key16] = st.l;
+    for (int h = 0; h < kHgW; ++h) {
+        float* mine = part + ((qrow * kGroups + hg0 + h) * splits + split) * kPartFloats;
+#pragma unroll
+        for (int db = 0; db < kSlice / 16; ++db)
+            *reinterpret_cast<f32x4*>(mine + key16 * kDim + kSlice * slice + 16 * db + 4 * G) =
+                st[h].o[db];
+        if (slice == 0 && G == 0) {
+            mine[kHg * kDim + key16] = st[h].m;
+            mine[kHg * kDim + kHg + key16] = st[h].l;
+        }
     }
 }
 
@@ -945,7 +983,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
         const int32_t splits = attn_splits(queries, k, n_win);
         float* part = static_cast<float*>(ws);
         const dim3 grid((uint32_t)(rows * kGroups * splits)), block(kGroupWaves * kWave);
-        attn_group_kernel<false><<<grid, block, 0, stream>>>(
+        attn_group_kernel<false, 1><<<grid, block, 0, stream>>>(
             q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
             scale_log2, splits, part, spec, lse);
         hipError_t e = hipGetLastError();
@@ -969,13 +1007,15 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, spec, lse);
     } else {
-        const dim3 grid((uint32_t)(rows * kGroups)), block(kGroupWaves * kWave);
+        // many rows: two head groups per workgroup
+        constexpr int kHgW = CSA2_ATTN_ROWS_HG_PER_WG;
+        const dim3 grid((uint32_t)(rows * (kGroups / kHgW))), block(kGroupWaves * kWave);
         if (out_bf16 == nullptr)
-            attn_group_kernel<false><<<grid, block, 0, stream>>>(
+            attn_group_kernel<false, kHgW><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, 1, nullptr, spec, lse);
         else
-            attn_group_kernel<true><<<grid, block, 0, stream>>>(
+            attn_group_kernel<true, kHgW><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, 1, nullptr, spec, lse);
     }
