@@ -631,9 +631,12 @@ __device__ __forceinline__ void emit(const f32x4 (&o)[kSlice / 16], float inv, i
 #ifndef CSA2_ATTN_WAVES_PER_EU
 #define CSA2_ATTN_WAVES_PER_EU 3
 #endif
-#ifndef CSA2_ATTN_ROWS_HG_PER_WG
-#define CSA2_ATTN_ROWS_HG_PER_WG 2
+// Query rows from which the many-row form takes two head groups per workgroup:
+// below it, half as many workgroups leave CUs idle (64 rows: 50 vs 34 us).
+#ifndef CSA2_ATTN_HG2_MIN_ROWS
+#define CSA2_ATTN_HG2_MIN_ROWS 512
 #endif
+constexpr int32_t kHg2MinRows = CSA2_ATTN_HG2_MIN_ROWS;
 
 // kHgW head groups per workgroup: 1 for the key-split (few rows) form; 2 for
 // many rows, where each dequantised key then serves 32 heads (half the
@@ -942,9 +945,14 @@ int64_t padded_rows(int32_t queries)
 // Key splits of the grouped form for few query rows: enough workgroups to
 // cover the CUs once, at least two tiles per split; 1 when the rows alone
 // fill the CUs.
+#ifndef CSA2_ATTN_SPLIT_HG_PER_WG
+#define CSA2_ATTN_SPLIT_HG_PER_WG 1
+#endif
+constexpr int kSplitHgW = CSA2_ATTN_SPLIT_HG_PER_WG;  // head groups per key-split workgroup
+
 int32_t attn_splits(int32_t queries, int32_t k, int32_t n_win)
 {
-    const int64_t groups = padded_rows(queries) * kGroups;
+    const int64_t groups = padded_rows(queries) * (kGroups / kSplitHgW);
     const int64_t tiles = ((int64_t)k + kTile - 1) / kTile + ((int64_t)n_win + kTile - 1) / kTile;
     int32_t s = 1;
     while (s < kMaxSplits && groups * s * 2 <= kSplitWgs && tiles >= kMinSplitTiles * 2 * s)
@@ -982,8 +990,9 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
         // orders the partials, with no cache maintenance inside the kernels)
         const int32_t splits = attn_splits(queries, k, n_win);
         float* part = static_cast<float*>(ws);
-        const dim3 grid((uint32_t)(rows * kGroups * splits)), block(kGroupWaves * kWave);
-        attn_group_kernel<false, 1><<<grid, block, 0, stream>>>(
+        const dim3 grid((uint32_t)(rows * (kGroups / kSplitHgW) * splits)),
+            block(kGroupWaves * kWave);
+        attn_group_kernel<false, kSplitHgW><<<grid, block, 0, stream>>>(
             q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
             scale_log2, splits, part, spec, lse);
         hipError_t e = hipGetLastError();
@@ -1006,16 +1015,26 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
             attn_spread_kernel<true><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, spec, lse);
-    } else {
-        // many rows: two head groups per workgroup
-        constexpr int kHgW = CSA2_ATTN_ROWS_HG_PER_WG;
-        const dim3 grid((uint32_t)(rows * (kGroups / kHgW))), block(kGroupWaves * kWave);
+    } else if (queries >= kHg2MinRows) {
+        // many rows: two head groups per workgroup (enough rows to fill the CUs
+        // with half as many workgroups)
+        const dim3 grid((uint32_t)(rows * (kGroups / 2))), block(kGroupWaves * kWave);
         if (out_bf16 == nullptr)
-            attn_group_kernel<false, kHgW><<<grid, block, 0, stream>>>(
+            attn_group_kernel<false, 2><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, 1, nullptr, spec, lse);
         else
-            attn_group_kernel<true, kHgW><<<grid, block, 0, stream>>>(
+            attn_group_kernel<true, 2><<<grid, block, 0, stream>>>(
+                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
+                n_win, scale_log2, 1, nullptr, spec, lse);
+    } else {
+        const dim3 grid((uint32_t)(rows * kGroups)), block(kGroupWaves * kWave);
+        if (out_bf16 == nullptr)
+            attn_group_kernel<false, 1><<<grid, block, 0, stream>>>(
+                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
+                n_win, scale_log2, 1, nullptr, spec, lse);
+        else
+            attn_group_kernel<true, 1><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, 1, nullptr, spec, lse);
     }

@@ -557,12 +557,12 @@ def test_sparse_attn_batched_kernel_many_rows():
         assert max_abs(lse[0, i], rl) <= 1e-4
 
 
-def _grouped_case(seed=21):
+def _grouped_case(seed=21, B=3, nq=8):
     """24 query rows (3 sequences x 8 queries): more rows than the spread form serves, so
     the grouped form runs.  Row r mixes top-k padding and window shapes by r % 6: plain,
     padded (-1 and out-of-range ids), window only, empty, window past the ring capacity,
     short window; k = 100 leaves a ragged last tile."""
-    B, nq, N, k, cap = 3, 8, 2000, 100, 160
+    N, k, cap = 2000, 100, 160
     rng = np.random.default_rng(seed)
     vc, vs, sw = [], [], []
     for b in range(B):
@@ -641,6 +641,46 @@ def test_sparse_attn_grouped_form_rope_bf16():
         o[:, 449::2] = (c * co) - (a * si)
         host = torch.from_numpy(o).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(got[b, i], host), f"row {r}"
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_sparse_attn_two_head_groups_bit_identical_to_one(bf16):
+    """From 512 query rows the many-row form takes two head groups per workgroup; the same
+    rows in calls of fewer rows take one.  Outputs and lse are bit-identical, and sampled
+    rows of every padding / window kind match the oracle."""
+    vc, vs, sw, sel, q, swa_end = _grouped_case(seed=24, B=1, nq=520)
+    nq = q.shape[1]
+    rng = np.random.default_rng(25)
+    ang = rng.uniform(-np.pi, np.pi, (nq, 32))
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+    def run(r0, r1):
+        n = r1 - r0
+        lse = torch.empty((1, n, 64), device=dev())
+        args = (t(q[:, r0:r1], torch.uint16), t(vc), t(vs), t(sel[:, r0:r1]), t(sw),
+                t(swa_end[:, r0:r1]))
+        if bf16:
+            out = torch.empty((1, n, 64, 512), dtype=torch.int16, device=dev())
+            L.sparse_attn_rope_bf16(*args, t(cos[r0:r1]), t(sin[r0:r1]), out, lse)
+        else:
+            out = torch.empty((1, n, 64, 512), device=dev())
+            L.sparse_attn(*args, out, lse)
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+    o2, l2 = run(0, nq)             # two head groups per workgroup
+    o1a, l1a = run(0, 260)          # one head group per workgroup
+    o1b, l1b = run(260, nq)
+    assert np.array_equal(o2, np.concatenate([o1a, o1b], axis=1))
+    assert np.array_equal(l2, np.concatenate([l1a, l1b], axis=1))
+    if not bf16:
+        for i in list(range(0, nq, 37)) + list(range(nq - 6, nq)):
+            ro, rl = oracle.attention(q[0, i], vc[0], vs[0], sel[0, i], sw[0],
+                                      int(swa_end[0, i]), 128, 1.0)
+            assert max_abs(o2[0, i], ro) <= ATTN_TOL, f"row {i}"
+            if np.all(np.isinf(rl)):
+                assert np.all(np.isneginf(l2[0, i])) and np.all(o2[0, i] == 0)
+            else:
+                assert max_abs(l2[0, i], rl) <= 1e-4, f"row {i}"
 
 
 def _bf16_to_f32(bits):
