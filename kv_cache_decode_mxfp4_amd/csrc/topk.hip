@@ -69,12 +69,13 @@ struct Pick {
 
 // Threshold of the k largest keys held by the workgroup (key 0 = invalid).
 // Expects sm.hist[0] cleared by the caller before the first barrier here.
-__device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm, int tid,
+template <int P>
+__device__ Pick find_threshold(const uint32_t (&key)[P], uint32_t k, Smem& sm, int tid,
                                int lane, int wave)
 {
     uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
+    for (int i = 0; i < P; ++i)
         if (key[i] != 0u) {
             ++cnt;
             lo = min(lo, key[i]);
@@ -114,7 +115,7 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
         const int shift = bits > kBinBits ? bits - kBinBits : 0;
         // key - lo wraps above span for keys below lo (the invalid key 0 too)
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
+        for (int i = 0; i < P; ++i) {
             const uint32_t d = key[i] - lo;
             if (d <= span)
                 atomicAdd(&sm.hist[buf][d >> shift], 1u);
@@ -162,7 +163,7 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
             // instead of another histogram pass.
             const uint32_t width = hi - lo;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i)
+            for (int i = 0; i < P; ++i)
                 if (key[i] - lo <= width) {
                     const uint32_t p = atomicAdd(&sm.few_n, 1u);
                     if (p < (uint32_t)kWave)
@@ -197,21 +198,24 @@ __device__ Pick find_threshold(const uint32_t (&key)[kPer], uint32_t k, Smem& sm
     return pk;
 }
 
-// Exclusive scan, in position order, of the 256 (slot, wave) counts part[] in
-// place by one wave (4 per lane); returns the total on every lane.
+// Exclusive scan, in position order, of the 16 * P (slot, wave) counts
+// part[] in place by one wave (P / 4 per lane); returns the total on every lane.
+template <int P>
 __device__ __forceinline__ uint32_t scan_parts(uint32_t* part, int lane)
 {
-    uint32_t c[4], sum = 0;
+    constexpr int kN = P * kNumWaves / kWave;
+    static_assert(kN >= 1 && kN * kWave == P * kNumWaves, "slots per thread: a multiple of 4");
+    uint32_t c[kN], sum = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        c[j] = part[4 * lane + j];
+    for (int j = 0; j < kN; ++j) {
+        c[j] = part[kN * lane + j];
         sum += c[j];
     }
     const uint32_t incl = wave_prefix_sum(sum, lane);
     uint32_t run = incl - sum;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        part[4 * lane + j] = run;
+    for (int j = 0; j < kN; ++j) {
+        part[kN * lane + j] = run;
         run += c[j];
     }
     return (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
@@ -220,13 +224,14 @@ __device__ __forceinline__ uint32_t scan_parts(uint32_t* part, int lane)
 // Marks the chosen slots and their output offsets (position order); returns
 // how many were chosen.  pk.need == 0 (every key equal to the threshold is
 // taken, or there is none) needs only the "above" ballots.
-__device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPer],
-                          uint32_t (&off)[kPer], Smem& sm, int lane, int wave)
+template <int P>
+__device__ uint32_t place(const uint32_t (&key)[P], Pick pk, bool (&take)[P],
+                          uint32_t (&off)[P], Smem& sm, int lane, int wave)
 {
     if (pk.need == 0u) {
-        uint32_t gt_below[kPer];
+        uint32_t gt_below[P];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
+        for (int i = 0; i < P; ++i) {
             const uint64_t bg = __ballot(key[i] > pk.T);
             gt_below[i] = lanes_below(bg, lane);
             if (lane == 0)
@@ -234,13 +239,13 @@ __device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPe
         }
         __syncthreads();
         if (wave == 0) {
-            const uint32_t all = scan_parts(sm.part_gt, lane);
+            const uint32_t all = scan_parts<P>(sm.part_gt, lane);
             if (lane == 0)
                 sm.totals[0] = all;
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
+        for (int i = 0; i < P; ++i) {
             take[i] = key[i] > pk.T;
             off[i] = sm.part_gt[i * kNumWaves + wave] + gt_below[i];
         }
@@ -248,9 +253,9 @@ __device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPe
         __syncthreads();
         return n_gt;
     }
-    uint32_t gt_below[kPer], eq_below[kPer];
+    uint32_t gt_below[P], eq_below[P];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         const uint64_t bg = __ballot(key[i] > pk.T);
         const uint64_t be = __ballot(key[i] == pk.T);
         gt_below[i] = lanes_below(bg, lane);
@@ -262,13 +267,13 @@ __device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPe
     }
     __syncthreads();
     if (wave < 2) {
-        const uint32_t all = scan_parts(wave == 0 ? sm.part_gt : sm.part_eq, lane);
+        const uint32_t all = scan_parts<P>(wave == 0 ? sm.part_gt : sm.part_eq, lane);
         if (lane == 0)
             sm.totals[wave] = all;
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         const uint32_t gt_before = sm.part_gt[i * kNumWaves + wave] + gt_below[i];
         const uint32_t eq_before = sm.part_eq[i * kNumWaves + wave] + eq_below[i];
         take[i] = key[i] > pk.T || (key[i] == pk.T && eq_before < pk.need);
@@ -279,22 +284,23 @@ __device__ uint32_t place(const uint32_t (&key)[kPer], Pick pk, bool (&take)[kPe
     return n_gt + (n_eq < pk.need ? n_eq : pk.need);
 }
 
-__device__ __forceinline__ void write_result(const bool (&take)[kPer], const uint32_t (&off)[kPer],
-                                             const uint32_t (&key)[kPer], const int32_t (&id)[kPer],
+template <int P>
+__device__ __forceinline__ void write_result(const bool (&take)[P], const uint32_t (&off)[P],
+                                             const uint32_t (&key)[P], const int32_t (&id)[P],
                                              uint32_t chosen, int32_t k, int tid,
                                              int32_t* __restrict__ out, float* __restrict__ cs,
                                              int32_t* __restrict__ ci)
 {
     if (cs == nullptr) {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
+        for (int i = 0; i < P; ++i)
             if (take[i] && off[i] < (uint32_t)k)
                 out[off[i]] = id[i];
         for (uint32_t p = chosen + tid; p < (uint32_t)k; p += kThreads)
             out[p] = -1;
     } else {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
+        for (int i = 0; i < P; ++i)
             if (take[i] && off[i] < (uint32_t)k) {
                 cs[off[i]] = key_value(key[i]);
                 ci[off[i]] = id[i];
@@ -308,21 +314,22 @@ __device__ __forceinline__ void write_result(const bool (&take)[kPer], const uin
 
 // Loads slot i of thread tid = element seg_start + 1024*i + tid (clamped
 // inside the row, masked by position < seg_end, index >= 0 and not NaN).
+template <int P>
 __device__ __forceinline__ void load_slots(const float* __restrict__ srow,
                                            const int32_t* __restrict__ irow, int64_t L,
                                            int64_t seg_start, int64_t seg_end, int tid,
-                                           uint32_t (&key)[kPer], int32_t (&id)[kPer])
+                                           uint32_t (&key)[P], int32_t (&id)[P])
 {
-    float f[kPer];
+    float f[P];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         int64_t pos = seg_start + (int64_t)kThreads * i + tid;
         pos = pos < L ? pos : L - 1;
         f[i] = srow[pos];
         id[i] = irow != nullptr ? irow[pos] : (int32_t)pos;
     }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         const int64_t pos = seg_start + (int64_t)kThreads * i + tid;
         const bool ok = pos < seg_end && id[i] >= 0 && !__builtin_isnan(f[i]);
         key[i] = ok ? order_key(f[i]) : 0u;
@@ -341,10 +348,13 @@ __device__ __forceinline__ int64_t valid_prefix(const int32_t* __restrict__ n_va
     return nv > L ? L : nv;
 }
 
-// Direct select within segments of up to 16384 entries.  Grid: rows * nseg.
+// Direct select within segments of up to 1024 * P entries (P slots per
+// thread; short rows take a smaller P, which drops the empty slots' ballots,
+// histogram adds and scans).  Grid: rows * nseg.
 // Final mode (cand_score == nullptr): out[row, 0..k) = ascending indices.
 // Candidate mode: cand_score/cand_idx[row, seg, 0..k) = chosen (score, index)
 // pairs in position order, padded with index -1.
+template <int P>
 __global__ void __launch_bounds__(kThreads)
 topk_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
             int64_t seg_len, int32_t nseg, const int32_t* __restrict__ n_valid,
@@ -364,21 +374,21 @@ topk_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, in
     for (int b = tid; b < kBins; b += kThreads)
         sm.hist[0][b] = 0u;
 
-    uint32_t key[kPer];
-    int32_t id[kPer];
+    uint32_t key[P];
+    int32_t id[P];
     if (L > 0) {
         load_slots(score + row * L, idx != nullptr ? idx + row * L : nullptr, L, seg_start,
                    seg_end, tid, key, id);
     } else {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
+        for (int i = 0; i < P; ++i) {
             key[i] = 0u;
             id[i] = -1;
         }
     }
     const Pick pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
-    bool take[kPer];
-    uint32_t off[kPer];
+    bool take[P];
+    uint32_t off[P];
     const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
     write_result(take, off, key, id, chosen, k, tid, out + row * k,
                  cand_score ? cand_score + (row * nseg + seg) * k : nullptr,
@@ -629,7 +639,7 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         const size_t n = (size_t)rows * nseg * k;
         float* cs = reinterpret_cast<float*>(bufs[flip]);
         int32_t* ci = reinterpret_cast<int32_t*>(bufs[flip] + n * sizeof(float));
-        topk_kernel<<<dim3((uint32_t)(rows * nseg)), dim3(kThreads), 0, stream>>>(
+        topk_kernel<kPer><<<dim3((uint32_t)(rows * nseg)), dim3(kThreads), 0, stream>>>(
             score, idx, L, kTopkSegment, (int32_t)nseg, n_valid, valid_div, k, nullptr, cs, ci);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -640,8 +650,16 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         n_valid = nullptr;
         flip ^= 1;
     }
-    topk_kernel<<<dim3((uint32_t)rows), dim3(kThreads), 0, stream>>>(
-        score, idx, L, L, 1, n_valid, valid_div, k, out, nullptr, nullptr);
+    const dim3 grid((uint32_t)rows), block(kThreads);
+    if (L <= 4 * kThreads)
+        topk_kernel<4><<<grid, block, 0, stream>>>(score, idx, L, L, 1, n_valid, valid_div, k,
+                                                   out, nullptr, nullptr);
+    else if (L <= 8 * kThreads)
+        topk_kernel<8><<<grid, block, 0, stream>>>(score, idx, L, L, 1, n_valid, valid_div, k,
+                                                   out, nullptr, nullptr);
+    else
+        topk_kernel<kPer><<<grid, block, 0, stream>>>(score, idx, L, L, 1, n_valid, valid_div,
+                                                      k, out, nullptr, nullptr);
     return hipGetLastError();
 }
 

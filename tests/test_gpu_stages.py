@@ -205,7 +205,8 @@ def _topk_case(rng, rows, Lr, kind, k=1):
     return s
 
 
-@pytest.mark.parametrize("Lr,k", [(1, 1), (100, 7), (2048, 64), (16384, 2048), (16385, 512),
+@pytest.mark.parametrize("Lr,k", [(1, 1), (100, 7), (2048, 64), (4096, 512), (4097, 2048),
+                                  (8192, 512), (8193, 512), (16384, 2048), (16385, 512),
                                   (40000, 512), (131072, 2048), (131072, 512), (300000, 512), (300000, 2048),
                                   (50000, 6000)])
 @pytest.mark.parametrize("kind", ["random", "ties", "near_ties"])
