@@ -6,8 +6,9 @@
 // indices in ascending order, -1 padded.
 //
 // Core: one workgroup of 1024 threads holds up to 16384 (key, index) pairs in
-// registers, 16 per thread (slot i of thread t is element 1024*i + t, so loads
-// are coalesced and position order is slot-major).  The k-th largest key is
+// registers, P per thread (slot i of thread t is element 1024*i + t, so loads
+// are coalesced and position order is slot-major; P = 16, or 4 / 8 for rows of
+// at most 4096 / 8192 keys, which skips the empty slots' work).  The k-th largest key is
 // found by an adaptive-range radix select: each pass histograms the live key
 // range [lo, hi] into at most 4096 equal LDS bins and keeps the bin holding the
 // k-th key, shrinking the span by at least 2^12 (three passes at most; 4096
