@@ -10,10 +10,11 @@
 // are coalesced and position order is slot-major; P = 16, or 4 / 8 for rows of
 // at most 4096 / 8192 keys, which skips the empty slots' work).  The k-th largest key is
 // found by an adaptive-range radix select: each pass histograms the live key
-// range [lo, hi] into at most 4096 equal LDS bins and keeps the bin holding the
-// k-th key, shrinking the span by at least 2^12 (three passes at most; 4096
-// bins, 4 per thread, keep a pass's prefix step short — measured faster than
-// 8192 or 2048 on score-like data).  Once the chosen bin holds at most 64
+// range [lo, hi] into at most 2048 equal LDS bins and keeps the bin holding the
+// k-th key, shrinking the span by at least 2^11 (three passes at most; 2048
+// bins, 2 per thread, keep a pass's prefix step short and the histograms at
+// 16 KB — on score-like data 1-5 % faster than 4096 bins on rows of 4096 to
+// 16384 keys, equal on the 1M-context block select, and faster than 1024).  Once the chosen bin holds at most 64
 // keys (on score-like data, after the first pass) they are gathered into LDS
 // and one wave ranks them against each other instead of running another
 // pass, whose cost is the same per key however few keys are live.  One
@@ -40,7 +41,7 @@ constexpr int kThreads = 1024;
 constexpr int kPer = kTopkSegment / kThreads;  // 16
 constexpr int kNumWaves = kThreads / kWave;    // 16
 #ifndef CSA2_TOPK_BIN_BITS
-#define CSA2_TOPK_BIN_BITS 12
+#define CSA2_TOPK_BIN_BITS 11
 #endif
 constexpr int kBinBits = CSA2_TOPK_BIN_BITS;
 constexpr int kBins = 1 << kBinBits;           // radix bins per pass
