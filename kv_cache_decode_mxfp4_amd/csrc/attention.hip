@@ -108,12 +108,15 @@ __device__ __forceinline__ void fold_tile(Online& st, const f32x4 (&s)[2],
             for (int r = 0; r < 4; ++r)
                 p[b][r] = 0.0f;
     } else {
-        alpha = exp2f(st.m - m_new);
+        // the hardware exp2 (no subnormal range fix-up): every argument here is
+        // <= 0, and a result below 2^-126 is lost next to the running maximum's
+        // term (exactly 1) in every sum and rounds to zero in the fp16 P pair
+        alpha = __builtin_amdgcn_exp2f(st.m - m_new);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[b][r] = exp2f(s[b][r] - m_new);
+                p[b][r] = __builtin_amdgcn_exp2f(s[b][r] - m_new);
                 psum += p[b][r];
             }
     }
