@@ -329,6 +329,19 @@ csa2_status csa2_sparse_attn_rope_bf16(const uint16_t* q, int32_t B, int32_t nq,
                                        int32_t rope_dim, uint16_t* out, float* lse, void* ws,
                                        size_t ws_bytes, void* stream);
 
+/*
+ * Streaming-read calibration (measurement only, no part of a layer): reads
+ * `bytes` bytes at `src` (16-byte aligned, bytes % 16 == 0) once with
+ * 16-byte loads, `workgroups` workgroups each taking one contiguous slice,
+ * `depth` loads per lane in flight (1, 2, 4 or 8).  sink: uint32
+ * [workgroups], written only when a workgroup's checksum equals one fixed
+ * value (the reads cannot be optimised away; in practice nothing is
+ * written).  The fastest setting is the practical read ceiling that the
+ * indexer scan's bandwidth is compared with.
+ */
+csa2_status csa2_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t depth,
+                             uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ EXPORTS = ("csa2_last_error", "csa2_version", "csa2_quantize_kv", "csa2_quantize
            "csa2_index_full", "csa2_index_full_pool", "csa2_index_full_pool_workspace",
            "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
            "csa2_sparse_attn", "csa2_sparse_attn_workspace", "csa2_sparse_attn_rope_bf16",
-           "csa2_encode_entries")
+           "csa2_encode_entries", "csa2_stream_read")
 
 
 class Csa2Error(RuntimeError):
@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i32, i32, vp, vp, vp]
     L.csa2_topk.restype = st
     L.csa2_topk.argtypes = [vp, vp, i64, i32, vp, i32, vp, vp, sz, vp]
+    L.csa2_stream_read.restype = st
+    L.csa2_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
     L.csa2_topk_workspace.restype = sz
     L.csa2_topk_workspace.argtypes = [i64, i32, i32]
     L.csa2_sparse_attn.restype = st
@@ -286,6 +288,13 @@ def topk(score, k, out, idx=None, n_valid=None, ws=None, stream=None):
     _check("csa2_topk", load().csa2_topk(
         _p(score), _p(idx), L, rows, _p(n_valid), k, _p(out), _p(ws), ws_bytes,
         _stream(stream)))
+
+
+def stream_read(src, workgroups, depth, sink, stream=None):
+    """Streaming read of every byte of src (calibration); sink int32/uint32 [workgroups]."""
+    nbytes = src.numel() * src.element_size()
+    _check("csa2_stream_read", load().csa2_stream_read(
+        _p(src), nbytes, workgroups, depth, _p(sink), _stream(stream)))
 
 
 def sparse_attn_workspace(B, nq, k, n_win) -> int:

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libcsa2.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "quantize.hip", "indexer.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.hip", "quantize.hip", "indexer.hip", "topk.hip", "attention.hip", "calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -ffp-contract=off: every floating-point operation rounds as written; fused

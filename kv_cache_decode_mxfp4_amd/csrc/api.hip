@@ -296,6 +296,26 @@ csa2_status csa2_topk(const float* score, const int32_t* idx, int64_t L, int32_t
                   "topk");
 }
 
+csa2_status csa2_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t depth,
+                             uint32_t* sink, void* stream)
+{
+    REQUIRE(bytes >= 0 && bytes % 16 == 0, CSA2_ERR_INVALID_ARG,
+            "stream_read: bytes must be a non-negative multiple of 16");
+    REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), CSA2_ERR_INVALID_ARG,
+            "stream_read: workgroups must be in [1, 2^20]");
+    REQUIRE(depth == 1 || depth == 2 || depth == 4 || depth == 8, CSA2_ERR_UNSUPPORTED,
+            "stream_read: depth must be 1, 2, 4 or 8");
+    REQUIRE(bytes / workgroups < (1ll << 30), CSA2_ERR_INVALID_ARG,
+            "stream_read: slices above 1 GiB");
+    if (bytes == 0)
+        return CSA2_OK;
+    REQUIRE(src && sink, CSA2_ERR_INVALID_ARG, "stream_read: null pointer");
+    REQUIRE(aligned(src, 16), CSA2_ERR_INVALID_ARG, "stream_read: src must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_stream_read(src, bytes, workgroups, depth, sink, s), s,
+                  "stream_read");
+}
+
 size_t csa2_sparse_attn_workspace(int32_t B, int32_t nq, int32_t k, int32_t n_win)
 {
     if (B < 0 || nq < 0 || k < 0 || n_win < 0)

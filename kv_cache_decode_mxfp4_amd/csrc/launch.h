@@ -73,4 +73,9 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                               int32_t rope_dim, float* lse, void* ws, size_t ws_bytes,
                               hipStream_t stream);
 
+// Streaming read of `bytes` bytes (calibration): `workgroups` slices, `depth`
+// 16-byte loads per lane in flight (1, 2, 4 or 8); sink [workgroups].
+hipError_t launch_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t depth,
+                              uint32_t* sink, hipStream_t stream);
+
 }  // namespace csa2
