@@ -269,6 +269,23 @@ csa2_status csa2_topk(const float* score, const int32_t* idx, int64_t L, int32_t
 size_t csa2_topk_workspace(int64_t L, int32_t rows, int32_t k);
 
 /*
+ * csa2_topk without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * allocation).  Same arguments, selection and output as csa2_topk; the
+ * workspace csa2_topk_workspace(L, rows, k) would need comes instead from a
+ * static device array of the library (8 MiB per GPU, allocated when the
+ * library is loaded and held until the process ends), whose device address
+ * is looked up once per GPU on the first call made with that GPU current.
+ * Calls whose workspace would exceed 8 MiB fail with CSA2_ERR_WORKSPACE
+ * (nothing enqueued).  The call itself allocates nothing.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  No part
+ * of the array needs clearing between calls.
+ */
+csa2_status csa2_topk_noalloc(const float* score, const int32_t* idx, int64_t L, int32_t rows,
+                              const int32_t* n_valid, int32_t k, int32_t* out, void* stream);
+
+/*
  * Sparse MLA attention ([N] 1: 64 heads x 512; [S]: K = V single-head MQA on
  * the 512-dim latent, top-k compressed entries plus 128 window entries).
  *   q          bf16 [B, nq, 64, 512], 16-byte aligned.

@@ -24,7 +24,7 @@ EXPORTS = ("csa2_last_error", "csa2_version", "csa2_quantize_kv", "csa2_quantize
            "csa2_index_full", "csa2_index_full_pool", "csa2_index_full_pool_workspace",
            "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
            "csa2_sparse_attn", "csa2_sparse_attn_workspace", "csa2_sparse_attn_rope_bf16",
-           "csa2_encode_entries", "csa2_stream_read")
+           "csa2_encode_entries", "csa2_topk_noalloc", "csa2_stream_read")
 
 
 class Csa2Error(RuntimeError):
@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i32, i32, vp, vp, vp]
     L.csa2_topk.restype = st
     L.csa2_topk.argtypes = [vp, vp, i64, i32, vp, i32, vp, vp, sz, vp]
+    L.csa2_topk_noalloc.restype = st
+    L.csa2_topk_noalloc.argtypes = [vp, vp, i64, i32, vp, i32, vp, vp]
     L.csa2_stream_read.restype = st
     L.csa2_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
     L.csa2_topk_workspace.restype = sz
@@ -288,6 +290,16 @@ def topk(score, k, out, idx=None, n_valid=None, ws=None, stream=None):
     _check("csa2_topk", load().csa2_topk(
         _p(score), _p(idx), L, rows, _p(n_valid), k, _p(out), _p(ws), ws_bytes,
         _stream(stream)))
+
+
+def topk_noalloc(score, k, out, idx=None, n_valid=None, stream=None):
+    """csa2_topk with the library's static device workspace (no workspace argument)."""
+    _dt(score, torch.float32, "score")
+    _dt(out, torch.int32, "out")
+    L = score.shape[-1]
+    rows = math.prod(score.shape[:-1])
+    _check("csa2_topk_noalloc", load().csa2_topk_noalloc(
+        _p(score), _p(idx), L, rows, _p(n_valid), k, _p(out), _stream(stream)))
 
 
 def stream_read(src, workgroups, depth, sink, stream=None):

@@ -296,6 +296,35 @@ csa2_status csa2_topk(const float* score, const int32_t* idx, int64_t L, int32_t
                   "topk");
 }
 
+csa2_status csa2_topk_noalloc(const float* score, const int32_t* idx, int64_t L, int32_t rows,
+                              const int32_t* n_valid, int32_t k, int32_t* out, void* stream)
+{
+    REQUIRE(L >= 0 && rows >= 0, CSA2_ERR_INVALID_ARG, "topk_noalloc: negative size");
+    REQUIRE(k >= 1 && k <= csa2::kTopkMaxK, CSA2_ERR_UNSUPPORTED,
+            "topk_noalloc: k must be in [1, %d]", csa2::kTopkMaxK);
+    REQUIRE(L <= (1ll << 31) - 1, CSA2_ERR_INVALID_ARG, "topk_noalloc: L above 2^31-1");
+    REQUIRE((int64_t)rows * ((L + csa2::kTopkSegment - 1) / csa2::kTopkSegment) <= (1ll << 31) - 1,
+            CSA2_ERR_INVALID_ARG, "topk_noalloc: too many segments");
+    if (rows == 0)
+        return CSA2_OK;
+    REQUIRE(out != nullptr, CSA2_ERR_INVALID_ARG, "topk_noalloc: null out");
+    REQUIRE(L == 0 || score != nullptr, CSA2_ERR_INVALID_ARG, "topk_noalloc: null score");
+    const size_t need = csa2::topk_workspace(L, rows, k);
+    REQUIRE(need <= csa2::kTopkScratchBytes, CSA2_ERR_WORKSPACE,
+            "topk_noalloc: needs %zu bytes of workspace, above the static %zu", need,
+            (size_t)csa2::kTopkScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = csa2::topk_scratch(&ws);
+        if (e != hipSuccess)
+            return fail(CSA2_ERR_LAUNCH, "topk_noalloc: static workspace address: %s",
+                        hipGetErrorString(e));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_topk(score, idx, L, rows, n_valid, 1, k, out, ws, false, s), s,
+                  "topk_noalloc");
+}
+
 csa2_status csa2_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t depth,
                              uint32_t* sink, void* stream)
 {

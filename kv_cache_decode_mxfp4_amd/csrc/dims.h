@@ -3,6 +3,8 @@
 // blocks x 8 positions; [N] 2.3: one scale per 16 channels).
 #pragma once
 
+#include <stddef.h>
+
 namespace csa2 {
 
 constexpr int kIdxHeads = 32;
@@ -13,6 +15,8 @@ constexpr int kGroup = 16;
 constexpr int kBlock = 8;
 constexpr int kTopkSegment = 16384;  // elements one top-k workgroup holds
 constexpr int kTopkMaxK = 8192;
+// Bytes of the static device workspace of csa2_topk_noalloc (per GPU).
+constexpr size_t kTopkScratchBytes = (size_t)8 << 20;
 
 // Indexer-key code cache layout: tiles of 32 consecutive entries (flat entry
 // index f = b * n_cap + j), each tile 2048 bytes stored as four planes of

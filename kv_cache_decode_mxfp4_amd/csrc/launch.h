@@ -56,6 +56,9 @@ int32_t topk_group_size(int64_t L, int32_t k);
 // n_valid[row] / valid_div (rounded up) is the row's valid prefix (valid_div 8:
 // visible entries -> visible blocks).  group_keys_ready: the workspace already
 // holds the group maxima (written by the scan), so they are not recomputed.
+// Device address of the calling thread's current GPU's static top-k scratch
+// (kTopkScratchBytes), looked up once per device.
+hipError_t topk_scratch(void** ptr);
 hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_t rows,
                        const int32_t* n_valid, int32_t valid_div, int32_t k, int32_t* out,
                        void* ws, bool group_keys_ready, hipStream_t stream);

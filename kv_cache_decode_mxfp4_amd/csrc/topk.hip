@@ -31,6 +31,8 @@
 //   otherwise exact levels: every segment of 16384 emits its own top-k
 //     candidates (the global top-k is a subset of their union, and the
 //     candidate lists keep position order) until one segment remains.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -663,6 +665,44 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
         topk_kernel<kPer><<<grid, block, 0, stream>>>(score, idx, L, L, 1, n_valid, valid_div,
                                                       k, out, nullptr, nullptr);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------ static scratch
+//
+// The workspace of csa2_topk_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  In host code the
+// array's name is only a host-side stand-in; the device address of each GPU's
+// copy comes from hipGetSymbolAddress, looked up once per device (with that
+// device current) and kept here.  Nothing in the top-k paths needs the
+// workspace cleared: the group maxima and the candidate lists are written in
+// full before they are read.
+
+static __device__ __align__(256) uint8_t scratch[kTopkScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t topk_scratch(void** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace csa2

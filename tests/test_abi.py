@@ -201,3 +201,17 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_topk_noalloc_rejects_workspace_above_static_size():
+    """csa2_topk_noalloc refuses, on the host, a call whose workspace would exceed its
+    8 MiB static device array (nothing is enqueued, no GPU needed)."""
+    lib = L.load()
+    vp = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    # 64 rows x 131072 keys, k 2048: group maxima of 64 x 16384 x 4 B = 4 MiB (fits);
+    # 256 rows: 16 MiB (does not fit)
+    assert lib.csa2_topk_workspace(131072, 256, 2048) > 8 << 20
+    st, msg = _status("csa2_topk_noalloc", vp, None, 131072, 256, None, 2048, vp, None)
+    assert st == 3 and "static" in msg
+    st, msg = _status("csa2_topk_noalloc", vp, None, 100, 1, None, 0, vp, None)
+    assert st == 2
