@@ -219,22 +219,10 @@ def make_step(st, torch, L, layers, kv_production="rows", attn_out="fp32"):
         if time_scan:
             evs = spare_events.pop() if spare_events else event_pair()
             scan_events.append(evs)
-        if w.nb >= w.k:
-            # scan + pool select in one call (the scan also writes the select's group
-            # maxima); the scan kernel's own dispatch records the timing events
-            L.index_full_pool(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], st["n_vis"],
-                              buf.block_max, buf.pool, ws=buf.ws_topk, scan_events=evs)
-        else:
-            if evs:
-                evs[0].record()
-            L.index_full(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], st["n_vis"],
-                         buf.block_max)
-            if evs:
-                evs[1].record()
-            layers.select_blocks(buf, n_blk, w.k, w.nb)
-        L.index_pool(st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"], buf.sel_blocks,
-                     st["n_vis"], buf.pool_score, buf.pool_idx)
-        L.topk(buf.pool_score, w.k, buf.topk, idx=buf.pool_idx, ws=buf.ws_topk)
+        # scan + pool + top-k blocks in one call (the scan kernel's own dispatch records
+        # the timing events), then the top-k blocks' positions rescored and the top-k
+        layers.full_indexer(buf, st["q_idx"][0], st["w_idx"][0], st["kc"], st["ks"],
+                            st["n_vis"], n_blk, w.k, w.nb, scan_events=evs)
         attn(0)
         mark(evl)
         if "reindex" in w.layers:
@@ -300,16 +288,13 @@ def scan_bytes(w: synth.Workload) -> int:
 
 def scan_write_bytes(w: synth.Workload) -> int:
     """Bytes the scan launch writes besides reading (not in scan_bytes): the block maxima
-    (fp32 per 8 visible entries) and, feeding the pool select, one uint32 group key per
-    g blocks of each row (the grouped select's input)."""
+    (fp32 per 8 visible entries) and, for rows of more than 16384 blocks, the block
+    select's inputs -- one uint32 group key per g blocks and each chunk's candidate
+    list (the workspace of csa2_index_full_select, minus nothing: an upper bound)."""
     nv = w.n_visible().astype(np.int64)
-    nblk_cap = (w.n_cap + 7) // 8
     b = int(((nv + 7) // 8).sum()) * 4
-    g = -(-nblk_cap // 16384) if nblk_cap > 16384 else 0
-    g = g if g * w.nb <= 16384 else 0
-    if w.nb >= w.k and w.nb > 0 and g > 0 and 64 % g == 0:
-        b += w.B * w.nq * (-(-nblk_cap // g)) * 4
-    return b
+    from kv_cache_decode_mxfp4_amd import _lib as L
+    return b + L.index_full_select_workspace(w.n_cap, w.B, w.nq, w.nb, w.k)
 
 
 def scan_flops(w: synth.Workload) -> int:

@@ -232,6 +232,39 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w,
                                  void* stream);
 
 /*
+ * Full-layer scan with the pool AND the top-k blocks in one call ([N] 2.2,
+ * [A] 3.4: the Full layer scores the whole visible range, keeps the nb blocks
+ * with the largest block scores as the pool, and selects its own top-k
+ * entries).  The top-k entries of a row always lie in its k best blocks (a
+ * block ranked above a winner's block holds a better entry, also under the
+ * lower-index tie-break), so the Full layer's top-k is csa2_index_pool over
+ * topk_blocks followed by csa2_topk(k): the scan itself keeps no per-entry
+ * scores.  Same arguments as csa2_index_full_pool, plus
+ *   nb           pool blocks, 0 <= nb <= 8192 (0: no pool, pool may be NULL).
+ *   k            1 <= k <= 8192.
+ *   pool         int32 [B, nq, nb]: csa2_topk(block_max, ceil(n_cap/8), B*nq,
+ *                n_valid = ceil(n_visible/8), nb), bit for bit.
+ *   topk_blocks  int32 [B, nq, k]: the same with k.
+ *   ws, ws_bytes device workspace of csa2_index_full_select_workspace(n_cap,
+ *                B, nq, nb, k) bytes, 256-byte aligned, any contents (0
+ *                bytes for rows of at most 16384 blocks, where ws may be NULL).
+ * For rows of more than 16384 blocks the one-row scan also writes each chunk's
+ * best blocks and the maxima of groups of blocks into the workspace: the
+ * select then ranks only those candidates, and falls back to an exact select
+ * over the group maxima for a row where a chunk could hold more winners than
+ * it listed.  Both give the same result.
+ */
+size_t      csa2_index_full_select_workspace(int64_t n_cap, int32_t B, int32_t nq, int32_t nb,
+                                             int32_t k);
+csa2_status csa2_index_full_select(const uint16_t* q, const float* w,
+                                   const uint8_t* k_codes, const uint8_t* k_scales,
+                                   int64_t n_cap, const int32_t* n_visible, int32_t B,
+                                   int32_t nq, int32_t block, int32_t nb, int32_t k,
+                                   float* block_max, int32_t* pool, int32_t* topk_blocks,
+                                   void* ws, size_t ws_bytes, void* scan_start,
+                                   void* scan_stop, void* stream);
+
+/*
  * Indexer scoring restricted to a pool of blocks ([N] 2.2, [A] 3.4: Reindex
  * layers score only the Full layer's 2048 x 8 pool with their own query).
  *   q, w, k_codes, k_scales, n_cap, n_visible, B, nq: as csa2_index_full.

@@ -246,6 +246,138 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w, const uint8_
     return finish(e, s, "index_full_pool");
 }
 
+// How csa2_index_full_select runs for a shape: the direct block select (rows of
+// at most 16384 blocks), the scan's per-chunk candidates (one-row scan, groups
+// of g blocks that the scan also writes as the exact fallback), or two
+// csa2_topk calls over the block maxima.
+struct FullSelectPlan {
+    int mode;          // 0 direct, 1 candidates, 2 two top-k calls
+    int64_t L;         // blocks per row
+    int32_t g;         // group size (mode 1)
+    int32_t chunks, kl;
+    size_t off_cand_key, off_cand_blk, off_cand_full, ws_bytes;
+};
+
+static FullSelectPlan full_select_plan(int64_t n_cap, int32_t B, int32_t nq, int32_t nb, int32_t k)
+{
+    FullSelectPlan P{};
+    const int64_t rows = (int64_t)B * nq;
+    P.L = (n_cap + csa2::kBlock - 1) / csa2::kBlock;
+    const int32_t tmax = nb > k ? nb : k;
+    if (P.L <= csa2::kTopkSegment) {
+        P.mode = 0;
+        return P;
+    }
+    const csa2::ScanShape sh = csa2::scan_shape(n_cap, B, nq);
+    const int32_t g = csa2::topk_group_size(P.L, tmax);
+    if (!sh.paired && g > 0 && 64 % g == 0) {
+        // about twice a chunk's share of the winners, at least 64, a power of two
+        const int32_t per = (tmax + sh.chunks_per_row - 1) / sh.chunks_per_row;
+        int32_t kl = 64;
+        while (kl < 2 * per)
+            kl *= 2;
+        if (kl <= sh.max_blocks_per_chunk && (int64_t)sh.chunks_per_row * kl <= csa2::kTopkSegment) {
+            P.mode = 1;
+            P.g = g;
+            P.chunks = sh.chunks_per_row;
+            P.kl = kl;
+            const size_t gk = (size_t)rows * (size_t)((P.L + g - 1) / g) * 4;
+            const size_t nc = (size_t)rows * P.chunks * kl;
+            auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+            P.off_cand_key = up(gk);
+            P.off_cand_blk = P.off_cand_key + up(nc * 4);
+            P.off_cand_full = P.off_cand_blk + up(nc * 4);
+            P.ws_bytes = P.off_cand_full + up((size_t)rows * P.chunks * 4);
+            return P;
+        }
+    }
+    P.mode = 2;
+    const size_t a = csa2::topk_workspace(P.L, (int32_t)rows, nb > 0 ? nb : 1);
+    const size_t b = csa2::topk_workspace(P.L, (int32_t)rows, k);
+    P.ws_bytes = a > b ? a : b;
+    return P;
+}
+
+size_t csa2_index_full_select_workspace(int64_t n_cap, int32_t B, int32_t nq, int32_t nb,
+                                        int32_t k)
+{
+    if (n_cap < 0 || B < 0 || nq < 0 || nb < 0 || k < 1 || nb > csa2::kTopkMaxK ||
+        k > csa2::kTopkMaxK)
+        return 0;
+    return full_select_plan(n_cap, B, nq, nb, k).ws_bytes;
+}
+
+csa2_status csa2_index_full_select(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                                   const uint8_t* k_scales, int64_t n_cap,
+                                   const int32_t* n_visible, int32_t B, int32_t nq,
+                                   int32_t block, int32_t nb, int32_t k, float* block_max,
+                                   int32_t* pool, int32_t* topk_blocks, void* ws,
+                                   size_t ws_bytes, void* scan_start, void* scan_stop,
+                                   void* stream)
+{
+    csa2_status st = check_indexer("index_full_select", q, w, k_codes, k_scales, n_cap,
+                                   n_visible, B, nq, block);
+    if (st != CSA2_OK)
+        return st;
+    REQUIRE(nb >= 0 && nb <= csa2::kTopkMaxK && k >= 1 && k <= csa2::kTopkMaxK,
+            CSA2_ERR_UNSUPPORTED, "index_full_select: nb must be in [0, %d], k in [1, %d]",
+            csa2::kTopkMaxK, csa2::kTopkMaxK);
+    const int64_t rows = (int64_t)B * nq;
+    const int64_t L = (n_cap + csa2::kBlock - 1) / csa2::kBlock;
+    REQUIRE(rows * ((L + csa2::kTopkSegment - 1) / csa2::kTopkSegment) <= (1ll << 31) - 1,
+            CSA2_ERR_INVALID_ARG, "index_full_select: too many segments");
+    if (rows == 0)
+        return CSA2_OK;
+    REQUIRE(topk_blocks != nullptr && (nb == 0 || pool != nullptr) &&
+                (n_cap == 0 || block_max != nullptr),
+            CSA2_ERR_INVALID_ARG, "index_full_select: null block_max, pool or topk_blocks");
+    const FullSelectPlan P = full_select_plan(n_cap, B, nq, nb, k);
+    REQUIRE(ws_bytes >= P.ws_bytes && (P.ws_bytes == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
+            "index_full_select: workspace of %zu bytes needed, %zu given", P.ws_bytes, ws_bytes);
+    REQUIRE(aligned(ws, 256), CSA2_ERR_INVALID_ARG,
+            "index_full_select: workspace must be 256-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* pool_out = nb > 0 ? pool : nullptr;
+    hipError_t e = hipSuccess;
+    char* wsb = static_cast<char*>(ws);
+    if (n_cap > 0) {
+        if (P.mode == 1) {
+            e = csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq, block_max,
+                                        nullptr, reinterpret_cast<uint32_t*>(wsb), P.g,
+                                        static_cast<hipEvent_t>(scan_start),
+                                        static_cast<hipEvent_t>(scan_stop), s,
+                                        reinterpret_cast<uint32_t*>(wsb + P.off_cand_key),
+                                        reinterpret_cast<int32_t*>(wsb + P.off_cand_blk),
+                                        reinterpret_cast<int32_t*>(wsb + P.off_cand_full), P.kl);
+        } else {
+            e = csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq, block_max,
+                                        nullptr, nullptr, 0, static_cast<hipEvent_t>(scan_start),
+                                        static_cast<hipEvent_t>(scan_stop), s);
+        }
+    }
+    if (e == hipSuccess) {
+        if (n_cap == 0 || P.mode == 0) {
+            e = csa2::launch_block_select(block_max, L, (int32_t)rows, n_visible, nullptr, 0, nullptr,
+                                          nullptr, nullptr, 0, 0, nb, k, pool_out, topk_blocks, s);
+        } else if (P.mode == 1) {
+            e = csa2::launch_block_select(
+                block_max, L, (int32_t)rows, n_visible, reinterpret_cast<const uint32_t*>(wsb), P.g,
+                reinterpret_cast<const uint32_t*>(wsb + P.off_cand_key),
+                reinterpret_cast<const int32_t*>(wsb + P.off_cand_blk),
+                reinterpret_cast<const int32_t*>(wsb + P.off_cand_full), P.chunks, P.kl, nb, k,
+                pool_out, topk_blocks, s);
+        } else {
+            if (nb > 0)
+                e = csa2::launch_topk(block_max, nullptr, L, (int32_t)rows, n_visible,
+                                      csa2::kBlock, nb, pool_out, ws, false, s);
+            if (e == hipSuccess)
+                e = csa2::launch_topk(block_max, nullptr, L, (int32_t)rows, n_visible,
+                                      csa2::kBlock, k, topk_blocks, ws, false, s);
+        }
+    }
+    return finish(e, s, "index_full_select");
+}
+
 csa2_status csa2_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
                             const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
                             int32_t n_blocks, int32_t block, const int32_t* n_visible, int32_t B,

@@ -26,6 +26,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace csa2 {
 namespace {
@@ -42,8 +43,14 @@ constexpr int kGroupEntries = kPrefetch * kStep;  // entries per prefetch round
 // the largest (up to kMaxChunk) that still gives kScanTargetWorkgroups
 // workgroups (256 CUs x 4 resident workgroups), so each workgroup loads its
 // query once and keeps its prefetch ring running over a long range.
-constexpr int kMaxChunk = 16384;
-constexpr int64_t kScanTargetWorkgroups = 1024;
+#ifndef CSA2_SCAN_MAX_CHUNK
+#define CSA2_SCAN_MAX_CHUNK 16384
+#endif
+#ifndef CSA2_SCAN_TARGET_WGS
+#define CSA2_SCAN_TARGET_WGS 1024
+#endif
+constexpr int kMaxChunk = CSA2_SCAN_MAX_CHUNK;
+constexpr int64_t kScanTargetWorkgroups = CSA2_SCAN_TARGET_WGS;
 // Query rows per sequence from which the scan pairs rows (prefill shapes);
 // decode (one row per sequence) streams its keys from HBM, one row each.
 #ifndef CSA2_SCAN_PAIR_MIN_ROWS
@@ -276,6 +283,67 @@ __device__ __attribute__((noinline)) void write_group_keys(const float* sblk, in
     }
 }
 
+// Candidates of one row's chunk for the block select (after the scan loop):
+// the kl best of the chunk's nb_here visible block maxima (held in sblk),
+// under the selection order (larger maximum first, lower block first), as
+// (order key, block id) pairs in block order at list[0..kl) of the chunk,
+// padded with (0, -1); full = whether the chunk had more than kl blocks (so
+// some were left out).  A NaN maximum has key 0 and is never a candidate.
+// kl <= the chunk's block count, a multiple of 64.
+constexpr int kCandThreads = kWaves * kWave;
+constexpr int kCandSlots = kMaxChunk / kBlock / kCandThreads;  // blocks per thread
+
+__device__ __attribute__((noinline)) void write_candidates(const float* sblk, int nb_here,
+                                                           int64_t blk0, int32_t kl,
+                                                           uint32_t* __restrict__ ckey,
+                                                           int32_t* __restrict__ cblk,
+                                                           int32_t* __restrict__ cfull)
+{
+    __shared__ sel::Smem<kCandThreads> sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    uint32_t key[kCandSlots];
+#pragma unroll
+    for (int i = 0; i < kCandSlots; ++i) {
+        const int b = kCandThreads * i + tid;
+        const float f = b < nb_here ? sblk[b] : 0.0f;
+        key[i] = b < nb_here && !__builtin_isnan(f) ? order_key(f) : 0u;
+    }
+    sel::clear_hist(sm, tid);
+    const sel::Pick pk = sel::find_threshold<kCandSlots, kCandThreads>(key, (uint32_t)kl, sm, tid,
+                                                                       lane, wave);
+    bool take[kCandSlots];
+    uint32_t off[kCandSlots];
+    const uint32_t chosen =
+        sel::place<kCandSlots, kCandThreads>(key, pk, take, off, sm, lane, wave);
+#pragma unroll
+    for (int i = 0; i < kCandSlots; ++i)
+        if (take[i] && off[i] < (uint32_t)kl) {
+            ckey[off[i]] = key[i];
+            cblk[off[i]] = (int32_t)(blk0 + kCandThreads * i + tid);
+        }
+    for (uint32_t p = chosen + tid; p < (uint32_t)kl; p += kCandThreads) {
+        ckey[p] = 0u;
+        cblk[p] = -1;
+    }
+    if (tid == 0)
+        *cfull = nb_here > kl ? 1 : 0;
+}
+
+// Empty candidate list of a chunk past the row's visible end.
+__device__ __forceinline__ void write_no_candidates(int32_t kl, uint32_t* __restrict__ ckey,
+                                                    int32_t* __restrict__ cblk,
+                                                    int32_t* __restrict__ cfull)
+{
+    for (int p = threadIdx.x; p < kl; p += kCandThreads) {
+        ckey[p] = 0u;
+        cblk[p] = -1;
+    }
+    if (threadIdx.x == 0)
+        *cfull = 0;
+}
+
 // Full-range scan: one workgroup scans `chunk` entries of one query row and
 // writes the maxima of the blocks of 8 it covers (and, with kScores, every
 // score).  Wave w scores tiles start + 32*(w + kWaves*i).
@@ -294,7 +362,9 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                   int64_t n_cap, const int32_t* __restrict__ n_visible, int32_t nq,
                   int32_t chunk, int32_t chunks_per_query, int64_t nblk_cap,
                   float* __restrict__ block_max, float* __restrict__ scores,
-                  uint32_t* __restrict__ gkey, int32_t gshift, int64_t ngroups)
+                  uint32_t* __restrict__ gkey, int32_t gshift, int64_t ngroups,
+                  uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_blk,
+                  int32_t* __restrict__ cand_full, int32_t kl)
 {
     __shared__ float sblk[kMaxChunk / kBlock];
 
@@ -303,9 +373,13 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     int64_t n_vis = n_visible[row];
     n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
     const int64_t start = (int64_t)(blockIdx.x % chunks_per_query) * chunk;
+    // this chunk's candidate list (block select), when asked for
+    const int64_t cslot = (int64_t)blockIdx.x * kl;
     if (start >= n_vis) {
         if (gkey != nullptr)
             write_group_keys(sblk, 0, row, start, chunk, gshift, ngroups, gkey);
+        if (cand_key != nullptr)
+            write_no_candidates(kl, cand_key + cslot, cand_blk + cslot, cand_full + blockIdx.x);
         return;
     }
     const int32_t n_here = (int32_t)(n_vis - start < chunk ? n_vis - start : chunk);
@@ -356,6 +430,9 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
         dst[t] = sblk[t];
     if (gkey != nullptr)
         write_group_keys(sblk, nb_here, row, start, chunk, gshift, ngroups, gkey);
+    if (cand_key != nullptr)
+        write_candidates(sblk, nb_here, start / kBlock, kl, cand_key + cslot, cand_blk + cslot,
+                         cand_full + blockIdx.x);
 }
 
 // Full-range scan of two query rows of one sequence (rows 2p and 2p + 1 of
@@ -562,11 +639,45 @@ hipError_t launch_scan(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t 
 
 }  // namespace
 
+ScanShape scan_shape(int64_t n_cap, int32_t B, int32_t nq)
+{
+    ScanShape sh{0, 0, 0, false};
+    if (nq >= kPairMinRows) {
+        const int32_t pairs_per_seq = (nq + 1) / 2;
+        const int64_t pairs = (int64_t)B * pairs_per_seq;
+        int32_t chunk = kMaxChunk;
+        while (chunk > kGroupEntries &&
+               pairs * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
+            chunk /= 2;
+        sh.chunk = chunk;
+        sh.chunks_per_row = (int32_t)((n_cap + chunk - 1) / chunk);
+        sh.paired = true;
+        sh.max_blocks_per_chunk = chunk / kBlock;
+        return sh;
+    }
+    const int64_t rows = (int64_t)B * nq;
+#ifdef CSA2_SCAN_EVEN_CHUNKS
+    // chunk = the even share of the target workgroup count, in whole prefetch rounds
+    int64_t want = (rows * n_cap + kScanTargetWorkgroups - 1) / kScanTargetWorkgroups;
+    want = (want + kGroupEntries - 1) / kGroupEntries * kGroupEntries;
+    int32_t chunk = (int32_t)(want < kGroupEntries ? kGroupEntries : (want > kMaxChunk ? kMaxChunk : want));
+#else
+    int32_t chunk = kMaxChunk;
+    while (chunk > kGroupEntries && rows * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
+        chunk /= 2;
+#endif
+    sh.chunk = chunk;
+    sh.chunks_per_row = (int32_t)((n_cap + chunk - 1) / chunk);
+    sh.max_blocks_per_chunk = chunk / kBlock;
+    return sh;
+}
+
 hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
                              int32_t B, int32_t nq, float* block_max, float* scores,
                              uint32_t* group_keys, int32_t group, hipEvent_t ev_start,
-                             hipEvent_t ev_stop, hipStream_t stream)
+                             hipEvent_t ev_stop, hipStream_t stream, uint32_t* cand_key,
+                             int32_t* cand_blk, int32_t* cand_full, int32_t kl)
 {
     const int64_t nblk_cap = (n_cap + kBlock - 1) / kBlock;
     int32_t gshift = 0;  // group = 1 << gshift (a power of two dividing 64)
@@ -593,17 +704,19 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
                            block_max, scores, group_keys, gshift, ngroups);
     }
     const int64_t rows = (int64_t)B * nq;
-    int32_t chunk = kMaxChunk;
-    while (chunk > kGroupEntries && rows * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
-        chunk /= 2;
-    const int64_t chunks = (n_cap + chunk - 1) / chunk;
+    const ScanShape sh = scan_shape(n_cap, B, nq);
+    const int32_t chunk = sh.chunk;
+    const int64_t chunks = sh.chunks_per_row;
     const int64_t grid = rows * chunks;
     if (grid == 0)
         return hipSuccess;
+    if (cand_key == nullptr)
+        kl = 0;
     return launch_scan(scores != nullptr ? index_full_kernel<true> : index_full_kernel<false>,
                        dim3((uint32_t)grid), dim3(kWaves * kWave), stream, ev_start, ev_stop, q, w,
                        k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,
-                       block_max, scores, group_keys, gshift, ngroups);
+                       block_max, scores, group_keys, gshift, ngroups, cand_key, cand_blk,
+                       cand_full, kl);
 }
 
 hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,

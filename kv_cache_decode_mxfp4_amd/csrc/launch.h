@@ -37,11 +37,38 @@ hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* c
 // (0 for groups with no visible block); group must be a power of two <= 64.
 // ev_start / ev_stop (or null): HIP events the scan kernel's dispatch records
 // at its start and end.
+// cand_key / cand_blk / cand_full (or null; one-row scan only): each chunk's
+// kl best blocks for the block select, [B*nq, chunks, kl] and [B*nq, chunks]
+// (ScanShape::chunks_per_row chunks per row).
 hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
                              int32_t B, int32_t nq, float* block_max, float* scores,
                              uint32_t* group_keys, int32_t group, hipEvent_t ev_start,
-                             hipEvent_t ev_stop, hipStream_t stream);
+                             hipEvent_t ev_stop, hipStream_t stream,
+                             uint32_t* cand_key = nullptr, int32_t* cand_blk = nullptr,
+                             int32_t* cand_full = nullptr, int32_t kl = 0);
+
+// How the scan cuts rows into chunks (one workgroup per chunk and row, or per
+// chunk and pair of rows when `paired`).
+struct ScanShape {
+    int32_t chunk;                 // entries per chunk
+    int32_t chunks_per_row;
+    int32_t max_blocks_per_chunk;  // chunk / 8
+    bool paired;
+};
+ScanShape scan_shape(int64_t n_cap, int32_t B, int32_t nq);
+
+// Pool (top-nb blocks) and top-k blocks of every row in one launch.  Direct
+// form (cand_key null): keys are the block maxima, L <= 16384.  Candidate
+// form: the scan's per-chunk lists [rows, chunks, kl] (chunks * kl <= 16384,
+// kl >= 64), with the exact grouped select over the group maxima gkey
+// ([rows, ceil(L/g)], groups of g) as the fallback.  pool / sel may be null
+// (target skipped).
+hipError_t launch_block_select(const float* block_max, int64_t L, int32_t rows,
+                               const int32_t* n_visible, const uint32_t* gkey, int32_t g,
+                               const uint32_t* cand_key, const int32_t* cand_blk,
+                               const int32_t* cand_full, int32_t chunks, int32_t kl, int32_t nb,
+                               int32_t k, int32_t* pool, int32_t* sel, hipStream_t stream);
 
 hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,

@@ -35,257 +35,30 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace csa2 {
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kPer = kTopkSegment / kThreads;  // 16
-constexpr int kNumWaves = kThreads / kWave;    // 16
-#ifndef CSA2_TOPK_BIN_BITS
-#define CSA2_TOPK_BIN_BITS 11
-#endif
-constexpr int kBinBits = CSA2_TOPK_BIN_BITS;
-constexpr int kBins = 1 << kBinBits;           // radix bins per pass
-constexpr int kBpt = kBins / kThreads;         // bins per thread
 
-__device__ __forceinline__ float key_value(uint32_t k)
+using sel::key_value;
+using sel::Pick;
+using Smem = sel::Smem<kThreads>;
+
+template <int P>
+__device__ __forceinline__ Pick find_threshold(const uint32_t (&key)[P], uint32_t k, Smem& sm,
+                                               int tid, int lane, int wave)
 {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+    return sel::find_threshold<P, kThreads>(key, k, sm, tid, lane, wave);
 }
 
-struct Smem {
-    uint32_t hist[2][kBins];
-    uint32_t part_gt[kPer * kNumWaves];
-    uint32_t part_eq[kPer * kNumWaves];
-    uint32_t wave_a[3][kNumWaves];
-    uint32_t bcast[2][3];
-    uint32_t totals[2];
-    uint32_t few_n;             // keys appended to few_key
-    uint32_t few_key[kWave];    // the keys of a small chosen bin
-    uint32_t few_pick[2];       // (threshold, keys equal to it to take)
-};
-
-struct Pick {
-    uint32_t T;     // threshold key (0 = take every valid key)
-    uint32_t need;  // keys equal to T to take, in position order
-};
-
-// Threshold of the k largest keys held by the workgroup (key 0 = invalid).
-// Expects sm.hist[0] cleared by the caller before the first barrier here.
 template <int P>
-__device__ Pick find_threshold(const uint32_t (&key)[P], uint32_t k, Smem& sm, int tid,
-                               int lane, int wave)
+__device__ __forceinline__ uint32_t place(const uint32_t (&key)[P], Pick pk, bool (&take)[P],
+                                          uint32_t (&off)[P], Smem& sm, int lane, int wave)
 {
-    uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-    for (int i = 0; i < P; ++i)
-        if (key[i] != 0u) {
-            ++cnt;
-            lo = min(lo, key[i]);
-            hi = max(hi, key[i]);
-        }
-    cnt = wave_sum_u32(cnt, lane);
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    if (lane == 0) {
-        sm.wave_a[0][wave] = cnt;
-        sm.wave_a[1][wave] = lo;
-        sm.wave_a[2][wave] = hi;
-    }
-    if (tid == 0)
-        sm.few_n = 0u;
-    __syncthreads();
-    uint32_t total = 0;
-    lo = 0xFFFFFFFFu;
-    hi = 0u;
-#pragma unroll
-    for (int i = 0; i < kNumWaves; ++i) {
-        total += sm.wave_a[0][i];
-        lo = min(lo, sm.wave_a[1][i]);
-        hi = max(hi, sm.wave_a[2][i]);
-    }
-    // no barrier here: wave_a is next written after the first pass's barrier (or
-    // in the next call, after place()'s barriers), when every wave has read it
-    Pick pk{0u, 0u};
-    if (total <= k)
-        return pk;
-    uint32_t need = k, live = total;  // live: keys inside [lo, hi]
-    // invariant: the threshold is the need-th largest key inside [lo, hi]
-    for (int pass = 0; pass < 4 && hi != lo; ++pass) {
-        const int buf = pass & 1;
-        const uint32_t span = hi - lo;
-        const int bits = 32 - __builtin_clz(span);
-        const int shift = bits > kBinBits ? bits - kBinBits : 0;
-        // key - lo wraps above span for keys below lo (the invalid key 0 too)
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            const uint32_t d = key[i] - lo;
-            if (d <= span)
-                atomicAdd(&sm.hist[buf][d >> shift], 1u);
-        }
-        __syncthreads();
-        // thread t owns bins kBpt*t .. kBpt*t + kBpt - 1
-        uint32_t c[kBpt], mine = 0;
-#pragma unroll
-        for (int j = 0; j < kBpt; ++j) {
-            c[j] = sm.hist[buf][kBpt * tid + j];
-            mine += c[j];
-            sm.hist[buf ^ 1][kBpt * tid + j] = 0u;  // clear the buffer of the next pass
-        }
-        const uint32_t incl = wave_prefix_sum(mine, lane);
-        if (lane == kWave - 1)
-            sm.wave_a[0][wave] = incl;
-        __syncthreads();
-        uint32_t before = 0, all = 0;
-#pragma unroll
-        for (int i = 0; i < kNumWaves; ++i) {
-            const uint32_t v = sm.wave_a[0][i];
-            before += i < wave ? v : 0u;
-            all += v;
-        }
-        uint32_t above = all - (before + incl);  // keys in bins above this thread's
-#pragma unroll
-        for (int j = kBpt - 1; j >= 0; --j) {
-            if (above < need && above + c[j] >= need) {
-                sm.bcast[buf][0] = (uint32_t)(kBpt * tid + j);
-                sm.bcast[buf][1] = above;
-                sm.bcast[buf][2] = c[j];
-            }
-            above += c[j];
-        }
-        __syncthreads();
-        const uint32_t bin = sm.bcast[buf][0];
-        const uint32_t in_bin = sm.bcast[buf][2];
-        need -= sm.bcast[buf][1];
-        live = in_bin;
-        lo = lo + (bin << shift);
-        const uint64_t top = (uint64_t)lo + ((1ull << shift) - 1ull);
-        hi = top < (uint64_t)hi ? (uint32_t)top : hi;
-        if (in_bin <= (uint32_t)kWave && hi != lo) {
-            // Few keys left in [lo, hi]: gather them and rank them in one wave
-            // instead of another histogram pass.
-            const uint32_t width = hi - lo;
-#pragma unroll
-            for (int i = 0; i < P; ++i)
-                if (key[i] - lo <= width) {
-                    const uint32_t p = atomicAdd(&sm.few_n, 1u);
-                    if (p < (uint32_t)kWave)
-                        sm.few_key[p] = key[i];
-                }
-            __syncthreads();
-            if (wave == 0) {
-                const uint32_t v = lane < (int)in_bin ? sm.few_key[lane] : 0u;
-                uint32_t gt = 0, eq = 0;
-                for (uint32_t j = 0; j < in_bin; ++j) {
-                    const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)j);
-                    gt += u > v ? 1u : 0u;
-                    eq += u == v ? 1u : 0u;
-                }
-                // the need-th largest of the gathered keys: gt < need <= gt + eq
-                if (lane < (int)in_bin && gt < need && need <= gt + eq) {
-                    // when every key equal to v is taken, "above v - 1" says the same
-                    const bool all = need == gt + eq;
-                    sm.few_pick[0] = all ? v - 1u : v;
-                    sm.few_pick[1] = all ? 0u : need - gt;
-                }
-            }
-            __syncthreads();
-            pk.T = sm.few_pick[0];
-            pk.need = sm.few_pick[1];
-            return pk;
-        }
-    }
-    // every key left equals lo
-    pk.T = need == live ? lo - 1u : lo;
-    pk.need = need == live ? 0u : need;
-    return pk;
-}
-
-// Exclusive scan, in position order, of the 16 * P (slot, wave) counts
-// part[] in place by one wave (P / 4 per lane); returns the total on every lane.
-template <int P>
-__device__ __forceinline__ uint32_t scan_parts(uint32_t* part, int lane)
-{
-    constexpr int kN = P * kNumWaves / kWave;
-    static_assert(kN >= 1 && kN * kWave == P * kNumWaves, "slots per thread: a multiple of 4");
-    uint32_t c[kN], sum = 0;
-#pragma unroll
-    for (int j = 0; j < kN; ++j) {
-        c[j] = part[kN * lane + j];
-        sum += c[j];
-    }
-    const uint32_t incl = wave_prefix_sum(sum, lane);
-    uint32_t run = incl - sum;
-#pragma unroll
-    for (int j = 0; j < kN; ++j) {
-        part[kN * lane + j] = run;
-        run += c[j];
-    }
-    return (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-}
-
-// Marks the chosen slots and their output offsets (position order); returns
-// how many were chosen.  pk.need == 0 (every key equal to the threshold is
-// taken, or there is none) needs only the "above" ballots.
-template <int P>
-__device__ uint32_t place(const uint32_t (&key)[P], Pick pk, bool (&take)[P],
-                          uint32_t (&off)[P], Smem& sm, int lane, int wave)
-{
-    if (pk.need == 0u) {
-        uint32_t gt_below[P];
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            const uint64_t bg = __ballot(key[i] > pk.T);
-            gt_below[i] = lanes_below(bg, lane);
-            if (lane == 0)
-                sm.part_gt[i * kNumWaves + wave] = (uint32_t)__popcll(bg);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const uint32_t all = scan_parts<P>(sm.part_gt, lane);
-            if (lane == 0)
-                sm.totals[0] = all;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            take[i] = key[i] > pk.T;
-            off[i] = sm.part_gt[i * kNumWaves + wave] + gt_below[i];
-        }
-        const uint32_t n_gt = sm.totals[0];
-        __syncthreads();
-        return n_gt;
-    }
-    uint32_t gt_below[P], eq_below[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const uint64_t bg = __ballot(key[i] > pk.T);
-        const uint64_t be = __ballot(key[i] == pk.T);
-        gt_below[i] = lanes_below(bg, lane);
-        eq_below[i] = lanes_below(be, lane);
-        if (lane == 0) {
-            sm.part_gt[i * kNumWaves + wave] = (uint32_t)__popcll(bg);
-            sm.part_eq[i * kNumWaves + wave] = (uint32_t)__popcll(be);
-        }
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const uint32_t all = scan_parts<P>(wave == 0 ? sm.part_gt : sm.part_eq, lane);
-        if (lane == 0)
-            sm.totals[wave] = all;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const uint32_t gt_before = sm.part_gt[i * kNumWaves + wave] + gt_below[i];
-        const uint32_t eq_before = sm.part_eq[i * kNumWaves + wave] + eq_below[i];
-        take[i] = key[i] > pk.T || (key[i] == pk.T && eq_before < pk.need);
-        off[i] = gt_before + (eq_before < pk.need ? eq_before : pk.need);
-    }
-    const uint32_t n_gt = sm.totals[0], n_eq = sm.totals[1];
-    __syncthreads();
-    return n_gt + (n_eq < pk.need ? n_eq : pk.need);
+    return sel::place<P, kThreads>(key, pk, take, off, sm, lane, wave);
 }
 
 template <int P>
@@ -375,8 +148,7 @@ topk_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, in
     const int64_t nv = valid_prefix(n_valid, row, L, valid_div);
     const int64_t seg_start = seg * seg_len;
     const int64_t seg_end = seg_start + seg_len < nv ? seg_start + seg_len : nv;
-    for (int b = tid; b < kBins; b += kThreads)
-        sm.hist[0][b] = 0u;
+    sel::clear_hist(sm, tid);
 
     uint32_t key[P];
     int32_t id[P];
@@ -479,35 +251,28 @@ struct GroupSmem {
     uint32_t chosen_groups[kTopkSegment / 2];  // k <= 16384 / g with g >= 2
 };
 
-// Grouped select for one row from its group maxima gkey[row, 0..ngroups)
-// (ngroups <= 16384, g * k <= 16384).  Grid: rows.  kG: the group size when
-// known at compile time (8: L up to 131072 with k <= 2048), else 0.
+// Grouped select of one row from its group maxima grow[0..ngroups) (ngroups
+// <= 16384, g * k <= 16384) into out[0..k): the k best groups by their
+// largest key, then the k best of those groups' g*k entries.  srow / irow:
+// the row's keys and indices (irow null = positions), nv its valid prefix.
+// kG: the group size when known at compile time (8: L up to 131072 with k <=
+// 2048), else 0 (g_runtime).  Expects gs.sm.hist[0] cleared.
 template <int kG>
-__global__ void __launch_bounds__(kThreads)
-topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
-                    int32_t g_runtime, int64_t ngroups, const uint32_t* __restrict__ gkey,
-                    const int32_t* __restrict__ n_valid, int32_t valid_div, int32_t k,
-                    int32_t* __restrict__ out)
+__device__ void grouped_select_row(const float* __restrict__ srow,
+                                   const int32_t* __restrict__ irow, int64_t nv,
+                                   int32_t g_runtime, int64_t ngroups,
+                                   const uint32_t* __restrict__ grow, int32_t k,
+                                   int32_t* __restrict__ out, GroupSmem& gs, int tid, int lane,
+                                   int wave)
 {
-    __shared__ GroupSmem gs;
     Smem& sm = gs.sm;
     const uint32_t g = kG > 0 ? (uint32_t)kG : (uint32_t)g_runtime;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int64_t row = blockIdx.x;
-    const int64_t nv = valid_prefix(n_valid, row, L, valid_div);
-    const float* srow = score + row * L;
-    const int32_t* irow = idx != nullptr ? idx + row * L : nullptr;
-    for (int b = tid; b < kBins; b += kThreads)
-        sm.hist[0][b] = 0u;
-
     uint32_t key[kPer];
     int32_t id[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int64_t grp = (int64_t)kThreads * i + tid;
-        key[i] = grp < ngroups ? gkey[row * ngroups + grp] : 0u;
+        key[i] = grp < ngroups ? grow[grp] : 0u;
         id[i] = (int32_t)grp;
     }
     Pick pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
@@ -519,8 +284,7 @@ topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__
     for (int i = 0; i < kPer; ++i)
         if (take[i] && off[i] < (uint32_t)k)
             gs.chosen_groups[off[i]] = (uint32_t)id[i];
-    for (int b = tid; b < kBins; b += kThreads)
-        sm.hist[0][b] = 0u;
+    sel::clear_hist(sm, tid);
     __syncthreads();
     const uint32_t n_chosen = chosen < (uint32_t)k ? chosen : (uint32_t)k;
     // candidate c*g + r is entry r of the c-th chosen group: position order.
@@ -564,7 +328,154 @@ topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__
     }
     pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
     chosen = place(key, pk, take, off, sm, lane, wave);
-    write_result(take, off, key, id, chosen, k, tid, out + row * k, nullptr, nullptr);
+    write_result(take, off, key, id, chosen, k, tid, out, nullptr, nullptr);
+}
+
+// Grouped select for one row from its group maxima gkey[row, 0..ngroups)
+// (ngroups <= 16384, g * k <= 16384).  Grid: rows.
+template <int kG>
+__global__ void __launch_bounds__(kThreads)
+topk_grouped_kernel(const float* __restrict__ score, const int32_t* __restrict__ idx, int64_t L,
+                    int32_t g_runtime, int64_t ngroups, const uint32_t* __restrict__ gkey,
+                    const int32_t* __restrict__ n_valid, int32_t valid_div, int32_t k,
+                    int32_t* __restrict__ out)
+{
+    __shared__ GroupSmem gs;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t nv = valid_prefix(n_valid, row, L, valid_div);
+    sel::clear_hist(gs.sm, tid);
+    grouped_select_row<kG>(score + row * L, idx != nullptr ? idx + row * L : nullptr, nv,
+                           g_runtime, ngroups, gkey + row * ngroups, k, out + row * k, gs, tid,
+                           lane, wave);
+}
+
+// ------------------------------------------------------------ block select
+//
+// Pool (top-nb blocks) and top-k blocks of one row in one workgroup ([N] 2.2,
+// [A] 3.4: the pool holds the 2048 blocks with the largest block scores; the
+// Full layer's top-k entries lie in its top-k blocks).  Keys come either
+// straight from the row's block maxima (rows of at most 16384 blocks), or
+// from the candidate lists the scan wrote: each scan chunk's kl best blocks
+// in block order, plus a flag telling whether the chunk had more than kl
+// valid blocks.
+//
+// The candidates' top-t (t = nb or k) is the row's top-t unless some chunk
+// left blocks out that could outrank the t-th chosen candidate.  A chunk's
+// left-out blocks all rank below its own lowest-ranked candidate u; if fewer
+// than kl of the chunk's candidates are chosen, u is not chosen and so ranks
+// below the t-th chosen candidate, as do the left-out blocks.  So the
+// selection is exact unless a full chunk has all kl candidates chosen; then
+// (rare on score-like data: a chunk holds about t / chunks of the winners,
+// kl is at least twice that) the row falls back to the exact grouped select
+// over the group maxima the scan also wrote.
+struct BlockSelJob {
+    const float* block_max;   // [rows, L] block maxima (fp32)
+    int64_t L;                // block slots per row
+    const int32_t* n_visible; // [rows] visible entries (valid blocks: ceil(n / 8))
+    const uint32_t* gkey;     // [rows, ngroups] group maxima (order keys), groups of g
+    int64_t ngroups;
+    int32_t g;
+    const uint32_t* cand_key; // [rows, chunks, kl] or null: the direct form
+    const int32_t* cand_blk;
+    const int32_t* cand_full; // [rows, chunks]
+    int32_t chunks, kl;
+    int32_t nb, k;            // targets (0: not wanted)
+    int32_t* pool;            // [rows, nb] ascending block ids, -1 padded
+    int32_t* sel;             // [rows, k]
+};
+
+struct BlockSelSmem {
+    GroupSmem gs;
+    uint32_t chunk_taken[kTopkSegment / 64];  // chosen candidates per chunk (kl >= 64)
+    uint32_t invalid;
+};
+
+// Grid: rows x 2 -- workgroup 2r selects row r's top-k blocks (what the Full
+// layer's own top-k waits for), workgroup 2r + 1 its pool, side by side.
+template <int P>
+__global__ void __launch_bounds__(kThreads)
+block_select_kernel(BlockSelJob J)
+{
+    __shared__ BlockSelSmem bs;
+    Smem& sm = bs.gs.sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t row = blockIdx.x / 2;
+    const int pass = blockIdx.x % 2;
+    const int32_t t = pass == 0 ? J.k : J.nb;
+    int32_t* out = pass == 0 ? J.sel : J.pool;
+    if (t <= 0 || out == nullptr)
+        return;
+    int64_t nvb = J.n_visible[row];
+    nvb = nvb < 0 ? 0 : (nvb + kBlock - 1) / kBlock;
+    nvb = nvb > J.L ? J.L : nvb;
+
+    uint32_t key[P];
+    int32_t id[P];
+    if (J.cand_key != nullptr) {
+        const int64_t n = (int64_t)J.chunks * J.kl;
+        const uint32_t* ck = J.cand_key + row * n;
+        const int32_t* cb = J.cand_blk + row * n;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int64_t e = (int64_t)kThreads * i + tid;
+            key[i] = e < n ? ck[e] : 0u;
+            id[i] = e < n ? cb[e] : -1;
+        }
+    } else {
+        const float* srow = J.block_max + row * J.L;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int64_t e = (int64_t)kThreads * i + tid;
+            const float f = J.L > 0 ? srow[e < nvb ? e : 0] : 0.0f;  // no block maxima when L == 0
+            key[i] = e < nvb && !__builtin_isnan(f) ? order_key(f) : 0u;
+            id[i] = (int32_t)e;
+        }
+    }
+    {
+        out += row * t;
+        sel::clear_hist(sm, tid);
+        const Pick pk = find_threshold(key, (uint32_t)t, sm, tid, lane, wave);
+        bool take[P];
+        uint32_t off[P];
+        const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
+        bool fallback = false;
+        if (J.cand_key != nullptr) {
+            for (int c = tid; c < J.chunks; c += kThreads)
+                bs.chunk_taken[c] = 0u;
+            if (tid == 0)
+                bs.invalid = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < P; ++i)
+                if (take[i])
+                    atomicAdd(&bs.chunk_taken[(kThreads * i + tid) / J.kl], 1u);
+            __syncthreads();
+            const int64_t frow = row * J.chunks;
+            for (int c = tid; c < J.chunks; c += kThreads)
+                if (J.cand_full[frow + c] != 0 && bs.chunk_taken[c] >= (uint32_t)J.kl)
+                    bs.invalid = 1u;
+            __syncthreads();
+            fallback = bs.invalid != 0u;
+        }
+        if (!fallback) {
+            write_result(take, off, key, id, chosen, t, tid, out, nullptr, nullptr);
+            return;
+        } else {
+            // exact: the grouped select over the row's group maxima
+            sel::clear_hist(sm, tid);
+            if (J.g == 8)
+                grouped_select_row<8>(J.block_max + row * J.L, nullptr, nvb, J.g, J.ngroups,
+                                      J.gkey + row * J.ngroups, t, out, bs.gs, tid, lane, wave);
+            else
+                grouped_select_row<0>(J.block_max + row * J.L, nullptr, nvb, J.g, J.ngroups,
+                                      J.gkey + row * J.ngroups, t, out, bs.gs, tid, lane, wave);
+        }
+    }
 }
 
 int64_t segments(int64_t L)
@@ -597,6 +508,27 @@ size_t topk_workspace(int64_t L, int32_t rows, int32_t k)
 int32_t topk_group_size(int64_t L, int32_t k)
 {
     return group_size(L, k);
+}
+
+hipError_t launch_block_select(const float* block_max, int64_t L, int32_t rows,
+                               const int32_t* n_visible, const uint32_t* gkey, int32_t g,
+                               const uint32_t* cand_key, const int32_t* cand_blk,
+                               const int32_t* cand_full, int32_t chunks, int32_t kl, int32_t nb,
+                               int32_t k, int32_t* pool, int32_t* sel, hipStream_t stream)
+{
+    if (rows == 0)
+        return hipSuccess;
+    BlockSelJob J{block_max, L, n_visible, gkey, g > 0 ? (L + g - 1) / g : 0, g,
+                  cand_key, cand_blk, cand_full, chunks, kl, nb, k, pool, sel};
+    const int64_t n = cand_key != nullptr ? (int64_t)chunks * kl : L;
+    const dim3 grid((uint32_t)(2 * rows)), block(kThreads);
+    if (n <= 4 * kThreads)
+        block_select_kernel<4><<<grid, block, 0, stream>>>(J);
+    else if (n <= 8 * kThreads)
+        block_select_kernel<8><<<grid, block, 0, stream>>>(J);
+    else
+        block_select_kernel<kPer><<<grid, block, 0, stream>>>(J);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_t rows,

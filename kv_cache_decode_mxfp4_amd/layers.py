@@ -12,11 +12,10 @@ notes, [A] 3.3-3.4 of the translated abstract):
 How the Full layer's top-k is found: its top-k entries always lie in its
 top-k blocks (a block ranked above a winner's block holds another winner,
 also under the lower-index tie-break), so the scan keeps only block maxima,
-the block select picks max(nb, k) ranked blocks, and the winners are
-selected among those blocks' rescored positions.  With nb >= k the pool
-itself is that block set, which makes a Full layer "block scan + pool +
-Reindex with its own query".  Every step is a libcsa2 kernel; this module
-only sequences calls and owns reusable buffers.
+one call selects both the pool (top-nb blocks) and the top-k blocks, and the
+winners are selected among the top-k blocks' rescored positions (k * 8 of
+them).  Every step is a libcsa2 kernel; this module only sequences calls and
+owns reusable buffers.
 """
 from __future__ import annotations
 
@@ -50,6 +49,7 @@ class Buffers:
     lse: torch.Tensor
     ws_topk: torch.Tensor | None
     ws_attn: torch.Tensor | None
+    ws_sel: torch.Tensor | None
 
     @staticmethod
     def create(B: int, nq: int, n_cap: int, k: int, nb: int, n_win: int,
@@ -58,11 +58,11 @@ class Buffers:
         nblk = (n_cap + BLOCK - 1) // BLOCK
         pool = torch.empty(B, nq, nb, dtype=i32, device=device) if nb > 0 else None
         nsel = max(nb, k)
-        sel = pool if (pool is not None and nb >= k) else torch.empty(B, nq, k, dtype=i32,
-                                                                        device=device)
+        sel = torch.empty(B, nq, k, dtype=i32, device=device)  # the top-k blocks
         ws_t = max(_lib.topk_workspace(nblk, B * nq, nsel), _lib.topk_workspace(nsel * BLOCK, B * nq, k),
                    _lib.topk_workspace(nblk, B * nq, k))
         ws_a = _lib.sparse_attn_workspace(B, nq, k, n_win)
+        ws_s = _lib.index_full_select_workspace(n_cap, B, nq, nb, k)
         return Buffers(
             block_max=torch.empty(B, nq, nblk, dtype=f32, device=device),
             pool=pool,
@@ -74,36 +74,40 @@ class Buffers:
             lse=torch.empty(B, nq, 64, dtype=f32, device=device),
             ws_topk=torch.empty(ws_t, dtype=torch.uint8, device=device) if ws_t else None,
             ws_attn=torch.empty(ws_a, dtype=torch.uint8, device=device) if ws_a else None,
+            ws_sel=torch.empty(ws_s, dtype=torch.uint8, device=device) if ws_s else None,
         )
 
 
 def select_blocks(buf: Buffers, n_blocks_valid: torch.Tensor, k: int, nb: int, stream=None):
-    """Pool (top-nb blocks) and, when nb < k, the top-k blocks that hold the top-k entries."""
+    """Pool (top-nb blocks) and the top-k blocks that hold the top-k entries, as two
+    csa2_topk calls over the block maxima."""
     if nb > 0:
         _lib.topk(buf.block_max, nb, buf.pool, n_valid=n_blocks_valid, ws=buf.ws_topk,
                   stream=stream)
-    if buf.sel_blocks is not buf.pool:
-        _lib.topk(buf.block_max, k, buf.sel_blocks, n_valid=n_blocks_valid, ws=buf.ws_topk,
-                  stream=stream)
+    _lib.topk(buf.block_max, k, buf.sel_blocks, n_valid=n_blocks_valid, ws=buf.ws_topk,
+              stream=stream)
 
 
 def full_indexer(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, n_blocks_valid,
-                 k: int, nb: int, scores=None, stream=None):
+                 k: int, nb: int, scores=None, stream=None, scan_events=None):
     """Full layer indexer: block scan, pool, top-k.  Leaves buf.pool and buf.topk.
 
-    With a pool of at least k blocks (and no per-entry scores asked for) the scan and
-    the pool select are one library call, whose scan also writes the select's group
-    maxima."""
-    if nb >= k and nb > 0 and scores is None:
-        _lib.index_full_pool(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, buf.pool,
-                             ws=buf.ws_topk, stream=stream)
+    The scan, the pool and the top-k blocks are one library call (csa2_index_full_select);
+    with per-entry scores asked for (tests), the scan and two csa2_topk calls instead."""
+    if scores is None:
+        _lib.index_full_select(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max,
+                               buf.sel_blocks, pool=buf.pool, ws=buf.ws_sel, stream=stream,
+                               scan_events=scan_events)
     else:
         _lib.index_full(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, scores=scores,
                         stream=stream)
         select_blocks(buf, n_blocks_valid, k, nb, stream=stream)
-    _lib.index_pool(q_idx, w_idx, k_codes, k_scales, buf.sel_blocks, n_visible, buf.pool_score,
-                    buf.pool_idx, stream=stream)
-    _lib.topk(buf.pool_score, k, buf.topk, idx=buf.pool_idx, ws=buf.ws_topk, stream=stream)
+    B, nq, _ = buf.sel_blocks.shape
+    score = _slots(buf.pool_score, B, nq, k * BLOCK)
+    idx = _slots(buf.pool_idx, B, nq, k * BLOCK)
+    _lib.index_pool(q_idx, w_idx, k_codes, k_scales, buf.sel_blocks, n_visible, score, idx,
+                    stream=stream)
+    _lib.topk(score, k, buf.topk, idx=idx, ws=buf.ws_topk, stream=stream)
 
 
 def _slots(t: torch.Tensor, B: int, nq: int, L: int) -> torch.Tensor:

@@ -1,0 +1,113 @@
+"""csa2_index_full_select (the Full-layer scan with its pool and top-k blocks in one
+call) against the same scan followed by two csa2_topk calls over its block maxima:
+bit-exact pools and top-k blocks, on shapes that take each of its paths -- the direct
+select (rows of at most 16384 blocks), the scan's per-chunk candidates, their exact
+fallback (a chunk holding more winners than it listed: a planted cluster of strong
+keys, and exact ties from a zero query or a periodic cache), and two csa2_topk calls
+(rows too long for the candidates) -- with ragged, empty and stale-workspace rows.
+csa2_topk itself is checked against the oracle's selection in test_gpu_stages.py."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_harness import cdiv, dev, t
+
+pytestmark = pytest.mark.gpu
+
+kv = pytest.importorskip("kv_cache_decode_mxfp4_amd")
+L = kv._lib
+
+STRONG = 0x77  # code byte: both nibbles +6; as a scale byte: E4M3 240
+
+
+def _caches(B, n_cap, seed, kind):
+    g = torch.Generator(device=dev())
+    g.manual_seed(seed)
+    codes = torch.randint(0, 256, (B, n_cap, 64), dtype=torch.uint8, device=dev(), generator=g)
+    scales = (torch.randint(0, 256, (B, n_cap, 8), dtype=torch.uint8, device=dev(), generator=g)
+              & 0x77) | 0x30  # finite E4M3 scales
+    if kind == "cluster":
+        # 300 blocks of the strongest key in a row: more winners in one scan chunk than
+        # it lists as candidates
+        a = n_cap // 3 // 8 * 8
+        codes[0, a:a + 2400] = STRONG
+        scales[0, a:a + 2400] = STRONG
+    elif kind == "periodic":
+        # every key repeats 4096 entries later: exact score ties across blocks
+        for b in range(B):
+            base = codes[b, :4096].clone(), scales[b, :4096].clone()
+            for s in range(4096, n_cap, 4096):
+                n = min(4096, n_cap - s)
+                codes[b, s:s + n] = base[0][:n]
+                scales[b, s:s + n] = base[1][:n]
+    # the library's tiled indexer-key layout: byte j of entry f at
+    # (f // 32) * 2048 + (j // 16) * 512 + (f % 32) * 16 + j % 16
+    flat = codes.reshape(-1, 64)
+    n = flat.shape[0]
+    tiles = cdiv(n, 32)
+    pad = torch.zeros((tiles * 32, 64), dtype=torch.uint8, device=dev())
+    pad[:n] = flat
+    kc = pad.reshape(tiles, 32, 4, 16).permute(0, 2, 1, 3).contiguous().reshape(-1)
+    return kc, scales
+
+
+CASES = [
+    # (B, nq, n_cap, nb, k, n_visible, kind)
+    (16, 1, 1 << 20, 2048, 512, None, "random"),                  # the 1M decode shape: candidates
+    (8, 1, 262144, 2048, 512, None, "random"),                    # groups of 2: candidates
+    (8, 1, 262144, 2048, 512, [262144, 200001, 131073, 131072, 70000, 9, 0, 262143], "random"),
+    (4, 1, 262144, 2048, 512, None, "cluster"),                   # fallback in row 0
+    (4, 1, 262144, 2048, 512, None, "zero_query"),                # all ties: fallback
+    (4, 1, 262144, 2048, 512, None, "periodic"),                  # exact ties across blocks
+    (16, 1, 1 << 20, 2048, 512, None, "periodic"),
+    (2, 1, 140003, 2048, 512, [140003, 70001], "random"),          # too many chunks: two top-k calls
+    (3, 1, 65536, 2048, 512, [65536, 40001, 3], "random"),         # direct select
+    (1, 4, 300000, 2048, 512, [300000, 299999, 150000, 5], "random"),  # paired scan rows
+    (2, 1, 2048, 32, 64, [2048, 1000], "random"),                 # pool smaller than k
+    (2, 1, 262144, 0, 512, None, "random"),                       # no pool
+    (1, 1, 0, 2048, 512, [5], "random"),                          # empty cache
+]
+
+
+@pytest.mark.parametrize("B,nq,n_cap,nb,k,nvis,kind", CASES)
+def test_index_full_select_matches_scan_then_topk(B, nq, n_cap, nb, k, nvis, kind):
+    print(f"[case] B={B} nq={nq} n_cap={n_cap} nb={nb} k={k} kind={kind}", flush=True)
+    kc, ks = _caches(B, n_cap, seed=n_cap + nb + len(kind), kind=kind)
+    q = synth.normal_bf16(synth.key(21, 1, 0, 0), 0, B * nq * 4096, 1 / np.sqrt(128)).reshape(B, nq, 32, 128)
+    if kind == "zero_query":
+        q[:] = 0
+    w = synth.uniform_f32(synth.key(21, 2, 0, 0), 0, B * nq * 32).reshape(B, nq, 32)
+    nv = np.full((B, nq), n_cap, np.int32) if nvis is None else np.array(nvis, np.int32).reshape(B, nq)
+    nblk = cdiv(n_cap, 8)
+    qd, wd, nvd = t(q, torch.uint16), t(w), t(nv)
+
+    ws_n = L.index_full_select_workspace(n_cap, B, nq, nb, k)
+    ws = torch.full((max(ws_n, 256),), 0xC3, dtype=torch.uint8, device=dev())  # stale contents
+    bm1 = torch.full((B, nq, max(nblk, 1)), 777.0, device=dev())
+    pool1 = torch.full((B, nq, max(nb, 1)), -7, dtype=torch.int32, device=dev())
+    sel1 = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
+    for rep in range(2):  # the second call finds the first call's workspace contents
+        L.index_full_select(qd, wd, kc, ks, nvd, bm1, sel1, pool=pool1 if nb else None, ws=ws)
+    torch.cuda.synchronize()
+
+    bm2 = torch.full((B, nq, max(nblk, 1)), 777.0, device=dev())
+    if n_cap:
+        L.index_full(qd, wd, kc, ks, nvd, bm2)
+    nvb = t(((np.maximum(nv.astype(np.int64), 0) + 7) // 8).astype(np.int32))
+    tw = torch.empty(max(L.topk_workspace(nblk, B * nq, max(nb, k)), 8), dtype=torch.uint8,
+                     device=dev())
+    sel2 = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
+    L.topk(bm2[..., :nblk], k, sel2, n_valid=nvb, ws=tw)
+    assert np.array_equal(bm1.cpu().numpy()[..., :nblk], bm2.cpu().numpy()[..., :nblk])
+    assert np.array_equal(sel1.cpu().numpy(), sel2.cpu().numpy()), "top-k blocks differ"
+    if nb:
+        pool2 = torch.full((B, nq, nb), -7, dtype=torch.int32, device=dev())
+        L.topk(bm2[..., :nblk], nb, pool2, n_valid=nvb, ws=tw)
+        assert np.array_equal(pool1.cpu().numpy(), pool2.cpu().numpy()), "pools differ"
+    # the k best blocks lie in the pool when the pool has at least k blocks
+    if nb >= k:
+        p, s = pool1.cpu().numpy(), sel1.cpu().numpy()
+        for r in range(B * nq):
+            sr = s.reshape(-1, k)[r]
+            assert set(sr[sr >= 0]) <= set(p.reshape(-1, nb)[r])
