@@ -1,9 +1,12 @@
 """ctypes binding of libcsa2.so: argument marshalling only.
 
-Each function takes torch tensors that live on the GPU, checks dtype, device,
-shape and contiguity, and forwards raw pointers to the C entry point of the
-same name in include/csa2.h on the current torch stream.  All computation
-happens in the library's HIP kernels; a missing library raises.
+Each function takes torch tensors that live on the GPU, checks every tensor's
+dtype and element count against the shape include/csa2.h documents for it
+(inputs and outputs alike, before any pointer is taken), then device and
+contiguity, and forwards raw pointers to the C entry point of the same name on
+the current torch stream.  An undersized tensor raises here, so the library
+never writes past a buffer it was handed.  All computation happens in the
+library's HIP kernels; a missing library raises.
 """
 from __future__ import annotations
 
@@ -24,7 +27,8 @@ EXPORTS = ("csa2_last_error", "csa2_version", "csa2_quantize_kv", "csa2_quantize
            "csa2_index_full", "csa2_index_full_pool", "csa2_index_full_pool_workspace",
            "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
            "csa2_sparse_attn", "csa2_sparse_attn_workspace", "csa2_sparse_attn_rope_bf16",
-           "csa2_encode_entries", "csa2_topk_noalloc", "csa2_stream_read")
+           "csa2_encode_entries", "csa2_topk_noalloc", "csa2_stream_read",
+           "csa2_index_full_select", "csa2_index_full_select_workspace")
 
 
 class Csa2Error(RuntimeError):
@@ -63,6 +67,11 @@ def load() -> ctypes.CDLL:
                                        vp, vp, vp]
     L.csa2_index_full_pool_workspace.restype = sz
     L.csa2_index_full_pool_workspace.argtypes = [i64, i32, i32]
+    L.csa2_index_full_select.restype = st
+    L.csa2_index_full_select.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp,
+                                         vp, vp, sz, vp, vp, vp]
+    L.csa2_index_full_select_workspace.restype = sz
+    L.csa2_index_full_select_workspace.argtypes = [i64, i32, i32, i32, i32]
     L.csa2_index_pool.restype = st
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i32, i32, vp, vp, vp]
     L.csa2_topk.restype = st
@@ -114,6 +123,22 @@ def _stream(stream):
     return s.cuda_stream
 
 
+_BF16 = (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def _need(t, dtype, numel, name, optional=False):
+    """t must have the dtype (a tuple: any of them) and at least `numel` elements."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: required")
+    ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+    if not ok:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+
+
 def _bf16_bits(t):
     """bf16 tensors are passed as their bit patterns (uint16 or int16 views accepted)."""
     if t.dtype == torch.bfloat16:
@@ -158,6 +183,8 @@ def quantize_kv(x, codes, scales, rope_cos=None, rope_sin=None, rope_offset=0, r
     rows, C = x.shape
     _rows_fit(codes, C // 2, dst_row, dst_stride, rows, "codes", tiled=(C == 128))
     _rows_fit(scales, C // 16, dst_row, dst_stride, rows, "scales")
+    _need(rope_cos, torch.float32, rows * (rope_dim // 2), "rope_cos", optional=rope_dim == 0)
+    _need(rope_sin, torch.float32, rows * (rope_dim // 2), "rope_sin", optional=rope_dim == 0)
     _check("csa2_quantize_kv", load().csa2_quantize_kv(
         _p(x), rows, C, _p(rope_cos), _p(rope_sin), rope_offset, rope_dim,
         _p(codes), _p(scales), dst_row, dst_stride, _stream(stream)))
@@ -192,10 +219,14 @@ def encode_entries(kv_x, kv_codes, kv_scales, idx_codes, idx_scales, idx_x=None,
     kv_cap = min(kv_codes.numel() // 256, kv_scales.numel() // 32,
                  idx_codes.numel() // KEY_TILE_BYTES * KEY_TILE, idx_scales.numel() // 8)
     if kv_dst is not None:
-        _dt(kv_dst, torch.int64, "kv_dst")
+        _need(kv_dst, torch.int64, rows, "kv_dst")
         dst_row = 0
-    if idx_x is not None:
-        _dt(idx_x, torch.float32, "idx_x")
+    _need(kv_x, torch.float32, rows * 512, "kv_x")
+    _need(rope_cos, torch.float32, rows * (rope_dim // 2), "rope_cos", optional=rope_dim == 0)
+    _need(rope_sin, torch.float32, rows * (rope_dim // 2), "rope_sin", optional=rope_dim == 0)
+    _need(idx_x, torch.float32, rows * 128, "idx_x", optional=True)
+    _need(w_idx, _BF16, 128 * 512, "w_idx", optional=True)
+    _need(idx_y, torch.float32, rows * 128, "idx_y", optional=True)
     if w_idx is not None:
         w_idx = _bf16_bits(w_idx)
     n_sw = 0
@@ -203,10 +234,11 @@ def encode_entries(kv_x, kv_codes, kv_scales, idx_codes, idx_scales, idx_x=None,
         _dt(swa_x, torch.float32, "swa_x")
         _dt(swa_out, torch.uint8, "swa_out")
         n_sw = swa_x.shape[0]
+        _need(swa_x, torch.float32, n_sw * 512, "swa_x")
         if swa_dst is None:
             _rows_fit(swa_out, 512, swa_row, swa_stride, n_sw, "swa_out")
         else:
-            _dt(swa_dst, torch.int64, "swa_dst")
+            _need(swa_dst, torch.int64, n_sw, "swa_dst")
             swa_row = 0
     swa_cap = swa_out.numel() // 512 if swa_out is not None else 0
     _check("csa2_encode_entries", load().csa2_encode_entries(
@@ -231,12 +263,23 @@ def _key_cache_rows(k_codes, k_scales, B) -> int:
     return n_cap
 
 
-def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block=8, stream=None):
-    q = _bf16_bits(q)
-    _dt(w, torch.float32, "w")
-    _dt(n_visible, torch.int32, "n_visible")
+def _indexer_inputs(q, w, k_codes, k_scales, n_visible):
+    """(B, nq, n_cap) of an indexer call after checking q [B, nq, 32, 128] bf16, w
+    [B, nq, 32] fp32, n_visible [B, nq] int32 and the key cache."""
+    if q.dim() != 4 or q.shape[2:] != (32, 128):
+        raise ValueError(f"q: expected [B, nq, 32, 128], got {tuple(q.shape)}")
     B, nq = q.shape[0], q.shape[1]
-    n_cap = _key_cache_rows(k_codes, k_scales, B)
+    _need(q, _BF16, B * nq * 4096, "q")
+    _need(w, torch.float32, B * nq * 32, "w")
+    _need(n_visible, torch.int32, B * nq, "n_visible")
+    return B, nq, _key_cache_rows(k_codes, k_scales, B)
+
+
+def index_full(q, w, k_codes, k_scales, n_visible, block_max, scores=None, block=8, stream=None):
+    B, nq, n_cap = _indexer_inputs(q, w, k_codes, k_scales, n_visible)
+    _need(block_max, torch.float32, B * nq * (-(-n_cap // 8)), "block_max", optional=n_cap == 0)
+    _need(scores, torch.float32, B * nq * n_cap, "scores", optional=True)
+    q = _bf16_bits(q)
     _check("csa2_index_full", load().csa2_index_full(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block,
         _p(block_max), _p(scores), _stream(stream)))
@@ -252,13 +295,12 @@ def index_full_pool(q, w, k_codes, k_scales, n_visible, block_max, pool, ws=None
     = the nb best blocks in ascending order (what topk over block_max returns).
     scan_events: optional (start, stop) torch.cuda.Event pair (timing enabled, already
     created by one record) that the scan kernel's dispatch records."""
-    q = _bf16_bits(q)
-    _dt(w, torch.float32, "w")
-    _dt(n_visible, torch.int32, "n_visible")
-    _dt(pool, torch.int32, "pool")
-    B, nq = q.shape[0], q.shape[1]
-    n_cap = _key_cache_rows(k_codes, k_scales, B)
+    B, nq, n_cap = _indexer_inputs(q, w, k_codes, k_scales, n_visible)
     nb = pool.shape[-1]
+    _need(pool, torch.int32, B * nq * nb, "pool")
+    _need(block_max, torch.float32, B * nq * (-(-n_cap // 8)), "block_max", optional=n_cap == 0)
+    _need(ws, torch.uint8, 0, "ws", optional=True)
+    q = _bf16_bits(q)
     _check("csa2_index_full_pool", load().csa2_index_full_pool(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block, nb,
         _p(block_max), _p(pool), _p(ws), ws.numel() if ws is not None else 0,
@@ -266,12 +308,39 @@ def index_full_pool(q, w, k_codes, k_scales, n_visible, block_max, pool, ws=None
         scan_events[1].cuda_event if scan_events else None, _stream(stream)))
 
 
+def index_full_select_workspace(n_cap, B, nq, nb, k) -> int:
+    return int(load().csa2_index_full_select_workspace(n_cap, B, nq, nb, k))
+
+
+def index_full_select(q, w, k_codes, k_scales, n_visible, block_max, topk_blocks, pool=None,
+                      ws=None, block=8, scan_events=None, stream=None):
+    """Full-layer scan, pool (top-nb blocks, nb = pool.shape[-1], or none) and the top-k
+    blocks (k = topk_blocks.shape[-1]) in one call; ws: uint8 device workspace of
+    index_full_select_workspace(...) bytes, 256-byte aligned."""
+    B, nq, n_cap = _indexer_inputs(q, w, k_codes, k_scales, n_visible)
+    nb = pool.shape[-1] if pool is not None else 0
+    k = topk_blocks.shape[-1]
+    _need(topk_blocks, torch.int32, B * nq * k, "topk_blocks")
+    _need(pool, torch.int32, B * nq * nb, "pool", optional=True)
+    _need(block_max, torch.float32, B * nq * (-(-n_cap // 8)), "block_max", optional=n_cap == 0)
+    _need(ws, torch.uint8, 0, "ws", optional=True)
+    q = _bf16_bits(q)
+    _check("csa2_index_full_select", load().csa2_index_full_select(
+        _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block, nb, k,
+        _p(block_max), _p(pool), _p(topk_blocks), _p(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0,
+        scan_events[0].cuda_event if scan_events else None,
+        scan_events[1].cuda_event if scan_events else None, _stream(stream)))
+
+
 def index_pool(q, w, k_codes, k_scales, blocks, n_visible, pool_score, pool_idx, block=8,
                stream=None):
+    B, nq, n_cap = _indexer_inputs(q, w, k_codes, k_scales, n_visible)
+    nbk = blocks.shape[-1]
+    _need(blocks, torch.int32, B * nq * nbk, "blocks")
+    _need(pool_score, torch.float32, B * nq * nbk * block, "pool_score")
+    _need(pool_idx, torch.int32, B * nq * nbk * block, "pool_idx")
     q = _bf16_bits(q)
-    _dt(blocks, torch.int32, "blocks")
-    B, nq = q.shape[0], q.shape[1]
-    n_cap = _key_cache_rows(k_codes, k_scales, B)
     _check("csa2_index_pool", load().csa2_index_pool(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(blocks), blocks.shape[-1], block,
         _p(n_visible), B, nq, _p(pool_score), _p(pool_idx), _stream(stream)))
@@ -281,11 +350,18 @@ def topk_workspace(L, rows, k) -> int:
     return int(load().csa2_topk_workspace(L, rows, k))
 
 
-def topk(score, k, out, idx=None, n_valid=None, ws=None, stream=None):
+def _topk_args(score, k, out, idx, n_valid):
     _dt(score, torch.float32, "score")
-    _dt(out, torch.int32, "out")
     L = score.shape[-1]
     rows = math.prod(score.shape[:-1])  # also for L == 0 (every row then all -1)
+    _need(out, torch.int32, rows * k, "out")
+    _need(idx, torch.int32, rows * L, "idx", optional=True)
+    _need(n_valid, torch.int32, rows, "n_valid", optional=True)
+    return L, rows
+
+
+def topk(score, k, out, idx=None, n_valid=None, ws=None, stream=None):
+    L, rows = _topk_args(score, k, out, idx, n_valid)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("csa2_topk", load().csa2_topk(
         _p(score), _p(idx), L, rows, _p(n_valid), k, _p(out), _p(ws), ws_bytes,
@@ -294,16 +370,14 @@ def topk(score, k, out, idx=None, n_valid=None, ws=None, stream=None):
 
 def topk_noalloc(score, k, out, idx=None, n_valid=None, stream=None):
     """csa2_topk with the library's static device workspace (no workspace argument)."""
-    _dt(score, torch.float32, "score")
-    _dt(out, torch.int32, "out")
-    L = score.shape[-1]
-    rows = math.prod(score.shape[:-1])
+    L, rows = _topk_args(score, k, out, idx, n_valid)
     _check("csa2_topk_noalloc", load().csa2_topk_noalloc(
         _p(score), _p(idx), L, rows, _p(n_valid), k, _p(out), _stream(stream)))
 
 
 def stream_read(src, workgroups, depth, sink, stream=None):
     """Streaming read of every byte of src (calibration); sink int32/uint32 [workgroups]."""
+    _need(sink, (torch.int32, torch.uint32), workgroups, "sink")
     nbytes = src.numel() * src.element_size()
     _check("csa2_stream_read", load().csa2_stream_read(
         _p(src), nbytes, workgroups, depth, _p(sink), _stream(stream)))
@@ -313,14 +387,35 @@ def sparse_attn_workspace(B, nq, k, n_win) -> int:
     return int(load().csa2_sparse_attn_workspace(B, nq, k, n_win))
 
 
+def _attn_inputs(q, kv_codes, kv_scales, topk_idx, swa, swa_end, lse):
+    """(B, nq, n_cap, k) of an attention call after checking q [B, nq, 64, 512] bf16,
+    kv_codes [B, n_cap, 256] u8, kv_scales [B, n_cap, 32] u8, topk [B, nq, k] int32,
+    swa [B, swa_cap, 512] u8, swa_end [B, nq] int32 and lse [B, nq, 64] fp32."""
+    if q.dim() != 4 or q.shape[2:] != (64, 512):
+        raise ValueError(f"q: expected [B, nq, 64, 512], got {tuple(q.shape)}")
+    B, nq = q.shape[0], q.shape[1]
+    _need(q, _BF16, B * nq * 64 * 512, "q")
+    if kv_codes.dim() != 3 or kv_codes.shape[0] != B or kv_codes.shape[2] != 256:
+        raise ValueError(f"kv_codes: expected [{B}, n_cap, 256], got {tuple(kv_codes.shape)}")
+    n_cap = kv_codes.shape[1]
+    _need(kv_codes, torch.uint8, B * n_cap * 256, "kv_codes")
+    _need(kv_scales, torch.uint8, B * n_cap * 32, "kv_scales")
+    k = topk_idx.shape[-1]
+    _need(topk_idx, torch.int32, B * nq * k, "topk")
+    if swa.dim() != 3 or swa.shape[0] != B or swa.shape[2] != 512:
+        raise ValueError(f"swa: expected [{B}, swa_cap, 512], got {tuple(swa.shape)}")
+    _need(swa, torch.uint8, swa.numel(), "swa")
+    _need(swa_end, torch.int32, B * nq, "swa_end")
+    _need(lse, torch.float32, B * nq * 64, "lse", optional=True)
+    return B, nq, n_cap, k
+
+
 def sparse_attn(q, kv_codes, kv_scales, topk_idx, swa, swa_end, out, lse=None, n_win=128,
                 softmax_scale=1.0, ws=None, stream=None):
+    B, nq, n_cap, k = _attn_inputs(q, kv_codes, kv_scales, topk_idx, swa, swa_end, lse)
+    _need(out, torch.float32, B * nq * 64 * 512, "out")
+    _need(ws, torch.uint8, 0, "ws", optional=True)
     q = _bf16_bits(q)
-    _dt(topk_idx, torch.int32, "topk")
-    _dt(out, torch.float32, "out")
-    B, nq = q.shape[0], q.shape[1]
-    n_cap = kv_codes.shape[1]
-    k = topk_idx.shape[-1]
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("csa2_sparse_attn", load().csa2_sparse_attn(
         _p(q), B, nq, _p(kv_codes), _p(kv_scales), n_cap, _p(topk_idx), k, _p(swa),
@@ -332,12 +427,13 @@ def sparse_attn_rope_bf16(q, kv_codes, kv_scales, topk_idx, swa, swa_end, rope_c
                           out, lse=None, n_win=128, softmax_scale=1.0, rope_offset=448,
                           rope_dim=64, ws=None, stream=None):
     """Attention with the inverse-rotary + bf16 epilogue; out is bf16 (or its uint16 bits)."""
+    B, nq, n_cap, k = _attn_inputs(q, kv_codes, kv_scales, topk_idx, swa, swa_end, lse)
+    _need(out, _BF16, B * nq * 64 * 512, "out")
+    _need(rope_cos, torch.float32, B * nq * (rope_dim // 2), "rope_cos", optional=rope_dim == 0)
+    _need(rope_sin, torch.float32, B * nq * (rope_dim // 2), "rope_sin", optional=rope_dim == 0)
+    _need(ws, torch.uint8, 0, "ws", optional=True)
     q = _bf16_bits(q)
-    _dt(topk_idx, torch.int32, "topk")
     out = _bf16_bits(out)
-    B, nq = q.shape[0], q.shape[1]
-    n_cap = kv_codes.shape[1]
-    k = topk_idx.shape[-1]
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("csa2_sparse_attn_rope_bf16", load().csa2_sparse_attn_rope_bf16(
         _p(q), B, nq, _p(kv_codes), _p(kv_scales), n_cap, _p(topk_idx), k, _p(swa),

@@ -215,3 +215,62 @@ def test_topk_noalloc_rejects_workspace_above_static_size():
     assert st == 3 and "static" in msg
     st, msg = _status("csa2_topk_noalloc", vp, None, 100, 1, None, 0, vp, None)
     assert st == 2
+
+
+def test_bindings_reject_undersized_or_mistyped_tensors_before_any_call():
+    """Every binding checks each tensor's dtype and element count against the shape
+    include/csa2.h documents, before it takes a pointer: an undersized output raises
+    here instead of becoming an out-of-bounds device write.  (CPU tensors: the checks
+    fail before the device check would.)"""
+    import torch
+    u8, i32, f32, bf = torch.uint8, torch.int32, torch.float32, torch.bfloat16
+    B, nq, n_cap, k, nb = 2, 1, 4096, 64, 32
+    q = torch.zeros(B, nq, 32, 128, dtype=bf)
+    w = torch.zeros(B, nq, 32, dtype=f32)
+    kc = torch.zeros(L.key_code_bytes(B * n_cap), dtype=u8)
+    ks = torch.zeros(B, n_cap, 8, dtype=u8)
+    nv = torch.zeros(B, nq, dtype=i32)
+    bm = torch.zeros(B, nq, n_cap // 8, dtype=f32)
+
+    def expect(fn, *a, match="elements", **kw):
+        with pytest.raises((ValueError, TypeError), match=match):
+            fn(*a, **kw)
+
+    expect(L.index_full, q, w, kc, ks, nv, bm[:, :, :-1].contiguous())          # block maxima
+    expect(L.index_full, q, w, kc, ks, nv, bm, scores=torch.zeros(B * n_cap - 1))
+    expect(L.index_full, q, w[:1].contiguous(), kc, ks, nv, bm)                   # weights
+    expect(L.index_full, q, w, kc, ks, nv.to(torch.int64), bm, match="int32")
+    sel = torch.zeros(B, nq, k, dtype=i32)
+    expect(L.index_full_select, q, w, kc, ks, nv, bm, sel[:1].contiguous())
+    expect(L.index_full_select, q, w, kc, ks, nv, bm, sel,
+           pool=torch.zeros(B - 1, nq, nb, dtype=i32))
+    blocks = torch.zeros(B, nq, nb, dtype=i32)
+    ps, pi = torch.zeros(B, nq, nb * 8, dtype=f32), torch.zeros(B, nq, nb * 8, dtype=i32)
+    expect(L.index_pool, q, w, kc, ks, blocks, nv, ps[:, :, :-1].contiguous(), pi)
+    expect(L.index_pool, q, w, kc, ks, blocks, nv, ps, pi[:, :, :-1].contiguous())
+    expect(L.index_pool, q, w, kc, ks, blocks, nv[:1].contiguous(), ps, pi)
+    sc = torch.zeros(3, 100, dtype=f32)
+    expect(L.topk, sc, 10, torch.zeros(3, 9, dtype=i32))                          # out
+    expect(L.topk, sc, 10, torch.zeros(3, 10, dtype=i32), idx=torch.zeros(3, 99, dtype=i32))
+    expect(L.topk, sc, 10, torch.zeros(3, 10, dtype=i32), n_valid=torch.zeros(2, dtype=i32))
+    expect(L.topk_noalloc, sc, 10, torch.zeros(3, 10, dtype=torch.int64), match="int32")
+    qm = torch.zeros(B, nq, 64, 512, dtype=bf)
+    vc, vs = torch.zeros(B, n_cap, 256, dtype=u8), torch.zeros(B, n_cap, 32, dtype=u8)
+    tk = torch.zeros(B, nq, k, dtype=i32)
+    sw, se = torch.zeros(B, 128, 512, dtype=u8), torch.zeros(B, nq, dtype=i32)
+    out = torch.zeros(B, nq, 64, 512, dtype=f32)
+    expect(L.sparse_attn, qm, vc, vs, tk, sw, se, out[:1].contiguous())
+    expect(L.sparse_attn, qm, vc, vs, tk, sw, se, out, lse=torch.zeros(B * nq * 64 - 1))
+    expect(L.sparse_attn, qm, vc, vs[:, :-1].contiguous(), tk, sw, se, out)
+    expect(L.sparse_attn, qm, vc, vs, tk, sw, se[:, :0].contiguous(), out)
+    expect(L.sparse_attn_rope_bf16, qm, vc, vs, tk, sw, se, torch.zeros(B * nq, 31),
+           torch.zeros(B * nq, 32), torch.zeros(B, nq, 64, 512, dtype=bf))        # rotary table
+    expect(L.sparse_attn_rope_bf16, qm, vc, vs, tk, sw, se, torch.zeros(B * nq, 32),
+           torch.zeros(B * nq, 32), torch.zeros(B, nq, 64, 511, dtype=bf))
+    x = torch.zeros(4, 512, dtype=f32)
+    expect(L.encode_entries, x, vc.view(-1, 256), vs.view(-1, 32), kc, ks.view(-1, 8),
+           idx_x=torch.zeros(3, 128), kv_dst=torch.zeros(4, dtype=torch.int64))
+    expect(L.encode_entries, x, vc.view(-1, 256), vs.view(-1, 32), kc, ks.view(-1, 8),
+           idx_x=torch.zeros(4, 128), kv_dst=torch.zeros(3, dtype=torch.int64))
+    expect(L.quantize_kv, x, vc.view(-1), vs.view(-1), torch.zeros(4, 31), torch.zeros(4, 32),
+           448, 64)
