@@ -282,6 +282,32 @@ csa2_status csa2_index_pool(const uint16_t* q, const float* w,
                             float* pool_score, int32_t* pool_idx, void* stream);
 
 /*
+ * Pool rescoring and its top-k in one call ([N] 2.2, [A] 3.4: Reindex layers
+ * score only the pool with their own query and keep its top-k; the Full layer
+ * does the same over its top-k blocks).  Exactly csa2_index_pool followed by
+ * csa2_topk(pool_score, k, idx = pool_idx) into topk [B, nq, k] (ascending
+ * positions, -1 padded), bit for bit, without the per-slot scores as an
+ * output.  Arguments as csa2_index_pool, plus
+ *   n_blocks   0 <= n_blocks <= 2048 (at most 16384 rescored positions).
+ *   k          1 <= k <= 8192.
+ *   ws, ws_bytes  device workspace of csa2_index_pool_topk_workspace(B, nq,
+ *              n_blocks) bytes, 256-byte aligned.  Its first bytes are one
+ *              arrival counter per query row: the workspace must be
+ *              zero-filled once before its first use (e.g. when it is
+ *              allocated); every call leaves the counters zero again, so the
+ *              same workspace serves any later call.  Calls that share a
+ *              workspace must not overlap in time.
+ * One launch: every workgroup scores its slots and stores them to the
+ * workspace; the last workgroup of a row to finish selects the row's top-k.
+ */
+size_t      csa2_index_pool_topk_workspace(int32_t B, int32_t nq, int32_t n_blocks);
+csa2_status csa2_index_pool_topk(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                                 const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
+                                 int32_t n_blocks, int32_t block, const int32_t* n_visible,
+                                 int32_t B, int32_t nq, int32_t k, int32_t* topk, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
  * Top-k select ([N] 1: top-k 512; [N] 2.2 / [A] 3.4: top-2048 blocks).
  *   score    fp32 [rows, L].
  *   idx      int32 [rows, L] or NULL (= 0..L-1).  Entries with idx < 0, NaN
@@ -337,9 +363,8 @@ csa2_status csa2_topk_noalloc(const float* score, const int32_t* idx, int64_t L,
  *              only for few query rows) each row's keys are split over several
  *              workgroups whose partial results are merged by a second launch;
  *              with NULL or fewer bytes the call still completes, with one
- *              workgroup per (row, 16 heads, 128 output dims) instead.  The
- *              result is deterministic for a given choice; the two differ only
- *              in fp32 rounding order.
+ *              workgroup per (row, 16 heads) over every key.  Each form is
+ *              deterministic; the two differ only in fp32 rounding order.
  * Dequantisation is exact in fp16; products accumulate in fp32.
  */
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq,

@@ -28,7 +28,8 @@ EXPORTS = ("csa2_last_error", "csa2_version", "csa2_quantize_kv", "csa2_quantize
            "csa2_index_pool", "csa2_topk", "csa2_topk_workspace",
            "csa2_sparse_attn", "csa2_sparse_attn_workspace", "csa2_sparse_attn_rope_bf16",
            "csa2_encode_entries", "csa2_topk_noalloc", "csa2_stream_read",
-           "csa2_index_full_select", "csa2_index_full_select_workspace")
+           "csa2_index_full_select", "csa2_index_full_select_workspace",
+           "csa2_index_pool_topk", "csa2_index_pool_topk_workspace")
 
 
 class Csa2Error(RuntimeError):
@@ -72,6 +73,11 @@ def load() -> ctypes.CDLL:
                                          vp, vp, sz, vp, vp, vp]
     L.csa2_index_full_select_workspace.restype = sz
     L.csa2_index_full_select_workspace.argtypes = [i64, i32, i32, i32, i32]
+    L.csa2_index_pool_topk.restype = st
+    L.csa2_index_pool_topk.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i32, i32, i32, vp,
+                                       vp, sz, vp]
+    L.csa2_index_pool_topk_workspace.restype = sz
+    L.csa2_index_pool_topk_workspace.argtypes = [i32, i32, i32]
     L.csa2_index_pool.restype = st
     L.csa2_index_pool.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i32, i32, vp, vp, vp]
     L.csa2_topk.restype = st
@@ -344,6 +350,26 @@ def index_pool(q, w, k_codes, k_scales, blocks, n_visible, pool_score, pool_idx,
     _check("csa2_index_pool", load().csa2_index_pool(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(blocks), blocks.shape[-1], block,
         _p(n_visible), B, nq, _p(pool_score), _p(pool_idx), _stream(stream)))
+
+
+def index_pool_topk_workspace(B, nq, n_blocks) -> int:
+    return int(load().csa2_index_pool_topk_workspace(B, nq, n_blocks))
+
+
+def index_pool_topk(q, w, k_codes, k_scales, blocks, n_visible, out, ws, block=8, stream=None):
+    """Pool rescoring and its top-k in one call: out [B, nq, k] = topk(index_pool(blocks)).
+    ws: uint8 device workspace of index_pool_topk_workspace(B, nq, n_blocks) bytes, zeroed
+    once before its first use (every call leaves its counters zero)."""
+    B, nq, n_cap = _indexer_inputs(q, w, k_codes, k_scales, n_visible)
+    nbk = blocks.shape[-1]
+    k = out.shape[-1]
+    _need(blocks, torch.int32, B * nq * nbk, "blocks")
+    _need(out, torch.int32, B * nq * k, "out")
+    _need(ws, torch.uint8, index_pool_topk_workspace(B, nq, nbk), "ws")
+    q = _bf16_bits(q)
+    _check("csa2_index_pool_topk", load().csa2_index_pool_topk(
+        _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(blocks), nbk, block, _p(n_visible),
+        B, nq, k, _p(out), _p(ws), ws.numel(), _stream(stream)))
 
 
 def topk_workspace(L, rows, k) -> int:

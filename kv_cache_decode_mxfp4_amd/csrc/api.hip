@@ -398,6 +398,42 @@ csa2_status csa2_index_pool(const uint16_t* q, const float* w, const uint8_t* k_
                   s, "index_pool");
 }
 
+size_t csa2_index_pool_topk_workspace(int32_t B, int32_t nq, int32_t n_blocks)
+{
+    if (B < 0 || nq < 0 || n_blocks < 0 || n_blocks > csa2::kTopkSegment / csa2::kBlock)
+        return 0;
+    return csa2::pool_topk_workspace(B * nq, n_blocks);
+}
+
+csa2_status csa2_index_pool_topk(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                                 const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
+                                 int32_t n_blocks, int32_t block, const int32_t* n_visible,
+                                 int32_t B, int32_t nq, int32_t k, int32_t* topk, void* ws,
+                                 size_t ws_bytes, void* stream)
+{
+    csa2_status st = check_indexer("index_pool_topk", q, w, k_codes, k_scales, n_cap, n_visible,
+                                   B, nq, block);
+    if (st != CSA2_OK)
+        return st;
+    REQUIRE(n_blocks >= 0 && n_blocks <= csa2::kTopkSegment / csa2::kBlock, CSA2_ERR_UNSUPPORTED,
+            "index_pool_topk: n_blocks must be in [0, %d]", csa2::kTopkSegment / csa2::kBlock);
+    REQUIRE(k >= 1 && k <= csa2::kTopkMaxK, CSA2_ERR_UNSUPPORTED,
+            "index_pool_topk: k must be in [1, %d]", csa2::kTopkMaxK);
+    if ((int64_t)B * nq == 0)
+        return CSA2_OK;
+    REQUIRE(topk != nullptr && (n_blocks == 0 || blocks != nullptr), CSA2_ERR_INVALID_ARG,
+            "index_pool_topk: null pointer");
+    const size_t need = csa2::pool_topk_workspace(B * nq, n_blocks);
+    REQUIRE(ws != nullptr && ws_bytes >= need, CSA2_ERR_WORKSPACE,
+            "index_pool_topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    REQUIRE(aligned(ws, 256), CSA2_ERR_INVALID_ARG,
+            "index_pool_topk: workspace must be 256-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(csa2::launch_pool_topk(q, w, k_codes, k_scales, n_cap, blocks, n_blocks,
+                                         n_visible, B, nq, k, topk, ws, s),
+                  s, "index_pool_topk");
+}
+
 size_t csa2_topk_workspace(int64_t L, int32_t rows, int32_t k)
 {
     if (L < 0 || rows < 0 || k < 1 || k > csa2::kTopkMaxK)

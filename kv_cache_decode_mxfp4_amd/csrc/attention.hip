@@ -4,40 +4,25 @@
 // 512-dim latent, top-k compressed entries plus 128 window entries).  One
 // joint softmax over both key sets; no de-duplication; no sink.
 //
-// Two decompositions of the same computation, picked by the number of query
-// rows (both: tiles of 32 keys, MFMA v_mfma_f32_16x16x32_f16, keys dequantised
-// exactly to fp16 straight into the MFMA operand and stored row-major to an
-// LDS tile (K = V), online softmax in the log2 domain, P split into two fp16
-// terms (hi + lo) so P V keeps ~22 bits of P):
-//
-// Spread (few rows, decode: 16 rows fill the 256 CUs): one workgroup per
-// (query row, group of 16 heads, slice of 128 output dims), 16 workgroups per
-// row, so a row's work is spread over 16 CUs and nothing is combined across
-// workgroups.  Each workgroup scores its 16 heads against the full 512
-// channels of every key (the four slices of a head group repeat that work, the
-// price of the spread).  Wave w of 8 takes every eighth tile and keeps its own
-// softmax state, with no barrier inside the loop; the waves meet in LDS at the
-// end and are merged in wave order.
-//   S^T[32 keys x 16 heads] = K Q^T: lane l holds key l%16 of each block of 16
-//     keys and the 128 channels [128G, 128G+128) of its lane group G = l/16
-//     (k-step t: channels 128G + 8t .. +8, the same on the Q^T operand, read
-//     from LDS); the lanes whose G is the output slice also store their 128
-//     channels to the wave's LDS tile.
-//
-// Grouped (many rows, prefill): one workgroup per (query row, group of 16
-// heads), 4 workgroups per row; the four waves walk the same tiles and wave w
+// The computation runs in one decomposition (tiles of 32 keys, MFMA
+// v_mfma_f32_16x16x32_f16, keys dequantised exactly to fp16 straight into the
+// MFMA operand and stored row-major to an LDS tile (K = V), online softmax in
+// the log2 domain, P split into two fp16 terms (hi + lo) so P V keeps ~22
+// bits of P): one workgroup per (query row, group of 16 heads), 4 workgroups
+// per row -- for few rows (decode) also split over the keys, the splits merged
+// by a second, short kernel; for many rows, two head groups per workgroup from
+// 512 rows.  The four waves of a workgroup walk the same tiles and wave w
 // owns the channels [128w, 128w+128): it dequantises only those channels of
 // each key, forms the partial scores over them and accumulates the output for
 // those 128 dims, so each key is dequantised once per head group and no score
-// or output is computed twice (about a quarter of the spread form's
-// dequantisation and half its MFMA work per row).
+// or output is computed twice.
 //   partial S^T over the wave's channels: lane l holds key l%16 and the 32
 //     channels [128w + 32G, +32) (k-step t: 128w + 32G + 8t .. +8; the Q^T
 //     operand stays in registers); the four partials meet in LDS (one barrier
 //     per tile) and every wave adds them in wave order, so all four hold
 //     bit-identical scores and softmax state.
 //
-// Common to both:
+// Operand layouts:
 //   P^T: the S^T accumulator of lane l holds keys 4G + r (r < 4) of both
 //     blocks for head l%16, which is the B-operand layout of P^T for
 //     O^T = V^T P^T once the 32 keys of a tile take MFMA k-index 8G + i <->
@@ -66,7 +51,6 @@ constexpr int kSlice = 128;                     // channels / output dims per sl
 constexpr int kSlices = kDim / kSlice;          // 4 slices
 constexpr int kVRow = kSlice + 16;              // halves per LDS row of V (288 B)
 constexpr int kXcds = 8;                        // MI355X dies: workgroups go round-robin
-constexpr int kCus = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -188,329 +172,6 @@ __device__ __forceinline__ uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
-// ============================================================== spread form
-
-constexpr int kSpreadWaves = 8;
-constexpr int kSpreadWgPerRow = kGroups * kSlices;  // 16 workgroups per query row
-constexpr int kQRow = kDim + 8;                     // halves per LDS row of Q (bank spread)
-constexpr int kChunkTiles = 2;                      // top-k tiles per wave loaded together
-
-struct SpreadSmem {
-    _Float16 q[kHg][kQRow];
-    union {
-        _Float16 v[kSpreadWaves][kTile][kVRow];
-        struct {
-            float o[kSpreadWaves][kHg][kSlice + 4];
-            float m[kSpreadWaves][kHg];
-            float l[kSpreadWaves][kHg];
-        } red;
-    } u;
-};
-
-// Raw bytes of one top-k tile for the calling lane: channels [128G, 128G+128)
-// of key l%16 of block b (64 code bytes, 8 scale bytes) and whether the key
-// is valid.
-struct MainRaw {
-    u32x4 c[2][4];
-    uint32_t s[2][2];
-    uint32_t valid;  // bit b: key of block b is valid
-};
-
-__device__ __forceinline__ half8 q_operand(const SpreadSmem& sm, int head, int G, int t)
-{
-    return *reinterpret_cast<const half8*>(&sm.q[head][kSlice * G + 8 * t]);
-}
-
-template <bool kRopeBf16>
-__global__ void __launch_bounds__(kSpreadWaves * kWave)
-attn_spread_kernel(const uint16_t* __restrict__ q, int32_t queries,
-                   const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
-                   int64_t n_cap, int32_t nq, const int32_t* __restrict__ topk, int32_t k,
-                   const uint8_t* __restrict__ swa, int32_t swa_cap,
-                   const int32_t* __restrict__ swa_end, int32_t n_win, float scale_log2,
-                   AttnOut dst_spec, float* __restrict__ lse)
-{
-    __shared__ SpreadSmem sm;
-    const int lane = threadIdx.x & 63;
-    // wave index as a scalar: everything derived from it (tile lists, counts,
-    // pointer choices) stays in scalar registers and branches
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int G = lane >> 4;
-    const int key16 = lane & 15;
-
-    // the 16 workgroups of a query row share one die (and its L2): with
-    // round-robin dispatch, workgroup x runs on die x % 8
-    const int64_t x = blockIdx.x;
-    const int64_t rest = x / kXcds;
-    const int64_t qrow = kXcds * (rest / kSpreadWgPerRow) + x % kXcds;
-    const int part = (int)(rest % kSpreadWgPerRow);
-    if (qrow >= queries)
-        return;
-    const int hg = part / kSlices;     // head group
-    const int slice = part % kSlices;  // output dims [128*slice, +128)
-    const int64_t b = qrow / nq;
-
-    // this wave's tiles: list positions wave + 8j over [top-k tiles, window
-    // tiles]; the top-k part does not depend on the window, so the index loads
-    // go out before the window's end is known
-    const int t_main = (k + kTile - 1) / kTile;
-    const int m_first = wave;
-    const int nm = (n_cap > 0 && m_first < t_main) ? (t_main - m_first + kSpreadWaves - 1) / kSpreadWaves : 0;
-
-    // loads that have no data to fetch (no top-k tile, no window tile for this
-    // wave) read the query row instead (64 KiB, always valid) and are masked,
-    // so every load is unconditional and the load counter stays exact
-    const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + qrow * kHeads * kDim);
-    const bool have_main = nm > 0;
-    const uint8_t* kc = have_main ? kv_codes + b * n_cap * (kDim / 2) : dummy;
-    const uint8_t* ks = have_main ? kv_scales + b * n_cap * (kDim / 16) : dummy;
-    const int32_t* tk = have_main ? topk + qrow * k : reinterpret_cast<const int32_t*>(dummy);
-
-    // index of this lane's key in block bb of main tile j of this wave (-1 if
-    // none); j is clamped to the wave's last tile so the load is always valid
-    auto load_idx = [&](int j, int32_t (&e)[2]) {
-        const int jj = j < nm ? j : nm - 1;
-        const int tile = m_first + kSpreadWaves * jj;
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int slot = tile * kTile + 16 * bb + key16;
-            e[bb] = tk[have_main ? (slot < k ? slot : k - 1) : 0];
-        }
-    };
-    // whether slot 16*bb + l%16 of main tile j of this wave is inside the list
-    auto in_list = [&](int j, int bb) {
-        const int jj = j < nm ? j : nm - 1;
-        return (m_first + kSpreadWaves * jj) * kTile + 16 * bb + key16 < k;
-    };
-    auto load_main = [&](int j, const int32_t (&e)[2], MainRaw& R) {
-        R.valid = 0;
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const bool ok = have_main && in_list(j, bb) && e[bb] >= 0 && e[bb] < n_cap;
-            const int64_t ee = ok ? e[bb] : 0;
-            const u32x4* c = reinterpret_cast<const u32x4*>(kc + ee * (kDim / 2) + 64 * G);
-            const uint32_t* s = reinterpret_cast<const uint32_t*>(ks + ee * (kDim / 16) + 8 * G);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                R.c[bb][i] = c[i];
-            R.s[bb][0] = s[0];
-            R.s[bb][1] = s[1];
-            R.valid |= ok ? (1u << bb) : 0u;
-        }
-    };
-
-    // ---- prologue: every load of the first top-k chunk and of the first window
-    // tile is issued before Q is staged, so their latencies overlap
-    int32_t e[kChunkTiles][2];
-    MainRaw R[kChunkTiles];
-#pragma unroll
-    for (int u = 0; u < kChunkTiles; ++u)
-        load_idx(u, e[u]);
-    // kQPer dims of one head per thread
-    constexpr int kQPer = kHg * kDim / (kSpreadWaves * kWave);
-    constexpr int kThreadsPerHead = kDim / kQPer;
-    const int qh = threadIdx.x / kThreadsPerHead;
-    const int qd0 = kQPer * (threadIdx.x % kThreadsPerHead);
-    uint4 qraw[kQPer / 8];
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(
-            q + (qrow * kHeads + kHg * hg + qh) * kDim + qd0);
-#pragma unroll
-        for (int i = 0; i < kQPer / 8; ++i)
-            qraw[i] = src[i];
-    }
-    // window rows [lo, hi); this wave's window tiles are sw_first + 8j
-    const int64_t end = swa_end[qrow];
-    int64_t lo = end - n_win;
-    lo = lo < 0 ? 0 : lo;
-    int64_t hi = end < swa_cap ? end : (int64_t)swa_cap;
-    hi = hi < lo ? lo : hi;
-    const int n_sw = (int)(hi - lo);
-    const int t_sw = (n_sw + kTile - 1) / kTile;
-    const int sw_first = ((wave - t_main) % kSpreadWaves + kSpreadWaves) % kSpreadWaves;
-    const uint8_t* sw = n_sw > 0 ? swa + b * (int64_t)swa_cap * kDim : dummy;
-    // window tile ts of this wave: raw FP8 bytes of key l%16 of both blocks
-    auto load_swa = [&](int ts, u32x4 (&raw)[2][8], uint32_t& valid) {
-        valid = 0;
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int64_t r = lo + ts * kTile + 16 * bb + key16;
-            const bool ok = ts < t_sw && r < hi;
-            const int64_t rr = ok ? r : (n_sw > 0 ? lo : 0);
-            const u32x4* c = reinterpret_cast<const u32x4*>(sw + rr * kDim + kSlice * G);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                raw[bb][i] = c[i];
-            valid |= ok ? (1u << bb) : 0u;
-        }
-    };
-    u32x4 swraw[2][8];
-    uint32_t swvalid = 0;
-    load_swa(sw_first, swraw, swvalid);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < kQPer / 8; ++i) {
-        const uint32_t d[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-        half8 v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[2 * j] = bf16_to_f16((uint16_t)(d[j] & 0xFFFFu));
-            v[2 * j + 1] = bf16_to_f16((uint16_t)(d[j] >> 16));
-        }
-        *reinterpret_cast<half8*>(&sm.q[qh][qd0 + 8 * i]) = v;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < kChunkTiles; ++u)
-        load_main(u, e[u], R[u]);
-    __syncthreads();
-
-    Online st;
-#pragma unroll
-    for (int db = 0; db < kSlice / 16; ++db)
-        st.o[db] = f32x4{};
-    _Float16* vtile = &sm.u.v[wave][0][0];
-    const bool writer = G == slice;
-
-    // ---- window tiles (FP8 rows, no scale)
-    for (int ts = sw_first; ts < t_sw; ts += kSpreadWaves) {
-        if (ts != sw_first)
-            load_swa(ts, swraw, swvalid);
-        const uint32_t valid = swvalid;
-        u32x4 (&raw)[2][8] = swraw;
-        f32x4 s[2];
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            f32x4 acc = {};
-            const bool ok = (valid >> bb) & 1u;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const uint32_t w0 = ok ? raw[bb][t / 2][2 * (t % 2)] : 0u;
-                const uint32_t w1 = ok ? raw[bb][t / 2][2 * (t % 2) + 1] : 0u;
-                const half4v x0 = e4m3x4_to_f16(w0), x1 = e4m3x4_to_f16(w1);
-                const half8 a = half8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                acc = mfma16(a, q_operand(sm, key16, G, t), acc);
-                if (writer)
-                    *reinterpret_cast<half8*>(vtile + (16 * bb + key16) * kVRow + 8 * t) = a;
-            }
-            s[bb] = acc;
-        }
-        scale_scores(s, valid, scale_log2, G);
-        fold_tile(st, s, vtile, lane);
-    }
-
-    // ---- top-k tiles, a chunk of kChunkTiles at a time (all loads of a chunk in flight together)
-    auto main_tile = [&](const MainRaw& R) {
-        f32x4 s[2];
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            f32x4 acc = {};
-            const bool ok = (R.valid >> bb) & 1u;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const uint32_t word = ok ? R.c[bb][t / 4][t % 4] : 0u;
-                const uint32_t sc = ok ? R.s[bb][t / 8] : 0u;
-                const half8 a = dequant8_fp4(word, e4m3_byte_to_f16(sc, (t / 2) % 4));
-                acc = mfma16(a, q_operand(sm, key16, G, t), acc);
-                if (writer)
-                    *reinterpret_cast<half8*>(vtile + (16 * bb + key16) * kVRow + 8 * t) = a;
-            }
-            s[bb] = acc;
-        }
-        scale_scores(s, R.valid, scale_log2, G);
-        fold_tile(st, s, vtile, lane);
-    };
-    for (int c = 0; c * kChunkTiles < nm; ++c) {
-        if (c > 0) {
-#pragma unroll
-            for (int u = 0; u < kChunkTiles; ++u)
-                load_idx(c * kChunkTiles + u, e[u]);
-#pragma unroll
-            for (int u = 0; u < kChunkTiles; ++u)
-                load_main(c * kChunkTiles + u, e[u], R[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < kChunkTiles; ++u)
-            if (c * kChunkTiles + u < nm)
-                main_tile(R[u]);
-    }
-
-    // ---- merge the waves in LDS (wave order), write the slice
-    __syncthreads();  // every wave is done with its V tile (aliased below)
-#pragma unroll
-    for (int db = 0; db < kSlice / 16; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sm.u.red.o[wave][key16][16 * db + 4 * G + r] = st.o[db][r];
-    if (G == 0) {
-        sm.u.red.m[wave][key16] = st.m;
-        sm.u.red.l[wave][key16] = st.l;
-    }
-    __syncthreads();
-    {
-        constexpr int kOPer = kHg * kSlice / (kSpreadWaves * kWave);  // dims per thread
-        constexpr int kThreadsPerHead = kSlice / kOPer;
-        const int t = threadIdx.x;
-        const int h = t / kThreadsPerHead;      // head within the group
-        const int d0 = kOPer * (t % kThreadsPerHead);
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kSpreadWaves; ++w)
-            M = fmaxf(M, sm.u.red.m[w][h]);
-        float f[kSpreadWaves];
-        float den = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kSpreadWaves; ++w) {
-            const float mw = sm.u.red.m[w][h];
-            f[w] = mw == -INFINITY ? 0.0f : exp2f(mw - M);
-            den += f[w] * sm.u.red.l[w][h];
-        }
-        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        float res[kOPer];
-#pragma unroll
-        for (int i = 0; i < kOPer; ++i) {
-            float num = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kSpreadWaves; ++w)
-                num += f[w] * sm.u.red.o[w][h][d0 + i];
-            res[i] = num * inv;
-        }
-        const int64_t o0 = (qrow * kHeads + kHg * hg + h) * kDim + kSlice * slice + d0;
-        if (!kRopeBf16) {
-            float4* dst = reinterpret_cast<float4*>(dst_spec.out + o0);
-#pragma unroll
-            for (int i = 0; i < kOPer / 4; ++i)
-                dst[i] = make_float4(res[4 * i], res[4 * i + 1], res[4 * i + 2], res[4 * i + 3]);
-        } else {
-            // rotate each rotary pair (a, b) back by the query's angle:
-            // a' = a*c + b*s, b' = b*c - a*s, every product and sum rounded to fp32
-            const int half = dst_spec.rope_dim / 2;
-#pragma unroll
-            for (int i = 0; i < kOPer; i += 2) {
-                const int d = kSlice * slice + d0 + i;
-                if (d >= dst_spec.rope_off && d < dst_spec.rope_off + dst_spec.rope_dim) {
-                    const int pi = (d - dst_spec.rope_off) / 2;
-                    const float c = dst_spec.cs[qrow * half + pi];
-                    const float sn = dst_spec.sn[qrow * half + pi];
-                    const float a = res[i], bb = res[i + 1];
-                    res[i] = __fadd_rn(__fmul_rn(a, c), __fmul_rn(bb, sn));
-                    res[i + 1] = __fsub_rn(__fmul_rn(bb, c), __fmul_rn(a, sn));
-                }
-            }
-            uint32_t packed[kOPer / 2];
-#pragma unroll
-            for (int i = 0; i < kOPer / 2; ++i)
-                packed[i] = (uint32_t)bf16_rne(res[2 * i]) | ((uint32_t)bf16_rne(res[2 * i + 1]) << 16);
-            uint2* dst = reinterpret_cast<uint2*>(dst_spec.out_bf16 + o0);
-#pragma unroll
-            for (int i = 0; i < kOPer / 4; ++i)
-                dst[i] = make_uint2(packed[2 * i], packed[2 * i + 1]);
-        }
-        if (lse != nullptr && slice == 0 && t % kThreadsPerHead == 0)
-            lse[qrow * kHeads + kHg * hg + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
-    }
-}
-
 // ============================================================= grouped form
 
 constexpr int kGroupWaves = kSlices;            // one wave per 128-channel slice
@@ -629,6 +290,99 @@ __device__ __forceinline__ void emit(const f32x4 (&o)[kSlice / 16], float inv, i
             *reinterpret_cast<uint2*>(dst.out_bf16 + base + 16 * db) = make_uint2(p0, p1);
         }
     }
+}
+
+constexpr int kBufferConfig = 0x00020000;  // raw (untyped) buffer, 32-bit data
+constexpr int kCachePolicy = 0;            // plain loads (the partials of the previous kernel)
+
+// The key-split partials of (row, head group): splits x kPartFloats floats.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float* part, int64_t qrow, int hg,
+                                                            int32_t splits)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(part + (qrow * kGroups + hg) * splits * kPartFloats,
+                                             0, splits * kPartFloats * 4, kBufferConfig);
+}
+
+// Merge of the key splits of one (row, head group) over one 128-dim slice, by
+// 256 threads: thread t takes head t/16 and the 8 dims 8*(t%16) .. +8 of the
+// slice.  Every split's (max, sum, 8 outputs) is loaded first (slots past
+// `splits` repeat the last split and are ignored), then they are combined in
+// split order (deterministic) and written through the epilogue.
+template <bool kRopeBf16>
+__device__ __forceinline__ void merge_slice(__amdgpu_buffer_rsrc_t rs, int32_t splits,
+                                            int64_t qrow, int hg, int slice, int t,
+                                            const AttnOut& dst, float* __restrict__ lse)
+{
+    const int h = t / 16;
+    const int d0 = kSlice * slice + 8 * (t % 16);
+    float ms[kMaxSplits], ls[kMaxSplits];
+    u32x4 va[kMaxSplits], vb[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        const int32_t ps = (s < splits ? s : splits - 1) * kPartFloats;
+        ms[s] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (ps + kHg * kDim + h), 0, kCachePolicy));
+        ls[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, 4 * (ps + kHg * kDim + kHg + h), 0, kCachePolicy));
+        va[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (ps + h * kDim + d0), 0, kCachePolicy);
+        vb[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (ps + h * kDim + d0 + 4), 0,
+                                                      kCachePolicy);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        M = s < splits ? fmaxf(M, ms[s]) : M;
+    float den = 0.0f;
+    float num[8] = {};
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        if (s < splits) {
+            const float f = ms[s] == -INFINITY ? 0.0f : exp2f(ms[s] - M);
+            den += f * ls[s];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                num[i] += f * __uint_as_float(va[s][i]);
+                num[4 + i] += f * __uint_as_float(vb[s][i]);
+            }
+        }
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    float res[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        res[i] = num[i] * inv;
+    const int head = kHg * hg + h;
+    const int64_t o0 = (qrow * kHeads + head) * kDim + d0;
+    if (!kRopeBf16) {
+        float4* o = reinterpret_cast<float4*>(dst.out + o0);
+        o[0] = make_float4(res[0], res[1], res[2], res[3]);
+        o[1] = make_float4(res[4], res[5], res[6], res[7]);
+    } else {
+        // rotate each rotary pair (a, b) back by the query's angle:
+        // a' = a*c + b*s, b' = b*c - a*s, every product and sum rounded to fp32
+        const int half = dst.rope_dim / 2;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            const int d = d0 + i;
+            if (d >= dst.rope_off && d < dst.rope_off + dst.rope_dim) {
+                const int pi = (d - dst.rope_off) / 2;
+                const float c = dst.cs[qrow * half + pi];
+                const float sn = dst.sn[qrow * half + pi];
+                const float a = res[i], bb = res[i + 1];
+                res[i] = __fadd_rn(__fmul_rn(a, c), __fmul_rn(bb, sn));
+                res[i + 1] = __fsub_rn(__fmul_rn(bb, c), __fmul_rn(a, sn));
+            }
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)bf16_rne(res[2 * i]) | ((uint32_t)bf16_rne(res[2 * i + 1]) << 16);
+        uint2* o = reinterpret_cast<uint2*>(dst.out_bf16 + o0);
+        o[0] = make_uint2(w[0], w[1]);
+        o[1] = make_uint2(w[2], w[3]);
+    }
+    if (lse != nullptr && slice == 0 && t % 16 == 0)
+        lse[qrow * kHeads + head] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
 }
 
 #ifndef CSA2_ATTN_WAVES_PER_EU
@@ -837,7 +591,7 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
         }
         return;
     }
-    // this split's unnormalised (O, max, sum) for attn_merge_kernel
+    // few rows: this split's unnormalised (O, max, sum) for attn_merge_kernel
 #pragma unroll
     for (int h = 0; h < kHgW; ++h) {
         float* mine = part + ((qrow * kGroups + hg0 + h) * splits + split) * kPartFloats;
@@ -853,15 +607,15 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
 }
 
 // Merge of the key splits of attn_group_kernel: one workgroup per (query row,
-// head group, 128-dim slice); thread t takes head t/16 and the 8 dims
-// 8*(t%16) .. +8 of the slice.  The splits are combined in split order
-// (deterministic), then written through the epilogue.
+// head group, 128-dim slice), on the die of the workgroups that wrote the
+// row's partials (the kernel boundary orders the partials: merging them inside
+// the attention kernel, by the last split to finish, measured slower -- one
+// workgroup then reads what 4 read here).
 template <bool kRopeBf16>
 __global__ void __launch_bounds__(256)
-attn_merge_kernel(const float* __restrict__ part, int32_t splits, int32_t queries,
-                  AttnOut dst, float* __restrict__ lse)
+attn_merge_kernel(float* __restrict__ part, int32_t splits, int32_t queries, AttnOut dst,
+                  float* __restrict__ lse)
 {
-    // the same die as the workgroups that wrote the partials of the row
     const int64_t x = blockIdx.x;
     const int64_t rest = x / kXcds;
     const int64_t qrow = kXcds * (rest / (kGroups * kSlices)) + x % kXcds;
@@ -869,75 +623,8 @@ attn_merge_kernel(const float* __restrict__ part, int32_t splits, int32_t querie
     const int slice = (int)(rest % (kGroups * kSlices)) % kSlices;
     if (qrow >= queries)
         return;
-    const int h = threadIdx.x / 16;
-    const int d0 = kSlice * slice + 8 * (threadIdx.x % 16);
-    const float* p0 = part + (qrow * kGroups + hg) * splits * kPartFloats;
-    // every split's (max, sum, 8 outputs) is loaded first (slots past `splits`
-    // repeat the last split and are ignored), then combined in split order
-    float ms[kMaxSplits], ls[kMaxSplits];
-    float4 va[kMaxSplits], vb[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        const float* ps = p0 + (s < splits ? s : splits - 1) * kPartFloats;
-        ms[s] = ps[kHg * kDim + h];
-        ls[s] = ps[kHg * kDim + kHg + h];
-        va[s] = *reinterpret_cast<const float4*>(ps + h * kDim + d0);
-        vb[s] = *reinterpret_cast<const float4*>(ps + h * kDim + d0 + 4);
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-        M = s < splits ? fmaxf(M, ms[s]) : M;
-    float den = 0.0f;
-    float num[8] = {};
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        if (s < splits) {
-            const float f = ms[s] == -INFINITY ? 0.0f : exp2f(ms[s] - M);
-            den += f * ls[s];
-            const float v[8] = {va[s].x, va[s].y, va[s].z, va[s].w, vb[s].x, vb[s].y, vb[s].z, vb[s].w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                num[i] += f * v[i];
-        }
-    }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    float res[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        res[i] = num[i] * inv;
-    const int head = kHg * hg + h;
-    const int64_t o0 = (qrow * kHeads + head) * kDim + d0;
-    if (!kRopeBf16) {
-        float4* o = reinterpret_cast<float4*>(dst.out + o0);
-        o[0] = make_float4(res[0], res[1], res[2], res[3]);
-        o[1] = make_float4(res[4], res[5], res[6], res[7]);
-    } else {
-        // rotate each rotary pair (a, b) back by the query's angle:
-        // a' = a*c + b*s, b' = b*c - a*s, every product and sum rounded to fp32
-        const int half = dst.rope_dim / 2;
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            const int d = d0 + i;
-            if (d >= dst.rope_off && d < dst.rope_off + dst.rope_dim) {
-                const int pi = (d - dst.rope_off) / 2;
-                const float c = dst.cs[qrow * half + pi];
-                const float sn = dst.sn[qrow * half + pi];
-                const float a = res[i], bb = res[i + 1];
-                res[i] = __fadd_rn(__fmul_rn(a, c), __fmul_rn(bb, sn));
-                res[i + 1] = __fsub_rn(__fmul_rn(bb, c), __fmul_rn(a, sn));
-            }
-        }
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)bf16_rne(res[2 * i]) | ((uint32_t)bf16_rne(res[2 * i + 1]) << 16);
-        uint2* o = reinterpret_cast<uint2*>(dst.out_bf16 + o0);
-        o[0] = make_uint2(w[0], w[1]);
-        o[1] = make_uint2(w[2], w[3]);
-    }
-    if (lse != nullptr && slice == 0 && threadIdx.x % 16 == 0)
-        lse[qrow * kHeads + head] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    merge_slice<kRopeBf16>(part_rsrc(part, qrow, hg, splits), splits, qrow, hg, slice,
+                           threadIdx.x, dst, lse);
 }
 
 int64_t padded_rows(int32_t queries)
@@ -987,18 +674,17 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
     const AttnOut spec{out, out_bf16, rope_cos, rope_sin, rope_off, rope_dim};
     const float scale_log2 = softmax_scale * kLog2e;
     const size_t need = attn_workspace(queries, k, n_win);
+    const dim3 block(kGroupWaves * kWave);
     if (need > 0 && ws != nullptr && ws_bytes >= need) {
-        // few rows: the grouped form with each row's keys split over workgroups,
-        // then the merge of the splits (a second launch: the kernel boundary
-        // orders the partials, with no cache maintenance inside the kernels)
+        // few rows: each row's keys split over workgroups, then the merge of the
+        // splits (a second launch: the kernel boundary orders the partials)
         const int32_t splits = attn_splits(queries, k, n_win);
         float* part = static_cast<float*>(ws);
-        const dim3 grid((uint32_t)(rows * (kGroups / kSplitHgW) * splits)),
-            block(kGroupWaves * kWave);
+        const dim3 grid((uint32_t)(rows * (kGroups / kSplitHgW) * splits));
         attn_group_kernel<false, kSplitHgW><<<grid, block, 0, stream>>>(
             q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end, n_win,
             scale_log2, splits, part, spec, lse);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
         const dim3 mgrid((uint32_t)(rows * kGroups * kSlices)), mblock(256);
@@ -1006,22 +692,10 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
             attn_merge_kernel<false><<<mgrid, mblock, 0, stream>>>(part, splits, queries, spec, lse);
         else
             attn_merge_kernel<true><<<mgrid, mblock, 0, stream>>>(part, splits, queries, spec, lse);
-    } else if (rows * kSpreadWgPerRow <= kCus) {
-        // few rows and no workspace: the spread form (one round of 16
-        // workgroups per row, nothing to combine)
-        const dim3 grid((uint32_t)(rows * kSpreadWgPerRow)), block(kSpreadWaves * kWave);
-        if (out_bf16 == nullptr)
-            attn_spread_kernel<false><<<grid, block, 0, stream>>>(
-                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
-                n_win, scale_log2, spec, lse);
-        else
-            attn_spread_kernel<true><<<grid, block, 0, stream>>>(
-                q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
-                n_win, scale_log2, spec, lse);
     } else if (queries >= kHg2MinRows) {
         // many rows: two head groups per workgroup (enough rows to fill the CUs
         // with half as many workgroups)
-        const dim3 grid((uint32_t)(rows * (kGroups / 2))), block(kGroupWaves * kWave);
+        const dim3 grid((uint32_t)(rows * (kGroups / 2)));
         if (out_bf16 == nullptr)
             attn_group_kernel<false, 2><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
@@ -1031,7 +705,9 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,
                 n_win, scale_log2, 1, nullptr, spec, lse);
     } else {
-        const dim3 grid((uint32_t)(rows * kGroups)), block(kGroupWaves * kWave);
+        // one workgroup per (row, head group) over every key (also the few-row form
+        // when no workspace is given)
+        const dim3 grid((uint32_t)(rows * kGroups));
         if (out_bf16 == nullptr)
             attn_group_kernel<false, 1><<<grid, block, 0, stream>>>(
                 q, queries, kv_codes, kv_scales, n_cap, nq, topk, k, swa, swa_cap, swa_end,

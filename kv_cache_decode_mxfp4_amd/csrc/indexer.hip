@@ -616,6 +616,133 @@ index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     }
 }
 
+// Pool rescoring and its top-k in one launch ([N] 2.2, [A] 3.4: the pool's
+// positions rescored with the layer's own query, then its top-k).  Workgroups
+// of 16 waves, kPtT tiles of 32 slots per wave, wgs_per_row workgroups per
+// row.  Every workgroup scores its slots exactly as index_pool_kernel (same
+// score function: bit-identical scores), stores (score, position) with
+// write-through stores (coherent at device scope without a cache flush),
+// waits for them, and counts itself in the row's arrival counter; the last
+// workgroup to arrive reads the row's slots back (device-coherent loads),
+// selects the top-k as csa2_topk does over (pool_score, pool_idx), writes it,
+// and returns the counter to zero for the next call.  Nothing waits on
+// another workgroup, so the kernel ends whatever the dispatch order.
+constexpr int kPtWaves = 16;
+constexpr int kPtThreads = kPtWaves * kWave;
+
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p)
+{
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct PoolTopkSmem {
+    sel::Smem<kPtThreads> sm;
+    uint32_t last;
+};
+
+template <int kPtT, int P>
+__global__ void __launch_bounds__(kPtThreads)
+pool_topk_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                 const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                 int64_t n_cap, const int32_t* __restrict__ blocks, int32_t n_blocks,
+                 const int32_t* __restrict__ n_visible, int32_t nq, int32_t wgs_per_row,
+                 int32_t k, int32_t* __restrict__ out, uint32_t* __restrict__ counters,
+                 uint32_t* __restrict__ ws_score, uint32_t* __restrict__ ws_idx)
+{
+    __shared__ PoolTopkSmem ps;
+    const int64_t row = blockIdx.x / wgs_per_row;
+    const int32_t part = blockIdx.x % wgs_per_row;
+    const int64_t b = row / nq;
+    int64_t n_vis = n_visible[row];
+    n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int64_t slots = (int64_t)n_blocks * kBlock;
+
+    // scoring, as index_pool_kernel (loads with nothing visible read the query row)
+    const uint8_t* qrow_bytes = reinterpret_cast<const uint8_t*>(q + row * (kIdxHeads * kIdxDim));
+    const uint8_t* kc = n_vis > 0 ? codes : qrow_bytes;
+    const uint8_t* ks = n_vis > 0 ? scales : qrow_bytes;
+    const int64_t f_seq = n_vis > 0 ? b * n_cap : 0;
+    const int32_t* blk = blocks + row * n_blocks;
+    const int64_t first = ((int64_t)part * kPtWaves + wave) * kPtT * kTileEntries;
+    int32_t bl[kPtT];
+#pragma unroll
+    for (int i = 0; i < kPtT; ++i) {
+        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        bl[i] = blk[(slot < slots ? slot : slots - 1) / kBlock];
+    }
+    int64_t pos[kPtT];
+    KeyTile K[kPtT];
+#pragma unroll
+    for (int i = 0; i < kPtT; ++i) {
+        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        const int64_t p = (int64_t)bl[i] * kBlock + slot % kBlock;
+        pos[i] = (slot < slots && bl[i] >= 0 && p < n_vis) ? p : -1;
+        load_key(kc, ks, f_seq + (pos[i] >= 0 ? pos[i] : 0), half, K[i]);
+    }
+    QueryOperand Q;
+    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
+    uint32_t* srow = ws_score + row * slots;
+    uint32_t* irow = ws_idx + row * slots;
+#pragma unroll
+    for (int i = 0; i < kPtT; ++i) {
+        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        if (slot - (lane & 31) >= slots)
+            break;
+        const float s = score_entry(Q, K[i]);
+        if (lane < 32 && slot < slots) {
+            store_coherent(srow + slot, __float_as_uint(pos[i] >= 0 ? s : -INFINITY));
+            store_coherent(irow + slot, (uint32_t)(int32_t)pos[i]);
+        }
+    }
+    // every store of this workgroup has completed before it counts itself
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0)
+        ps.last = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(wgs_per_row - 1);
+    __syncthreads();
+    if (ps.last == 0u)
+        return;
+    if (tid == 0)
+        store_coherent(counters + row, 0u);  // every workgroup of the row has arrived
+    __asm__ volatile("" ::: "memory");
+
+    // the last workgroup: top-k over the row's slots (csa2_topk's order and output)
+    uint32_t key[P];
+    int32_t id[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int64_t e = (int64_t)kPtThreads * i + tid;
+        const uint32_t sb = e < slots ? load_coherent(srow + e) : 0u;
+        const int32_t ix = e < slots ? (int32_t)load_coherent(irow + e) : -1;
+        const float f = __uint_as_float(sb);
+        id[i] = ix;
+        key[i] = ix >= 0 && !__builtin_isnan(f) ? order_key(f) : 0u;
+    }
+    sel::clear_hist(ps.sm, tid);
+    const sel::Pick pk = sel::find_threshold<P, kPtThreads>(key, (uint32_t)k, ps.sm, tid, lane, wave);
+    bool take[P];
+    uint32_t off[P];
+    const uint32_t chosen = sel::place<P, kPtThreads>(key, pk, take, off, ps.sm, lane, wave);
+    int32_t* orow = out + row * k;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        if (take[i] && off[i] < (uint32_t)k)
+            orow[off[i]] = id[i];
+    for (uint32_t p = chosen + tid; p < (uint32_t)k; p += kPtThreads)
+        orow[p] = -1;
+}
+
 template <typename T>
 struct same_type {
     using type = T;
@@ -717,6 +844,46 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
                        k_codes, k_scales, n_cap, n_visible, nq, chunk, (int32_t)chunks, nblk_cap,
                        block_max, scores, group_keys, gshift, ngroups, cand_key, cand_blk,
                        cand_full, kl);
+}
+
+size_t pool_topk_workspace(int32_t rows, int32_t n_blocks)
+{
+    const size_t slots = (size_t)n_blocks * kBlock;
+    const size_t cnt = ((size_t)rows * 4 + 255) / 256 * 256;
+    return cnt + 2 * (((size_t)rows * slots * 4 + 255) / 256 * 256);
+}
+
+hipError_t launch_pool_topk(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                            const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
+                            int32_t n_blocks, const int32_t* n_visible, int32_t B, int32_t nq,
+                            int32_t k, int32_t* out, void* ws, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)B * nq;
+    const int64_t slots = (int64_t)n_blocks * kBlock;
+    if (rows == 0)
+        return hipSuccess;
+    char* base = static_cast<char*>(ws);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(base);
+    const size_t cnt = ((size_t)rows * 4 + 255) / 256 * 256;
+    uint32_t* sc = reinterpret_cast<uint32_t*>(base + cnt);
+    uint32_t* ix = reinterpret_cast<uint32_t*>(base + cnt + ((size_t)rows * slots * 4 + 255) / 256 * 256);
+    // one tile per wave for the decode pool sizes, two for longer pools
+    const int tpw = slots <= 4096 ? 1 : 2;
+    const int64_t per_wg = (int64_t)kPtWaves * tpw * kTileEntries;
+    const int64_t wgs = slots > 0 ? (slots + per_wg - 1) / per_wg : 1;
+    const dim3 grid((uint32_t)(rows * wgs)), block(kPtThreads);
+#define CSA2_POOL_TOPK(T, P)                                                                     \
+    pool_topk_kernel<T, P><<<grid, block, 0, stream>>>(q, w, k_codes, k_scales, n_cap, blocks,   \
+                                                       n_blocks, n_visible, nq, (int32_t)wgs, k, \
+                                                       out, counters, sc, ix)
+    if (slots <= 4 * kPtThreads)
+        CSA2_POOL_TOPK(1, 4);
+    else if (slots <= 8 * kPtThreads)
+        CSA2_POOL_TOPK(2, 8);
+    else
+        CSA2_POOL_TOPK(2, 16);
+#undef CSA2_POOL_TOPK
+    return hipGetLastError();
 }
 
 hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,

@@ -75,6 +75,15 @@ hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k
                              int32_t n_blocks, const int32_t* n_visible, int32_t B, int32_t nq,
                              float* pool_score, int32_t* pool_idx, hipStream_t stream);
 
+// Pool rescoring + top-k in one launch (n_blocks * 8 <= 16384).  ws: rows
+// arrival counters (zero before the first use; every call leaves them zero)
+// then the slots' scores and positions.
+size_t pool_topk_workspace(int32_t rows, int32_t n_blocks);
+hipError_t launch_pool_topk(const uint16_t* q, const float* w, const uint8_t* k_codes,
+                            const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
+                            int32_t n_blocks, const int32_t* n_visible, int32_t B, int32_t nq,
+                            int32_t k, int32_t* out, void* ws, hipStream_t stream);
+
 size_t topk_workspace(int64_t L, int32_t rows, int32_t k);
 // Group size of the grouped select for a row of L keys and k winners (0: the
 // direct or segment path); its group maxima live at the front of the workspace

@@ -251,6 +251,13 @@ struct GroupSmem {
     uint32_t chosen_groups[kTopkSegment / 2];  // k <= 16384 / g with g >= 2
 };
 
+// The grouped select as an out-of-line call, for the block select's rare
+// fallback: its registers then do not weigh on the common path's.
+template <int kG>
+__device__ __attribute__((noinline)) void grouped_select_row_call(
+    const float* __restrict__ srow, int64_t nv, int32_t g_runtime, int64_t ngroups,
+    const uint32_t* __restrict__ grow, int32_t k, int32_t* __restrict__ out, GroupSmem& gs);
+
 // Grouped select of one row from its group maxima grow[0..ngroups) (ngroups
 // <= 16384, g * k <= 16384) into out[0..k): the k best groups by their
 // largest key, then the k best of those groups' g*k entries.  srow / irow:
@@ -329,6 +336,16 @@ __device__ void grouped_select_row(const float* __restrict__ srow,
     pk = find_threshold(key, (uint32_t)k, sm, tid, lane, wave);
     chosen = place(key, pk, take, off, sm, lane, wave);
     write_result(take, off, key, id, chosen, k, tid, out, nullptr, nullptr);
+}
+
+template <int kG>
+__device__ __attribute__((noinline)) void grouped_select_row_call(
+    const float* __restrict__ srow, int64_t nv, int32_t g_runtime, int64_t ngroups,
+    const uint32_t* __restrict__ grow, int32_t k, int32_t* __restrict__ out, GroupSmem& gs)
+{
+    const int tid = threadIdx.x;
+    grouped_select_row<kG>(srow, nullptr, nv, g_runtime, ngroups, grow, k, out, gs, tid, tid & 63,
+                           tid >> 6);
 }
 
 // Grouped select for one row from its group maxima gkey[row, 0..ngroups)
@@ -416,6 +433,7 @@ block_select_kernel(BlockSelJob J)
 
     uint32_t key[P];
     int32_t id[P];
+    int32_t full = 0;  // thread c < chunks: whether chunk c left blocks out
     if (J.cand_key != nullptr) {
         const int64_t n = (int64_t)J.chunks * J.kl;
         const uint32_t* ck = J.cand_key + row * n;
@@ -426,6 +444,11 @@ block_select_kernel(BlockSelJob J)
             key[i] = e < n ? ck[e] : 0u;
             id[i] = e < n ? cb[e] : -1;
         }
+        full = tid < J.chunks ? J.cand_full[row * J.chunks + tid] : 0;  // chunks <= 256
+        if (tid < J.chunks)
+            bs.chunk_taken[tid] = 0u;
+        if (tid == 0)
+            bs.invalid = 0u;
     } else {
         const float* srow = J.block_max + row * J.L;
 #pragma unroll
@@ -445,20 +468,19 @@ block_select_kernel(BlockSelJob J)
         const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
         bool fallback = false;
         if (J.cand_key != nullptr) {
-            for (int c = tid; c < J.chunks; c += kThreads)
-                bs.chunk_taken[c] = 0u;
-            if (tid == 0)
-                bs.invalid = 0u;
-            __syncthreads();
+            // chosen candidates per chunk: kl is a multiple of 64, so the 64 lanes of a
+            // wave's slot all belong to one chunk and one ballot counts them (the counters
+            // were cleared before find_threshold's first barrier)
 #pragma unroll
-            for (int i = 0; i < P; ++i)
-                if (take[i])
-                    atomicAdd(&bs.chunk_taken[(kThreads * i + tid) / J.kl], 1u);
+            for (int i = 0; i < P; ++i) {
+                const uint64_t bt = __ballot(take[i]);
+                if (lane == 0 && bt != 0ull)
+                    atomicAdd(&bs.chunk_taken[(kThreads * i + 64 * wave) / J.kl],
+                              (uint32_t)__popcll(bt));
+            }
             __syncthreads();
-            const int64_t frow = row * J.chunks;
-            for (int c = tid; c < J.chunks; c += kThreads)
-                if (J.cand_full[frow + c] != 0 && bs.chunk_taken[c] >= (uint32_t)J.kl)
-                    bs.invalid = 1u;
+            if (tid < J.chunks && full != 0 && bs.chunk_taken[tid] >= (uint32_t)J.kl)
+                bs.invalid = 1u;
             __syncthreads();
             fallback = bs.invalid != 0u;
         }
@@ -469,11 +491,11 @@ block_select_kernel(BlockSelJob J)
             // exact: the grouped select over the row's group maxima
             sel::clear_hist(sm, tid);
             if (J.g == 8)
-                grouped_select_row<8>(J.block_max + row * J.L, nullptr, nvb, J.g, J.ngroups,
-                                      J.gkey + row * J.ngroups, t, out, bs.gs, tid, lane, wave);
+                grouped_select_row_call<8>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
+                                           J.gkey + row * J.ngroups, t, out, bs.gs);
             else
-                grouped_select_row<0>(J.block_max + row * J.L, nullptr, nvb, J.g, J.ngroups,
-                                      J.gkey + row * J.ngroups, t, out, bs.gs, tid, lane, wave);
+                grouped_select_row_call<0>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
+                                           J.gkey + row * J.ngroups, t, out, bs.gs);
         }
     }
 }

@@ -26,6 +26,7 @@ import torch
 from . import _lib
 
 BLOCK = 8
+FUSED_MAX_BLOCKS = 2048  # csa2_index_pool_topk rescores at most 16384 positions
 
 
 def n_valid_blocks(n_visible: torch.Tensor) -> torch.Tensor:
@@ -50,6 +51,7 @@ class Buffers:
     ws_topk: torch.Tensor | None
     ws_attn: torch.Tensor | None
     ws_sel: torch.Tensor | None
+    ws_pool_topk: torch.Tensor
 
     @staticmethod
     def create(B: int, nq: int, n_cap: int, k: int, nb: int, n_win: int,
@@ -63,6 +65,8 @@ class Buffers:
                    _lib.topk_workspace(nblk, B * nq, k))
         ws_a = _lib.sparse_attn_workspace(B, nq, k, n_win)
         ws_s = _lib.index_full_select_workspace(n_cap, B, nq, nb, k)
+        # arrival counters of the fused pool rescoring + top-k: zeroed once here
+        ws_pt = _lib.index_pool_topk_workspace(B, nq, min(nsel, FUSED_MAX_BLOCKS))
         return Buffers(
             block_max=torch.empty(B, nq, nblk, dtype=f32, device=device),
             pool=pool,
@@ -75,6 +79,7 @@ class Buffers:
             ws_topk=torch.empty(ws_t, dtype=torch.uint8, device=device) if ws_t else None,
             ws_attn=torch.empty(ws_a, dtype=torch.uint8, device=device) if ws_a else None,
             ws_sel=torch.empty(ws_s, dtype=torch.uint8, device=device) if ws_s else None,
+            ws_pool_topk=torch.zeros(ws_pt, dtype=torch.uint8, device=device),
         )
 
 
@@ -102,11 +107,21 @@ def full_indexer(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, n_blo
         _lib.index_full(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, scores=scores,
                         stream=stream)
         select_blocks(buf, n_blocks_valid, k, nb, stream=stream)
-    B, nq, _ = buf.sel_blocks.shape
-    score = _slots(buf.pool_score, B, nq, k * BLOCK)
-    idx = _slots(buf.pool_idx, B, nq, k * BLOCK)
-    _lib.index_pool(q_idx, w_idx, k_codes, k_scales, buf.sel_blocks, n_visible, score, idx,
-                    stream=stream)
+    _pool_topk(buf, q_idx, w_idx, k_codes, k_scales, n_visible, buf.sel_blocks, k, stream)
+
+
+def _pool_topk(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, blocks, k: int,
+               stream=None):
+    """Rescore the positions of `blocks` with this query and select the top-k into buf.topk:
+    one fused call for pools of at most 2048 blocks, else the pool scan and csa2_topk."""
+    B, nq, nbk = blocks.shape
+    if nbk <= FUSED_MAX_BLOCKS:
+        _lib.index_pool_topk(q_idx, w_idx, k_codes, k_scales, blocks, n_visible, buf.topk,
+                             buf.ws_pool_topk, stream=stream)
+        return
+    score = _slots(buf.pool_score, B, nq, nbk * BLOCK)
+    idx = _slots(buf.pool_idx, B, nq, nbk * BLOCK)
+    _lib.index_pool(q_idx, w_idx, k_codes, k_scales, blocks, n_visible, score, idx, stream=stream)
     _lib.topk(score, k, buf.topk, idx=idx, ws=buf.ws_topk, stream=stream)
 
 
@@ -118,11 +133,7 @@ def _slots(t: torch.Tensor, B: int, nq: int, L: int) -> torch.Tensor:
 def reindex_indexer(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, pool, k: int,
                     stream=None):
     """Reindex layer indexer: score the given pool with this layer's query, top-k."""
-    B, nq, nbk = pool.shape
-    score = _slots(buf.pool_score, B, nq, nbk * BLOCK)
-    idx = _slots(buf.pool_idx, B, nq, nbk * BLOCK)
-    _lib.index_pool(q_idx, w_idx, k_codes, k_scales, pool, n_visible, score, idx, stream=stream)
-    _lib.topk(score, k, buf.topk, idx=idx, ws=buf.ws_topk, stream=stream)
+    _pool_topk(buf, q_idx, w_idx, k_codes, k_scales, n_visible, pool, k, stream)
 
 
 def attention(buf: Buffers, q, kv_codes, kv_scales, topk, swa, swa_end, n_win: int = 128,

@@ -111,3 +111,58 @@ def test_index_full_select_matches_scan_then_topk(B, nq, n_cap, nb, k, nvis, kin
         for r in range(B * nq):
             sr = s.reshape(-1, k)[r]
             assert set(sr[sr >= 0]) <= set(p.reshape(-1, nb)[r])
+
+
+POOL_CASES = [
+    # (B, nq, n_cap, n_blocks, k, n_visible): decode Full (k blocks) and Reindex (pool) sizes
+    (16, 1, 1 << 20, 512, 512, None),
+    (16, 1, 1 << 20, 2048, 512, None),
+    (5, 1, 100000, 2048, 512, [100000, 50001, 4000, 7, 0]),   # blocks past the visible end
+    (3, 1, 65536, 64, 512, None),                             # fewer positions than k
+    (1, 64, 40000, 2048, 512, "causal"),                      # decoder prefill rows
+    (2, 1, 20000, 1, 8, None),                                # a single block
+]
+
+
+@pytest.mark.parametrize("B,nq,n_cap,nbk,k,nvis", POOL_CASES)
+def test_index_pool_topk_matches_pool_scan_then_topk(B, nq, n_cap, nbk, k, nvis):
+    """csa2_index_pool_topk (rescoring and top-k in one launch; the last workgroup of a
+    row selects) gives exactly csa2_index_pool then csa2_topk, on consecutive calls that
+    reuse one workspace (its arrival counters return to zero)."""
+    print(f"[case] B={B} nq={nq} n_cap={n_cap} n_blocks={nbk} k={k}", flush=True)
+    kc, ks = _caches(B, n_cap, seed=n_cap + nbk, kind="random")
+    rng = np.random.default_rng(nbk + k)
+    rows = B * nq
+    if nvis is None:
+        nv = np.full((B, nq), n_cap, np.int32)
+    elif nvis == "causal":
+        nv = (n_cap - nq + 1 + np.arange(nq, dtype=np.int32))[None, :].repeat(B, 0)
+    else:
+        nv = np.array(nvis, np.int32).reshape(B, nq)
+    nblk = cdiv(n_cap, 8)
+    blocks = np.full((rows, nbk), -1, np.int32)
+    for r in range(rows):
+        m = min(nbk, nblk) - (r % 3)  # some rows padded with -1
+        if m > 0:
+            blocks[r, :m] = np.sort(rng.choice(nblk, m, replace=False))
+    blocks = blocks.reshape(B, nq, nbk)
+    qd = t(synth.normal_bf16(synth.key(22, 1, 0, 0), 0, rows * 4096, 1 / np.sqrt(128))
+           .reshape(B, nq, 32, 128), torch.uint16)
+    wd = t(synth.uniform_f32(synth.key(22, 2, 0, 0), 0, rows * 32).reshape(B, nq, 32))
+    nvd, bd = t(nv), t(blocks)
+
+    ps = torch.empty(B, nq, nbk * 8, device=dev())
+    pi = torch.empty(B, nq, nbk * 8, dtype=torch.int32, device=dev())
+    L.index_pool(qd, wd, kc, ks, bd, nvd, ps, pi)
+    ref = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
+    tw = torch.empty(max(L.topk_workspace(nbk * 8, rows, k), 8), dtype=torch.uint8, device=dev())
+    L.topk(ps, k, ref, idx=pi, ws=tw)
+    ws = torch.zeros(L.index_pool_topk_workspace(B, nq, max(nbk, 2048)), dtype=torch.uint8,
+                     device=dev())
+    for rep in range(3):
+        got = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
+        L.index_pool_topk(qd, wd, kc, ks, bd, nvd, got, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), ref.cpu().numpy()), f"call {rep}"
+    cnt = ws[: 4 * rows].view(torch.int32).cpu().numpy()
+    assert np.all(cnt == 0), "arrival counters not returned to zero"

@@ -701,7 +701,7 @@ def test_sparse_attn_rope_bf16_epilogue():
     out16 = torch.full((B, 1, 64, 512), 0x7777, dtype=torch.int16, device=dev())
     lse16 = torch.empty((B, 1, 64), device=dev())
     # the same key split as _run_attn's fp32 call, so both sum in the same order
-    ws = torch.empty(max(L.sparse_attn_workspace(B, 1, sel.shape[-1], 128), 16),
+    ws = torch.zeros(max(L.sparse_attn_workspace(B, 1, sel.shape[-1], 128), 16),
                      dtype=torch.uint8, device=dev())
     L.sparse_attn_rope_bf16(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end),
                             t(cos), t(sin), out16, lse16, ws=ws)
@@ -845,3 +845,27 @@ def test_window_ring_replay_matches_linear_window(P):
     assert max_abs(o_ring, o_lin) <= 1e-5 and max_abs(l_ring, l_lin) <= 1e-5
     ro, rl = oracle.attention(q[0, 0], vc[0], vs[0], sel[0, 0], lin.cpu().numpy()[0], P, 128)
     assert max_abs(o_ring[0, 0], ro) <= ATTN_TOL and max_abs(l_ring[0, 0], rl) <= 1e-4
+
+
+def test_sparse_attn_key_splits_repeated_calls_bit_identical():
+    """Few rows: the key splits and their merge.  Three calls on one workspace (stale
+    partials from the previous call) give bit-identical outputs that match the oracle."""
+    vc, vs, sw, sel, q = _attn_case(B=3, N=2500, k=512, swa_cap=128, seed=21)
+    B = 3
+    swa_end = np.full((B, 1), 128, np.int32)
+    n = L.sparse_attn_workspace(B, 1, 512, 128)
+    assert n > 0
+    ws = torch.full((n,), 0x5A, dtype=torch.uint8, device=dev())
+    outs = []
+    for rep in range(3):
+        out = torch.full((B, 1, 64, 512), 777.0, device=dev())
+        lse = torch.full((B, 1, 64), 777.0, device=dev())
+        L.sparse_attn(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end), out, lse, ws=ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+    for b in range(B):
+        ro, rl = oracle.attention(q[b, 0], vc[b], vs[b], sel[b, 0], sw[b], 128, 128)
+        assert max_abs(outs[0][0][b, 0], ro) <= ATTN_TOL
+        assert max_abs(outs[0][1][b, 0], rl) <= 1e-4
