@@ -3,29 +3,14 @@
 // and ranks blocks of 8 positions by their largest score; Reindex layers score
 // only the pool of selected blocks).
 //
-// Score of entry j for one query:  s_j = sum_h w_h * max(0, q_h . k_j),
-// h < 32 heads, dot over 128 channels (reading: the pages fix the 32 x 128
-// shape, not the formula).
-//
-// Both kernels compute scores with the same device function, so a position's
+// Every kernel here scores with score.h's score function (its MFMA mapping and
+// the reading of the score formula are described there), so a position's
 // score is bit-identical whether it comes from the full scan or a pool scan.
-//
-// MFMA mapping (v_mfma_f32_32x32x16_f16, one wave):
-//   A = q   [32 heads x 16 channels per k-step], B = k^T [16 channels x 32
-//   entries], D [32 heads x 32 entries] in fp32.  Lane l owns entry l%32 and
-//   the channel half h = l/32: k-step t covers channels 64h + 8t .. +8 on both
-//   operands, so a lane reads code bytes [32h, 32h + 32) of its entry (chunks
-//   2h and 2h + 1 of the tiled key layout: each load instruction of the wave
-//   reads two whole 512-byte planes) and one dword of scales.  Keys are dequantised in registers (exact in fp16, the
-//   E4M3-per-16 scale is not gfx950's E8M0-per-32 MX scale, so the scaled MFMA
-//   cannot take it).  Each query head is pre-multiplied by a power of two that
-//   brings its largest |q| to [2^14, 2^15), which keeps the bf16 -> fp16 cast
-//   exact for every value within 2^28 of that maximum; the head weight absorbs
-//   the inverse power, so the score is unchanged.
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
 #include "launch.h"
+#include "score.h"
 #include "select.h"
 
 namespace csa2 {
@@ -57,87 +42,6 @@ constexpr int64_t kScanTargetWorkgroups = CSA2_SCAN_TARGET_WGS;
 #define CSA2_SCAN_PAIR_MIN_ROWS 2
 #endif
 constexpr int32_t kPairMinRows = CSA2_SCAN_PAIR_MIN_ROWS;
-#ifndef CSA2_SCAN_NONTEMPORAL
-#define CSA2_SCAN_NONTEMPORAL 1
-#endif
-
-struct QueryOperand {
-    half8 a[8];      // A operand of k-steps 0..7
-    float wr[16];    // weight (times 2^-shift) of the head of accumulator row r
-};
-
-// Load one query's indexer q (bf16 [32, 128]) and w (fp32 [32]) into the
-// operand layout of the calling wave.
-__device__ __forceinline__ void load_query(const uint16_t* __restrict__ q,
-                                           const float* __restrict__ w, int lane,
-                                           QueryOperand& Q)
-{
-    const int head = lane & 31;
-    const int half = lane >> 5;
-    const uint4* src = reinterpret_cast<const uint4*>(q + head * kIdxDim + 64 * half);
-    float m = 0.0f;
-    uint4 raw[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-        raw[t] = src[t];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const uint32_t d[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m = fmaxf(m, fabsf(__uint_as_float(d[i] << 16)));
-            m = fmaxf(m, fabsf(__uint_as_float(d[i] & 0xFFFF0000u)));
-        }
-    }
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    // power of two bringing max|q_h| into [2^14, 2^15); 0 for an all-zero head
-    int shift = 0;
-    if (m > 0.0f) {
-        const int e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127;
-        shift = 14 - e;
-        shift = shift < -100 ? -100 : (shift > 100 ? 100 : shift);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const uint32_t d[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Q.a[t][2 * i] = (_Float16)ldexpf(__uint_as_float(d[i] << 16), shift);
-            Q.a[t][2 * i + 1] = (_Float16)ldexpf(__uint_as_float(d[i] & 0xFFFF0000u), shift);
-        }
-    }
-    // accumulator row r of lane l is head 8*(r/4) + 4*(l/32) + r%4
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int hr = 8 * (r / 4) + 4 * half + (r % 4);
-        const int sh = __shfl(shift, hr, kWave);
-        Q.wr[r] = ldexpf(w[hr], -sh);
-    }
-}
-
-struct KeyTile {
-    u32x4 c0, c1;   // code bytes [32h, 32h+32) of the lane's entry
-    uint32_t sc;    // scale bytes [4h, 4h+4)
-};
-
-// Key of flat entry f (tiled codes, row-major scales), channel half `half`.
-__device__ __forceinline__ void load_key(const uint8_t* __restrict__ codes,
-                                         const uint8_t* __restrict__ scales, int64_t f,
-                                         int half, KeyTile& K)
-{
-    const u32x4* c = reinterpret_cast<const u32x4*>(codes + key_code_offset(f, 32 * half));
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(scales + f * (kIdxDim / 16) + 4 * half);
-#if CSA2_SCAN_NONTEMPORAL
-    // streamed once: do not keep the keys in the caches
-    K.c0 = __builtin_nontemporal_load(c);
-    K.c1 = __builtin_nontemporal_load(c + kKeyPlane / 16);
-    K.sc = __builtin_nontemporal_load(sp);
-#else
-    K.c0 = c[0];
-    K.c1 = c[kKeyPlane / 16];
-    K.sc = *sp;
-#endif
-}
 
 // Keys of one chunk, read with raw buffer loads: the descriptors hold the
 // chunk's base addresses and sizes in bytes (scalar registers), a lane keeps
@@ -187,39 +91,6 @@ __device__ __forceinline__ void load_key(const ChunkKeys& C, int32_t first_entry
     K.c0 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc, 0, kNonTemporal);
     K.c1 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc + kKeyPlane, 0, kNonTemporal);
     K.sc = __builtin_amdgcn_raw_buffer_load_b32(C.scales, os, 0, kNonTemporal);
-}
-
-// Weighted ReLU head sum of one query's accumulators (both lanes of an entry
-// return the same value).
-__device__ __forceinline__ float head_sum(const QueryOperand& Q, const f32x16& acc)
-{
-    // max(0, x) as a signed-integer max of the bit pattern: one instruction,
-    // the same value as fmaxf for every non-NaN x (-0 and negatives give +0)
-    float part = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float relu = __int_as_float(max(__float_as_int(acc[r]), 0));
-        part = __builtin_fmaf(Q.wr[r], relu, part);
-    }
-    // add the two channel halves: lanes l and l^32 hold the same entry, and
-    // the swap hands every lane both partial sums (the same addition on both)
-    const auto pair = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
-                                                       __float_as_uint(part), false, false);
-    return __uint_as_float(pair[0]) + __uint_as_float(pair[1]);
-}
-
-// Score of the lane's entry (both lanes of an entry return the same value).
-__device__ __forceinline__ float score_entry(const QueryOperand& Q, const KeyTile& K)
-{
-    const uint32_t words[8] = {K.c0[0], K.c0[1], K.c0[2], K.c0[3], K.c1[0], K.c1[1], K.c1[2], K.c1[3]};
-    f32x16 acc = {};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const _Float16 s = e4m3_byte_to_f16(K.sc, t / 2);
-        const half8 b = dequant8_fp4(words[t], s);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q.a[t], b, acc, 0, 0, 0);
-    }
-    return head_sum(Q, acc);
 }
 
 // Scores of the lane's entry for two queries: the key is dequantised once and
