@@ -137,8 +137,9 @@ __device__ __forceinline__ void fold_tile(Online& st, const f32x4 (&s)[2],
     }
 }
 
-// S^T of one tile to the log2 domain, -inf for invalid keys (bit b of `valid`
-// tells whether this lane's key of block b is valid).
+// S^T of one tile to the log2 domain (scale_log2: the softmax scale times
+// log2(e), divided by the lane's head's query scaling), -inf for invalid keys
+// (bit b of `valid` tells whether this lane's key of block b is valid).
 __device__ __forceinline__ void scale_scores(f32x4 (&s)[2], uint32_t valid, float scale_log2,
                                              int G)
 {
@@ -198,6 +199,7 @@ struct GroupSmem {
     // contiguous with its neighbours' (a 32-byte lane stride made lanes l and
     // l + 8 share banks)
     f32x4 part[2][kHgW][kGroupWaves][2][kWave];
+    float qmax[kHgW][kGroupWaves][kHg];  // largest |q| of each head over each wave's slice
 };
 
 // Raw bytes of one tile for the calling lane, for key l%16 of block b:
@@ -516,6 +518,48 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
     for (int u = 0; u < kDepth; ++u)
         load_idx(pos(u + kDepth), eidx[u]);
 
+    // Each head's query is scaled by a power of two bringing its largest |q| into
+    // [2^14, 2^15), so the bf16 -> fp16 cast is exact for every value within 2^28 of
+    // it and never overflows; the head's score scale takes the inverse power.  A
+    // power of two scales every product and partial sum exactly, so the scores are
+    // those of the unscaled query.  The largest |q| of a head spans the four waves'
+    // channel slices: one exchange through LDS.
+    float head_scale[kHgW];  // scale_log2 * 2^-shift for this lane's head (l % 16)
+    int qshift[kHgW];
+    {
+#pragma unroll
+        for (int h = 0; h < kHgW; ++h) {
+            float m = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t d[4] = {qraw[h][t].x, qraw[h][t].y, qraw[h][t].z, qraw[h][t].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    m = fmaxf(m, fabsf(__uint_as_float(d[i] << 16)));
+                    m = fmaxf(m, fabsf(__uint_as_float(d[i] & 0xFFFF0000u)));
+                }
+            }
+            m = fmaxf(m, __shfl_xor(m, 16, kWave));
+            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            if (lane < kHg)
+                sm.qmax[h][slice][lane] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < kHgW; ++h) {
+            float m = sm.qmax[h][0][key16];
+#pragma unroll
+            for (int w = 1; w < kGroupWaves; ++w)
+                m = fmaxf(m, sm.qmax[h][w][key16]);
+            int sh = 0;  // 0 for an all-zero head
+            if (m > 0.0f && !__builtin_isinf(m) && !__builtin_isnan(m)) {
+                sh = 14 - ((int)((__float_as_uint(m) >> 23) & 0xFF) - 127);
+                sh = sh < -100 ? -100 : (sh > 100 ? 100 : sh);
+            }
+            qshift[h] = sh;
+            head_scale[h] = ldexpf(scale_log2, -sh);
+        }
+    }
     half8 qop[kHgW][4];
 #pragma unroll
     for (int h = 0; h < kHgW; ++h)
@@ -524,8 +568,9 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
             const uint32_t d[4] = {qraw[h][t].x, qraw[h][t].y, qraw[h][t].z, qraw[h][t].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qop[h][t][2 * i] = bf16_to_f16((uint16_t)(d[i] & 0xFFFFu));
-                qop[h][t][2 * i + 1] = bf16_to_f16((uint16_t)(d[i] >> 16));
+                qop[h][t][2 * i] = (_Float16)ldexpf(__uint_as_float(d[i] << 16), qshift[h]);
+                qop[h][t][2 * i + 1] = (_Float16)ldexpf(__uint_as_float(d[i] & 0xFFFF0000u),
+                                                        qshift[h]);
             }
         }
 
@@ -570,7 +615,7 @@ attn_group_kernel(const uint16_t* __restrict__ q, int32_t queries,
                     }
                     s[h][0] = tot0;
                     s[h][1] = tot1;
-                    scale_scores(s[h], ring[u].valid, scale_log2, G);
+                    scale_scores(s[h], ring[u].valid, head_scale[h], G);
                     fold_tile(st[h], s[h], vtile, lane);
                 }
             }

@@ -5,8 +5,12 @@ query steps, and compare.
 Inputs come only from `synth` (seeded).  The oracle encodes its own caches; the
 GPU encodes its own with csa2_quantize_kv / csa2_quantize_swa, and the tests
 assert the two encodings are bit-identical before comparing anything
-downstream, so every later stage sees identical inputs on both sides.  No GPU
-result is ever fed to the oracle.
+downstream, so every later stage sees identical inputs on both sides.  The only
+GPU outputs the oracle ever takes are selections (index sets: a pool, a top-k)
+that were first checked against the oracle's own selection with check_set;
+the next stage (attention, Reindex) is then compared on that same validated
+set, so a near-tie swap cannot hide a downstream comparison.  No GPU score,
+code or floating-point value is ever fed to the oracle.
 """
 from __future__ import annotations
 
@@ -80,11 +84,16 @@ class Case:
     o_swa: list = field(default_factory=list)
 
 
-def build_case(w: synth.Workload, n_layers: int | None = None) -> Case:
+def build_case(w: synth.Workload, n_layers: int | None = None, idx_transform=None) -> Case:
+    """Inputs of one workload from synth, and the oracle's encodings of them.
+    idx_transform(idx_x [B, n_cap, 128]) -> idx_x: changes the indexer-key rows before
+    both sides encode them (adversarial cases: duplicated keys)."""
     n_layers = len(w.layers) if n_layers is None else n_layers
     c = Case(w=w, n_layers=n_layers)
     B, N = w.B, w.n_cap
     c.idx_x = np.stack([synth.idx_k_rows(w, b, 0, N) for b in range(B)])
+    if idx_transform is not None:
+        c.idx_x = np.ascontiguousarray(idx_transform(c.idx_x), dtype=np.float32)
     c.kv_x = np.stack([synth.kv_rows(w, b, 0, N) for b in range(B)])
     c.cos, c.sin = synth.rope_rows(0, N)
     for layer in range(n_layers):
