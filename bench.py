@@ -289,8 +289,9 @@ def scan_bytes(w: synth.Workload) -> int:
 def scan_write_bytes(w: synth.Workload) -> int:
     """Bytes the scan launch writes besides reading (not in scan_bytes): the block maxima
     (fp32 per 8 visible entries) and, for rows of more than 16384 blocks, the block
-    select's inputs -- one uint32 group key per g blocks and each chunk's candidate
-    list (the workspace of csa2_index_full_select, minus nothing: an upper bound)."""
+    select's inputs -- one uint32 group key per g blocks and each chunk's block and
+    entry candidate lists (bounded by the workspace of csa2_index_full_select, which
+    also holds the exact fallback's buffers: an upper bound)."""
     nv = w.n_visible().astype(np.int64)
     b = int(((nv + 7) // 8).sum()) * 4
     from kv_cache_decode_mxfp4_amd import _lib as L

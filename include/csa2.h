@@ -68,7 +68,7 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Library ABI version (major * 100 + minor): 103. */
+/* Library ABI version (major * 100 + minor): 104. */
 int32_t csa2_version(void);
 
 /*
@@ -232,27 +232,31 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w,
                                  void* stream);
 
 /*
- * Full-layer scan with the pool AND the top-k blocks in one call ([N] 2.2,
- * [A] 3.4: the Full layer scores the whole visible range, keeps the nb blocks
- * with the largest block scores as the pool, and selects its own top-k
- * entries).  The top-k entries of a row always lie in its k best blocks (a
+ * The Full layer's indexer in one call ([N] 2.2, [A] 3.4: the Full layer
+ * scores the whole visible range, keeps the nb blocks with the largest block
+ * scores as the pool for the Reindex layers, and selects its own top-k
+ * entries): scan, pool and top-k.  Same arguments as csa2_index_full_pool,
+ * plus
+ *   nb        pool blocks, 0 <= nb <= 8192 (0: no pool, pool may be NULL).
+ *   k         1 <= k <= 8192.
+ *   pool      int32 [B, nq, nb]: csa2_topk(block_max, ceil(n_cap/8), B*nq,
+ *             n_valid = ceil(n_visible/8), nb), bit for bit.
+ *   topk      int32 [B, nq, k]: the Full layer's top-k positions, ascending,
+ *             -1 padded: the k best visible entries under (score descending,
+ *             position ascending), exactly what csa2_topk over every score
+ *             of csa2_index_full would select.
+ *   ws, ws_bytes  device workspace of csa2_index_full_select_workspace(n_cap,
+ *             B, nq, nb, k) bytes, 256-byte aligned, any contents.
+ * The scan writes only block maxima (and, for long rows, candidate lists), no
+ * per-entry scores.  The top-k entries of a row lie in its k best blocks (a
  * block ranked above a winner's block holds a better entry, also under the
- * lower-index tie-break), so the Full layer's top-k is csa2_index_pool over
- * topk_blocks followed by csa2_topk(k): the scan itself keeps no per-entry
- * scores.  Same arguments as csa2_index_full_pool, plus
- *   nb           pool blocks, 0 <= nb <= 8192 (0: no pool, pool may be NULL).
- *   k            1 <= k <= 8192.
- *   pool         int32 [B, nq, nb]: csa2_topk(block_max, ceil(n_cap/8), B*nq,
- *                n_valid = ceil(n_visible/8), nb), bit for bit.
- *   topk_blocks  int32 [B, nq, k]: the same with k.
- *   ws, ws_bytes device workspace of csa2_index_full_select_workspace(n_cap,
- *                B, nq, nb, k) bytes, 256-byte aligned, any contents (0
- *                bytes for rows of at most 16384 blocks, where ws may be NULL).
- * For rows of more than 16384 blocks the one-row scan also writes each chunk's
- * best blocks and the maxima of groups of blocks into the workspace: the
- * select then ranks only those candidates, and falls back to an exact select
- * over the group maxima for a row where a chunk could hold more winners than
- * it listed.  Both give the same result.
+ * lower-index tie-break), so the call selects the pool and the k best blocks
+ * (for rows of more than 16384 blocks among the scan's per-chunk candidates
+ * -- each chunk's best blocks -- with an exact fallback over group maxima
+ * that the scan also writes, for a row where a chunk could hold more winners
+ * than it listed), then rescores the k best blocks' k * 8 positions with the
+ * scan's own score function (bit-identical scores) and keeps the best k.
+ * Every path gives the same result.
  */
 size_t      csa2_index_full_select_workspace(int64_t n_cap, int32_t B, int32_t nq, int32_t nb,
                                              int32_t k);
@@ -260,7 +264,7 @@ csa2_status csa2_index_full_select(const uint16_t* q, const float* w,
                                    const uint8_t* k_codes, const uint8_t* k_scales,
                                    int64_t n_cap, const int32_t* n_visible, int32_t B,
                                    int32_t nq, int32_t block, int32_t nb, int32_t k,
-                                   float* block_max, int32_t* pool, int32_t* topk_blocks,
+                                   float* block_max, int32_t* pool, int32_t* topk,
                                    void* ws, size_t ws_bytes, void* scan_start,
                                    void* scan_stop, void* stream);
 

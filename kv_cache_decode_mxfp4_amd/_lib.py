@@ -318,22 +318,22 @@ def index_full_select_workspace(n_cap, B, nq, nb, k) -> int:
     return int(load().csa2_index_full_select_workspace(n_cap, B, nq, nb, k))
 
 
-def index_full_select(q, w, k_codes, k_scales, n_visible, block_max, topk_blocks, pool=None,
+def index_full_select(q, w, k_codes, k_scales, n_visible, block_max, topk, pool=None,
                       ws=None, block=8, scan_events=None, stream=None):
-    """Full-layer scan, pool (top-nb blocks, nb = pool.shape[-1], or none) and the top-k
-    blocks (k = topk_blocks.shape[-1]) in one call; ws: uint8 device workspace of
-    index_full_select_workspace(...) bytes, 256-byte aligned."""
+    """The Full layer's indexer in one call: the scan, the pool (top-nb blocks,
+    nb = pool.shape[-1], or none) and the top-k positions (k = topk.shape[-1]); ws:
+    uint8 device workspace of index_full_select_workspace(...) bytes, 256-byte aligned."""
     B, nq, n_cap = _indexer_inputs(q, w, k_codes, k_scales, n_visible)
     nb = pool.shape[-1] if pool is not None else 0
-    k = topk_blocks.shape[-1]
-    _need(topk_blocks, torch.int32, B * nq * k, "topk_blocks")
+    k = topk.shape[-1]
+    _need(topk, torch.int32, B * nq * k, "topk")
     _need(pool, torch.int32, B * nq * nb, "pool", optional=True)
     _need(block_max, torch.float32, B * nq * (-(-n_cap // 8)), "block_max", optional=n_cap == 0)
     _need(ws, torch.uint8, 0, "ws", optional=True)
     q = _bf16_bits(q)
     _check("csa2_index_full_select", load().csa2_index_full_select(
         _p(q), _p(w), _p(k_codes), _p(k_scales), n_cap, _p(n_visible), B, nq, block, nb, k,
-        _p(block_max), _p(pool), _p(topk_blocks), _p(ws),
+        _p(block_max), _p(pool), _p(topk), _p(ws),
         ws.numel() * ws.element_size() if ws is not None else 0,
         scan_events[0].cuda_event if scan_events else None,
         scan_events[1].cuda_event if scan_events else None, _stream(stream)))

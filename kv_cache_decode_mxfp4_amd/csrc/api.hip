@@ -62,7 +62,7 @@ const char* csa2_last_error(void)
 
 int32_t csa2_version(void)
 {
-    return 103;
+    return 104;
 }
 
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
@@ -246,16 +246,25 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w, const uint8_
     return finish(e, s, "index_full_pool");
 }
 
-// How csa2_index_full_select runs for a shape: the direct block select (rows of
-// at most 16384 blocks), the scan's per-chunk candidates (one-row scan, groups
-// of g blocks that the scan also writes as the exact fallback), or two
-// csa2_topk calls over the block maxima.
+// How csa2_index_full_select runs for a shape.  The pool and the top-k blocks
+// come from the direct block select (mode 0: rows of at most 16384 blocks),
+// the scan's per-chunk candidates (mode 1: one-row scan, groups of g blocks
+// that the scan also writes as the exact fallback), or two csa2_topk calls
+// over the block maxima (mode 2).  The top-k entries are the top-k blocks'
+// positions rescored: pool rescoring + top-k in one launch (rescore_fused;
+// its arrival counters are cleared by the block select), or a pool scan and
+// csa2_topk.
 struct FullSelectPlan {
-    int mode;          // 0 direct, 1 candidates, 2 two top-k calls
-    int64_t L;         // blocks per row
-    int32_t g;         // group size (mode 1)
-    int32_t chunks, kl;
-    size_t off_cand_key, off_cand_blk, off_cand_full, ws_bytes;
+    int mode;
+    int64_t L;            // blocks per row
+    int32_t g;            // group size (mode 1)
+    int32_t chunks, kl;   // block candidate lists (mode 1)
+    bool rescore_fused;
+    size_t off_cand_key, off_cand_blk, off_cand_full;
+    size_t off_tb;        // top-k blocks [rows, k]
+    size_t off_rescore;   // pool_topk workspace (rescore_fused)
+    size_t off_pscore, off_pidx, off_topk_ws;
+    size_t ws_bytes;
 };
 
 static FullSelectPlan full_select_plan(int64_t n_cap, int32_t B, int32_t nq, int32_t nb, int32_t k)
@@ -264,37 +273,56 @@ static FullSelectPlan full_select_plan(int64_t n_cap, int32_t B, int32_t nq, int
     const int64_t rows = (int64_t)B * nq;
     P.L = (n_cap + csa2::kBlock - 1) / csa2::kBlock;
     const int32_t tmax = nb > k ? nb : k;
-    if (P.L <= csa2::kTopkSegment) {
-        P.mode = 0;
-        return P;
-    }
-    const csa2::ScanShape sh = csa2::scan_shape(n_cap, B, nq);
-    const int32_t g = csa2::topk_group_size(P.L, tmax);
-    if (!sh.paired && g > 0 && 64 % g == 0) {
-        // about twice a chunk's share of the winners, at least 64, a power of two
-        const int32_t per = (tmax + sh.chunks_per_row - 1) / sh.chunks_per_row;
-        int32_t kl = 64;
-        while (kl < 2 * per)
-            kl *= 2;
-        if (kl <= sh.max_blocks_per_chunk && (int64_t)sh.chunks_per_row * kl <= csa2::kTopkSegment) {
-            P.mode = 1;
-            P.g = g;
-            P.chunks = sh.chunks_per_row;
-            P.kl = kl;
-            const size_t gk = (size_t)rows * (size_t)((P.L + g - 1) / g) * 4;
-            const size_t nc = (size_t)rows * P.chunks * kl;
-            auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-            P.off_cand_key = up(gk);
-            P.off_cand_blk = P.off_cand_key + up(nc * 4);
-            P.off_cand_full = P.off_cand_blk + up(nc * 4);
-            P.ws_bytes = P.off_cand_full + up((size_t)rows * P.chunks * 4);
-            return P;
+    size_t off = 0;
+    auto take = [&off](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) / 256 * 256;
+        return o;
+    };
+    P.mode = P.L <= csa2::kTopkSegment ? 0 : 2;
+    if (P.mode == 2) {
+        const csa2::ScanShape sh = csa2::scan_shape(n_cap, B, nq);
+        const int32_t g = csa2::topk_group_size(P.L, tmax);
+        if (!sh.paired && g > 0 && 64 % g == 0) {
+            // about twice a chunk's share of the winners, at least 64, a power of two
+            const int32_t per = (tmax + sh.chunks_per_row - 1) / sh.chunks_per_row;
+            int32_t kl = 64;
+            while (kl < 2 * per)
+                kl *= 2;
+            if (kl <= sh.max_blocks_per_chunk && (int64_t)sh.chunks_per_row * kl <= csa2::kTopkSegment) {
+                P.mode = 1;
+                P.g = g;
+                P.chunks = sh.chunks_per_row;
+                P.kl = kl;
+                const size_t nc = (size_t)rows * P.chunks * kl;
+                take((size_t)rows * (size_t)((P.L + g - 1) / g) * 4);  // group keys, at 0
+                P.off_cand_key = take(nc * 4);
+                P.off_cand_blk = take(nc * 4);
+                P.off_cand_full = take((size_t)rows * P.chunks * 4);
+            }
         }
     }
-    P.mode = 2;
-    const size_t a = csa2::topk_workspace(P.L, (int32_t)rows, nb > 0 ? nb : 1);
-    const size_t b = csa2::topk_workspace(P.L, (int32_t)rows, k);
-    P.ws_bytes = a > b ? a : b;
+    // the top-k blocks, then their positions rescored
+    const size_t L8 = (size_t)k * csa2::kBlock;
+    if (P.mode == 2) {
+        size_t t = csa2::topk_workspace(P.L, (int32_t)rows, nb > 0 ? nb : 1);
+        const size_t t2 = csa2::topk_workspace(P.L, (int32_t)rows, k);
+        const size_t t3 = csa2::topk_workspace((int64_t)L8, (int32_t)rows, k);
+        t = t > t2 ? t : t2;
+        P.off_topk_ws = take(t > t3 ? t : t3);
+    }
+    P.off_tb = take((size_t)rows * k * 4);
+    P.rescore_fused = P.mode != 2 && (int64_t)L8 <= csa2::kTopkSegment;
+    if (P.rescore_fused) {
+        P.off_rescore = take(csa2::pool_topk_workspace((int32_t)rows, k));
+    } else {
+        const size_t pos_bytes = (size_t)rows * L8 * 4;  // rows x k blocks x 8 positions
+        P.off_pscore = take(pos_bytes);
+        P.off_pidx = take(pos_bytes);
+        if (P.mode != 2)
+            P.off_topk_ws = take(csa2::topk_workspace((int64_t)L8, (int32_t)rows, k));
+    }
+    P.ws_bytes = off;
     return P;
 }
 
@@ -311,9 +339,8 @@ csa2_status csa2_index_full_select(const uint16_t* q, const float* w, const uint
                                    const uint8_t* k_scales, int64_t n_cap,
                                    const int32_t* n_visible, int32_t B, int32_t nq,
                                    int32_t block, int32_t nb, int32_t k, float* block_max,
-                                   int32_t* pool, int32_t* topk_blocks, void* ws,
-                                   size_t ws_bytes, void* scan_start, void* scan_stop,
-                                   void* stream)
+                                   int32_t* pool, int32_t* topk, void* ws, size_t ws_bytes,
+                                   void* scan_start, void* scan_stop, void* stream)
 {
     csa2_status st = check_indexer("index_full_select", q, w, k_codes, k_scales, n_cap,
                                    n_visible, B, nq, block);
@@ -326,11 +353,13 @@ csa2_status csa2_index_full_select(const uint16_t* q, const float* w, const uint
     const int64_t L = (n_cap + csa2::kBlock - 1) / csa2::kBlock;
     REQUIRE(rows * ((L + csa2::kTopkSegment - 1) / csa2::kTopkSegment) <= (1ll << 31) - 1,
             CSA2_ERR_INVALID_ARG, "index_full_select: too many segments");
+    REQUIRE(rows * k * csa2::kBlock <= (1ll << 31) - 1, CSA2_ERR_INVALID_ARG,
+            "index_full_select: too many rescored positions");
     if (rows == 0)
         return CSA2_OK;
-    REQUIRE(topk_blocks != nullptr && (nb == 0 || pool != nullptr) &&
+    REQUIRE(topk != nullptr && (nb == 0 || pool != nullptr) &&
                 (n_cap == 0 || block_max != nullptr),
-            CSA2_ERR_INVALID_ARG, "index_full_select: null block_max, pool or topk_blocks");
+            CSA2_ERR_INVALID_ARG, "index_full_select: null block_max, pool or topk");
     const FullSelectPlan P = full_select_plan(n_cap, B, nq, nb, k);
     REQUIRE(ws_bytes >= P.ws_bytes && (P.ws_bytes == 0 || ws != nullptr), CSA2_ERR_WORKSPACE,
             "index_full_select: workspace of %zu bytes needed, %zu given", P.ws_bytes, ws_bytes);
@@ -338,41 +367,67 @@ csa2_status csa2_index_full_select(const uint16_t* q, const float* w, const uint
             "index_full_select: workspace must be 256-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* pool_out = nb > 0 ? pool : nullptr;
-    hipError_t e = hipSuccess;
     char* wsb = static_cast<char*>(ws);
-    if (n_cap > 0) {
-        if (P.mode == 1) {
-            e = csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq, block_max,
-                                        nullptr, reinterpret_cast<uint32_t*>(wsb), P.g,
-                                        static_cast<hipEvent_t>(scan_start),
-                                        static_cast<hipEvent_t>(scan_stop), s,
-                                        reinterpret_cast<uint32_t*>(wsb + P.off_cand_key),
-                                        reinterpret_cast<int32_t*>(wsb + P.off_cand_blk),
-                                        reinterpret_cast<int32_t*>(wsb + P.off_cand_full), P.kl);
-        } else {
-            e = csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq, block_max,
-                                        nullptr, nullptr, 0, static_cast<hipEvent_t>(scan_start),
-                                        static_cast<hipEvent_t>(scan_stop), s);
-        }
+    auto at = [wsb](size_t off) { return static_cast<void*>(wsb + off); };
+    int32_t* tb = static_cast<int32_t*>(at(P.off_tb));
+    hipError_t e = hipSuccess;
+    const hipEvent_t ev0 = static_cast<hipEvent_t>(scan_start);
+    const hipEvent_t ev1 = static_cast<hipEvent_t>(scan_stop);
+
+    csa2::BlockSelect S;
+    S.block_max = block_max;
+    S.L = L;
+    S.rows = (int32_t)rows;
+    S.n_visible = n_visible;
+    S.nb = nb;
+    S.k = k;
+    S.pool = pool_out;
+    S.sel = tb;
+    if (P.mode == 1) {
+        uint32_t* ck = static_cast<uint32_t*>(at(P.off_cand_key));
+        int32_t* cb = static_cast<int32_t*>(at(P.off_cand_blk));
+        int32_t* cf = static_cast<int32_t*>(at(P.off_cand_full));
+        e = csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq, block_max,
+                                    nullptr, static_cast<uint32_t*>(at(0)), P.g, ev0, ev1, s, ck,
+                                    cb, cf, P.kl);
+        S.gkey = static_cast<const uint32_t*>(at(0));
+        S.g = P.g;
+        S.cand_key = ck;
+        S.cand_blk = cb;
+        S.cand_full = cf;
+        S.chunks = P.chunks;
+        S.kl = P.kl;
+    } else if (n_cap > 0) {
+        e = csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq, block_max,
+                                    nullptr, nullptr, 0, ev0, ev1, s);
     }
+    if (P.rescore_fused)
+        S.zero_counters = static_cast<uint32_t*>(at(P.off_rescore));  // its arrival counters
     if (e == hipSuccess) {
-        if (n_cap == 0 || P.mode == 0) {
-            e = csa2::launch_block_select(block_max, L, (int32_t)rows, n_visible, nullptr, 0, nullptr,
-                                          nullptr, nullptr, 0, 0, nb, k, pool_out, topk_blocks, s);
-        } else if (P.mode == 1) {
-            e = csa2::launch_block_select(
-                block_max, L, (int32_t)rows, n_visible, reinterpret_cast<const uint32_t*>(wsb), P.g,
-                reinterpret_cast<const uint32_t*>(wsb + P.off_cand_key),
-                reinterpret_cast<const int32_t*>(wsb + P.off_cand_blk),
-                reinterpret_cast<const int32_t*>(wsb + P.off_cand_full), P.chunks, P.kl, nb, k,
-                pool_out, topk_blocks, s);
+        if (P.mode != 2) {
+            e = csa2::launch_block_select(S, s);
         } else {
             if (nb > 0)
                 e = csa2::launch_topk(block_max, nullptr, L, (int32_t)rows, n_visible,
-                                      csa2::kBlock, nb, pool_out, ws, false, s);
+                                      csa2::kBlock, nb, pool_out, at(P.off_topk_ws), false, s);
             if (e == hipSuccess)
                 e = csa2::launch_topk(block_max, nullptr, L, (int32_t)rows, n_visible,
-                                      csa2::kBlock, k, topk_blocks, ws, false, s);
+                                      csa2::kBlock, k, tb, at(P.off_topk_ws), false, s);
+        }
+    }
+    if (e == hipSuccess) {
+        // the top-k entries: the top-k blocks' positions rescored
+        if (P.rescore_fused) {
+            e = csa2::launch_pool_topk(q, w, k_codes, k_scales, n_cap, tb, k, n_visible, B, nq, k,
+                                       topk, at(P.off_rescore), s);
+        } else {
+            float* ps = static_cast<float*>(at(P.off_pscore));
+            int32_t* pi = static_cast<int32_t*>(at(P.off_pidx));
+            e = csa2::launch_index_pool(q, w, k_codes, k_scales, n_cap, tb, k, n_visible, B, nq,
+                                        ps, pi, s);
+            if (e == hipSuccess)
+                e = csa2::launch_topk(ps, pi, (int64_t)k * csa2::kBlock, (int32_t)rows, nullptr, 1,
+                                      k, topk, at(P.off_topk_ws), false, s);
         }
     }
     return finish(e, s, "index_full_select");

@@ -154,13 +154,12 @@ __device__ __attribute__((noinline)) void write_group_keys(const float* sblk, in
     }
 }
 
-// Candidates of one row's chunk for the block select (after the scan loop):
-// the kl best of the chunk's nb_here visible block maxima (held in sblk),
-// under the selection order (larger maximum first, lower block first), as
-// (order key, block id) pairs in block order at list[0..kl) of the chunk,
-// padded with (0, -1); full = whether the chunk had more than kl blocks (so
-// some were left out).  A NaN maximum has key 0 and is never a candidate.
-// kl <= the chunk's block count, a multiple of 64.
+// Block candidates of one row's chunk for the block select (after the scan
+// loop; the chunk's nb_here visible block maxima are in sblk): the kl best
+// blocks under the selection order (larger maximum first, lower block first),
+// (order key, block id) in block order, (0, -1) padded; full = the chunk had
+// more than kl visible blocks.  A NaN maximum has key 0 and is never a
+// candidate.  kl <= the chunk's block count, a multiple of 64.
 constexpr int kCandThreads = kWaves * kWave;
 constexpr int kCandSlots = kMaxChunk / kBlock / kCandThreads;  // blocks per thread
 

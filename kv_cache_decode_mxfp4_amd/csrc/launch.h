@@ -61,14 +61,27 @@ ScanShape scan_shape(int64_t n_cap, int32_t B, int32_t nq);
 // Pool (top-nb blocks) and top-k blocks of every row in one launch.  Direct
 // form (cand_key null): keys are the block maxima, L <= 16384.  Candidate
 // form: the scan's per-chunk lists [rows, chunks, kl] (chunks * kl <= 16384,
-// kl >= 64), with the exact grouped select over the group maxima gkey
-// ([rows, ceil(L/g)], groups of g) as the fallback.  pool / sel may be null
-// (target skipped).
-hipError_t launch_block_select(const float* block_max, int64_t L, int32_t rows,
-                               const int32_t* n_visible, const uint32_t* gkey, int32_t g,
-                               const uint32_t* cand_key, const int32_t* cand_blk,
-                               const int32_t* cand_full, int32_t chunks, int32_t kl, int32_t nb,
-                               int32_t k, int32_t* pool, int32_t* sel, hipStream_t stream);
+// kl a multiple of 64), with the exact grouped select over the group maxima
+// gkey ([rows, ceil(L/g)], groups of g) as the fallback.  pool / sel may be
+// null (target skipped).  zero_counters (or null): [rows] set to zero (the
+// arrival counters of a following pool rescoring).
+struct BlockSelect {
+    const float* block_max = nullptr;
+    int64_t L = 0;
+    int32_t rows = 0;
+    const int32_t* n_visible = nullptr;
+    const uint32_t* gkey = nullptr;
+    int32_t g = 0;
+    const uint32_t* cand_key = nullptr;
+    const int32_t* cand_blk = nullptr;
+    const int32_t* cand_full = nullptr;
+    int32_t chunks = 0, kl = 0;
+    int32_t nb = 0, k = 0;
+    int32_t* pool = nullptr;
+    int32_t* sel = nullptr;
+    uint32_t* zero_counters = nullptr;
+};
+hipError_t launch_block_select(const BlockSelect& S, hipStream_t stream);
 
 hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,

@@ -402,13 +402,56 @@ struct BlockSelJob {
     int32_t nb, k;            // targets (0: not wanted)
     int32_t* pool;            // [rows, nb] ascending block ids, -1 padded
     int32_t* sel;             // [rows, k]
+    uint32_t* zero_counters;  // [rows] or null: set to zero (by workgroup 2r)
 };
 
 struct BlockSelSmem {
     GroupSmem gs;
     uint32_t chunk_taken[kTopkSegment / 64];  // chosen candidates per chunk (kl >= 64)
-    uint32_t invalid;
 };
+
+// Top-t of one row's candidate lists (chunks lists of kl, a multiple of 64)
+// into out[0..t) -- unless a full chunk had all kl of its candidates chosen:
+// then nothing is written and the result is false.
+template <int P>
+__device__ __forceinline__ bool select_candidates(const uint32_t* __restrict__ ck,
+                                                  const int32_t* __restrict__ ci,
+                                                  const int32_t* __restrict__ cf, int32_t chunks,
+                                                  int32_t kl, int32_t t, int32_t* __restrict__ out,
+                                                  BlockSelSmem& bs, int tid, int lane, int wave)
+{
+    Smem& sm = bs.gs.sm;
+    const int64_t n = (int64_t)chunks * kl;
+    uint32_t key[P];
+    int32_t id[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int64_t e = (int64_t)kThreads * i + tid;
+        key[i] = e < n ? ck[e] : 0u;
+        id[i] = e < n ? ci[e] : -1;
+    }
+    const int32_t full = tid < chunks ? cf[tid] : 0;  // chunks <= 256
+    if (tid < chunks)
+        bs.chunk_taken[tid] = 0u;  // ordered before the counts by find_threshold's barriers
+    sel::clear_hist(sm, tid);
+    const Pick pk = find_threshold(key, (uint32_t)t, sm, tid, lane, wave);
+    bool take[P];
+    uint32_t off[P];
+    const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
+    // chosen candidates per chunk: the 64 lanes of a wave's slot lie in one chunk
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const uint64_t bt = __ballot(take[i]);
+        if (lane == 0 && bt != 0ull)
+            atomicAdd(&bs.chunk_taken[(kThreads * i + 64 * wave) / kl], (uint32_t)__popcll(bt));
+    }
+    __syncthreads();
+    const bool bad = tid < chunks && full != 0 && bs.chunk_taken[tid] >= (uint32_t)kl;
+    if (__syncthreads_or(bad ? 1 : 0) != 0)
+        return false;
+    write_result(take, off, key, id, chosen, t, tid, out, nullptr, nullptr);
+    return true;
+}
 
 // Grid: rows x 2 -- workgroup 2r selects row r's top-k blocks (what the Full
 // layer's own top-k waits for), workgroup 2r + 1 its pool, side by side.
@@ -423,81 +466,50 @@ block_select_kernel(BlockSelJob J)
     const int wave = tid >> 6;
     const int64_t row = blockIdx.x / 2;
     const int pass = blockIdx.x % 2;
+    if (pass == 0 && J.zero_counters != nullptr && tid == 0)
+        J.zero_counters[row] = 0u;
     const int32_t t = pass == 0 ? J.k : J.nb;
     int32_t* out = pass == 0 ? J.sel : J.pool;
     if (t <= 0 || out == nullptr)
         return;
+    out += row * t;
     int64_t nvb = J.n_visible[row];
     nvb = nvb < 0 ? 0 : (nvb + kBlock - 1) / kBlock;
     nvb = nvb > J.L ? J.L : nvb;
 
-    uint32_t key[P];
-    int32_t id[P];
-    int32_t full = 0;  // thread c < chunks: whether chunk c left blocks out
     if (J.cand_key != nullptr) {
         const int64_t n = (int64_t)J.chunks * J.kl;
-        const uint32_t* ck = J.cand_key + row * n;
-        const int32_t* cb = J.cand_blk + row * n;
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            const int64_t e = (int64_t)kThreads * i + tid;
-            key[i] = e < n ? ck[e] : 0u;
-            id[i] = e < n ? cb[e] : -1;
-        }
-        full = tid < J.chunks ? J.cand_full[row * J.chunks + tid] : 0;  // chunks <= 256
-        if (tid < J.chunks)
-            bs.chunk_taken[tid] = 0u;
-        if (tid == 0)
-            bs.invalid = 0u;
-    } else {
-        const float* srow = J.block_max + row * J.L;
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            const int64_t e = (int64_t)kThreads * i + tid;
-            const float f = J.L > 0 ? srow[e < nvb ? e : 0] : 0.0f;  // no block maxima when L == 0
-            key[i] = e < nvb && !__builtin_isnan(f) ? order_key(f) : 0u;
-            id[i] = (int32_t)e;
-        }
-    }
-    {
-        out += row * t;
-        sel::clear_hist(sm, tid);
-        const Pick pk = find_threshold(key, (uint32_t)t, sm, tid, lane, wave);
-        bool take[P];
-        uint32_t off[P];
-        const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
-        bool fallback = false;
-        if (J.cand_key != nullptr) {
-            // chosen candidates per chunk: kl is a multiple of 64, so the 64 lanes of a
-            // wave's slot all belong to one chunk and one ballot counts them (the counters
-            // were cleared before find_threshold's first barrier)
-#pragma unroll
-            for (int i = 0; i < P; ++i) {
-                const uint64_t bt = __ballot(take[i]);
-                if (lane == 0 && bt != 0ull)
-                    atomicAdd(&bs.chunk_taken[(kThreads * i + 64 * wave) / J.kl],
-                              (uint32_t)__popcll(bt));
-            }
-            __syncthreads();
-            if (tid < J.chunks && full != 0 && bs.chunk_taken[tid] >= (uint32_t)J.kl)
-                bs.invalid = 1u;
-            __syncthreads();
-            fallback = bs.invalid != 0u;
-        }
-        if (!fallback) {
-            write_result(take, off, key, id, chosen, t, tid, out, nullptr, nullptr);
+        if (select_candidates<P>(J.cand_key + row * n, J.cand_blk + row * n,
+                                 J.cand_full + row * J.chunks, J.chunks, J.kl, t, out, bs, tid,
+                                 lane, wave))
             return;
-        } else {
-            // exact: the grouped select over the row's group maxima
-            sel::clear_hist(sm, tid);
-            if (J.g == 8)
-                grouped_select_row_call<8>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
-                                           J.gkey + row * J.ngroups, t, out, bs.gs);
-            else
-                grouped_select_row_call<0>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
-                                           J.gkey + row * J.ngroups, t, out, bs.gs);
-        }
+        // exact: the grouped select over the row's group maxima
+        sel::clear_hist(sm, tid);
+        if (J.g == 8)
+            grouped_select_row_call<8>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
+                                       J.gkey + row * J.ngroups, t, out, bs.gs);
+        else
+            grouped_select_row_call<0>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
+                                       J.gkey + row * J.ngroups, t, out, bs.gs);
+        return;
     }
+    // direct: the row's block maxima
+    uint32_t key[P];
+    int32_t id[P];
+    const float* srow = J.block_max + row * J.L;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int64_t e = (int64_t)kThreads * i + tid;
+        const float f = J.L > 0 ? srow[e < nvb ? e : 0] : 0.0f;  // no block maxima when L == 0
+        key[i] = e < nvb && !__builtin_isnan(f) ? order_key(f) : 0u;
+        id[i] = (int32_t)e;
+    }
+    sel::clear_hist(sm, tid);
+    const Pick pk = find_threshold(key, (uint32_t)t, sm, tid, lane, wave);
+    bool take[P];
+    uint32_t off[P];
+    const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
+    write_result(take, off, key, id, chosen, t, tid, out, nullptr, nullptr);
 }
 
 int64_t segments(int64_t L)
@@ -532,18 +544,16 @@ int32_t topk_group_size(int64_t L, int32_t k)
     return group_size(L, k);
 }
 
-hipError_t launch_block_select(const float* block_max, int64_t L, int32_t rows,
-                               const int32_t* n_visible, const uint32_t* gkey, int32_t g,
-                               const uint32_t* cand_key, const int32_t* cand_blk,
-                               const int32_t* cand_full, int32_t chunks, int32_t kl, int32_t nb,
-                               int32_t k, int32_t* pool, int32_t* sel, hipStream_t stream)
+hipError_t launch_block_select(const BlockSelect& S, hipStream_t stream)
 {
-    if (rows == 0)
+    if (S.rows == 0)
         return hipSuccess;
-    BlockSelJob J{block_max, L, n_visible, gkey, g > 0 ? (L + g - 1) / g : 0, g,
-                  cand_key, cand_blk, cand_full, chunks, kl, nb, k, pool, sel};
-    const int64_t n = cand_key != nullptr ? (int64_t)chunks * kl : L;
-    const dim3 grid((uint32_t)(2 * rows)), block(kThreads);
+    const int32_t g = S.g;
+    BlockSelJob J{S.block_max, S.L, S.n_visible, S.gkey, g > 0 ? (S.L + g - 1) / g : 0, g,
+                  S.cand_key, S.cand_blk, S.cand_full, S.chunks, S.kl, S.nb, S.k, S.pool, S.sel,
+                  S.zero_counters};
+    const int64_t n = S.cand_key != nullptr ? (int64_t)S.chunks * S.kl : S.L;
+    const dim3 grid((uint32_t)(2 * S.rows)), block(kThreads);
     if (n <= 4 * kThreads)
         block_select_kernel<4><<<grid, block, 0, stream>>>(J);
     else if (n <= 8 * kThreads)

@@ -11,11 +11,12 @@ notes, [A] 3.3-3.4 of the translated abstract):
 
 How the Full layer's top-k is found: its top-k entries always lie in its
 top-k blocks (a block ranked above a winner's block holds another winner,
-also under the lower-index tie-break), so the scan keeps only block maxima,
-one call selects both the pool (top-nb blocks) and the top-k blocks, and the
-winners are selected among the top-k blocks' rescored positions (k * 8 of
-them).  Every step is a libcsa2 kernel; this module only sequences calls and
-owns reusable buffers.
+also under the lower-index tie-break), so the scan keeps no per-entry
+scores: one call (csa2_index_full_select) scans, selects the pool (top-nb
+blocks) and finds the winners among the top-k blocks' positions (from the
+scan's per-chunk candidates on long rows, else by rescoring those k * 8
+positions).  Every step is a libcsa2 kernel; this module only sequences
+calls and owns reusable buffers.
 """
 from __future__ import annotations
 
@@ -97,16 +98,17 @@ def full_indexer(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, n_blo
                  k: int, nb: int, scores=None, stream=None, scan_events=None):
     """Full layer indexer: block scan, pool, top-k.  Leaves buf.pool and buf.topk.
 
-    The scan, the pool and the top-k blocks are one library call (csa2_index_full_select);
-    with per-entry scores asked for (tests), the scan and two csa2_topk calls instead."""
+    One library call (csa2_index_full_select); with per-entry scores asked for
+    (tests), the scan, two csa2_topk calls over the block maxima and the top-k
+    blocks' rescoring instead."""
     if scores is None:
         _lib.index_full_select(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max,
-                               buf.sel_blocks, pool=buf.pool, ws=buf.ws_sel, stream=stream,
+                               buf.topk, pool=buf.pool, ws=buf.ws_sel, stream=stream,
                                scan_events=scan_events)
-    else:
-        _lib.index_full(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, scores=scores,
-                        stream=stream)
-        select_blocks(buf, n_blocks_valid, k, nb, stream=stream)
+        return
+    _lib.index_full(q_idx, w_idx, k_codes, k_scales, n_visible, buf.block_max, scores=scores,
+                    stream=stream)
+    select_blocks(buf, n_blocks_valid, k, nb, stream=stream)
     _pool_topk(buf, q_idx, w_idx, k_codes, k_scales, n_visible, buf.sel_blocks, k, stream)
 
 

@@ -1,8 +1,8 @@
 """Adversarial end-to-end parity of the Full layer ([N] 2.2, [A] 3.4: the block score
 is the largest index score of its positions; the pool holds the 2048 best blocks; the
 top-k entries are ranked over the whole visible range with the lower index winning a
-tie) through the production call sequence (csa2_index_full_select -> csa2_index_pool_topk
--> csa2_sparse_attn), against the oracle's literal full-range top-k:
+tie) through the production call sequence (csa2_index_full_select -> csa2_sparse_attn),
+against the oracle's literal full-range top-k:
 
 * duplicated indexer keys -- every key repeats with a period, so scores and block
   maxima tie EXACTLY across periods, at the k-th score and at the 2048-th block maximum;

@@ -1,11 +1,13 @@
-"""csa2_index_full_select (the Full-layer scan with its pool and top-k blocks in one
-call) against the same scan followed by two csa2_topk calls over its block maxima:
-bit-exact pools and top-k blocks, on shapes that take each of its paths -- the direct
-select (rows of at most 16384 blocks), the scan's per-chunk candidates, their exact
-fallback (a chunk holding more winners than it listed: a planted cluster of strong
-keys, and exact ties from a zero query or a periodic cache), and two csa2_topk calls
-(rows too long for the candidates) -- with ragged, empty and stale-workspace rows.
-csa2_topk itself is checked against the oracle's selection in test_gpu_stages.py."""
+"""csa2_index_full_select (the Full layer's scan, pool and top-k in one call) against
+the same scan's per-entry scores: bit-exact pools (csa2_topk over the block maxima) and
+top-k positions (csa2_topk over every score of the row: the literal full-range
+definition, on the same fp32 scores), on shapes that take each of its paths -- the
+direct block select with the top-k blocks rescored (rows of at most 16384 blocks), the
+scan's per-chunk block and entry candidates, their exact fallbacks (a chunk holding
+more winners than it listed: a planted cluster of strong keys, and exact ties from a
+zero query or a periodic cache), and csa2_topk calls (rows too long for the
+candidates) -- with ragged, empty and stale-workspace rows.  csa2_topk itself is
+checked against the oracle's selection in test_gpu_stages.py."""
 import numpy as np
 import pytest
 import torch
@@ -86,31 +88,35 @@ def test_index_full_select_matches_scan_then_topk(B, nq, n_cap, nb, k, nvis, kin
     ws = torch.full((max(ws_n, 256),), 0xC3, dtype=torch.uint8, device=dev())  # stale contents
     bm1 = torch.full((B, nq, max(nblk, 1)), 777.0, device=dev())
     pool1 = torch.full((B, nq, max(nb, 1)), -7, dtype=torch.int32, device=dev())
-    sel1 = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
+    top1 = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
     for rep in range(2):  # the second call finds the first call's workspace contents
-        L.index_full_select(qd, wd, kc, ks, nvd, bm1, sel1, pool=pool1 if nb else None, ws=ws)
+        L.index_full_select(qd, wd, kc, ks, nvd, bm1, top1, pool=pool1 if nb else None, ws=ws)
     torch.cuda.synchronize()
 
+    # the same scan with every score, then csa2_topk over the scores and block maxima
     bm2 = torch.full((B, nq, max(nblk, 1)), 777.0, device=dev())
+    sc = torch.full((B, nq, max(n_cap, 1)), -1.0, device=dev())
     if n_cap:
-        L.index_full(qd, wd, kc, ks, nvd, bm2)
+        L.index_full(qd, wd, kc, ks, nvd, bm2, scores=sc)
     nvb = t(((np.maximum(nv.astype(np.int64), 0) + 7) // 8).astype(np.int32))
-    tw = torch.empty(max(L.topk_workspace(nblk, B * nq, max(nb, k)), 8), dtype=torch.uint8,
-                     device=dev())
-    sel2 = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
-    L.topk(bm2[..., :nblk], k, sel2, n_valid=nvb, ws=tw)
+    nve = t(np.clip(nv, 0, n_cap).astype(np.int32))
+    tw_n = max(L.topk_workspace(max(n_cap, 1), B * nq, k), L.topk_workspace(max(nblk, 1), B * nq, max(nb, 1)))
+    tw = torch.empty(max(tw_n, 8), dtype=torch.uint8, device=dev())
+    top2 = torch.full((B, nq, k), -7, dtype=torch.int32, device=dev())
+    L.topk(sc if n_cap else sc[..., :0].contiguous(), k, top2, n_valid=nve, ws=tw)
     assert np.array_equal(bm1.cpu().numpy()[..., :nblk], bm2.cpu().numpy()[..., :nblk])
-    assert np.array_equal(sel1.cpu().numpy(), sel2.cpu().numpy()), "top-k blocks differ"
+    t1, t2 = top1.cpu().numpy(), top2.cpu().numpy()
+    assert np.array_equal(t1, t2), f"top-k differs in {int((t1 != t2).any(-1).sum())} rows"
     if nb:
         pool2 = torch.full((B, nq, nb), -7, dtype=torch.int32, device=dev())
         L.topk(bm2[..., :nblk], nb, pool2, n_valid=nvb, ws=tw)
-        assert np.array_equal(pool1.cpu().numpy(), pool2.cpu().numpy()), "pools differ"
-    # the k best blocks lie in the pool when the pool has at least k blocks
-    if nb >= k:
-        p, s = pool1.cpu().numpy(), sel1.cpu().numpy()
-        for r in range(B * nq):
-            sr = s.reshape(-1, k)[r]
-            assert set(sr[sr >= 0]) <= set(p.reshape(-1, nb)[r])
+        p1 = pool1.cpu().numpy()
+        assert np.array_equal(p1, pool2.cpu().numpy()), "pools differ"
+        # the top-k positions lie in the pool when the pool has at least k blocks
+        if nb >= k:
+            for r in range(B * nq):
+                tr = t1.reshape(-1, k)[r]
+                assert set((tr[tr >= 0] // 8).tolist()) <= set(p1.reshape(-1, nb)[r].tolist())
 
 
 POOL_CASES = [
