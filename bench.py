@@ -45,7 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_full_scan_1M_b16_traffic.tx
 # and the build script (flags); the traffic counters are valid only for this exact
 # input (launch.h holds only host launcher declarations)
 SCAN_SOURCES = [os.path.join(ROOT, "kv_cache_decode_mxfp4_amd", *p) for p in (
-    ("csrc", "indexer.hip"), ("csrc", "device_common.h"), ("csrc", "dims.h"), ("build.py",))]
+    ("csrc", "indexer.hip"), ("csrc", "score.h"), ("csrc", "select.h"),
+    ("csrc", "device_common.h"), ("csrc", "dims.h"), ("build.py",))]
 CHUNK_ROWS = 1 << 18
 SCAN_EVENT_EVERY = 4
 

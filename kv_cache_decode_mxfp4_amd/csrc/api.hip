@@ -254,6 +254,13 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w, const uint8_
 // positions rescored: pool rescoring + top-k in one launch (rescore_fused;
 // its arrival counters are cleared by the block select), or a pool scan and
 // csa2_topk.
+// The fused rescoring (pool_topk_kernel) wins while few positions are rescored
+// (latency-bound: one launch instead of two); beyond about 32 rows x 4096
+// positions the pool scan (8 key tiles per wave in flight) and csa2_topk are
+// faster -- measured on the MI355X: 16 x 4096 positions 14.2 vs 18.2 us,
+// 64 x 4096 26.1 vs 18.3 us, 128 x 16384 139.4 vs 58.5 us.
+constexpr int64_t kFusedRescoreMaxPositions = 32 * 4096;
+
 struct FullSelectPlan {
     int mode;
     int64_t L;            // blocks per row
@@ -312,7 +319,8 @@ static FullSelectPlan full_select_plan(int64_t n_cap, int32_t B, int32_t nq, int
         P.off_topk_ws = take(t > t3 ? t : t3);
     }
     P.off_tb = take((size_t)rows * k * 4);
-    P.rescore_fused = P.mode != 2 && (int64_t)L8 <= csa2::kTopkSegment;
+    P.rescore_fused = P.mode != 2 && (int64_t)L8 <= csa2::kTopkSegment &&
+                      rows * (int64_t)L8 <= kFusedRescoreMaxPositions;
     if (P.rescore_fused) {
         P.off_rescore = take(csa2::pool_topk_workspace((int32_t)rows, k));
     } else {

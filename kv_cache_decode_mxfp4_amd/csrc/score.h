@@ -1,5 +1,5 @@
-// Indexer score of one entry for one query on MFMA, shared by the full scan,
-// the pool scans and the block select's rescoring ([N] 2.2 and [A] 3.4 of
+// Indexer score of one entry for one query on MFMA, shared by the full scan
+// and the pool scans ([N] 2.2 and [A] 3.4 of
 // the DeepSeek-V4.1 pages: the indexer scores entries with 32 heads x 128
 // dims; reading: s_j = sum_h w_h * max(0, q_h . k_j), the pages fixing the
 // shape, not the formula).  Every caller scores with these functions, so a

@@ -27,7 +27,12 @@ import torch
 from . import _lib
 
 BLOCK = 8
-FUSED_MAX_BLOCKS = 2048  # csa2_index_pool_topk rescores at most 16384 positions
+FUSED_MAX_BLOCKS = 2048  # csa2_index_pool_topk rescores at most 16384 positions per row
+# Beyond about 32 rows x 4096 rescored positions the pool scan (more key gathers in
+# flight) and csa2_topk beat the one-launch rescoring + top-k: measured on the MI355X,
+# 16 x 4096 positions 14.2 vs 18.2 us, 64 x 4096 26.1 vs 18.3 us, 128 x 16384 139.4 vs
+# 58.5 us (the same choice as inside csa2_index_full_select).
+FUSED_MAX_POSITIONS = 32 * 4096
 
 
 def n_valid_blocks(n_visible: torch.Tensor) -> torch.Tensor:
@@ -67,7 +72,9 @@ class Buffers:
         ws_a = _lib.sparse_attn_workspace(B, nq, k, n_win)
         ws_s = _lib.index_full_select_workspace(n_cap, B, nq, nb, k)
         # arrival counters of the fused pool rescoring + top-k: zeroed once here
-        ws_pt = _lib.index_pool_topk_workspace(B, nq, min(nsel, FUSED_MAX_BLOCKS))
+        # (sized for the largest pool that takes the fused path at this row count)
+        fused_blocks = min(nsel, FUSED_MAX_BLOCKS, FUSED_MAX_POSITIONS // max(B * nq * BLOCK, 1))
+        ws_pt = _lib.index_pool_topk_workspace(B, nq, fused_blocks)
         return Buffers(
             block_max=torch.empty(B, nq, nblk, dtype=f32, device=device),
             pool=pool,
@@ -115,9 +122,9 @@ def full_indexer(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, n_blo
 def _pool_topk(buf: Buffers, q_idx, w_idx, k_codes, k_scales, n_visible, blocks, k: int,
                stream=None):
     """Rescore the positions of `blocks` with this query and select the top-k into buf.topk:
-    one fused call for pools of at most 2048 blocks, else the pool scan and csa2_topk."""
+    one fused call for few rescored positions, else the pool scan and csa2_topk."""
     B, nq, nbk = blocks.shape
-    if nbk <= FUSED_MAX_BLOCKS:
+    if nbk <= FUSED_MAX_BLOCKS and B * nq * nbk * BLOCK <= FUSED_MAX_POSITIONS:
         _lib.index_pool_topk(q_idx, w_idx, k_codes, k_scales, blocks, n_visible, buf.topk,
                              buf.ws_pool_topk, stream=stream)
         return

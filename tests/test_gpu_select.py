@@ -2,12 +2,13 @@
 the same scan's per-entry scores: bit-exact pools (csa2_topk over the block maxima) and
 top-k positions (csa2_topk over every score of the row: the literal full-range
 definition, on the same fp32 scores), on shapes that take each of its paths -- the
-direct block select with the top-k blocks rescored (rows of at most 16384 blocks), the
-scan's per-chunk block and entry candidates, their exact fallbacks (a chunk holding
-more winners than it listed: a planted cluster of strong keys, and exact ties from a
-zero query or a periodic cache), and csa2_topk calls (rows too long for the
-candidates) -- with ragged, empty and stale-workspace rows.  csa2_topk itself is
-checked against the oracle's selection in test_gpu_stages.py."""
+direct block select (rows of at most 16384 blocks), the scan's per-chunk block
+candidates and their exact fallback (a chunk holding more winners than it listed: a
+planted cluster of strong keys, and exact ties from a zero query or a periodic cache),
+csa2_topk calls (rows too long for the candidates); the top-k blocks' positions
+rescored in one launch (few rows) or by a pool scan and csa2_topk (many rows) -- with
+ragged, empty and stale-workspace rows.  csa2_topk itself is checked against the
+oracle's selection in test_gpu_stages.py."""
 import numpy as np
 import pytest
 import torch
@@ -63,6 +64,8 @@ CASES = [
     (4, 1, 262144, 2048, 512, None, "zero_query"),                # all ties: fallback
     (4, 1, 262144, 2048, 512, None, "periodic"),                  # exact ties across blocks
     (16, 1, 1 << 20, 2048, 512, None, "periodic"),
+    (40, 1, 262144, 2048, 512, None, "random"),                   # candidates; rescoring by pool scan + top-k
+    (64, 1, 65536, 2048, 512, None, "random"),                    # direct select; pool scan + top-k
     (2, 1, 140003, 2048, 512, [140003, 70001], "random"),          # too many chunks: two top-k calls
     (3, 1, 65536, 2048, 512, [65536, 40001, 3], "random"),         # direct select
     (1, 4, 300000, 2048, 512, [300000, 299999, 150000, 5], "random"),  # paired scan rows
