@@ -18,16 +18,24 @@
  *       window entries; K = V single-head MQA on a 512-dim latent.
  *
  * Layer call sequences (one query row per (sequence, query)):
- *   Full     csa2_index_full -> csa2_topk(block maxima, nb) = pool
- *            (or both in one call: csa2_index_full_pool)
- *            -> csa2_index_pool(own query, pool) -> csa2_topk(k) = top-k
- *            -> csa2_sparse_attn.
- *            When the pool has fewer than k blocks (or there is no pool, as
- *            in the encoder), select the top-k blocks instead of the pool for
- *            the pool step: the top-k entries always lie in the top-k blocks.
- *   Reindex  csa2_index_pool(own query, Full layer's pool) -> csa2_topk(k)
- *            -> csa2_sparse_attn.
+ *   Full     csa2_index_full_select (the scan, the pool of nb blocks and the
+ *            top-k entries in one call) -> csa2_sparse_attn.
+ *            Step by step: csa2_index_full -> csa2_topk(block maxima, nb) =
+ *            pool and csa2_topk(block maxima, k) = top-k blocks ->
+ *            csa2_index_pool(own query, top-k blocks) -> csa2_topk(k).
+ *   Reindex  csa2_index_pool_topk(own query, Full layer's pool) (or
+ *            csa2_index_pool -> csa2_topk(k)) -> csa2_sparse_attn.
  *   Reuse    csa2_sparse_attn with the latest top-k.
+ *
+ * How the Full layer's top-k is found: the scan keeps no per-entry scores
+ * and emits no per-entry candidates; the top-k entries of a row always lie
+ * in its k best blocks (a block ranked above a winner's block holds a better
+ * entry, also under the lower-index tie-break), so the top-k is selected
+ * among those blocks' k * 8 positions, rescored with the scan's own score
+ * function (bit-identical scores).  Per-entry candidates from the scan were
+ * measured slower on the MI355X than this rescoring.  The scan_start /
+ * scan_stop arguments of the fused calls are timing instrumentation (events
+ * the scan kernel's dispatch records) and change nothing else.
  *
  * Conventions for every call:
  *   - All tensors are row-major and contiguous, except the indexer-key code

@@ -568,8 +568,8 @@ def test_sparse_attn_batched_kernel_many_rows():
 
 
 def _grouped_case(seed=21, B=3, nq=8):
-    """24 query rows (3 sequences x 8 queries): more rows than the spread form serves, so
-    the grouped form runs.  Row r mixes top-k padding and window shapes by r % 6: plain,
+    """24 query rows (3 sequences x 8 queries), called without a workspace: the grouped
+    form without key splits runs.  Row r mixes top-k padding and window shapes by r % 6: plain,
     padded (-1 and out-of-range ids), window only, empty, window past the ring capacity,
     short window; k = 100 leaves a ragged last tile."""
     N, k, cap = 2000, 100, 160
