@@ -32,6 +32,7 @@
 //     candidates (the global top-k is a subset of their union, and the
 //     candidate lists keep position order) until one segment remains.
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -453,19 +454,44 @@ __device__ __forceinline__ bool select_candidates(const uint32_t* __restrict__ c
     return true;
 }
 
-// Grid: rows x 2 -- workgroup 2r selects row r's top-k blocks (what the Full
-// layer's own top-k waits for), workgroup 2r + 1 its pool, side by side.
+// Direct form: the t best of the row's nvb block maxima into out[0..t).
 template <int P>
-__global__ void __launch_bounds__(kThreads)
-block_select_kernel(BlockSelJob J)
+__device__ __forceinline__ void select_direct(const float* __restrict__ srow, int64_t L,
+                                              int64_t nvb, int32_t t, int32_t* __restrict__ out,
+                                              Smem& sm, int tid, int lane, int wave)
 {
-    __shared__ BlockSelSmem bs;
-    Smem& sm = bs.gs.sm;
+    uint32_t key[P];
+    int32_t id[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int64_t e = (int64_t)kThreads * i + tid;
+        const float f = L > 0 ? srow[e < nvb ? e : 0] : 0.0f;  // no block maxima when L == 0
+        key[i] = e < nvb && !__builtin_isnan(f) ? order_key(f) : 0u;
+        id[i] = (int32_t)e;
+    }
+    sel::clear_hist(sm, tid);
+    const Pick pk = find_threshold(key, (uint32_t)t, sm, tid, lane, wave);
+    bool take[P];
+    uint32_t off[P];
+    const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
+    write_result(take, off, key, id, chosen, t, tid, out, nullptr, nullptr);
+}
+
+// Grid: rows x passes -- with two passes workgroup 2r selects row r's top-k
+// blocks (what the Full layer's own top-k waits for) and 2r + 1 its pool, side
+// by side; with one pass (no pool) workgroup r selects the top-k blocks.
+// kCand: the candidate form, with its out-of-line grouped fallback; the direct
+// form is compiled without it (no scratch memory, 16 KB of LDS).
+template <int P, bool kCand>
+__global__ void __launch_bounds__(kThreads)
+block_select_kernel(BlockSelJob J, int32_t passes)
+{
+    __shared__ std::conditional_t<kCand, BlockSelSmem, Smem> shm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t row = blockIdx.x / 2;
-    const int pass = blockIdx.x % 2;
+    const int64_t row = blockIdx.x / passes;
+    const int pass = blockIdx.x % passes;
     if (pass == 0 && J.zero_counters != nullptr && tid == 0)
         J.zero_counters[row] = 0u;
     const int32_t t = pass == 0 ? J.k : J.nb;
@@ -476,40 +502,23 @@ block_select_kernel(BlockSelJob J)
     int64_t nvb = J.n_visible[row];
     nvb = nvb < 0 ? 0 : (nvb + kBlock - 1) / kBlock;
     nvb = nvb > J.L ? J.L : nvb;
-
-    if (J.cand_key != nullptr) {
+    if constexpr (kCand) {
         const int64_t n = (int64_t)J.chunks * J.kl;
         if (select_candidates<P>(J.cand_key + row * n, J.cand_blk + row * n,
-                                 J.cand_full + row * J.chunks, J.chunks, J.kl, t, out, bs, tid,
+                                 J.cand_full + row * J.chunks, J.chunks, J.kl, t, out, shm, tid,
                                  lane, wave))
             return;
         // exact: the grouped select over the row's group maxima
-        sel::clear_hist(sm, tid);
+        sel::clear_hist(shm.gs.sm, tid);
         if (J.g == 8)
             grouped_select_row_call<8>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
-                                       J.gkey + row * J.ngroups, t, out, bs.gs);
+                                       J.gkey + row * J.ngroups, t, out, shm.gs);
         else
             grouped_select_row_call<0>(J.block_max + row * J.L, nvb, J.g, J.ngroups,
-                                       J.gkey + row * J.ngroups, t, out, bs.gs);
-        return;
+                                       J.gkey + row * J.ngroups, t, out, shm.gs);
+    } else {
+        select_direct<P>(J.block_max + row * J.L, J.L, nvb, t, out, shm, tid, lane, wave);
     }
-    // direct: the row's block maxima
-    uint32_t key[P];
-    int32_t id[P];
-    const float* srow = J.block_max + row * J.L;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const int64_t e = (int64_t)kThreads * i + tid;
-        const float f = J.L > 0 ? srow[e < nvb ? e : 0] : 0.0f;  // no block maxima when L == 0
-        key[i] = e < nvb && !__builtin_isnan(f) ? order_key(f) : 0u;
-        id[i] = (int32_t)e;
-    }
-    sel::clear_hist(sm, tid);
-    const Pick pk = find_threshold(key, (uint32_t)t, sm, tid, lane, wave);
-    bool take[P];
-    uint32_t off[P];
-    const uint32_t chosen = place(key, pk, take, off, sm, lane, wave);
-    write_result(take, off, key, id, chosen, t, tid, out, nullptr, nullptr);
 }
 
 int64_t segments(int64_t L)
@@ -552,14 +561,23 @@ hipError_t launch_block_select(const BlockSelect& S, hipStream_t stream)
     BlockSelJob J{S.block_max, S.L, S.n_visible, S.gkey, g > 0 ? (S.L + g - 1) / g : 0, g,
                   S.cand_key, S.cand_blk, S.cand_full, S.chunks, S.kl, S.nb, S.k, S.pool, S.sel,
                   S.zero_counters};
-    const int64_t n = S.cand_key != nullptr ? (int64_t)S.chunks * S.kl : S.L;
-    const dim3 grid((uint32_t)(2 * S.rows)), block(kThreads);
-    if (n <= 4 * kThreads)
-        block_select_kernel<4><<<grid, block, 0, stream>>>(J);
-    else if (n <= 8 * kThreads)
-        block_select_kernel<8><<<grid, block, 0, stream>>>(J);
-    else
-        block_select_kernel<kPer><<<grid, block, 0, stream>>>(J);
+    const bool cand = S.cand_key != nullptr;
+    const int64_t n = cand ? (int64_t)S.chunks * S.kl : S.L;
+    const int32_t passes = S.nb > 0 && S.pool != nullptr ? 2 : 1;
+    const dim3 grid((uint32_t)(passes * S.rows)), block(kThreads);
+#define CSA2_BLOCK_SELECT(PP)                                                            \
+    if (cand)                                                                            \
+        block_select_kernel<PP, true><<<grid, block, 0, stream>>>(J, passes);           \
+    else                                                                                 \
+        block_select_kernel<PP, false><<<grid, block, 0, stream>>>(J, passes);
+    if (n <= 4 * kThreads) {
+        CSA2_BLOCK_SELECT(4)
+    } else if (n <= 8 * kThreads) {
+        CSA2_BLOCK_SELECT(8)
+    } else {
+        CSA2_BLOCK_SELECT(kPer)
+    }
+#undef CSA2_BLOCK_SELECT
     return hipGetLastError();
 }
 
