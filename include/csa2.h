@@ -361,10 +361,12 @@ csa2_status csa2_topk_noalloc(const float* score, const int32_t* idx, int64_t L,
  * the 512-dim latent, top-k compressed entries plus 128 window entries).
  *   q          bf16 [B, nq, 64, 512], 16-byte aligned.
  *   kv_codes   u8 [B, n_cap, 256], kv_scales u8 [B, n_cap, 32]: MXFP4 main KV
- *              (NULL allowed when n_cap == 0: no compressed entries yet).
+ *              (NULL allowed when n_cap == 0: no compressed entries yet);
+ *              n_cap <= 2^24, else CSA2_ERR_UNSUPPORTED.
  *   topk       int32 [B, nq, k]: entry ids; ids outside [0, n_cap) skipped.
- *   swa        u8 [B, swa_cap, 512] E4M3FN window rows; query (b, i) uses rows
- *              [max(0, swa_end[b,i] - n_win), min(swa_end[b,i], swa_cap)).
+ *   swa        u8 [B, swa_cap, 512] E4M3FN window rows, swa_cap <= 2^22; query
+ *              (b, i) uses rows [max(0, swa_end[b,i] - n_win),
+ *              min(swa_end[b,i], swa_cap)).
  *   softmax_scale  multiplies q . v before the softmax.
  *   out        fp32 [B, nq, 64, 512], 16-byte aligned: o_h = sum_j p_j v_j, p = softmax over the
  *              union of selected entries and window rows (one joint softmax);
@@ -375,8 +377,8 @@ csa2_status csa2_topk_noalloc(const float* score, const int32_t* idx, int64_t L,
  *              only for few query rows) each row's keys are split over several
  *              workgroups whose partial results are merged by a second launch;
  *              with NULL or fewer bytes the call still completes, with one
- *              workgroup per (row, 16 heads) over every key.  Each form is
- *              deterministic; the two differ only in fp32 rounding order.
+ *              workgroup per (row, group of heads) over every key.  Each form
+ *              is deterministic; the forms differ only in fp32 rounding order.
  * Dequantisation is exact in fp16; products accumulate in fp32.
  */
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t nq,

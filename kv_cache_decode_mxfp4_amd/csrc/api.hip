@@ -596,6 +596,9 @@ static csa2_status attn_common(const uint16_t* q, int32_t B, int32_t nq,
             CSA2_ERR_INVALID_ARG, "%s: negative size", name);
     REQUIRE((int64_t)B * nq <= (1ll << 24), CSA2_ERR_INVALID_ARG, "%s: too many query rows", name);
     REQUIRE(k <= 65536 && n_win <= 65536, CSA2_ERR_UNSUPPORTED, "%s: k or n_win too large", name);
+    // the kernels address a sequence's rows with 32-bit byte offsets
+    REQUIRE(n_cap <= (1ll << 24) && swa_cap <= (1 << 22), CSA2_ERR_UNSUPPORTED,
+            "%s: more than 2^24 main entries or 2^22 window rows per sequence", name);
     const int32_t queries = B * nq;
     if (queries == 0)
         return CSA2_OK;

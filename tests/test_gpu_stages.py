@@ -544,7 +544,7 @@ def test_sparse_attn_k_not_multiple_of_tile_and_large_k():
 
 
 def test_sparse_attn_batched_kernel_many_rows():
-    """300 query rows of one sequence (the grouped form: one workgroup per 16 heads,
+    """300 query rows of one sequence (one workgroup per row and its 64 heads, the
     channels split over the waves), sampled rows against the oracle."""
     N, nq, k, cap = 3000, 300, 96, 500
     x = synth.latent_rows(synth.key(13, 2), synth.key(13, 3), 0, N, 512)
@@ -654,11 +654,12 @@ def test_sparse_attn_grouped_form_rope_bf16():
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-def test_sparse_attn_two_head_groups_bit_identical_to_one(bf16):
-    """From 512 query rows the many-row form takes two head groups per workgroup; the same
-    rows in calls of fewer rows take one.  Outputs and lse are bit-identical, and sampled
-    rows of every padding / window kind match the oracle."""
-    vc, vs, sw, sel, q, swa_end = _grouped_case(seed=24, B=1, nq=520)
+def test_sparse_attn_head_group_sizes(bf16):
+    """A workgroup serves 64 heads from 256 query rows, 32 heads from 128 and 16 below.  The
+    16- and 64-head forms (both on 32-key tiles) give bit-identical outputs and lse; the
+    32-head form (64-key tiles) differs from them only in fp32 rounding.  Sampled rows of
+    every padding / window kind match the oracle."""
+    vc, vs, sw, sel, q, swa_end = _grouped_case(seed=24, B=1, nq=300)
     nq = q.shape[1]
     rng = np.random.default_rng(25)
     ang = rng.uniform(-np.pi, np.pi, (nq, 32))
@@ -677,20 +678,33 @@ def test_sparse_attn_two_head_groups_bit_identical_to_one(bf16):
             L.sparse_attn(*args, out, lse)
         return out.cpu().numpy(), lse.cpu().numpy()
 
-    o2, l2 = run(0, nq)             # two head groups per workgroup
-    o1a, l1a = run(0, 260)          # one head group per workgroup
-    o1b, l1b = run(260, nq)
-    assert np.array_equal(o2, np.concatenate([o1a, o1b], axis=1))
-    assert np.array_equal(l2, np.concatenate([l1a, l1b], axis=1))
-    if not bf16:
+    def chunks(size):
+        parts = [run(r0, min(r0 + size, nq)) for r0 in range(0, nq, size)]
+        return (np.concatenate([p[0] for p in parts], axis=1),
+                np.concatenate([p[1] for p in parts], axis=1))
+
+    o64, l64 = run(0, nq)        # 64 heads per workgroup
+    o16, l16 = chunks(100)       # 16 heads
+    o32, l32 = chunks(150)       # 32 heads
+    assert np.array_equal(o64, o16) and np.array_equal(l64, l16)
+    fin = np.isfinite(l64)
+    assert np.array_equal(fin, np.isfinite(l32))
+    assert np.all(np.abs(l32[fin] - l64[fin]) <= 1e-5)
+    if bf16:
+        a, b = _bf16_to_f32(o32.view(np.uint16)), _bf16_to_f32(o64.view(np.uint16))
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(b), 1e-30))) - 7)
+        assert np.all(np.abs(a - b) <= 1e-5 + ulp)
+    else:
+        assert max_abs(o32, o64) <= 1e-5
         for i in list(range(0, nq, 37)) + list(range(nq - 6, nq)):
             ro, rl = oracle.attention(q[0, i], vc[0], vs[0], sel[0, i], sw[0],
                                       int(swa_end[0, i]), 128, 1.0)
-            assert max_abs(o2[0, i], ro) <= ATTN_TOL, f"row {i}"
-            if np.all(np.isinf(rl)):
-                assert np.all(np.isneginf(l2[0, i])) and np.all(o2[0, i] == 0)
-            else:
-                assert max_abs(l2[0, i], rl) <= 1e-4, f"row {i}"
+            for o, lz in ((o64, l64), (o32, l32)):
+                assert max_abs(o[0, i], ro) <= ATTN_TOL, f"row {i}"
+                if np.all(np.isinf(rl)):
+                    assert np.all(np.isneginf(lz[0, i])) and np.all(o[0, i] == 0)
+                else:
+                    assert max_abs(lz[0, i], rl) <= 1e-4, f"row {i}"
 
 
 def _bf16_to_f32(bits):
