@@ -774,17 +774,30 @@ int64_t padded_rows(int32_t queries)
     return ((int64_t)queries + kXcds - 1) / kXcds * kXcds;
 }
 
-// Key splits for few query rows (16 heads per workgroup): enough workgroups to
-// cover the CUs once, at least two tiles per split; 1 when the rows alone
-// fill the CUs.
-int32_t attn_splits(int32_t queries, int32_t k, int32_t n_win)
+// Key splits for few query rows: enough workgroups to cover the CUs once, at
+// least two 32-key tiles per split; 1 when the rows alone fill the CUs.  From
+// 64 rows the split workgroups take 32 heads (64 rows: 2 splits, 30.1 against
+// 32.9 us for 16 heads without splits); below, 16 (16 rows: 4 splits, 15.9
+// against 19.1 us for 32 heads in 8 splits, whose splits get too few tiles).
+#ifndef CSA2_ATTN_SPLIT32_MIN_ROWS
+#define CSA2_ATTN_SPLIT32_MIN_ROWS 64
+#endif
+constexpr int32_t kSplit32MinRows = CSA2_ATTN_SPLIT32_MIN_ROWS;
+
+struct SplitPlan {
+    int heads;       // heads per workgroup
+    int32_t splits;  // key splits per (row, head group)
+};
+
+SplitPlan split_plan(int32_t queries, int32_t k, int32_t n_win)
 {
-    const int64_t groups = padded_rows(queries) * kGroups;
+    const int heads = queries >= kSplit32MinRows ? 32 : 16;
+    const int64_t groups = padded_rows(queries) * (kHeads / heads);
     const int64_t tiles = ((int64_t)k + kTile - 1) / kTile + ((int64_t)n_win + kTile - 1) / kTile;
     int32_t s = 1;
     while (s < kMaxSplits && groups * s * 2 <= kSplitWgs && tiles >= kMinSplitTiles * 2 * s)
         s *= 2;
-    return s;
+    return {heads, s};
 }
 
 template <int kHW>
@@ -813,7 +826,8 @@ hipError_t launch_heads(const uint16_t* q, int32_t queries, int32_t nq,
 
 size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win)
 {
-    const int32_t s = attn_splits(queries, k, n_win);
+    const int32_t s = split_plan(queries, k, n_win).splits;
+    // one partial record per (row, 16 heads, split)
     return s > 1 ? (size_t)padded_rows(queries) * kGroups * s * kPartFloats * sizeof(float) : 0;
 }
 
@@ -833,15 +847,19 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t queries, int32_t nq,
     const bool bf16_out = out_bf16 != nullptr;
     const size_t need = attn_workspace(queries, k, n_win);
     if (need > 0 && ws != nullptr && ws_bytes >= need) {
-        // few rows: each row's keys split over workgroups of 16 heads, then the
-        // merge of the splits (a second launch: the kernel boundary orders the
-        // partials)
-        const int32_t splits = attn_splits(queries, k, n_win);
+        // few rows: each row's keys split over workgroups, then the merge of
+        // the splits (a second launch: the kernel boundary orders the partials)
+        const SplitPlan sp = split_plan(queries, k, n_win);
+        const int32_t splits = sp.splits;
         float* part = static_cast<float*>(ws);
         const hipError_t e =
-            launch_heads<16>(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k, swa, swa_cap,
-                             swa_end, n_win, scale_log2, splits, part, spec, bf16_out, nullptr,
-                             stream);
+            sp.heads == 32
+                ? launch_heads<32>(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k, swa,
+                                   swa_cap, swa_end, n_win, scale_log2, splits, part, spec,
+                                   bf16_out, nullptr, stream)
+                : launch_heads<16>(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k, swa,
+                                   swa_cap, swa_end, n_win, scale_log2, splits, part, spec,
+                                   bf16_out, nullptr, stream);
         if (e != hipSuccess)
             return e;
         const dim3 mgrid((uint32_t)(padded_rows(queries) * kGroups * kSlices)), mblock(256);

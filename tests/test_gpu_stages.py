@@ -707,6 +707,40 @@ def test_sparse_attn_head_group_sizes(bf16):
                     assert max_abs(lz[0, i], rl) <= 1e-4, f"row {i}"
 
 
+def test_sparse_attn_split_form_32_heads():
+    """64 query rows with the workspace: key splits over workgroups of 32 heads (2 splits)
+    and the merge.  Every row of every padding / window kind matches the oracle, and the
+    outputs differ from the unsplit form (no workspace: 16 heads per workgroup) only in
+    fp32 rounding."""
+    vc, vs, sw, sel, q, swa_end = _grouped_case(seed=26, B=8, nq=8)
+    B, nq = q.shape[:2]
+    assert L.sparse_attn_workspace(B, nq, sel.shape[-1], 128) == B * nq * 4 * 2 * (16 * 512 + 32) * 4
+    res = []
+    for use_ws in (True, False):
+        out = torch.full((B, nq, 64, 512), 777.0, device=dev())
+        lse = torch.full((B, nq, 64), 777.0, device=dev())
+        ws = None
+        if use_ws:
+            ws = torch.empty(L.sparse_attn_workspace(B, nq, sel.shape[-1], 128), dtype=torch.uint8,
+                             device=dev())
+        L.sparse_attn(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end), out, lse,
+                      ws=ws)
+        res.append((out.cpu().numpy(), lse.cpu().numpy()))
+    (o, l), (o1, l1) = res
+    assert max_abs(o, o1) <= 1e-5
+    fin = np.isfinite(l1)
+    assert np.array_equal(fin, np.isfinite(l)) and np.all(np.abs(l[fin] - l1[fin]) <= 1e-5)
+    for b in range(B):
+        for i in range(nq):
+            ro, rl = oracle.attention(q[b, i], vc[b], vs[b], sel[b, i], sw[b],
+                                      int(swa_end[b, i]), 128, 1.0)
+            assert max_abs(o[b, i], ro) <= ATTN_TOL, f"row {b},{i}"
+            if np.all(np.isinf(rl)):
+                assert np.all(np.isneginf(l[b, i])) and np.all(o[b, i] == 0)
+            else:
+                assert max_abs(l[b, i], rl) <= 1e-4, f"row {b},{i}"
+
+
 def _bf16_to_f32(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
