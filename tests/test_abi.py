@@ -97,6 +97,12 @@ def test_host_validation_rejects_bad_arguments():
     st, msg = _status("csa2_sparse_attn", ctypes.c_void_p(18), 1, 1, vp, vp, 100, vp, 4, vp, 128,
                       vp, 128, ctypes.c_float(1.0), vp, None, None, 0, None)
     assert st == 1 and "misaligned" in msg
+    # caches beyond the 32-bit row offsets of the attention: over 2^24 main entries or
+    # 2^22 window rows per sequence
+    for n_cap, swa_cap in (((1 << 24) + 1, 128), (100, (1 << 22) + 1)):
+        st, msg = _status("csa2_sparse_attn", vp, 1, 1, vp, vp, n_cap, vp, 4, vp, swa_cap, vp,
+                          128, ctypes.c_float(1.0), vp, None, None, 0, None)
+        assert st == 2 and "2^24" in msg, (st, msg)
 
 
 def test_empty_inputs_are_no_ops():
