@@ -290,7 +290,7 @@ static FullSelectPlan full_select_plan(int64_t n_cap, int32_t B, int32_t nq, int
     if (P.mode == 2) {
         const csa2::ScanShape sh = csa2::scan_shape(n_cap, B, nq);
         const int32_t g = csa2::topk_group_size(P.L, tmax);
-        if (!sh.paired && g > 0 && 64 % g == 0) {
+        if (!sh.multi_row && g > 0 && 64 % g == 0) {
             // about twice a chunk's share of the winners, at least 64, a power of two
             const int32_t per = (tmax + sh.chunks_per_row - 1) / sh.chunks_per_row;
             int32_t kl = 64;

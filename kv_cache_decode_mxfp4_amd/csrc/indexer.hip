@@ -36,12 +36,13 @@ constexpr int kGroupEntries = kPrefetch * kStep;  // entries per prefetch round
 #endif
 constexpr int kMaxChunk = CSA2_SCAN_MAX_CHUNK;
 constexpr int64_t kScanTargetWorkgroups = CSA2_SCAN_TARGET_WGS;
-// Query rows per sequence from which the scan pairs rows (prefill shapes);
-// decode (one row per sequence) streams its keys from HBM, one row each.
-#ifndef CSA2_SCAN_PAIR_MIN_ROWS
-#define CSA2_SCAN_PAIR_MIN_ROWS 2
+// Query rows per sequence from which the scan takes several rows per
+// workgroup (prefill shapes); decode (one row per sequence) streams its keys
+// from HBM, one row each.
+#ifndef CSA2_SCAN_MULTI_MIN_ROWS
+#define CSA2_SCAN_MULTI_MIN_ROWS 2
 #endif
-constexpr int32_t kPairMinRows = CSA2_SCAN_PAIR_MIN_ROWS;
+constexpr int32_t kMultiMinRows = CSA2_SCAN_MULTI_MIN_ROWS;
 
 // Keys of one chunk, read with raw buffer loads: the descriptors hold the
 // chunk's base addresses and sizes in bytes (scalar registers), a lane keeps
@@ -91,25 +92,6 @@ __device__ __forceinline__ void load_key(const ChunkKeys& C, int32_t first_entry
     K.c0 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc, 0, kNonTemporal);
     K.c1 = __builtin_amdgcn_raw_buffer_load_b128(C.codes, oc + kKeyPlane, 0, kNonTemporal);
     K.sc = __builtin_amdgcn_raw_buffer_load_b32(C.scales, os, 0, kNonTemporal);
-}
-
-// Scores of the lane's entry for two queries: the key is dequantised once and
-// feeds both MFMA chains; each chain is the one score_entry runs (same operands,
-// same order), so both scores are bit-identical to score_entry's.
-__device__ __forceinline__ void score_entry2(const QueryOperand& Q0, const QueryOperand& Q1,
-                                             const KeyTile& K, float& s0, float& s1)
-{
-    const uint32_t words[8] = {K.c0[0], K.c0[1], K.c0[2], K.c0[3], K.c1[0], K.c1[1], K.c1[2], K.c1[3]};
-    f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const _Float16 s = e4m3_byte_to_f16(K.sc, t / 2);
-        const half8 b = dequant8_fp4(words[t], s);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q0.a[t], b, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q1.a[t], b, acc1, 0, 0, 0);
-    }
-    s0 = head_sum(Q0, acc0);
-    s1 = head_sum(Q1, acc1);
 }
 
 // Maximum over the 8 lanes of each aligned group of 8 (DPP: swap neighbours,
@@ -305,116 +287,186 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                          cand_full + blockIdx.x);
 }
 
-// Full-range scan of two query rows of one sequence (rows 2p and 2p + 1 of
-// its nq; the second is absent when nq is odd): the many-row (prefill) form.
-// Each key tile is loaded and dequantised once for both rows, which halves
-// the dequantisation per score, the VALU work that bounds the one-row scan
-// when its keys come from the caches rather than HBM.  Same chunking, key
-// ring, masking and outputs per row as index_full_kernel; a row whose visible
-// range ends before the chunk writes nothing for it.  Two waves per SIMD (the
-// two queries' operands and accumulators take twice the registers).
+// Full-range scan of up to kRowGroup query rows of one sequence (the many-row,
+// prefill form): each 32-entry key tile is loaded and dequantised once by the
+// whole workgroup into an LDS tile, from which every wave takes its MFMA B
+// operands for two rows.  The dequantisation is then shared by 8 rows
+// (against 2 when each wave dequantised its own tiles for two rows: 23 %
+// fewer VALU instructions), leaving the per-row epilogue (the weighted ReLU
+// head sum) as the VALU work per score.  Each row's MFMA chain is the one
+// score_entry runs (the same A operand, the same exactly dequantised B values,
+// the same k-step order), so the scores are bit-identical to the one-row
+// scan's.  Tiles are double-buffered: one barrier per tile.  Rows past nq or
+// whose visible range ends before the chunk write nothing for it.
+constexpr int kRowGroup = 2 * kWaves;              // query rows per workgroup (two per wave)
+#ifndef CSA2_ROWS_CHUNK
+#define CSA2_ROWS_CHUNK 4096
+#endif
+constexpr int kRowsChunk = CSA2_ROWS_CHUNK;        // entries per workgroup
+constexpr int kTileRow = kIdxDim + 8;              // halves per LDS row of a key tile (272 B)
+constexpr int kRowsPrefetch = 4;                   // raw key tiles in flight
+
 template <bool kScores>
 __global__ void __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
-index_full_pair_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+index_full_rows_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                        const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                        int64_t n_cap, const int32_t* __restrict__ n_visible, int32_t nq,
-                       int32_t pairs_per_seq, int32_t chunk, int32_t chunks_per_pair,
-                       int64_t nblk_cap, float* __restrict__ block_max,
-                       float* __restrict__ scores, uint32_t* __restrict__ gkey, int32_t gshift,
-                       int64_t ngroups)
+                       int32_t groups_per_seq, int32_t chunks_per_group, int64_t nblk_cap,
+                       float* __restrict__ block_max, float* __restrict__ scores,
+                       uint32_t* __restrict__ gkey, int32_t gshift, int64_t ngroups)
 {
-    __shared__ float sblk[2][kMaxChunk / kBlock];
+    __shared__ _Float16 tile[2][kTileEntries][kTileRow];
+    __shared__ float sblk[kRowGroup][kRowsChunk / kBlock];
 
-    const int64_t pair = blockIdx.x / chunks_per_pair;
-    const int64_t b = pair / pairs_per_seq;
-    const int64_t i0 = 2 * (pair % pairs_per_seq);
-    const bool two = i0 + 1 < nq;
-    const int64_t row0 = b * nq + i0;
-    const int64_t row1 = two ? row0 + 1 : row0;
-    int64_t nv0 = n_visible[row0];
-    nv0 = nv0 < 0 ? 0 : (nv0 > n_cap ? n_cap : nv0);
-    int64_t nv1 = two ? (int64_t)n_visible[row1] : 0;
-    nv1 = nv1 < 0 ? 0 : (nv1 > n_cap ? n_cap : nv1);
-    const int64_t start = (int64_t)(blockIdx.x % chunks_per_pair) * chunk;
-    const int64_t nv_max = nv0 > nv1 ? nv0 : nv1;
-    if (start >= nv_max) {
-        if (gkey != nullptr) {
-            write_group_keys(sblk[0], 0, row0, start, chunk, gshift, ngroups, gkey);
-            if (two)
-                write_group_keys(sblk[1], 0, row1, start, chunk, gshift, ngroups, gkey);
-        }
+    const int64_t grp = blockIdx.x / chunks_per_group;
+    const int64_t b = grp / groups_per_seq;
+    const int64_t i0 = (int64_t)kRowGroup * (grp % groups_per_seq);
+    const int64_t start = (int64_t)(blockIdx.x % chunks_per_group) * kRowsChunk;
+    // visible entries of row slot r in this chunk (0 for a slot past nq)
+    auto here = [&](int r) -> int32_t {
+        if (i0 + r >= nq)
+            return 0;
+        int64_t nv = n_visible[b * nq + i0 + r];
+        nv = nv < 0 ? 0 : (nv > n_cap ? n_cap : nv);
+        return (int32_t)(nv <= start ? 0 : (nv - start < kRowsChunk ? nv - start : kRowsChunk));
+    };
+    int32_t n_max = 0;
+#pragma unroll
+    for (int r = 0; r < kRowGroup; ++r)
+        n_max = max(n_max, here(r));
+    if (n_max == 0) {
+        if (gkey != nullptr)
+            for (int r = 0; r < kRowGroup && i0 + r < nq; ++r)
+                write_group_keys(sblk[r], 0, b * nq + i0 + r, start, kRowsChunk, gshift, ngroups,
+                                 gkey);
         return;
     }
-    auto here = [&](int64_t nv) {
-        return (int32_t)(nv <= start ? 0 : (nv - start < chunk ? nv - start : chunk));
-    };
-    const int32_t n_here0 = here(nv0), n_here1 = here(nv1);
-    const int32_t n_here = n_here0 > n_here1 ? n_here0 : n_here1;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5;
-    const int entry0 = kTileEntries * wave + (lane & 31);
+    const int ent = lane & 31;  // the lane's entry in a tile (MFMA column)
 
-    const ChunkKeys C = chunk_keys(codes, scales, b * n_cap + start, n_here, entry0, half);
-    KeyTile ring[kPrefetch];
+    // key bytes of the chunk (range-checked: loads past the visible end read zeros)
+    const int64_t f0 = b * n_cap + start;
+    const int64_t t0 = f0 >> 5;
+    const int64_t t_end = (f0 + n_max + kKeyTile - 1) >> 5;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes + t0 * kKeyTileBytes), 0,
+        (int32_t)((t_end - t0) * kKeyTileBytes), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scales + f0 * (kIdxDim / 16)), 0, n_max * (kIdxDim / 16),
+        kBufferConfig);
+    // dequantisation share of thread T: entry T % 32 of each tile, channels
+    // [16 cg, 16 cg + 16) with cg = T / 32 (code bytes [8 cg, 8 cg + 8), scale byte cg)
+    const int de = threadIdx.x & 31;
+    const int dcg = threadIdx.x >> 5;
+    const int e_in = (int)(f0 & 31) + de;  // the thread's entry counted from tile t0's first
+    const int32_t voc = (e_in >> 5) * kKeyTileBytes + (dcg >> 1) * kKeyPlane + (e_in & 31) * 16 +
+                        8 * (dcg & 1);
+    const int32_t vos = de * (kIdxDim / 16) + (dcg & ~3);
+    uint2 raw_c[kRowsPrefetch];
+    uint32_t raw_s[kRowsPrefetch];
+    auto load_raw = [&](int j, int u) {
+        const auto c = __builtin_amdgcn_raw_buffer_load_b64(rc, voc + j * kKeyTileBytes, 0,
+                                                            kNonTemporal);
+        raw_c[u] = make_uint2(c[0], c[1]);
+        raw_s[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, vos + j * kTileEntries * (kIdxDim / 16),
+                                                        0, kNonTemporal);
+    };
+    auto dequant_store = [&](int u, int buf) {
+        const _Float16 s = e4m3_byte_to_f16(raw_s[u] >> (8 * (dcg & 3)), 0);
+        half8* dst = reinterpret_cast<half8*>(&tile[buf][de][16 * dcg]);
+        dst[0] = dequant8_fp4(raw_c[u].x, s);
+        dst[1] = dequant8_fp4(raw_c[u].y, s);
+    };
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p)
-        load_key(C, p * kStep, ring[p]);
+    for (int u = 0; u < kRowsPrefetch; ++u)
+        load_raw(u, u);
     __builtin_amdgcn_sched_barrier(0);
-    QueryOperand Q0, Q1;
-    load_query(q + row0 * (kIdxHeads * kIdxDim), w + row0 * kIdxHeads, lane, Q0);
-    load_query(q + row1 * (kIdxHeads * kIdxDim), w + row1 * kIdxHeads, lane, Q1);
+
+    // this wave's two rows (a slot past nq takes the group's first row and writes nothing)
+    const int ra = 2 * wave, rb = 2 * wave + 1;
+    const bool has_a = i0 + ra < nq, has_b = i0 + rb < nq;
+    const int64_t row_a = b * nq + i0 + (has_a ? ra : 0);
+    const int64_t row_b = b * nq + i0 + (has_b ? rb : 0);
+    const int32_t nh_a = here(ra), nh_b = here(rb);
+    QueryOperand Qa, Qb;
+    load_query(q + row_a * (kIdxHeads * kIdxDim), w + row_a * kIdxHeads, lane, Qa);
+    load_query(q + row_b * (kIdxHeads * kIdxDim), w + row_b * kIdxHeads, lane, Qb);
 
     const bool writer = lane < 32 && (lane & 7) == 0;
-    const int blk0 = entry0 / kBlock;
-    const int groups = (n_here + kGroupEntries - 1) / kGroupEntries;
-    auto finish = [&](int i, float s0, float s1) {
-        const int e = entry0 + i * kStep;
-        s0 = e < n_here0 ? s0 : -INFINITY;
-        s1 = e < n_here1 ? s1 : -INFINITY;
-        if (kScores && lane < 32) {
-            if (e < n_here0)
-                scores[row0 * n_cap + start + e] = s0;
-            if (e < n_here1)
-                scores[row1 * n_cap + start + e] = s1;
+    const int ntiles = (n_max + kTileEntries - 1) / kTileEntries;
+    // tile j's products go to accumulator pair j&1 and its epilogue runs in
+    // the next body, beside tile j+1's products (the matrix cores then work
+    // while the vector units finish the previous tile)
+    f32x16 acc_a[2], acc_b[2];
+    auto products = [&](int j) {
+        const _Float16* src = &tile[j & 1][ent][64 * half];
+        f32x16 xa = {}, xb = {};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const half8 bt = *reinterpret_cast<const half8*>(src + 8 * t);
+            xa = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qa.a[t], bt, xa, 0, 0, 0);
+            xb = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qb.a[t], bt, xb, 0, 0, 0);
         }
-        const float m0 = max8(s0);
-        const float m1 = max8(s1);
+        acc_a[j & 1] = xa;
+        acc_b[j & 1] = xb;
+    };
+    auto epilogue = [&](int j) {
+        const int e = kTileEntries * j + ent;
+        float sa = head_sum(Qa, acc_a[j & 1]), sb = head_sum(Qb, acc_b[j & 1]);
+        sa = e < nh_a ? sa : -INFINITY;
+        sb = e < nh_b ? sb : -INFINITY;
+        if (kScores && lane < 32) {
+            if (e < nh_a)
+                scores[row_a * n_cap + start + e] = sa;
+            if (e < nh_b)
+                scores[row_b * n_cap + start + e] = sb;
+        }
+        const float ma = max8(sa), mb = max8(sb);
         if (writer) {
-            sblk[0][blk0 + i * (kStep / kBlock)] = m0;
-            sblk[1][blk0 + i * (kStep / kBlock)] = m1;
+            sblk[ra][e / kBlock] = ma;
+            sblk[rb][e / kBlock] = mb;
         }
     };
-    for (int g = 0; g < groups - 1; ++g) {
+
+    dequant_store(0, 0);
+    load_raw(kRowsPrefetch, 0);
+    __syncthreads();
+    // slot u of the raw ring holds tile j0 + u; body j stores tile j + 1 into
+    // the other LDS buffer (last read before the previous barrier), refills
+    // its slot with tile j + 1 + kRowsPrefetch, runs tile j's products and
+    // tile j-1's epilogue
+    for (int j0 = 0; j0 < ntiles; j0 += kRowsPrefetch) {
 #pragma unroll
-        for (int p = 0; p < kPrefetch; ++p) {
-            const int i = g * kPrefetch + p;
-            float s0, s1;
-            score_entry2(Q0, Q1, ring[p], s0, s1);
-            load_key(C, (i + kPrefetch) * kStep, ring[p]);
-            finish(i, s0, s1);
+        for (int u = 0; u < kRowsPrefetch; ++u) {
+            const int j = j0 + u;
+            if (j < ntiles) {  // the same for every wave: the barrier below is uniform
+                const int next = (u + 1) % kRowsPrefetch;
+                if (j + 1 < ntiles) {
+                    dequant_store(next, (j + 1) & 1);
+                    load_raw(j + 1 + kRowsPrefetch, next);
+                }
+                products(j);
+                if (j > 0)
+                    epilogue(j - 1);
+                __syncthreads();
+            }
         }
     }
-#pragma unroll
-    for (int p = 0; p < kPrefetch; ++p) {
-        const int i = (groups - 1) * kPrefetch + p;
-        float s0, s1;
-        score_entry2(Q0, Q1, ring[p], s0, s1);
-        finish(i, s0, s1);
-    }
+    epilogue(ntiles - 1);
     __syncthreads();
-    const int nb0 = (n_here0 + kBlock - 1) / kBlock;
-    const int nb1 = (n_here1 + kBlock - 1) / kBlock;
-    float* dst0 = block_max + row0 * nblk_cap + start / kBlock;
-    float* dst1 = block_max + row1 * nblk_cap + start / kBlock;
-    for (int t = threadIdx.x; t < nb0; t += kWaves * kWave)
-        dst0[t] = sblk[0][t];
-    for (int t = threadIdx.x; t < nb1; t += kWaves * kWave)
-        dst1[t] = sblk[1][t];
-    if (gkey != nullptr) {
-        write_group_keys(sblk[0], nb0, row0, start, chunk, gshift, ngroups, gkey);
-        if (two)
-            write_group_keys(sblk[1], nb1, row1, start, chunk, gshift, ngroups, gkey);
+#pragma unroll
+    for (int r = 0; r < kRowGroup; ++r) {
+        if (i0 + r >= nq)
+            break;
+        const int nb = (here(r) + kBlock - 1) / kBlock;
+        float* dst = block_max + (b * nq + i0 + r) * nblk_cap + start / kBlock;
+        for (int t = threadIdx.x; t < nb; t += kWaves * kWave)
+            dst[t] = sblk[r][t];
+        if (gkey != nullptr)
+            write_group_keys(sblk[r], nb, b * nq + i0 + r, start, kRowsChunk, gshift, ngroups,
+                             gkey);
     }
 }
 
@@ -639,17 +691,11 @@ hipError_t launch_scan(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t 
 ScanShape scan_shape(int64_t n_cap, int32_t B, int32_t nq)
 {
     ScanShape sh{0, 0, 0, false};
-    if (nq >= kPairMinRows) {
-        const int32_t pairs_per_seq = (nq + 1) / 2;
-        const int64_t pairs = (int64_t)B * pairs_per_seq;
-        int32_t chunk = kMaxChunk;
-        while (chunk > kGroupEntries &&
-               pairs * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
-            chunk /= 2;
-        sh.chunk = chunk;
-        sh.chunks_per_row = (int32_t)((n_cap + chunk - 1) / chunk);
-        sh.paired = true;
-        sh.max_blocks_per_chunk = chunk / kBlock;
+    if (nq >= kMultiMinRows) {
+        sh.chunk = kRowsChunk;
+        sh.chunks_per_row = (int32_t)((n_cap + kRowsChunk - 1) / kRowsChunk);
+        sh.multi_row = true;
+        sh.max_blocks_per_chunk = kRowsChunk / kBlock;
         return sh;
     }
     const int64_t rows = (int64_t)B * nq;
@@ -681,24 +727,20 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
     while (group_keys != nullptr && (1 << gshift) < group)
         ++gshift;
     const int64_t ngroups = (nblk_cap + (1 << gshift) - 1) >> gshift;
-    if (nq >= kPairMinRows) {
-        // many rows per sequence (prefill): two rows per workgroup
-        const int32_t pairs_per_seq = (nq + 1) / 2;
-        const int64_t pairs = (int64_t)B * pairs_per_seq;
-        int32_t chunk = kMaxChunk;
-        while (chunk > kGroupEntries &&
-               pairs * ((n_cap + chunk - 1) / chunk) < kScanTargetWorkgroups)
-            chunk /= 2;
-        const int64_t chunks = (n_cap + chunk - 1) / chunk;
-        const int64_t grid = pairs * chunks;
+    if (nq >= kMultiMinRows) {
+        // many rows per sequence (prefill): 8 rows per workgroup sharing each
+        // dequantised key tile
+        const int32_t groups_per_seq = (nq + kRowGroup - 1) / kRowGroup;
+        const int64_t chunks = (n_cap + kRowsChunk - 1) / kRowsChunk;
+        const int64_t grid = (int64_t)B * groups_per_seq * chunks;
         if (grid == 0)
             return hipSuccess;
-        return launch_scan(scores != nullptr ? index_full_pair_kernel<true>
-                                             : index_full_pair_kernel<false>,
+        return launch_scan(scores != nullptr ? index_full_rows_kernel<true>
+                                             : index_full_rows_kernel<false>,
                            dim3((uint32_t)grid), dim3(kWaves * kWave), stream, ev_start, ev_stop,
                            reinterpret_cast<const uint16_t*>(q), w, k_codes, k_scales, n_cap,
-                           n_visible, nq, pairs_per_seq, chunk, (int32_t)chunks, nblk_cap,
-                           block_max, scores, group_keys, gshift, ngroups);
+                           n_visible, nq, groups_per_seq, (int32_t)chunks, nblk_cap, block_max,
+                           scores, group_keys, gshift, ngroups);
     }
     const int64_t rows = (int64_t)B * nq;
     const ScanShape sh = scan_shape(n_cap, B, nq);

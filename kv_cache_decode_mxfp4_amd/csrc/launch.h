@@ -49,12 +49,12 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
                              int32_t* cand_full = nullptr, int32_t kl = 0);
 
 // How the scan cuts rows into chunks (one workgroup per chunk and row, or per
-// chunk and pair of rows when `paired`).
+// chunk and group of 8 rows when `multi_row`).
 struct ScanShape {
     int32_t chunk;                 // entries per chunk
     int32_t chunks_per_row;
     int32_t max_blocks_per_chunk;  // chunk / 8
-    bool paired;
+    bool multi_row;
 };
 ScanShape scan_shape(int64_t n_cap, int32_t B, int32_t nq);
 

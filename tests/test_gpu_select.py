@@ -68,7 +68,7 @@ CASES = [
     (64, 1, 65536, 2048, 512, None, "random"),                    # direct select; pool scan + top-k
     (2, 1, 140003, 2048, 512, [140003, 70001], "random"),          # too many chunks: two top-k calls
     (3, 1, 65536, 2048, 512, [65536, 40001, 3], "random"),         # direct select
-    (1, 4, 300000, 2048, 512, [300000, 299999, 150000, 5], "random"),  # paired scan rows
+    (1, 4, 300000, 2048, 512, [300000, 299999, 150000, 5], "random"),  # multi-row scan rows
     (2, 1, 2048, 32, 64, [2048, 1000], "random"),                 # pool smaller than k
     (2, 1, 262144, 0, 512, None, "random"),                       # no pool
     (1, 1, 0, 2048, 512, [5], "random"),                          # empty cache

@@ -329,14 +329,15 @@ def test_index_pool_scores_bit_identical_to_scan():
         assert np.all(np.isneginf(ps[b, 0][~ok]))
 
 
-@pytest.mark.parametrize("B", [1, 2])
-def test_paired_scan_bit_identical_to_one_row_scan_and_pool(B):
-    """Several query rows of one sequence take the paired scan (two rows per workgroup,
-    one dequantisation per key): every score and block maximum must equal, bit for bit,
-    the one-row scan of the same row and the pool scan of the same positions; an odd
-    row count leaves one row unpaired, and rows see different causal lengths.  With two
-    sequences of 5003 entries the second sequence starts inside a key tile."""
-    N, nq = 5003, 5
+@pytest.mark.parametrize("B,nq", [(1, 5), (2, 5), (1, 11)])
+def test_multirow_scan_bit_identical_to_one_row_scan_and_pool(B, nq):
+    """Several query rows of one sequence take the multi-row scan (8 rows per workgroup,
+    one dequantisation per key tile, shared through LDS): every score and block maximum
+    must equal, bit for bit, the one-row scan of the same row and the pool scan of the
+    same positions; 5 or 11 rows leave slots of a row group empty, rows see different
+    causal lengths (0 to all 5003 entries, over two 4096-entry chunks), and with two
+    sequences the second starts inside a key tile."""
+    N = 5003
     rng = np.random.default_rng(6)
     x = rng.standard_normal((B, N, 128)).astype(np.float32)
     enc = [oracle.quantize_rows(x[b]) for b in range(B)]
@@ -346,13 +347,16 @@ def test_paired_scan_bit_identical_to_one_row_scan_and_pool(B):
     q = synth.normal_bf16(synth.key(11, 10, 0, 0), 0, B * nq * 4096, 1 / np.sqrt(128)).reshape(B, nq, 32, 128)
     w = synth.uniform_f32(synth.key(11, 11, 0, 0), 0, B * nq * 32).reshape(B, nq, 32)
     nv = np.array([[N, N - 1, 700, 0, 4099], [4097, N, 1, 33, N - 31]], np.int32)[:B]
+    if nq > 5:
+        extra = np.array([[4096, 4095, 31, 32, 2048, N]], np.int32)[:, :nq - 5]
+        nv = np.concatenate([nv, np.repeat(extra, B, axis=0)], axis=1)
     nblk = cdiv(N, 8)
     sc = torch.full((B, nq, N), 12345.0, device=dev())
     bm = torch.full((B, nq, nblk), 12345.0, device=dev())
     L.index_full(t(q, torch.uint16), t(w), kct, kst, t(nv), bm, sc)
     sc, bm = sc.cpu().numpy(), bm.cpu().numpy()
-    blocks = np.sort(np.stack([rng.choice(nblk, (nq, 64), replace=False) for _ in range(B)]),
-                     axis=-1).astype(np.int32)
+    blocks = np.sort(np.stack([[rng.choice(nblk, 64, replace=False) for _ in range(nq)]
+                               for _ in range(B)]), axis=-1).astype(np.int32)
     ps = torch.empty(B, nq, 64 * 8, device=dev())
     pi = torch.empty(B, nq, 64 * 8, dtype=torch.int32, device=dev())
     L.index_pool(t(q, torch.uint16), t(w), kct, kst, t(blocks), t(nv), ps, pi)
@@ -382,7 +386,7 @@ def test_paired_scan_bit_identical_to_one_row_scan_and_pool(B):
 @pytest.mark.parametrize("B,nq,n_cap,nb,nvis", [
     (1, 1, 1 << 20, 2048, [1 << 20]),                      # groups of 8 blocks
     (2, 1, 1 << 20, 2048, [(1 << 20) - 5000, 300001]),     # chunks past the end, partial groups
-    (1, 2, 1 << 20, 2048, [1 << 20, 999999]),              # paired rows write group keys too
+    (1, 2, 1 << 20, 2048, [1 << 20, 999999]),              # multi-row scans write group keys too
     (1, 1, 1 << 20, 512, [654321]),                        # groups of 8, k = 512
     (2, 1, 140003, 2048, [140003, 70001]),                 # groups of 2
     (1, 3, 300000, 2048, [300000, 299999, 5]),             # groups of 3: the select's own pass
