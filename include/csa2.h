@@ -76,7 +76,7 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Library ABI version (major * 100 + minor): 104. */
+/* Library ABI version (major * 100 + minor): 105. */
 int32_t csa2_version(void);
 
 /*

@@ -62,7 +62,7 @@ const char* csa2_last_error(void)
 
 int32_t csa2_version(void)
 {
-    return 104;
+    return 105;
 }
 
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,

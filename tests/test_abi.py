@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = L.load()
-    assert lib.csa2_version() == 104
+    assert lib.csa2_version() == 105
     assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
     assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels

@@ -743,6 +743,28 @@ def test_sparse_attn_split_form_32_heads():
                 assert np.all(np.isneginf(l[b, i])) and np.all(o[b, i] == 0)
             else:
                 assert max_abs(l[b, i], rl) <= 1e-4, f"row {b},{i}"
+    # the bf16 epilogue through the same 32-head splits and merge: the fp32 split
+    # output rotated and rounded with the same fp32 operations, bit for bit
+    rng = np.random.default_rng(27)
+    ang = rng.uniform(-np.pi, np.pi, (B * nq, 32))
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    out16 = torch.full((B, nq, 64, 512), 0x7777, dtype=torch.int16, device=dev())
+    lse16 = torch.empty((B, nq, 64), device=dev())
+    ws = torch.empty(L.sparse_attn_workspace(B, nq, sel.shape[-1], 128), dtype=torch.uint8,
+                     device=dev())
+    L.sparse_attn_rope_bf16(t(q, torch.uint16), t(vc), t(vs), t(sel), t(sw), t(swa_end),
+                            t(cos), t(sin), out16, lse16, ws=ws)
+    got = out16.cpu().numpy().view(np.uint16)
+    assert np.array_equal(lse16.cpu().numpy(), l)
+    for r in range(B * nq):
+        b, i = divmod(r, nq)
+        x = o[b, i].astype(np.float32).copy()
+        a_, c_ = x[:, 448::2].copy(), x[:, 449::2].copy()
+        co, si = cos[r][None, :], sin[r][None, :]
+        x[:, 448::2] = (a_ * co) + (c_ * si)
+        x[:, 449::2] = (c_ * co) - (a_ * si)
+        host = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got[b, i], host), f"row {b},{i}"
 
 
 def _bf16_to_f32(bits):
