@@ -74,13 +74,6 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
 }
 
 template <int kCtrl>
-__device__ __forceinline__ float dpp_f32(float v)
-{
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-
-template <int kCtrl>
 __device__ __forceinline__ int dpp_i32(int v)
 {
     return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
@@ -165,11 +158,11 @@ constexpr int kDepth = CSA2_ATTN_DEPTH;          // tiles in flight per wave
 #define CSA2_ATTN_SPLIT_WGS 256
 #endif
 constexpr int64_t kSplitWgs = CSA2_ATTN_SPLIT_WGS;  // workgroup budget of the key splits
-constexpr int kMaxSplits = 8;                   // key splits per (row, 16 heads)
+constexpr int kMaxSplits = 8;                   // key splits per (row, head group)
 #ifndef CSA2_ATTN_MIN_SPLIT_TILES
 #define CSA2_ATTN_MIN_SPLIT_TILES 2
 #endif
-constexpr int kMinSplitTiles = CSA2_ATTN_MIN_SPLIT_TILES;  // fewest key tiles per split
+constexpr int kMinSplitTiles = CSA2_ATTN_MIN_SPLIT_TILES;  // fewest 32-key tiles per split
 constexpr int kPartFloats = kHg * kDim + 2 * kHg;  // one split's O [16][512], max, sum
 
 // Who owns which scores in the softmax step, for kHW heads per workgroup and
