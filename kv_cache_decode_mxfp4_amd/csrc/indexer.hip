@@ -303,6 +303,8 @@ constexpr int kRowGroup = 2 * kWaves;              // query rows per workgroup (
 #define CSA2_ROWS_CHUNK 4096
 #endif
 constexpr int kRowsChunk = CSA2_ROWS_CHUNK;        // entries per workgroup
+// whole groups of group keys (up to 64 blocks per group) per chunk
+static_assert(kRowsChunk % 512 == 0, "chunks start on 64-block group boundaries");
 constexpr int kTileRow = kIdxDim + 8;              // halves per LDS row of a key tile (272 B)
 // Raw key tiles in flight (the prefill keys come from the caches: 2 measured
 // 2-5 % faster than 4, 8 no better)
