@@ -95,13 +95,22 @@ __device__ __forceinline__ void load_key(const ChunkKeys& C, int32_t first_entry
 }
 
 // Maximum over the 8 lanes of each aligned group of 8 (DPP: swap neighbours,
-// swap pairs, then mirror within the half-row of 8).
+// swap pairs, then mirror within the half-row of 8).  Each level is one
+// v_max_f32 with the DPP lane move folded in: written through fmaxf the
+// compiler adds a move and a canonicalisation of the moved value per level.
+// v_max_f32 returns the other operand for one NaN and NaN for two, as fmaxf.
+// The s_nop gives the two wait states a DPP read of a just-written VGPR needs.
+#define CSA2_MAX_DPP(m, ctrl) \
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf" : "=v"(m) : "v"(m))
 __device__ __forceinline__ float max8(float s)
 {
-    float m = fmaxf(s, __uint_as_float(dpp_u32<0xB1>(0u, __float_as_uint(s))));
-    m = fmaxf(m, __uint_as_float(dpp_u32<0x4E>(0u, __float_as_uint(m))));
-    return fmaxf(m, __uint_as_float(dpp_u32<0x141>(0u, __float_as_uint(m))));
+    float m = s;
+    CSA2_MAX_DPP(m, "quad_perm:[1,0,3,2]");
+    CSA2_MAX_DPP(m, "quad_perm:[2,3,0,1]");
+    CSA2_MAX_DPP(m, "row_half_mirror");
+    return m;
 }
+#undef CSA2_MAX_DPP
 
 // Group keys of one row's chunk for the block select (after the scan loop):
 // group t of the chunk -- blocks [t*g, t*g + g) of the chunk, g = 1 << gshift,
@@ -252,9 +261,12 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const bool writer = lane < 32 && (lane & 7) == 0;
     const int blk0 = entry0 / kBlock;  // chunk block of the lane's entry in tile 0
     const int groups = (n_here + kGroupEntries - 1) / kGroupEntries;
-    auto finish = [&](int i, float s) {
+    // every entry of the groups before the last is visible ((groups - 1) *
+    // kGroupEntries < n_here), so only the last group masks
+    auto finish = [&](int i, float s, bool last_group) {
         const int e = entry0 + i * kStep;
-        s = e < n_here ? s : -INFINITY;
+        if (last_group)
+            s = e < n_here ? s : -INFINITY;
         if (kScores && lane < 32 && e < n_here)
             scores[row * n_cap + start + e] = s;
         const float m = max8(s);
@@ -267,13 +279,13 @@ index_full_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
             const int i = g * kPrefetch + p;
             const float s = score_entry(Q, ring[p]);
             load_key(C, (i + kPrefetch) * kStep, ring[p]);
-            finish(i, s);
+            finish(i, s, false);
         }
     }
 #pragma unroll
     for (int p = 0; p < kPrefetch; ++p) {
         const int i = (groups - 1) * kPrefetch + p;
-        finish(i, score_entry(Q, ring[p]));
+        finish(i, score_entry(Q, ring[p]), true);
     }
     __syncthreads();
     const int nb_here = (n_here + kBlock - 1) / kBlock;
@@ -324,6 +336,7 @@ index_full_rows_kernel(const uint16_t* __restrict__ q, const float* __restrict__
 {
     __shared__ _Float16 tile[2][kTileEntries][kTileRow];
     __shared__ float sblk[kRowGroup][kRowsChunk / kBlock];
+    __shared__ float spare[2][kWaves * kWave];  // block-max stores of lanes that own none
 
     const int64_t grp = blockIdx.x / chunks_per_group;
     const int64_t b = grp / groups_per_seq;
@@ -405,8 +418,9 @@ index_full_rows_kernel(const uint16_t* __restrict__ q, const float* __restrict__
     const int ntiles = (n_max + kTileEntries - 1) / kTileEntries;
     // tile j's products go to accumulator pair j&1 and its epilogue runs in
     // the next body, beside tile j+1's products (the matrix cores then work
-    // while the vector units finish the previous tile)
-    f32x16 acc_a[2], acc_b[2];
+    // while the vector units finish the previous tile); pair 1 starts at zero
+    // for the first body's epilogue of tile -1
+    f32x16 acc_a[2] = {}, acc_b[2] = {};
     auto products = [&](int j) {
         const _Float16* src = &tile[j & 1][ent][64 * half];
         f32x16 xa = {}, xb = {};
@@ -419,22 +433,24 @@ index_full_rows_kernel(const uint16_t* __restrict__ q, const float* __restrict__
         acc_a[j & 1] = xa;
         acc_b[j & 1] = xb;
     };
-    auto epilogue = [&](int j) {
+    auto epilogue = [&](int j) {  // j = -1: nothing to finish, the stores go to spare
         const int e = kTileEntries * j + ent;
         float sa = head_sum(Qa, acc_a[j & 1]), sb = head_sum(Qb, acc_b[j & 1]);
         sa = e < nh_a ? sa : -INFINITY;
         sb = e < nh_b ? sb : -INFINITY;
-        if (kScores && lane < 32) {
+        if (kScores && lane < 32 && e >= 0) {
             if (e < nh_a)
                 scores[row_a * n_cap + start + e] = sa;
             if (e < nh_b)
                 scores[row_b * n_cap + start + e] = sb;
         }
         const float ma = max8(sa), mb = max8(sb);
-        if (writer) {
-            sblk[ra][e / kBlock] = ma;
-            sblk[rb][e / kBlock] = mb;
-        }
+        // every lane stores, so the body has no branch: a lane that owns no
+        // block (or tile -1) stores into a spare slot of its own
+        const bool own = writer && j >= 0;
+        const int eb = max(e, 0) / kBlock;  // < kRowsChunk / kBlock: e < 32 * padded tiles
+        *(own ? &sblk[ra][eb] : &spare[0][threadIdx.x]) = ma;
+        *(own ? &sblk[rb][eb] : &spare[1][threadIdx.x]) = mb;
     };
 
     dequant_store(0, 0);
@@ -443,25 +459,32 @@ index_full_rows_kernel(const uint16_t* __restrict__ q, const float* __restrict__
     // slot u of the raw ring holds tile j0 + u; body j stores tile j + 1 into
     // the other LDS buffer (last read before the previous barrier), refills
     // its slot with tile j + 1 + kRowsPrefetch, runs tile j's products and
-    // tile j-1's epilogue
-    for (int j0 = 0; j0 < ntiles; j0 += kRowsPrefetch) {
+    // tile j-1's epilogue.  The bodies have no branch, so each is one
+    // scheduling region: the tile count is rounded up to whole ring turns (at
+    // most kRowsChunk / 32 tiles, so every LDS index stays in its array), and
+    // padded tiles read zeros (range-checked loads) and score -inf.
+    static_assert((kRowsChunk / kTileEntries) % kRowsPrefetch == 0, "padded tiles fit the chunk");
+    const int ntiles_p = (ntiles + kRowsPrefetch - 1) / kRowsPrefetch * kRowsPrefetch;
+    for (int j0 = 0; j0 < ntiles_p; j0 += kRowsPrefetch) {
 #pragma unroll
         for (int u = 0; u < kRowsPrefetch; ++u) {
             const int j = j0 + u;
-            if (j < ntiles) {  // the same for every wave: the barrier below is uniform
-                const int next = (u + 1) % kRowsPrefetch;
-                if (j + 1 < ntiles) {
-                    dequant_store(next, (j + 1) & 1);
-                    load_raw(j + 1 + kRowsPrefetch, next);
-                }
-                products(j);
-                if (j > 0)
-                    epilogue(j - 1);
-                __syncthreads();
+            const int next = (u + 1) % kRowsPrefetch;
+            dequant_store(next, (j + 1) & 1);
+            load_raw(j + 1 + kRowsPrefetch, next);
+            products(j);
+            epilogue(j - 1);
+            // one MFMA, then up to five vector instructions, sixteen times
+            // (measured 2-2.5 % faster than the compiler's own interleave)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
             }
+            __syncthreads();
         }
     }
-    epilogue(ntiles - 1);
+    epilogue(ntiles_p - 1);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kRowGroup; ++r) {
