@@ -383,6 +383,42 @@ def test_multirow_scan_bit_identical_to_one_row_scan_and_pool(B, nq):
             assert np.array_equal(ps[b, i][ok], sc[b, i][pi[b, i][ok]])
 
 
+@pytest.mark.parametrize("nv", [[20, 7], [64, 40], [96, 1], [33, 0]])
+def test_multirow_scan_short_row_groups(nv):
+    """Row groups whose longest row covers 1, 2 or 3 key tiles (the multi-row scan pads
+    its tile loop to whole prefetch rounds: the padded tile and the epilogue of the tile
+    before the first must write nothing): scores and block maxima equal the one-row scan
+    bit for bit, entries past each row's end keep the sentinel, scores match the oracle."""
+    N = 200
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((N, 128)).astype(np.float32)
+    kc, ks = oracle.quantize_rows(x)
+    kct, kst = t(tile_keys(kc[None])), t(ks[None])
+    nq = len(nv)
+    q = synth.normal_bf16(synth.key(11, 12, 0, 0), 0, nq * 4096, 1 / np.sqrt(128)).reshape(1, nq, 32, 128)
+    w = synth.uniform_f32(synth.key(11, 13, 0, 0), 0, nq * 32).reshape(1, nq, 32)
+    nva = np.array([nv], np.int32)
+    nblk = cdiv(N, 8)
+    sc = torch.full((1, nq, N), 12345.0, device=dev())
+    bm = torch.full((1, nq, nblk), 12345.0, device=dev())
+    L.index_full(t(q, torch.uint16), t(w), kct, kst, t(nva), bm, sc)
+    sc, bm = sc.cpu().numpy(), bm.cpu().numpy()
+    for i, n in enumerate(nv):
+        s1 = torch.full((1, 1, N), 12345.0, device=dev())
+        b1 = torch.full((1, 1, nblk), 12345.0, device=dev())
+        L.index_full(t(q[:, i:i + 1].copy(), torch.uint16), t(w[:, i:i + 1].copy()), kct, kst,
+                     t(np.array([[n]], np.int32)), b1, s1)
+        assert np.array_equal(sc[0, i], s1.cpu().numpy()[0, 0]), f"row {i}: scores"
+        assert np.array_equal(bm[0, i], b1.cpu().numpy()[0, 0]), f"row {i}: maxima"
+        assert np.all(sc[0, i, n:] == 12345.0), f"row {i}: scores past the end"
+        assert np.all(bm[0, i, cdiv(n, 8):] == 12345.0), f"row {i}: maxima past the end"
+        if n:
+            ok, err = finite_close(sc[0, i, :n], oracle.index_scores(q[0, i], w[0, i], kc, ks, n))
+            assert ok, f"row {i}: max err {err}"
+            ref_bm = [sc[0, i, 8 * j:min(8 * j + 8, n)].max() for j in range(cdiv(n, 8))]
+            assert np.array_equal(bm[0, i, :cdiv(n, 8)], np.array(ref_bm, np.float32))
+
+
 @pytest.mark.parametrize("B,nq,n_cap,nb,nvis", [
     (1, 1, 1 << 20, 2048, [1 << 20]),                      # groups of 8 blocks
     (2, 1, 1 << 20, 2048, [(1 << 20) - 5000, 300001]),     # chunks past the end, partial groups
