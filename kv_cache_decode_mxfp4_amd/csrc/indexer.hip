@@ -386,12 +386,13 @@ index_full_rows_kernel(const uint16_t* __restrict__ q, const float* __restrict__
     const int32_t vos = de * (kIdxDim / 16) + (dcg & ~3);
     uint2 raw_c[kRowsPrefetch];
     uint32_t raw_s[kRowsPrefetch];
+    // cached loads (no non-temporal hint): the sequence's other row groups read
+    // the same keys (measured 0.3-0.5 % faster)
     auto load_raw = [&](int j, int u) {
-        const auto c = __builtin_amdgcn_raw_buffer_load_b64(rc, voc + j * kKeyTileBytes, 0,
-                                                            kNonTemporal);
+        const auto c = __builtin_amdgcn_raw_buffer_load_b64(rc, voc + j * kKeyTileBytes, 0, 0);
         raw_c[u] = make_uint2(c[0], c[1]);
         raw_s[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, vos + j * kTileEntries * (kIdxDim / 16),
-                                                        0, kNonTemporal);
+                                                        0, 0);
     };
     auto dequant_store = [&](int u, int buf) {
         const _Float16 s = e4m3_byte_to_f16(raw_s[u] >> (8 * (dcg & 3)), 0);
