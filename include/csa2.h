@@ -76,7 +76,7 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Library ABI version (major * 100 + minor): 105. */
+/* Library ABI version (major * 100 + minor): 106. */
 int32_t csa2_version(void);
 
 /*
@@ -245,6 +245,8 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w,
  * scores as the pool for the Reindex layers, and selects its own top-k
  * entries): scan, pool and top-k.  Same arguments as csa2_index_full_pool,
  * plus
+ *   n_cap     at most 2^24 entries per sequence (the rescoring gathers use
+ *             32-bit offsets), else CSA2_ERR_UNSUPPORTED.
  *   nb        pool blocks, 0 <= nb <= 8192 (0: no pool, pool may be NULL).
  *   k         1 <= k <= 8192.
  *   pool      int32 [B, nq, nb]: csa2_topk(block_max, ceil(n_cap/8), B*nq,
@@ -279,7 +281,9 @@ csa2_status csa2_index_full_select(const uint16_t* q, const float* w,
 /*
  * Indexer scoring restricted to a pool of blocks ([N] 2.2, [A] 3.4: Reindex
  * layers score only the Full layer's 2048 x 8 pool with their own query).
- *   q, w, k_codes, k_scales, n_cap, n_visible, B, nq: as csa2_index_full.
+ *   q, w, k_codes, k_scales, n_visible, B, nq: as csa2_index_full.
+ *   n_cap      as csa2_index_full, at most 2^24 (the gathers use 32-bit
+ *              offsets), else CSA2_ERR_UNSUPPORTED.
  *   blocks     int32 [B, nq, n_blocks]: block ids (ascending, -1 padding).
  *   pool_score fp32 [B, nq, n_blocks*block]: slot t*block + r holds the score
  *              of position blocks[t]*block + r, or -inf if that position is

@@ -62,7 +62,7 @@ const char* csa2_last_error(void)
 
 int32_t csa2_version(void)
 {
-    return 105;
+    return 106;
 }
 
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
@@ -173,6 +173,14 @@ static csa2_status check_indexer(const char* fn, const uint16_t* q, const float*
     REQUIRE(n_cap == 0 || (k_codes && k_scales), CSA2_ERR_INVALID_ARG, "%s: null key cache", fn);
     REQUIRE(aligned(q, 16) && aligned(k_codes, 16) && aligned(k_scales, 4), CSA2_ERR_INVALID_ARG,
             "%s: q and k_codes must be 16-byte, k_scales 4-byte aligned", fn);
+    return CSA2_OK;
+}
+
+// The pool gathers address a sequence's keys with 32-bit offsets.
+static csa2_status check_gather_cap(const char* fn, int64_t n_cap)
+{
+    REQUIRE(n_cap <= (1ll << 24), CSA2_ERR_UNSUPPORTED,
+            "%s: more than 2^24 entries per sequence", fn);
     return CSA2_OK;
 }
 
@@ -354,6 +362,9 @@ csa2_status csa2_index_full_select(const uint16_t* q, const float* w, const uint
                                    n_visible, B, nq, block);
     if (st != CSA2_OK)
         return st;
+    st = check_gather_cap("index_full_select", n_cap);
+    if (st != CSA2_OK)
+        return st;
     REQUIRE(nb >= 0 && nb <= csa2::kTopkMaxK && k >= 1 && k <= csa2::kTopkMaxK,
             CSA2_ERR_UNSUPPORTED, "index_full_select: nb must be in [0, %d], k in [1, %d]",
             csa2::kTopkMaxK, csa2::kTopkMaxK);
@@ -450,6 +461,9 @@ csa2_status csa2_index_pool(const uint16_t* q, const float* w, const uint8_t* k_
                                    nq, block);
     if (st != CSA2_OK)
         return st;
+    st = check_gather_cap("index_pool", n_cap);
+    if (st != CSA2_OK)
+        return st;
     REQUIRE(n_blocks >= 0 && n_blocks <= (1 << 20), CSA2_ERR_INVALID_ARG,
             "index_pool: n_blocks out of range");
     if ((int64_t)B * nq == 0 || n_blocks == 0)
@@ -476,6 +490,9 @@ csa2_status csa2_index_pool_topk(const uint16_t* q, const float* w, const uint8_
 {
     csa2_status st = check_indexer("index_pool_topk", q, w, k_codes, k_scales, n_cap, n_visible,
                                    B, nq, block);
+    if (st != CSA2_OK)
+        return st;
+    st = check_gather_cap("index_pool_topk", n_cap);
     if (st != CSA2_OK)
         return st;
     REQUIRE(n_blocks >= 0 && n_blocks <= csa2::kTopkSegment / csa2::kBlock, CSA2_ERR_UNSUPPORTED,

@@ -94,6 +94,72 @@ __device__ __forceinline__ void load_key(const ChunkKeys& C, int32_t first_entry
     K.sc = __builtin_amdgcn_raw_buffer_load_b32(C.scales, os, 0, kNonTemporal);
 }
 
+// Keys of one sequence for the pool gathers: buffer descriptors over the key
+// tiles and scale rows of its visible entries, addressed with 32-bit offsets
+// from the tile holding its entry 0 (the boundary keeps a gathering call's
+// sequences at 2^24 entries or fewer, so every offset is below 2^31).  A
+// position past the visible end, and every position of a sequence with
+// nothing visible, reads zeros.  The loads go through the caches: in
+// prefill every row's pool gathers from the same sequence.
+struct SeqKeys {
+    __amdgpu_buffer_rsrc_t codes, scales;
+    int32_t e0;  // position of the sequence's entry 0 inside its tile
+};
+
+__device__ __forceinline__ SeqKeys seq_keys(const uint8_t* codes, const uint8_t* scales,
+                                            int64_t f_seq, int32_t n_vis)
+{
+    SeqKeys S;
+    const int64_t t0 = f_seq >> 5;
+    const int64_t t_end = (f_seq + n_vis + kKeyTile - 1) >> 5;
+    S.codes = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes + t0 * kKeyTileBytes), 0,
+        n_vis > 0 ? (int32_t)((t_end - t0) * kKeyTileBytes) : 0, kBufferConfig);
+    S.scales = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scales + f_seq * (kIdxDim / 16)), 0, n_vis * (kIdxDim / 16),
+        kBufferConfig);
+    S.e0 = (int32_t)(f_seq & 31);
+    return S;
+}
+
+// Key at position p of the sequence, channel half `half`.
+__device__ __forceinline__ void gather_key(const SeqKeys& S, int32_t p, int half, KeyTile& K)
+{
+    const int32_t e = S.e0 + p;
+    const int32_t oc = (e >> 5) * kKeyTileBytes + 2 * half * kKeyPlane + (e & 31) * 16;
+    K.c0 = __builtin_amdgcn_raw_buffer_load_b128(S.codes, oc, 0, 0);
+    K.c1 = __builtin_amdgcn_raw_buffer_load_b128(S.codes, oc + kKeyPlane, 0, 0);
+    K.sc = __builtin_amdgcn_raw_buffer_load_b32(S.scales, p * (kIdxDim / 16) + 4 * half, 0, 0);
+}
+
+// Gathers of one wave's kT pool tiles (slots first + 32 t + lane % 32): pos[t]
+// = the slot's position in the sequence, -1 for a slot past the pool, a
+// negative block id or a position past the visible end; every load is issued
+// (masked slots read position 0), so all of them are in flight together.
+template <int kT>
+__device__ __forceinline__ void gather_pool_tiles(const SeqKeys& S, const int32_t* __restrict__ blk,
+                                                  int32_t slots, int32_t n_vis, int32_t first,
+                                                  int lane, int half, int32_t (&pos)[kT],
+                                                  KeyTile (&K)[kT])
+{
+    const int32_t nb_vis = (n_vis + kBlock - 1) / kBlock;
+    int32_t bl[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+        const int32_t slot = first + t * kTileEntries + (lane & 31);
+        bl[t] = blk[(slot < slots ? slot : slots - 1) / kBlock];
+    }
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+        const int32_t slot = first + t * kTileEntries + (lane & 31);
+        // bl < nb_vis keeps bl * 8 far from overflow
+        const bool in = slot < slots && bl[t] >= 0 && bl[t] < nb_vis;
+        const int32_t p = bl[t] * kBlock + slot % kBlock;
+        pos[t] = in && p < n_vis ? p : -1;
+        gather_key(S, pos[t] >= 0 ? pos[t] : 0, half, K[t]);
+    }
+}
+
 // Maximum over the 8 lanes of each aligned group of 8 (DPP: swap neighbours,
 // swap pairs, then mirror within the half-row of 8).  Each level is one
 // v_max_f32 with the DPP lane move folded in: written through fmaxf the
@@ -510,7 +576,7 @@ index_full_rows_kernel(const uint16_t* __restrict__ q, const float* __restrict__
 #endif
 constexpr int kPoolTilesPerWave = CSA2_POOL_TILES_PER_WAVE;
 
-__global__ void __launch_bounds__(kWaves * kWave)
+__global__ void __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(3)))
 index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                   const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                   int64_t n_cap, const int32_t* __restrict__ blocks, int32_t n_blocks,
@@ -520,51 +586,33 @@ index_pool_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const int64_t row = blockIdx.x / wgs_per_query;
     const int32_t part = blockIdx.x % wgs_per_query;
     const int64_t b = row / nq;
-    int64_t n_vis = n_visible[row];
-    n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
+    int64_t nv = n_visible[row];
+    const int32_t n_vis = (int32_t)(nv < 0 ? 0 : (nv > n_cap ? n_cap : nv));
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5;
-    const int64_t slots = (int64_t)n_blocks * kBlock;
-
-    // with nothing visible the loads read the query row instead (8 KiB, always
-    // valid: entry 0 of the tiled layout lies in its first 1552 bytes) and are
-    // masked: every load below is unconditional, so all of a wave's loads are
-    // in flight together
-    const uint8_t* qrow_bytes = reinterpret_cast<const uint8_t*>(q + row * (kIdxHeads * kIdxDim));
-    const uint8_t* kc = n_vis > 0 ? codes : qrow_bytes;
-    const uint8_t* ks = n_vis > 0 ? scales : qrow_bytes;
-    const int64_t f_seq = n_vis > 0 ? b * n_cap : 0;  // flat index of the sequence's entry 0
-    const int32_t* blk = blocks + row * n_blocks;
-
-    const int64_t first = ((int64_t)part * kWaves + wave) * kPoolTilesPerWave * kTileEntries;
-    // every block id of this wave's tiles first, then every key
-    int32_t bl[kPoolTilesPerWave];
-#pragma unroll
-    for (int i = 0; i < kPoolTilesPerWave; ++i) {
-        const int64_t slot = first + i * kTileEntries + (lane & 31);
-        bl[i] = blk[(slot < slots ? slot : slots - 1) / kBlock];
-    }
-    int64_t pos[kPoolTilesPerWave];
+    const int32_t slots = n_blocks * kBlock;
+    const int32_t first = (part * kWaves + wave) * kPoolTilesPerWave * kTileEntries;
+    // the query first: prepared while the gathers are in flight it would hold
+    // its conversion registers beside the gathered tiles (spills at 168 VGPRs)
+    __shared__ QueryLds sq;
+    QueryOperand Q;
+    shared_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, wave, sq, Q);
+    int32_t pos[kPoolTilesPerWave];
     KeyTile K[kPoolTilesPerWave];
+    gather_pool_tiles(seq_keys(codes, scales, b * n_cap, n_vis), blocks + row * n_blocks, slots,
+                      n_vis, first, lane, half, pos, K);
+    float* srow = pool_score + row * slots;
+    int32_t* irow = pool_idx + row * slots;
 #pragma unroll
     for (int i = 0; i < kPoolTilesPerWave; ++i) {
-        const int64_t slot = first + i * kTileEntries + (lane & 31);
-        const int64_t p = (int64_t)bl[i] * kBlock + slot % kBlock;
-        pos[i] = (slot < slots && bl[i] >= 0 && p < n_vis) ? p : -1;
-        load_key(kc, ks, f_seq + (pos[i] >= 0 ? pos[i] : 0), half, K[i]);
-    }
-    QueryOperand Q;  // loaded while the gathers are in flight
-    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
-#pragma unroll
-    for (int i = 0; i < kPoolTilesPerWave; ++i) {
-        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        const int32_t slot = first + i * kTileEntries + (lane & 31);
         if (slot - (lane & 31) >= slots)
             break;
         const float s = score_entry(Q, K[i]);
         if (lane < 32 && slot < slots) {
-            pool_score[row * slots + slot] = pos[i] >= 0 ? s : -INFINITY;
-            pool_idx[row * slots + slot] = (int32_t)pos[i];
+            srow[slot] = pos[i] >= 0 ? s : -INFINITY;
+            irow[slot] = pos[i];
         }
     }
 }
@@ -596,6 +644,7 @@ __device__ __forceinline__ uint32_t load_coherent(const uint32_t* p)
 
 struct PoolTopkSmem {
     sel::Smem<kPtThreads> sm;
+    QueryLds query;
     uint32_t last;
 };
 
@@ -612,49 +661,33 @@ pool_topk_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
     const int64_t row = blockIdx.x / wgs_per_row;
     const int32_t part = blockIdx.x % wgs_per_row;
     const int64_t b = row / nq;
-    int64_t n_vis = n_visible[row];
-    n_vis = n_vis < 0 ? 0 : (n_vis > n_cap ? n_cap : n_vis);
+    int64_t nv = n_visible[row];
+    const int32_t n_vis = (int32_t)(nv < 0 ? 0 : (nv > n_cap ? n_cap : nv));
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int half = lane >> 5;
-    const int64_t slots = (int64_t)n_blocks * kBlock;
+    const int32_t slots = n_blocks * kBlock;
 
-    // scoring, as index_pool_kernel (loads with nothing visible read the query row)
-    const uint8_t* qrow_bytes = reinterpret_cast<const uint8_t*>(q + row * (kIdxHeads * kIdxDim));
-    const uint8_t* kc = n_vis > 0 ? codes : qrow_bytes;
-    const uint8_t* ks = n_vis > 0 ? scales : qrow_bytes;
-    const int64_t f_seq = n_vis > 0 ? b * n_cap : 0;
-    const int32_t* blk = blocks + row * n_blocks;
-    const int64_t first = ((int64_t)part * kPtWaves + wave) * kPtT * kTileEntries;
-    int32_t bl[kPtT];
-#pragma unroll
-    for (int i = 0; i < kPtT; ++i) {
-        const int64_t slot = first + i * kTileEntries + (lane & 31);
-        bl[i] = blk[(slot < slots ? slot : slots - 1) / kBlock];
-    }
-    int64_t pos[kPtT];
+    // scoring, as index_pool_kernel
+    const int32_t first = (part * kPtWaves + wave) * kPtT * kTileEntries;
+    int32_t pos[kPtT];
     KeyTile K[kPtT];
-#pragma unroll
-    for (int i = 0; i < kPtT; ++i) {
-        const int64_t slot = first + i * kTileEntries + (lane & 31);
-        const int64_t p = (int64_t)bl[i] * kBlock + slot % kBlock;
-        pos[i] = (slot < slots && bl[i] >= 0 && p < n_vis) ? p : -1;
-        load_key(kc, ks, f_seq + (pos[i] >= 0 ? pos[i] : 0), half, K[i]);
-    }
+    gather_pool_tiles(seq_keys(codes, scales, b * n_cap, n_vis), blocks + row * n_blocks, slots,
+                      n_vis, first, lane, half, pos, K);
     QueryOperand Q;
-    load_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, Q);
+    shared_query(q + row * (kIdxHeads * kIdxDim), w + row * kIdxHeads, lane, wave, ps.query, Q);
     uint32_t* srow = ws_score + row * slots;
     uint32_t* irow = ws_idx + row * slots;
 #pragma unroll
     for (int i = 0; i < kPtT; ++i) {
-        const int64_t slot = first + i * kTileEntries + (lane & 31);
+        const int32_t slot = first + i * kTileEntries + (lane & 31);
         if (slot - (lane & 31) >= slots)
             break;
         const float s = score_entry(Q, K[i]);
         if (lane < 32 && slot < slots) {
             store_coherent(srow + slot, __float_as_uint(pos[i] >= 0 ? s : -INFINITY));
-            store_coherent(irow + slot, (uint32_t)(int32_t)pos[i]);
+            store_coherent(irow + slot, (uint32_t)pos[i]);
         }
     }
     // every store of this workgroup has completed before it counts itself

@@ -82,19 +82,44 @@ struct KeyTile {
     uint32_t sc;    // scale bytes [4h, 4h+4)
 };
 
-// Key of flat entry f (tiled codes, row-major scales), channel half `half`.
-// Gathers through the caches: in prefill every row's pool gathers from the
-// same sequence (measured: a non-temporal hint made the decoder prefill's
-// Reindex layer 4 % slower and did not help the decode rescoring).
-__device__ __forceinline__ void load_key(const uint8_t* __restrict__ codes,
-                                         const uint8_t* __restrict__ scales, int64_t f,
-                                         int half, KeyTile& K)
+// The query operand of a workgroup's row, prepared once: wave 0 converts it
+// (load_query) and stores it lane-major to LDS; after the barrier every other
+// wave reads it back, so the workgroup does the conversion once instead of
+// once per wave.  The values are load_query's, bit for bit.  Every wave of
+// the workgroup must call it (one barrier).
+struct QueryLds {
+    uint4 v[12][kWave];  // a[0..7], then wr in groups of four
+};
+
+__device__ __forceinline__ void shared_query(const uint16_t* __restrict__ q,
+                                             const float* __restrict__ w, int lane, int wave,
+                                             QueryLds& sl, QueryOperand& Q)
 {
-    const u32x4* c = reinterpret_cast<const u32x4*>(codes + key_code_offset(f, 32 * half));
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(scales + f * (kIdxDim / 16) + 4 * half);
-    K.c0 = c[0];
-    K.c1 = c[kKeyPlane / 16];
-    K.sc = *sp;
+    if (wave == 0) {
+        load_query(q, w, lane, Q);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            sl.v[t][lane] = __builtin_bit_cast(uint4, Q.a[t]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sl.v[8 + j][lane] = make_uint4(__float_as_uint(Q.wr[4 * j]), __float_as_uint(Q.wr[4 * j + 1]),
+                                           __float_as_uint(Q.wr[4 * j + 2]),
+                                           __float_as_uint(Q.wr[4 * j + 3]));
+    }
+    __syncthreads();
+    if (wave != 0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            Q.a[t] = __builtin_bit_cast(half8, sl.v[t][lane]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 u = sl.v[8 + j][lane];
+            Q.wr[4 * j] = __uint_as_float(u.x);
+            Q.wr[4 * j + 1] = __uint_as_float(u.y);
+            Q.wr[4 * j + 2] = __uint_as_float(u.z);
+            Q.wr[4 * j + 3] = __uint_as_float(u.w);
+        }
+    }
 }
 
 // Weighted ReLU head sum of one query's accumulators (both lanes of an entry

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = L.load()
-    assert lib.csa2_version() == 105
+    assert lib.csa2_version() == 106
     assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
     assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
@@ -103,6 +103,17 @@ def test_host_validation_rejects_bad_arguments():
         st, msg = _status("csa2_sparse_attn", vp, 1, 1, vp, vp, n_cap, vp, 4, vp, swa_cap, vp,
                           128, ctypes.c_float(1.0), vp, None, None, 0, None)
         assert st == 2 and "2^24" in msg, (st, msg)
+    # the pool gathers' 32-bit offsets: over 2^24 entries per sequence (rejected before
+    # anything is launched)
+    big = (1 << 24) + 1
+    st, msg = _status("csa2_index_pool", vp, vp, vp, vp, big, vp, 8, 8, vp, 1, 1, vp, vp, None)
+    assert st == 2 and "2^24" in msg, (st, msg)
+    st, msg = _status("csa2_index_pool_topk", vp, vp, vp, vp, big, vp, 8, 8, vp, 1, 1, 4, vp, vp,
+                      ctypes.c_size_t(1 << 20), None)
+    assert st == 2 and "2^24" in msg, (st, msg)
+    st, msg = _status("csa2_index_full_select", vp, vp, vp, vp, big, vp, 1, 1, 8, 16, 4, vp, vp,
+                      vp, vp, ctypes.c_size_t(1 << 30), None, None, None)
+    assert st == 2 and "2^24" in msg, (st, msg)
 
 
 def test_empty_inputs_are_no_ops():
