@@ -152,9 +152,9 @@ __device__ __forceinline__ void gather_pool_tiles(const SeqKeys& S, const int32_
 #pragma unroll
     for (int t = 0; t < kT; ++t) {
         const int32_t slot = first + t * kTileEntries + (lane & 31);
-        // bl < nb_vis keeps bl * 8 far from overflow
+        // only a checked block id (0 <= bl < nb_vis <= 2^21) is multiplied
         const bool in = slot < slots && bl[t] >= 0 && bl[t] < nb_vis;
-        const int32_t p = bl[t] * kBlock + slot % kBlock;
+        const int32_t p = (in ? bl[t] : 0) * kBlock + slot % kBlock;
         pos[t] = in && p < n_vis ? p : -1;
         gather_key(S, pos[t] >= 0 ? pos[t] : 0, half, K[t]);
     }
