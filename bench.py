@@ -304,12 +304,12 @@ def scan_flops(w: synth.Workload) -> int:
     return int(w.n_visible().astype(np.int64).sum()) * 32 * 128 * 2
 
 
-def survey_step_bytes(w: synth.Workload) -> int:
-    """Algorithmic bytes of one decode step as the spec bar counts them: per query row
-    the visible indexer keys (72 B each), the indexer query and weights, the top-k and pool
-    written (2 KiB + 8 KiB), and the attention's reads and writes (k MXFP4 rows of 288 B
-    and their ids, the window rows, the main query, the fp32 output) -- 1,215 MB per step
-    at 16 x 1M, so 70 % of 8 TB/s is 217 us per step."""
+def step_algorithmic_bytes(w: synth.Workload) -> int:
+    """Algorithmic bytes of one decode step, the bytes the method itself must move: per
+    query row the visible indexer keys (72 B each), the indexer query and weights, the
+    top-k and pool written (2 KiB + 8 KiB), and the attention's reads and writes (k MXFP4
+    rows of 288 B and their ids, the window rows, the main query, the fp32 output) --
+    1,215 MB per step at 16 x 1M (at 0.70 of 8 TB/s: 217 us per step)."""
     rows = w.B * w.nq
     nv = int(w.n_visible().astype(np.int64).sum())
     b = nv * 72 + rows * (32 * 128 * 2 + 32 * 4)
@@ -604,7 +604,7 @@ def main():
     }
     if w.decode:
         out["step_tbps"] = round(step_bytes(w) / (ms_step / 1e3) / 1e12, 3)
-        sbytes = survey_step_bytes(w)
+        sbytes = step_algorithmic_bytes(w)
         out["step_roofline"] = {
             "bound": "hbm", "algorithmic_bytes": sbytes,
             "achieved": round(sbytes / (ms_step / 1e3) / 1e9, 1), "peak": PEAK_HBM / 1e9,
