@@ -130,6 +130,7 @@ POOL_CASES = [
     (3, 1, 65536, 64, 512, None),                             # fewer positions than k
     (1, 64, 40000, 2048, 512, "causal"),                      # decoder prefill rows
     (2, 1, 20000, 1, 8, None),                                # a single block
+    (3, 1, 50003, 2048, 512, [50003, 20001, 0]),              # sequences start inside key tiles
 ]
 
 
