@@ -191,7 +191,8 @@ csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* ro
  *              is row f = b*n_cap + j, in tile f/32; the array holds
  *              ceil(B*n_cap/32) tiles of 2048 B (16-byte aligned).
  *   k_scales   u8 [B, n_cap, 8] row-major scales (shared by every query of a
- *              sequence, like the codes).
+ *              sequence, like the codes).  n_cap <= 2^30 (CSA2_ERR_INVALID_ARG
+ *              above; the calls that gather keys allow 2^24).
  *   n_visible  int32 [B, nq]: query (b, i) sees entries [0, min(n_visible, n_cap)).
  *   block      positions per block (8).
  *   block_max  fp32 [B, nq, ceil(n_cap/block)]: block beta of query (b,i)
