@@ -54,6 +54,16 @@
  *     heads x 128, attention 64 heads x 512, scale group 16, block 8.
  *   - Index inputs that are out of range are skipped (treated as -1), never
  *     dereferenced.
+ *   - One kernel launch holds at most 2^32 - 1 work-items (the dispatch
+ *     counts its grid in 32 bits).  A call that would need more in any of
+ *     its launches fails with CSA2_ERR_UNSUPPORTED before anything is
+ *     enqueued.  The limits this sets, by call: csa2_topk about 2^22 rows
+ *     (one 1024-thread workgroup per row; fewer for rows whose group maxima
+ *     or segments need more threads), as the selects of csa2_index_full_pool;
+ *     csa2_index_full_select about 2^21 rows (two such workgroups per row);
+ *     the scans rows x ceil(n_cap / 16384)
+ *     below 2^24 (decode) or ceil(nq / 8) x ceil(n_cap / 4096) per sequence
+ *     (prefill); csa2_sparse_attn below 2^23 query rows.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -76,7 +86,7 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Library ABI version (major * 100 + minor): 106. */
+/* Library ABI version (major * 100 + minor): 107. */
 int32_t csa2_version(void);
 
 /*

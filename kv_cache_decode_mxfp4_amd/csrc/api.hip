@@ -46,6 +46,9 @@ csa2_status finish(hipError_t e, hipStream_t stream, const char* what)
             return fail((st), __VA_ARGS__);    \
     } while (0)
 
+// A call whose launch would exceed one dispatch's 2^32 - 1 work-items.
+constexpr const char* kTooLarge = "%s: a launch would need more than 2^32 - 1 work-items";
+
 inline bool aligned(const void* p, size_t a)
 {
     return (reinterpret_cast<uintptr_t>(p) % a) == 0;
@@ -62,7 +65,7 @@ const char* csa2_last_error(void)
 
 int32_t csa2_version(void)
 {
-    return 106;
+    return 107;
 }
 
 csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
@@ -87,6 +90,7 @@ csa2_status csa2_quantize_kv(const float* x, int64_t rows, int32_t channels,
             "quantize_kv: rope_dim > 0 needs cos/sin tables");
     REQUIRE(aligned(x, 16) && aligned(codes, 8), CSA2_ERR_INVALID_ARG,
             "quantize_kv: x must be 16-byte and codes 8-byte aligned");
+    REQUIRE(csa2::quantize_kv_fits(rows, channels), CSA2_ERR_UNSUPPORTED, kTooLarge, "quantize_kv");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_quantize_kv(x, rows, channels, rope_cos, rope_sin, rope_offset,
                                            rope_dim, codes, scales, dst_row, dst_stride, s),
@@ -105,6 +109,7 @@ csa2_status csa2_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_
     REQUIRE(x && out, CSA2_ERR_INVALID_ARG, "quantize_swa: null pointer");
     REQUIRE(aligned(x, 16) && aligned(out, 4), CSA2_ERR_INVALID_ARG,
             "quantize_swa: x must be 16-byte and out 4-byte aligned");
+    REQUIRE(csa2::quantize_swa_fits(n), CSA2_ERR_UNSUPPORTED, kTooLarge, "quantize_swa");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_quantize_swa(x, n, row_len, out, dst_stride, s), s,
                   "quantize_swa");
@@ -149,6 +154,8 @@ csa2_status csa2_encode_entries(int32_t rows, const float* kv_x, const float* ro
         REQUIRE(aligned(swa_x, 16) && aligned(swa_out, 4), CSA2_ERR_INVALID_ARG,
                 "encode_entries: misaligned window pointer");
     }
+    REQUIRE(csa2::encode_entries_fits(rows, idx_x != nullptr, swa_rows), CSA2_ERR_UNSUPPORTED,
+            kTooLarge, "encode_entries");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_encode_entries(rows, kv_x, rope_cos, rope_sin, rope_offset,
                                               rope_dim, kv_codes, kv_scales, kv_stride, kv_dst,
@@ -196,6 +203,7 @@ csa2_status csa2_index_full(const uint16_t* q, const float* w, const uint8_t* k_
     if ((int64_t)B * nq == 0 || n_cap == 0)
         return CSA2_OK;
     REQUIRE(block_max != nullptr, CSA2_ERR_INVALID_ARG, "index_full: null block_max");
+    REQUIRE(csa2::index_full_fits(n_cap, B, nq), CSA2_ERR_UNSUPPORTED, kTooLarge, "index_full");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_index_full(q, w, k_codes, k_scales, n_cap, n_visible, B, nq,
                                           block_max, scores, nullptr, 0, nullptr, nullptr, s),
@@ -237,6 +245,8 @@ csa2_status csa2_index_full_pool(const uint16_t* q, const float* w, const uint8_
             "index_full_pool: workspace of %zu bytes needed, %zu given", need, ws_bytes);
     REQUIRE(aligned(ws, 8), CSA2_ERR_INVALID_ARG,
             "index_full_pool: workspace must be 8-byte aligned");
+    REQUIRE(csa2::index_full_fits(n_cap, B, nq) && csa2::topk_fits(L, rows, nb),
+            CSA2_ERR_UNSUPPORTED, kTooLarge, "index_full_pool");
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the scan writes the block select's group maxima itself when the groups
     // align with its chunks (group size dividing 64 blocks)
@@ -384,8 +394,20 @@ csa2_status csa2_index_full_select(const uint16_t* q, const float* w, const uint
             "index_full_select: workspace of %zu bytes needed, %zu given", P.ws_bytes, ws_bytes);
     REQUIRE(aligned(ws, 256), CSA2_ERR_INVALID_ARG,
             "index_full_select: workspace must be 256-byte aligned");
-    hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* pool_out = nb > 0 ? pool : nullptr;
+    {
+        // every launch the plan below makes
+        const bool select_fits =
+            P.mode != 2 ? csa2::block_select_fits(rows, pool_out != nullptr ? 2 : 1)
+                        : (nb == 0 || csa2::topk_fits(L, rows, nb)) && csa2::topk_fits(L, rows, k);
+        const bool rescore_fits =
+            P.rescore_fused ? csa2::pool_topk_fits(rows, k)
+                            : csa2::index_pool_fits(rows, k) &&
+                                  csa2::topk_fits((int64_t)k * csa2::kBlock, rows, k);
+        REQUIRE(csa2::index_full_fits(n_cap, B, nq) && select_fits && rescore_fits,
+                CSA2_ERR_UNSUPPORTED, kTooLarge, "index_full_select");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
     char* wsb = static_cast<char*>(ws);
     auto at = [wsb](size_t off) { return static_cast<void*>(wsb + off); };
     int32_t* tb = static_cast<int32_t*>(at(P.off_tb));
@@ -469,6 +491,8 @@ csa2_status csa2_index_pool(const uint16_t* q, const float* w, const uint8_t* k_
     if ((int64_t)B * nq == 0 || n_blocks == 0)
         return CSA2_OK;
     REQUIRE(blocks && pool_score && pool_idx, CSA2_ERR_INVALID_ARG, "index_pool: null pointer");
+    REQUIRE(csa2::index_pool_fits((int64_t)B * nq, n_blocks), CSA2_ERR_UNSUPPORTED, kTooLarge,
+            "index_pool");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_index_pool(q, w, k_codes, k_scales, n_cap, blocks, n_blocks,
                                           n_visible, B, nq, pool_score, pool_idx, s),
@@ -508,6 +532,8 @@ csa2_status csa2_index_pool_topk(const uint16_t* q, const float* w, const uint8_
             "index_pool_topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
     REQUIRE(aligned(ws, 256), CSA2_ERR_INVALID_ARG,
             "index_pool_topk: workspace must be 256-byte aligned");
+    REQUIRE(csa2::pool_topk_fits((int64_t)B * nq, n_blocks), CSA2_ERR_UNSUPPORTED, kTooLarge,
+            "index_pool_topk");
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_pool_topk(q, w, k_codes, k_scales, n_cap, blocks, n_blocks,
                                          n_visible, B, nq, k, topk, ws, s),
@@ -531,6 +557,7 @@ csa2_status csa2_topk(const float* score, const int32_t* idx, int64_t L, int32_t
     REQUIRE(L <= (1ll << 31) - 1, CSA2_ERR_INVALID_ARG, "topk: L above 2^31-1");
     REQUIRE((int64_t)rows * ((L + csa2::kTopkSegment - 1) / csa2::kTopkSegment) <= (1ll << 31) - 1,
             CSA2_ERR_INVALID_ARG, "topk: too many segments");
+    REQUIRE(csa2::topk_fits(L, rows, k), CSA2_ERR_UNSUPPORTED, kTooLarge, "topk");
     if (rows == 0)
         return CSA2_OK;
     REQUIRE(out != nullptr, CSA2_ERR_INVALID_ARG, "topk: null out");
@@ -553,6 +580,7 @@ csa2_status csa2_topk_noalloc(const float* score, const int32_t* idx, int64_t L,
     REQUIRE(L <= (1ll << 31) - 1, CSA2_ERR_INVALID_ARG, "topk_noalloc: L above 2^31-1");
     REQUIRE((int64_t)rows * ((L + csa2::kTopkSegment - 1) / csa2::kTopkSegment) <= (1ll << 31) - 1,
             CSA2_ERR_INVALID_ARG, "topk_noalloc: too many segments");
+    REQUIRE(csa2::topk_fits(L, rows, k), CSA2_ERR_UNSUPPORTED, kTooLarge, "topk_noalloc");
     if (rows == 0)
         return CSA2_OK;
     REQUIRE(out != nullptr, CSA2_ERR_INVALID_ARG, "topk_noalloc: null out");
@@ -638,6 +666,7 @@ static csa2_status attn_common(const uint16_t* q, int32_t B, int32_t nq,
     }
     REQUIRE(ws == nullptr || aligned(ws, 16), CSA2_ERR_INVALID_ARG, "%s: misaligned workspace",
             name);
+    REQUIRE(csa2::sparse_attn_fits(queries), CSA2_ERR_UNSUPPORTED, kTooLarge, name);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(csa2::launch_sparse_attn(q, queries, nq, kv_codes, kv_scales, n_cap, topk, k,
                                            swa, swa_cap, swa_end, n_win, softmax_scale, out,

@@ -834,7 +834,10 @@ hipError_t launch_heads(const uint16_t* q, int32_t queries, int32_t nq,
                         int32_t splits, float* part, const AttnOut& spec, bool bf16_out,
                         float* lse, hipStream_t stream)
 {
-    const dim3 grid((uint32_t)(padded_rows(queries) * (kHeads / kHW) * splits));
+    const int64_t wgs = padded_rows(queries) * (kHeads / kHW) * splits;
+    if (!grid_fits(wgs, kWaves * kWave))
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((uint32_t)wgs);
     const dim3 block(kWaves * kWave);
     // the split form writes unnormalised partials; the merge applies the epilogue
     if (bf16_out && splits == 1)
@@ -849,6 +852,15 @@ hipError_t launch_heads(const uint16_t* q, int32_t queries, int32_t nq,
 }
 
 }  // namespace
+
+// The key-split form launches at most kSplitWgs workgroups (and its merge 16
+// per row of the few rows it serves), so the largest grid is the one-launch
+// form's: one workgroup per row and head group.
+bool sparse_attn_fits(int32_t queries)
+{
+    const int hw = queries >= kHw64MinRows ? 64 : (queries >= kHw32MinRows ? 32 : 16);
+    return grid_fits(padded_rows(queries) * (kHeads / hw), kWaves * kWave);
+}
 
 size_t attn_workspace(int32_t queries, int32_t k, int32_t n_win)
 {

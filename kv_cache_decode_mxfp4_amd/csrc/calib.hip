@@ -52,6 +52,8 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, int32_t workgroups
 {
     if (bytes == 0)
         return hipSuccess;
+    if (!grid_fits(workgroups, kThreads))
+        return hipErrorInvalidConfiguration;
     // slices of whole 16-byte units
     const int64_t slice = ((bytes + workgroups - 1) / workgroups + 15) / 16 * 16;
     const dim3 grid((uint32_t)workgroups), block(kThreads);

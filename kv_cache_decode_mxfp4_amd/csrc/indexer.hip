@@ -795,6 +795,21 @@ ScanShape scan_shape(int64_t n_cap, int32_t B, int32_t nq)
     return sh;
 }
 
+// Workgroups of the scan launch: one per chunk and row, or per chunk and group
+// of 8 rows (multi-row form).
+static int64_t scan_workgroups(int64_t n_cap, int32_t B, int32_t nq)
+{
+    const ScanShape sh = scan_shape(n_cap, B, nq);
+    const int64_t row_units = sh.multi_row ? (int64_t)B * ((nq + kRowGroup - 1) / kRowGroup)
+                                           : (int64_t)B * nq;
+    return row_units * sh.chunks_per_row;
+}
+
+bool index_full_fits(int64_t n_cap, int32_t B, int32_t nq)
+{
+    return grid_fits(scan_workgroups(n_cap, B, nq), kWaves * kWave);
+}
+
 hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_visible,
                              int32_t B, int32_t nq, float* block_max, float* scores,
@@ -802,6 +817,11 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
                              hipEvent_t ev_stop, hipStream_t stream, uint32_t* cand_key,
                              int32_t* cand_blk, int32_t* cand_full, int32_t kl)
 {
+    const int64_t grid = scan_workgroups(n_cap, B, nq);
+    if (grid == 0)
+        return hipSuccess;
+    if (!grid_fits(grid, kWaves * kWave))
+        return hipErrorInvalidConfiguration;
     const int64_t nblk_cap = (n_cap + kBlock - 1) / kBlock;
     int32_t gshift = 0;  // group = 1 << gshift (a power of two dividing 64)
     while (group_keys != nullptr && (1 << gshift) < group)
@@ -812,9 +832,6 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
         // dequantised key tile
         const int32_t groups_per_seq = (nq + kRowGroup - 1) / kRowGroup;
         const int64_t chunks = (n_cap + kRowsChunk - 1) / kRowsChunk;
-        const int64_t grid = (int64_t)B * groups_per_seq * chunks;
-        if (grid == 0)
-            return hipSuccess;
         return launch_scan(scores != nullptr ? index_full_rows_kernel<true>
                                              : index_full_rows_kernel<false>,
                            dim3((uint32_t)grid), dim3(kWaves * kWave), stream, ev_start, ev_stop,
@@ -822,13 +839,9 @@ hipError_t launch_index_full(const uint16_t* q, const float* w, const uint8_t* k
                            n_visible, nq, groups_per_seq, (int32_t)chunks, nblk_cap, block_max,
                            scores, group_keys, gshift, ngroups);
     }
-    const int64_t rows = (int64_t)B * nq;
     const ScanShape sh = scan_shape(n_cap, B, nq);
     const int32_t chunk = sh.chunk;
     const int64_t chunks = sh.chunks_per_row;
-    const int64_t grid = rows * chunks;
-    if (grid == 0)
-        return hipSuccess;
     if (cand_key == nullptr)
         kl = 0;
     return launch_scan(scores != nullptr ? index_full_kernel<true> : index_full_kernel<false>,
@@ -845,6 +858,20 @@ size_t pool_topk_workspace(int32_t rows, int32_t n_blocks)
     return cnt + 2 * (((size_t)rows * slots * 4 + 255) / 256 * 256);
 }
 
+// Workgroups per row of the fused rescoring: one key tile per wave for the
+// decode pool sizes, two for longer pools.
+static int64_t pool_topk_wgs_per_row(int64_t slots)
+{
+    const int tpw = slots <= 4096 ? 1 : 2;
+    const int64_t per_wg = (int64_t)kPtWaves * tpw * kTileEntries;
+    return slots > 0 ? (slots + per_wg - 1) / per_wg : 1;
+}
+
+bool pool_topk_fits(int64_t rows, int32_t n_blocks)
+{
+    return grid_fits(rows * pool_topk_wgs_per_row((int64_t)n_blocks * kBlock), kPtThreads);
+}
+
 hipError_t launch_pool_topk(const uint16_t* q, const float* w, const uint8_t* k_codes,
                             const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
                             int32_t n_blocks, const int32_t* n_visible, int32_t B, int32_t nq,
@@ -854,15 +881,14 @@ hipError_t launch_pool_topk(const uint16_t* q, const float* w, const uint8_t* k_
     const int64_t slots = (int64_t)n_blocks * kBlock;
     if (rows == 0)
         return hipSuccess;
+    const int64_t wgs = pool_topk_wgs_per_row(slots);
+    if (!grid_fits(rows * wgs, kPtThreads))
+        return hipErrorInvalidConfiguration;
     char* base = static_cast<char*>(ws);
     uint32_t* counters = reinterpret_cast<uint32_t*>(base);
     const size_t cnt = ((size_t)rows * 4 + 255) / 256 * 256;
     uint32_t* sc = reinterpret_cast<uint32_t*>(base + cnt);
     uint32_t* ix = reinterpret_cast<uint32_t*>(base + cnt + ((size_t)rows * slots * 4 + 255) / 256 * 256);
-    // one tile per wave for the decode pool sizes, two for longer pools
-    const int tpw = slots <= 4096 ? 1 : 2;
-    const int64_t per_wg = (int64_t)kPtWaves * tpw * kTileEntries;
-    const int64_t wgs = slots > 0 ? (slots + per_wg - 1) / per_wg : 1;
     const dim3 grid((uint32_t)(rows * wgs)), block(kPtThreads);
 #define CSA2_POOL_TOPK(T, P)                                                                     \
     pool_topk_kernel<T, P><<<grid, block, 0, stream>>>(q, w, k_codes, k_scales, n_cap, blocks,   \
@@ -878,17 +904,30 @@ hipError_t launch_pool_topk(const uint16_t* q, const float* w, const uint8_t* k_
     return hipGetLastError();
 }
 
+// Workgroups per row of the pool scan (kPoolTilesPerWave key tiles per wave).
+static int64_t index_pool_wgs_per_row(int32_t n_blocks)
+{
+    const int64_t slots = (int64_t)n_blocks * kBlock;
+    const int64_t per_wg = (int64_t)kWaves * kPoolTilesPerWave * kTileEntries;
+    return (slots + per_wg - 1) / per_wg;
+}
+
+bool index_pool_fits(int64_t rows, int32_t n_blocks)
+{
+    return grid_fits(rows * index_pool_wgs_per_row(n_blocks), kWaves * kWave);
+}
+
 hipError_t launch_index_pool(const uint16_t* q, const float* w, const uint8_t* k_codes,
                              const uint8_t* k_scales, int64_t n_cap, const int32_t* blocks,
                              int32_t n_blocks, const int32_t* n_visible, int32_t B, int32_t nq,
                              float* pool_score, int32_t* pool_idx, hipStream_t stream)
 {
-    const int64_t slots = (int64_t)n_blocks * kBlock;
-    const int64_t per_wg = (int64_t)kWaves * kPoolTilesPerWave * kTileEntries;
-    const int64_t wgs = (slots + per_wg - 1) / per_wg;
+    const int64_t wgs = index_pool_wgs_per_row(n_blocks);
     const int64_t grid = (int64_t)B * nq * wgs;
     if (grid == 0)
         return hipSuccess;
+    if (!grid_fits(grid, kWaves * kWave))
+        return hipErrorInvalidConfiguration;
     index_pool_kernel<<<dim3((uint32_t)grid), dim3(kWaves * kWave), 0, stream>>>(
         q, w, k_codes, k_scales, n_cap, blocks, n_blocks, n_visible, nq, (int32_t)wgs,
         pool_score, pool_idx);

@@ -11,6 +11,26 @@
 
 namespace csa2 {
 
+// A dispatch counts its grid in work-items with 32 bits, so one launch holds
+// at most 2^32 - 1 work-items.  Each launcher checks its grids against that
+// before enqueueing anything (hipErrorInvalidConfiguration otherwise), and the
+// *_fits functions below answer the same question for the C ABI's argument
+// validation, which rejects an oversized call before any of its launches.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+inline bool grid_fits(int64_t workgroups, int64_t threads)
+{
+    return workgroups >= 0 && workgroups <= kMaxWorkItems / threads;
+}
+bool quantize_kv_fits(int64_t rows, int32_t channels);
+bool quantize_swa_fits(int64_t n);
+bool encode_entries_fits(int32_t rows, bool idx_rows_given, int32_t swa_rows);
+bool index_full_fits(int64_t n_cap, int32_t B, int32_t nq);
+bool index_pool_fits(int64_t rows, int32_t n_blocks);
+bool pool_topk_fits(int64_t rows, int32_t n_blocks);
+bool block_select_fits(int64_t rows, int32_t passes);
+bool topk_fits(int64_t L, int64_t rows, int32_t k);
+bool sparse_attn_fits(int32_t queries);
+
 hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, const float* cs,
                               const float* sn, int32_t rope_off, int32_t rope_dim, uint8_t* codes,
                               uint8_t* scales, int64_t dst_row, int64_t dst_stride,

@@ -335,15 +335,60 @@ encode_entries_kernel(EntryJob J)
 
 }  // namespace
 
+namespace {
+
+// Workgroups of the encoding launches (256 threads each): one thread per
+// 16-channel MXFP4 group, per 4 window bytes, and for the one-launch encoder
+// the sum of its three parts.
+int64_t quantize_kv_workgroups(int64_t rows, int32_t channels)
+{
+    return (rows * (channels / 16) + 255) / 256;
+}
+
+int64_t quantize_swa_workgroups(int64_t n)
+{
+    return (n / 4 + 255) / 256;
+}
+
+struct EntryGrid {
+    int64_t kv, idx, swa;
+};
+
+EntryGrid encode_entries_grid(int32_t rows, bool idx_rows_given, int32_t swa_rows)
+{
+    return {((int64_t)rows * (kDim / 16) + 255) / 256,
+            idx_rows_given ? ((int64_t)rows * (kIdxDim / 16) + 255) / 256 : (int64_t)rows,
+            ((int64_t)swa_rows * (kDim / 4) + 255) / 256};
+}
+
+}  // namespace
+
+bool quantize_kv_fits(int64_t rows, int32_t channels)
+{
+    return grid_fits(quantize_kv_workgroups(rows, channels), 256);
+}
+
+bool quantize_swa_fits(int64_t n)
+{
+    return grid_fits(quantize_swa_workgroups(n), 256);
+}
+
+bool encode_entries_fits(int32_t rows, bool idx_rows_given, int32_t swa_rows)
+{
+    const EntryGrid g = encode_entries_grid(rows, idx_rows_given, swa_rows);
+    return grid_fits(g.kv + g.idx + g.swa, 256);
+}
+
 hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, const float* cs,
                               const float* sn, int32_t rope_off, int32_t rope_dim, uint8_t* codes,
                               uint8_t* scales, int64_t dst_row, int64_t dst_stride,
                               hipStream_t stream)
 {
-    const int64_t threads = rows * (channels / 16);
-    if (threads == 0)
+    const int64_t grid = quantize_kv_workgroups(rows, channels);
+    if (grid == 0)
         return hipSuccess;
-    const int64_t grid = (threads + 255) / 256;
+    if (!grid_fits(grid, 256))
+        return hipErrorInvalidConfiguration;
     quantize_kv_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
         x, rows, channels, cs, sn, rope_off, rope_dim, codes, scales, dst_row, dst_stride);
     return hipGetLastError();
@@ -352,10 +397,11 @@ hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, co
 hipError_t launch_quantize_swa(const float* x, int64_t n, int32_t row_len, uint8_t* out,
                                int64_t dst_stride, hipStream_t stream)
 {
-    const int64_t threads = n / 4;
-    if (threads == 0)
+    const int64_t grid = quantize_swa_workgroups(n);
+    if (grid == 0)
         return hipSuccess;
-    const int64_t grid = (threads + 255) / 256;
+    if (!grid_fits(grid, 256))
+        return hipErrorInvalidConfiguration;
     quantize_swa_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(x, n, row_len, out,
                                                                         dst_stride);
     return hipGetLastError();
@@ -374,13 +420,14 @@ hipError_t launch_encode_entries(int32_t rows, const float* kv_x, const float* c
     EntryJob J{rows, kv_x, cs, sn, rope_off, rope_dim, kv_codes, kv_scales, kv_stride, kv_dst,
                dst_row, kv_cap, idx_x, w_idx, idx_codes, idx_scales, idx_stride, idx_y,
                swa_x, swa_rows, swa_out, swa_stride, swa_dst, swa_cap, 0, 0};
-    J.wg_kv = (int32_t)(((int64_t)rows * (kDim / 16) + 255) / 256);
-    J.wg_idx = idx_x != nullptr ? (int32_t)(((int64_t)rows * (kIdxDim / 16) + 255) / 256)
-                                : rows;
-    const int64_t w_swa = ((int64_t)swa_rows * (kDim / 4) + 255) / 256;
-    const int64_t grid = (int64_t)J.wg_kv + J.wg_idx + w_swa;
+    const EntryGrid eg = encode_entries_grid(rows, idx_x != nullptr, swa_rows);
+    const int64_t grid = eg.kv + eg.idx + eg.swa;
     if (grid == 0)
         return hipSuccess;
+    if (!grid_fits(grid, 256))
+        return hipErrorInvalidConfiguration;
+    J.wg_kv = (int32_t)eg.kv;
+    J.wg_idx = (int32_t)eg.idx;
     encode_entries_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(J);
     return hipGetLastError();
 }

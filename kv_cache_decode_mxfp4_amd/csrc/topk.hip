@@ -553,6 +553,28 @@ int32_t topk_group_size(int64_t L, int32_t k)
     return group_size(L, k);
 }
 
+bool block_select_fits(int64_t rows, int32_t passes)
+{
+    return grid_fits(rows * passes, kThreads);
+}
+
+// Every launch of launch_topk: one workgroup per row (the final select or the
+// grouped one), the group maxima (counted in the larger of their two forms,
+// the vectorised one at one thread per 4 keys) or the first (largest) level of
+// segments.
+bool topk_fits(int64_t L, int64_t rows, int32_t k)
+{
+    if (!grid_fits(rows, kThreads))
+        return false;
+    const int32_t g = group_size(L, k);
+    if (g > 0) {
+        const int64_t ngroups = (L + g - 1) / g;
+        return grid_fits(rows * ((ngroups + 255) / 256), 256) &&
+               grid_fits((rows * (L / 4) + 255) / 256, 256);
+    }
+    return L <= kTopkSegment || grid_fits(rows * segments(L), kThreads);
+}
+
 hipError_t launch_block_select(const BlockSelect& S, hipStream_t stream)
 {
     if (S.rows == 0)
@@ -564,6 +586,8 @@ hipError_t launch_block_select(const BlockSelect& S, hipStream_t stream)
     const bool cand = S.cand_key != nullptr;
     const int64_t n = cand ? (int64_t)S.chunks * S.kl : S.L;
     const int32_t passes = S.nb > 0 && S.pool != nullptr ? 2 : 1;
+    if (!block_select_fits(S.rows, passes))
+        return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)(passes * S.rows)), block(kThreads);
 #define CSA2_BLOCK_SELECT(PP)                                                            \
     if (cand)                                                                            \
@@ -587,6 +611,8 @@ hipError_t launch_topk(const float* score, const int32_t* idx, int64_t L, int32_
 {
     if (rows == 0)
         return hipSuccess;
+    if (!topk_fits(L, rows, k))
+        return hipErrorInvalidConfiguration;
     const int32_t g = group_size(L, k);
     if (g > 0) {
         const int64_t ngroups = (L + g - 1) / g;

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_workspace_queries():
     lib = L.load()
-    assert lib.csa2_version() == 106
+    assert lib.csa2_version() == 107
     assert lib.csa2_topk_workspace(16384, 16, 2048) == 0
     assert lib.csa2_topk_workspace(131072, 16, 2048) == 16 * 16384 * 4  # group maxima
     assert lib.csa2_topk_workspace(300000, 4, 2048) == 2 * 4 * 19 * 2048 * 8  # segment levels
@@ -114,6 +114,57 @@ def test_host_validation_rejects_bad_arguments():
     st, msg = _status("csa2_index_full_select", vp, vp, vp, vp, big, vp, 1, 1, 8, 16, 4, vp, vp,
                       vp, vp, ctypes.c_size_t(1 << 30), None, None, None)
     assert st == 2 and "2^24" in msg, (st, msg)
+
+
+def test_launches_beyond_one_dispatch_are_rejected():
+    """A dispatch counts its grid in 32-bit work-items: every call whose launch would
+    need more than 2^32 - 1 of them is rejected on the host (status 2) before
+    anything is enqueued, one shape just past each launch's limit."""
+    vp = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    big = ctypes.c_size_t(1 << 46)  # workspace size: never the reason
+    f1 = ctypes.c_float(1.0)
+    cases = {
+        # one 256-thread workgroup per 16-channel group of 256 rows: 2^34 threads
+        "quantize_kv": ("csa2_quantize_kv", vp, 1 << 29, 512, None, None, 0, 0, vp, vp, 0, 1,
+                        None),
+        "quantize_swa": ("csa2_quantize_swa", vp, 1 << 34, 512, vp, 1, None),
+        "encode_entries": ("csa2_encode_entries", 1 << 27, vp, None, None, 0, 0, vp, vp, 1,
+                           None, 0, 1 << 27, vp, None, vp, vp, 1, None, None, 0, None, 1, None,
+                           0, None),
+        # one-row scan: 256 rows x 65536 chunks of 16384 entries = 2^24 workgroups
+        "index_full": ("csa2_index_full", vp, vp, vp, vp, 1 << 30, vp, 256, 1, 8, vp, None,
+                       None),
+        # multi-row scan: 2^21 groups of 8 rows x 256 chunks
+        "index_full rows": ("csa2_index_full", vp, vp, vp, vp, 1 << 20, vp, 1, 1 << 24, 8, vp,
+                            None, None),
+        "index_full_pool": ("csa2_index_full_pool", vp, vp, vp, vp, 65536, vp, 1 << 22, 1, 8, 16,
+                            vp, vp, vp, big, None, None, None),
+        # 2^22 rows: the scan and the block select (2 x 1024 threads per row)
+        "index_full_select": ("csa2_index_full_select", vp, vp, vp, vp, 65536, vp, 1 << 22, 1, 8,
+                              16, 4, vp, vp, vp, vp, big, None, None, None),
+        # 4096 rows x 8192 workgroups of 2^20 blocks' positions
+        "index_pool": ("csa2_index_pool", vp, vp, vp, vp, 1 << 24, vp, 1 << 20, 8, vp, 4096, 1,
+                       vp, vp, None),
+        # 2^18 rows x 16 workgroups of 1024 threads
+        "index_pool_topk": ("csa2_index_pool_topk", vp, vp, vp, vp, 1 << 24, vp, 2048, 8, vp,
+                            1 << 18, 1, 512, vp, vp, big, None),
+        # one 1024-thread workgroup per row
+        "topk": ("csa2_topk", vp, None, 4096, 1 << 22, None, 8, vp, None, 0, None),
+        "topk_noalloc": ("csa2_topk_noalloc", vp, None, 4096, 1 << 22, None, 8, vp, None),
+        # one 512-thread workgroup per row and its 64 heads
+        "sparse_attn": ("csa2_sparse_attn", vp, 1, 1 << 23, vp, vp, 100, vp, 4, vp, 128, vp, 128,
+                        f1, vp, None, None, 0, None),
+    }
+    for name, (fn, *args) in cases.items():
+        st, msg = _status(fn, *args)
+        assert st == 2 and "2^32 - 1 work-items" in msg, (name, st, msg)
+    # the limit itself: rows of 131072 keys take their group maxima at one thread per 4
+    # keys, 2^15 per row, so 2^17 - 1 rows fit (the call then stops at its missing
+    # workspace, before any launch) and 2^17 do not
+    st, msg = _status("csa2_topk", vp, None, 131072, (1 << 17) - 1, None, 8, vp, None, 0, None)
+    assert st == 3 and "workspace" in msg, (st, msg)
+    st, msg = _status("csa2_topk", vp, None, 131072, 1 << 17, None, 8, vp, None, 0, None)
+    assert st == 2 and "2^32 - 1 work-items" in msg, (st, msg)
 
 
 def test_empty_inputs_are_no_ops():
