@@ -72,6 +72,7 @@ CASES = [
     (2, 1, 2048, 32, 64, [2048, 1000], "random"),                 # pool smaller than k
     (2, 1, 262144, 0, 512, None, "random"),                       # no pool
     (1, 1, 0, 2048, 512, [5], "random"),                          # empty cache
+    (1, 1, 1 << 24, 2048, 512, None, "random"),                   # the most a gathering call takes
 ]
 
 
@@ -131,6 +132,7 @@ POOL_CASES = [
     (1, 64, 40000, 2048, 512, "causal"),                      # decoder prefill rows
     (2, 1, 20000, 1, 8, None),                                # a single block
     (3, 1, 50003, 2048, 512, [50003, 20001, 0]),              # sequences start inside key tiles
+    (1, 1, 1 << 24, 2048, 512, None),                         # 32-bit gather offsets near 2^30 bytes
 ]
 
 

@@ -306,6 +306,45 @@ def test_index_full_long_chunks_ragged_rows():
         assert np.all(sc[i, n:] == 12345.0) and np.all(bm[i, rb.size:] == 12345.0)
 
 
+def test_index_full_at_the_largest_sequence():
+    """The scan at its limit: one sequence of 2^30 entries (64 GiB of key codes, 8 GiB of
+    scales), so its addresses pass 2^32 bytes.  Every key byte is seeded random (any
+    code, any finite E4M3 scale); the scores and block maxima of key tiles at the start,
+    the middle and the end, and of sampled tiles, against the oracle's."""
+    N = 1 << 30
+    print(f"[case] scan of one sequence of {N} entries", flush=True)
+    g = torch.Generator(device=dev())
+    g.manual_seed(30)
+    kc = torch.empty(N * 64, dtype=torch.uint8, device=dev())
+    ks = torch.empty((1, N, 8), dtype=torch.uint8, device=dev())
+    part = 1 << 30  # bytes per fill: every fill launch stays below 2^31 elements
+    for o in range(0, kc.numel(), part):
+        kc[o:o + part].random_(0, 256, generator=g)
+    for o in range(0, N, part // 8):
+        sl = ks[0, o:o + part // 8]
+        sl.random_(0, 256, generator=g)
+        sl.bitwise_and_(0x77).bitwise_or_(0x30)  # finite E4M3 scales
+    q = synth.normal_bf16(synth.key(11, 30, 0, 0), 0, 4096, 1 / np.sqrt(128)).reshape(1, 1, 32, 128)
+    w = synth.uniform_f32(synth.key(11, 31, 0, 0), 0, 32).reshape(1, 1, 32)
+    bm = torch.full((1, 1, N // 8), 12345.0, device=dev())
+    sc = torch.full((1, 1, N), 12345.0, device=dev())
+    L.index_full(t(q, torch.uint16), t(w), kc, ks, t(np.array([[N]], np.int32)), bm, sc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(30)
+    n_tiles = N // 32
+    tiles = [0, 1, n_tiles // 2, n_tiles - 2, n_tiles - 1] + rng.integers(0, n_tiles, 11).tolist()
+    for tl in tiles:
+        codes = untile_keys(kc[tl * 2048:(tl + 1) * 2048], 32)
+        scales = ks[0, 32 * tl:32 * tl + 32].cpu().numpy()
+        ref = oracle.index_scores(q[0, 0], w[0, 0], codes, scales, 32)
+        ok, err = finite_close(sc[0, 0, 32 * tl:32 * tl + 32].cpu().numpy(), ref)
+        assert ok, f"scores of tile {tl}: max err {err}"
+        ok, err = finite_close(bm[0, 0, 4 * tl:4 * tl + 4].cpu().numpy(), oracle.block_max(ref, 8))
+        assert ok, f"block maxima of tile {tl}: max err {err}"
+    del kc, ks, bm, sc
+    torch.cuda.empty_cache()
+
+
 def test_index_pool_scores_bit_identical_to_scan():
     x, kc, ks, q, w, nv = _index_case(seed=1)
     B, N = kc.shape[0], kc.shape[1]
@@ -572,6 +611,39 @@ def test_sparse_attn_matches_oracle(variant):
             assert np.all(np.isneginf(lse[b, 0])) and np.all(out[b, 0] == 0)
         else:
             assert max_abs(lse[b, 0], rl) <= 1e-4
+
+
+@pytest.mark.parametrize("use_ws", [True, False])
+def test_sparse_attn_rows_at_the_top_of_the_largest_caches(use_ws):
+    """The attention addresses rows with 32-bit byte offsets, so its caches hold at most
+    2^24 main entries (256 code bytes each: offsets up to 2^32 - 256) and 2^22 window
+    rows: selected entries up to the very last of a 2^24-entry cache and window rows
+    ending at 2^22, against the oracle over the same rows in small arrays."""
+    N, W, n = 1 << 24, 1 << 22, 600
+    print(f"[case] attention rows below {N} / {W}, workspace {use_ws}", flush=True)
+    vc, vs, sw, sel, q = _attn_case(B=1, N=n, k=100, seed=31)
+    sel[0, 0, -1] = n - 1  # the cache's last entry (sel stays sorted and distinct)
+    vcd = torch.zeros((1, N, 256), dtype=torch.uint8, device=dev())
+    vsd = torch.zeros((1, N, 32), dtype=torch.uint8, device=dev())
+    swd = torch.zeros((1, W, 512), dtype=torch.uint8, device=dev())
+    vcd[0, N - n:] = t(vc[0])
+    vsd[0, N - n:] = t(vs[0])
+    swd[0, W - sw.shape[1]:] = t(sw[0])
+    out = torch.full((1, 1, 64, 512), 777.0, device=dev())
+    lse = torch.full((1, 1, 64), 777.0, device=dev())
+    ws = None
+    if use_ws:
+        ws = torch.empty(max(L.sparse_attn_workspace(1, 1, 100, 128), 16), dtype=torch.uint8,
+                         device=dev())
+    L.sparse_attn(t(q, torch.uint16), vcd, vsd, t(sel + (N - n)), swd,
+                  t(np.array([[W]], np.int32)), out, lse, n_win=128, softmax_scale=1.0, ws=ws)
+    torch.cuda.synchronize()
+    # the window rows [W - 128, W) are rows [32, 160) of the small window
+    ro, rl = oracle.attention(q[0, 0], vc[0], vs[0], sel[0, 0], sw[0], sw.shape[1], 128, 1.0)
+    assert max_abs(out.cpu().numpy()[0, 0], ro) <= ATTN_TOL
+    assert max_abs(lse.cpu().numpy()[0, 0], rl) <= 1e-4
+    del vcd, vsd, swd
+    torch.cuda.empty_cache()
 
 
 def test_sparse_attn_k_not_multiple_of_tile_and_large_k():
