@@ -64,6 +64,8 @@
  *     the scans rows x ceil(n_cap / 16384)
  *     below 2^24 (decode) or ceil(nq / 8) x ceil(n_cap / 4096) per sequence
  *     (prefill); csa2_sparse_attn below 2^23 query rows.
+ *   - The *_workspace queries return 0 for sizes the matching call rejects
+ *     (negative sizes, more than 2^24 query rows, k or nb out of range).
  */
 #ifndef CSA2_H
 #define CSA2_H

@@ -46,6 +46,9 @@ csa2_status finish(hipError_t e, hipStream_t stream, const char* what)
             return fail((st), __VA_ARGS__);    \
     } while (0)
 
+// Query rows (B * nq) a call takes; the workspace queries return 0 beyond it.
+constexpr int64_t kMaxRows = 1ll << 24;
+
 // A call whose launch would exceed one dispatch's 2^32 - 1 work-items.
 constexpr const char* kTooLarge = "%s: a launch would need more than 2^32 - 1 work-items";
 
@@ -172,7 +175,7 @@ static csa2_status check_indexer(const char* fn, const uint16_t* q, const float*
     REQUIRE(B >= 0 && nq >= 0 && n_cap >= 0, CSA2_ERR_INVALID_ARG, "%s: negative size", fn);
     REQUIRE(block == csa2::kBlock, CSA2_ERR_UNSUPPORTED, "%s: block must be %d (got %d)", fn,
             csa2::kBlock, block);
-    REQUIRE((int64_t)B * nq <= (1ll << 24), CSA2_ERR_INVALID_ARG, "%s: too many query rows", fn);
+    REQUIRE((int64_t)B * nq <= kMaxRows, CSA2_ERR_INVALID_ARG, "%s: too many query rows", fn);
     REQUIRE(n_cap <= (1ll << 30), CSA2_ERR_INVALID_ARG, "%s: n_cap above 2^30", fn);
     if ((int64_t)B * nq == 0)
         return CSA2_OK;
@@ -212,7 +215,7 @@ csa2_status csa2_index_full(const uint16_t* q, const float* w, const uint8_t* k_
 
 size_t csa2_index_full_pool_workspace(int64_t n_cap, int32_t rows, int32_t nb)
 {
-    if (n_cap < 0 || rows < 0 || nb < 1)
+    if (n_cap < 0 || rows < 0 || nb < 1 || nb > csa2::kTopkMaxK || rows > kMaxRows)
         return 0;
     return csa2::topk_workspace((n_cap + csa2::kBlock - 1) / csa2::kBlock, rows, nb);
 }
@@ -356,7 +359,7 @@ size_t csa2_index_full_select_workspace(int64_t n_cap, int32_t B, int32_t nq, in
                                         int32_t k)
 {
     if (n_cap < 0 || B < 0 || nq < 0 || nb < 0 || k < 1 || nb > csa2::kTopkMaxK ||
-        k > csa2::kTopkMaxK)
+        k > csa2::kTopkMaxK || (int64_t)B * nq > kMaxRows)
         return 0;
     return full_select_plan(n_cap, B, nq, nb, k).ws_bytes;
 }
@@ -501,7 +504,8 @@ csa2_status csa2_index_pool(const uint16_t* q, const float* w, const uint8_t* k_
 
 size_t csa2_index_pool_topk_workspace(int32_t B, int32_t nq, int32_t n_blocks)
 {
-    if (B < 0 || nq < 0 || n_blocks < 0 || n_blocks > csa2::kTopkSegment / csa2::kBlock)
+    if (B < 0 || nq < 0 || n_blocks < 0 || n_blocks > csa2::kTopkSegment / csa2::kBlock ||
+        (int64_t)B * nq > kMaxRows)
         return 0;
     return csa2::pool_topk_workspace(B * nq, n_blocks);
 }
@@ -623,7 +627,7 @@ csa2_status csa2_stream_read(const void* src, int64_t bytes, int32_t workgroups,
 
 size_t csa2_sparse_attn_workspace(int32_t B, int32_t nq, int32_t k, int32_t n_win)
 {
-    if (B < 0 || nq < 0 || k < 0 || n_win < 0)
+    if (B < 0 || nq < 0 || k < 0 || n_win < 0 || (int64_t)B * nq > kMaxRows)
         return 0;
     return csa2::attn_workspace(B * nq, k, n_win);
 }
@@ -639,7 +643,7 @@ static csa2_status attn_common(const uint16_t* q, int32_t B, int32_t nq,
 {
     REQUIRE(B >= 0 && nq >= 0 && n_cap >= 0 && k >= 0 && swa_cap >= 0 && n_win >= 0,
             CSA2_ERR_INVALID_ARG, "%s: negative size", name);
-    REQUIRE((int64_t)B * nq <= (1ll << 24), CSA2_ERR_INVALID_ARG, "%s: too many query rows", name);
+    REQUIRE((int64_t)B * nq <= kMaxRows, CSA2_ERR_INVALID_ARG, "%s: too many query rows", name);
     REQUIRE(k <= 65536 && n_win <= 65536, CSA2_ERR_UNSUPPORTED, "%s: k or n_win too large", name);
     // the kernels address a sequence's rows with 32-bit byte offsets
     REQUIRE(n_cap <= (1ll << 24) && swa_cap <= (1 << 22), CSA2_ERR_UNSUPPORTED,

@@ -53,6 +53,12 @@ def test_version_and_workspace_queries():
     # 16 rows: 4 key splits per (row, 16 heads), each an O [16, 512] plus max and sum
     assert lib.csa2_sparse_attn_workspace(16, 1, 512, 128) == 16 * 4 * 4 * (16 * 512 + 32) * 4
     assert lib.csa2_sparse_attn_workspace(1, 1, 512, 128) == 8 * 4 * 8 * (16 * 512 + 32) * 4
+    # sizes the calls reject (here more than 2^24 query rows, whose product would also
+    # wrap in 32 bits) get 0, not a wrapped size
+    assert lib.csa2_sparse_attn_workspace(1 << 16, 1 << 16, 512, 128) == 0
+    assert lib.csa2_index_pool_topk_workspace(1 << 16, 1 << 16, 512) == 0
+    assert lib.csa2_index_full_select_workspace(1 << 20, 1 << 16, 1 << 16, 2048, 512) == 0
+    assert lib.csa2_index_pool_topk_workspace(1 << 12, 1 << 12, 512) > 0  # 2^24 rows: taken
 
 
 def _status(fn, *args):
