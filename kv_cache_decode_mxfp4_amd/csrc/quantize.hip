@@ -365,7 +365,8 @@ EntryGrid encode_entries_grid(int32_t rows, bool idx_rows_given, int32_t swa_row
 
 bool quantize_kv_fits(int64_t rows, int32_t channels)
 {
-    return grid_fits(quantize_kv_workgroups(rows, channels), 256);
+    // rows first: the product of a larger count would overflow
+    return rows <= kMaxWorkItems && grid_fits(quantize_kv_workgroups(rows, channels), 256);
 }
 
 bool quantize_swa_fits(int64_t n)
@@ -384,11 +385,11 @@ hipError_t launch_quantize_kv(const float* x, int64_t rows, int32_t channels, co
                               uint8_t* scales, int64_t dst_row, int64_t dst_stride,
                               hipStream_t stream)
 {
+    if (!quantize_kv_fits(rows, channels))
+        return hipErrorInvalidConfiguration;
     const int64_t grid = quantize_kv_workgroups(rows, channels);
     if (grid == 0)
         return hipSuccess;
-    if (!grid_fits(grid, 256))
-        return hipErrorInvalidConfiguration;
     quantize_kv_kernel<<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
         x, rows, channels, cs, sn, rope_off, rope_dim, codes, scales, dst_row, dst_stride);
     return hipGetLastError();

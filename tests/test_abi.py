@@ -133,6 +133,8 @@ def test_launches_beyond_one_dispatch_are_rejected():
         # one 256-thread workgroup per 16-channel group of 256 rows: 2^34 threads
         "quantize_kv": ("csa2_quantize_kv", vp, 1 << 29, 512, None, None, 0, 0, vp, vp, 0, 1,
                         None),
+        "quantize_kv rows": ("csa2_quantize_kv", vp, 1 << 60, 4096, None, None, 0, 0, vp, vp, 0,
+                             1, None),
         "quantize_swa": ("csa2_quantize_swa", vp, 1 << 34, 512, vp, 1, None),
         "encode_entries": ("csa2_encode_entries", 1 << 27, vp, None, None, 0, 0, vp, vp, 1,
                            None, 0, 1 << 27, vp, None, vp, vp, 1, None, None, 0, None, 1, None,
