@@ -310,7 +310,8 @@ def test_index_full_at_the_largest_sequence():
     """The scan at its limit: one sequence of 2^30 entries (64 GiB of key codes, 8 GiB of
     scales), so its addresses pass 2^32 bytes.  Every key byte is seeded random (any
     code, any finite E4M3 scale); the scores and block maxima of key tiles at the start,
-    the middle and the end, and of sampled tiles, against the oracle's."""
+    the middle and the end, and of sampled tiles, against the oracle's; then the
+    multi-row form over the same cache."""
     N = 1 << 30
     print(f"[case] scan of one sequence of {N} entries", flush=True)
     g = torch.Generator(device=dev())
@@ -341,7 +342,32 @@ def test_index_full_at_the_largest_sequence():
         assert ok, f"scores of tile {tl}: max err {err}"
         ok, err = finite_close(bm[0, 0, 4 * tl:4 * tl + 4].cpu().numpy(), oracle.block_max(ref, 8))
         assert ok, f"block maxima of tile {tl}: max err {err}"
-    del kc, ks, bm, sc
+    # two query rows of the sequence take the multi-row scan: row 0 (the same query)
+    # gives the one-row scan's block maxima bit for bit, row 1 (its own query, visible
+    # up to N - 12345) the oracle's on sampled tiles and its edge tile, and nothing
+    # past its visible blocks
+    print("[case] multi-row scan of the same sequence", flush=True)
+    n1 = N - 12345
+    q1 = synth.normal_bf16(synth.key(11, 32, 0, 0), 0, 4096, 1 / np.sqrt(128)).reshape(32, 128)
+    w1 = synth.uniform_f32(synth.key(11, 33, 0, 0), 0, 32)
+    q2 = np.stack([q[0, 0], q1])[None]
+    w2 = np.stack([w[0, 0], w1])[None]
+    bm2 = torch.full((1, 2, N // 8), 12345.0, device=dev())
+    L.index_full(t(q2, torch.uint16), t(w2), kc, ks, t(np.array([[N, n1]], np.int32)), bm2)
+    torch.cuda.synchronize()
+    assert torch.equal(bm2[0, 0], bm[0, 0]), "multi-row block maxima differ from the one-row scan's"
+    edge = (n1 - 1) // 32
+    for tl in tiles + [edge]:
+        if tl > edge:
+            continue
+        nv = min(32, n1 - 32 * tl)
+        codes = untile_keys(kc[tl * 2048:(tl + 1) * 2048], 32)[:nv]
+        scales = ks[0, 32 * tl:32 * tl + nv].cpu().numpy()
+        rb = oracle.block_max(oracle.index_scores(q1, w1, codes, scales, nv), 8)
+        ok, err = finite_close(bm2[0, 1, 4 * tl:4 * tl + rb.size].cpu().numpy(), rb)
+        assert ok, f"row 1 block maxima of tile {tl}: max err {err}"
+    assert bool((bm2[0, 1, (n1 + 7) // 8:] == 12345.0).all()), "row 1 wrote past its visible blocks"
+    del kc, ks, bm, sc, bm2
     torch.cuda.empty_cache()
 
 
