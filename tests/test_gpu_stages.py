@@ -309,7 +309,9 @@ def test_index_full_long_chunks_ragged_rows():
 def test_index_full_at_the_largest_sequence():
     """The scan at its limit: one sequence of 2^30 entries (64 GiB of key codes, 8 GiB of
     scales), so its addresses pass 2^32 bytes.  Every key byte is seeded random (any
-    code, any finite E4M3 scale); the scores and block maxima of key tiles at the start,
+    code, any finite E4M3 scale) except the last 40 entries, which csa2_quantize_kv
+    writes from known rows (bytes against the oracle's encoding); the scores and block
+    maxima of key tiles at the start,
     the middle and the end, and of sampled tiles, against the oracle's; then the
     multi-row form over the same cache."""
     N = 1 << 30
@@ -325,6 +327,14 @@ def test_index_full_at_the_largest_sequence():
         sl = ks[0, o:o + part // 8]
         sl.random_(0, 256, generator=g)
         sl.bitwise_and_(0x77).bitwise_or_(0x30)  # finite E4M3 scales
+    # the writer at the top of the cache: 40 rows (across the last key-tile boundary)
+    # encoded by csa2_quantize_kv into the last 40 entries, byte-exact against the oracle
+    xr = np.random.default_rng(31).standard_normal((40, 128)).astype(np.float32)
+    L.quantize_kv(t(xr), kc, ks.view(-1), dst_row=N - 40)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_rows(xr)
+    assert np.array_equal(untile_keys(kc[(N // 32 - 2) * 2048:], 64)[24:], rc)
+    assert np.array_equal(ks[0, N - 40:].cpu().numpy(), rs)
     q = synth.normal_bf16(synth.key(11, 30, 0, 0), 0, 4096, 1 / np.sqrt(128)).reshape(1, 1, 32, 128)
     w = synth.uniform_f32(synth.key(11, 31, 0, 0), 0, 32).reshape(1, 1, 32)
     bm = torch.full((1, 1, N // 8), 12345.0, device=dev())
