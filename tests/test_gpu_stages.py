@@ -1089,6 +1089,44 @@ def test_encode_entries_per_sequence_destinations_and_ring():
     assert np.all(sw[np.setdiff1d(np.arange(R * ring), swa_dst[sok])] == 0xA5)
 
 
+def test_encode_entries_at_the_top_of_the_largest_caches():
+    """Destinations at the top of the largest caches the attention takes (2^24 main and
+    indexer-key entries, 2^22 window rows), written in one launch in reverse order: the
+    bytes against the oracle's encodings, the rows just below untouched."""
+    N, W, R = 1 << 24, 1 << 22, 40
+    print(f"[case] encoder destinations below {N} / {W}", flush=True)
+
+    def filled(n):  # 0xA5 in fills of at most 2^30 elements each
+        a = torch.empty(n, dtype=torch.uint8, device=dev())
+        for o in range(0, n, 1 << 30):
+            a[o:o + (1 << 30)].fill_(0xA5)
+        return a
+
+    kv_x, cos, sin, idx_x, swa_x = _entries_case(R, R, seed=24)
+    kc, ks = filled(N * 256).view(N, 256), filled(N * 32).view(N, 32)
+    ic, isc = filled(L.key_code_bytes(N)), filled(N * 8).view(N, 8)
+    sw = filled(W * 512).view(W, 512)
+    kv_dst = np.arange(N - 1, N - 1 - R, -1, dtype=np.int64)  # the last entry first
+    swa_dst = np.arange(W - R, W, dtype=np.int64)
+    L.encode_entries(t(kv_x), kc, ks, ic, isc, idx_x=t(idx_x), rope_cos=t(cos), rope_sin=t(sin),
+                     rope_offset=448, rope_dim=64, kv_dst=t(kv_dst), swa_x=t(swa_x), swa_out=sw,
+                     swa_dst=t(swa_dst))
+    torch.cuda.synchronize()
+    lo = N - 64  # the top two key tiles
+    got = (kc[lo:].cpu().numpy(), ks[lo:].cpu().numpy(),
+           untile_keys(ic[(lo // 32) * 2048:], 64), isc[lo:].cpu().numpy())
+    ref_c, ref_s = oracle.quantize_rows(kv_x, cos, sin, 448, 64)
+    ref_ic, ref_is = oracle.quantize_rows(idx_x)
+    at = kv_dst - lo
+    for g, r, name in zip(got, (ref_c, ref_s, ref_ic, ref_is), ("codes", "scales", "key codes", "key scales")):
+        assert np.array_equal(g[at], r), name
+        assert np.all(g[:64 - R] == 0xA5), f"{name}: rows below the destinations touched"
+    gw = sw[W - 64:].cpu().numpy()
+    assert np.array_equal(gw[64 - R:], oracle.encode_fp8(swa_x)) and np.all(gw[:64 - R] == 0xA5)
+    del kc, ks, ic, isc, sw
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("P", [50, 300])
 def test_window_ring_replay_matches_linear_window(P):
     """Bounded replay of a prompt's last 128 tokens into the ring (slot p % 128) gives the
