@@ -228,6 +228,40 @@ def test_topk_bit_exact(Lr, k, kind):
         assert np.array_equal(got[r], ref), f"row {r}"
 
 
+def test_topk_of_the_longest_row():
+    """csa2_topk at its limit, one row of 2^31 - 1 keys (8 GiB; positions up to 2^31 - 2
+    pass through four levels of segment candidates): 512 planted keys above every other
+    key, at positions including the first and the last, are exactly the selection, in
+    position order.  The other keys are seeded uniform in [0, 1), the planted ones
+    2 + i; a valid prefix one short of the row leaves the last planted key out."""
+    Lr, k = (1 << 31) - 1, 512
+    print(f"[case] top-{k} of one row of {Lr} keys", flush=True)
+    g = torch.Generator(device=dev())
+    g.manual_seed(31)
+    sc = torch.empty(Lr, device=dev())
+    for o in range(0, Lr, 1 << 28):
+        sc[o:o + (1 << 28)].uniform_(0.0, 1.0, generator=g)
+    rng = np.random.default_rng(31)
+    pos = np.unique(np.concatenate([[0, Lr - 1, (1 << 30), (1 << 31) - 16384],
+                                    rng.integers(1, Lr - 1, 600)]))[:k]
+    pos[-1] = Lr - 1
+    pos = np.unique(pos)
+    assert pos.size == k
+    sc[t(pos.astype(np.int64))] = t(2.0 + np.arange(k, dtype=np.float32))
+    ws = torch.empty(L.topk_workspace(Lr, 1, k), dtype=torch.uint8, device=dev())
+    out = torch.full((1, k), -7, dtype=torch.int32, device=dev())
+    L.topk(sc[None], k, out, ws=ws)
+    assert np.array_equal(out.cpu().numpy()[0], pos), "top-k of the full row"
+    # valid prefix Lr - 1: the last planted key is out, the best unplanted key comes in
+    nv = t(np.array([Lr - 1], np.int32))
+    L.topk(sc[None], k, out, n_valid=nv, ws=ws)
+    got = out.cpu().numpy()[0]
+    best = int(torch.argmax(torch.where(sc < 2.0, sc, torch.zeros((), device=dev()))[:Lr - 1]))
+    assert np.array_equal(got, np.sort(np.concatenate([pos[:-1], [best]]))), "top-k of the prefix"
+    del sc, ws
+    torch.cuda.empty_cache()
+
+
 def test_topk_with_index_array_and_all_equal():
     rng = np.random.default_rng(9)
     rows, Lr, k = 2, 16384, 512
